@@ -1,0 +1,24 @@
+"""MI355X-native RMSNorm: forward, fused residual-add + RMSNorm, and VJP.
+
+The computation runs in hand-written gfx950 HIP kernels behind a C ABI
+(``include/rmsnorm_mi355x.h``); this package is the thin binding over it.
+The binding loads on first use of one of its names, so that the synthetic
+input generators (``backward_rmsnorm_fwd_two_amd.inputs``) import without
+the library.  A missing library raises ImportError -- there is no fallback.
+"""
+
+_BINDING_NAMES = {
+    "rmsnorm_fwd", "fused_add_rmsnorm_fwd", "rmsnorm_vjp", "rmsnorm_vjp_workspace_bytes",
+    "workspace_for", "query_config", "Config", "RMSNormError", "LIB_PATH", "raw",
+    "RMSN_F32", "RMSN_F16", "RMSN_BF16", "RMSN_OP_FWD", "RMSN_OP_FUSED", "RMSN_OP_VJP",
+    "RMSN_MAX_D", "STATUS",
+}
+
+__all__ = sorted(_BINDING_NAMES)
+
+
+def __getattr__(name):
+    if name in _BINDING_NAMES:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)

@@ -1,0 +1,231 @@
+"""ctypes binding of the gfx950 RMSNorm library (``librmsnorm_mi355x.so``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  PyTorch supplies device memory (outputs,
+workspace) and the current HIP stream.  There is no fallback path: if the
+library is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librmsnorm_mi355x.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m backward_rmsnorm_fwd_two_amd.build` "
+        "(or __graft_entry__.build()) first")
+
+# torch is imported first so that its HIP runtime (same soname) is the one
+# the library binds to: streams from torch are then valid in the library.
+_lib = ctypes.CDLL(LIB_PATH)
+
+RMSN_F32, RMSN_F16, RMSN_BF16 = 0, 1, 2
+RMSN_OP_FWD, RMSN_OP_FUSED, RMSN_OP_VJP = 0, 1, 2
+RMSN_MAX_D = 1 << 24
+
+STATUS = {
+    0: "RMSN_OK", -1: "RMSN_E_NULLPTR", -2: "RMSN_E_SHAPE", -3: "RMSN_E_DTYPE",
+    -4: "RMSN_E_WORKSPACE", -5: "RMSN_E_OVERLAP", -6: "RMSN_E_HIP", -7: "RMSN_E_ALIGN",
+    -8: "RMSN_E_CONFIG",
+}
+
+_DT = {torch.float32: RMSN_F32, torch.float16: RMSN_F16, torch.bfloat16: RMSN_BF16}
+
+
+class Config(ctypes.Structure):
+    """Mirror of ``rmsn_config_t`` (0 in a field = automatic)."""
+    _fields_ = [
+        ("lanes_per_row", ctypes.c_int32),
+        ("vecs_per_lane", ctypes.c_int32),
+        ("vec_bytes", ctypes.c_int32),
+        ("block_threads", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+    ]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+_vp, _i64, _int, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_cfgp = ctypes.POINTER(Config)
+
+_lib.rmsnorm_fwd.argtypes = [_vp, _vp, _vp, _i64, _i64, _int, _f32, _f32, _vp]
+_lib.rmsnorm_fwd_cfg.argtypes = [_vp, _vp, _vp, _i64, _i64, _int, _f32, _f32, _cfgp, _vp]
+_lib.fused_add_rmsnorm_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, _f32, _f32, _vp]
+_lib.fused_add_rmsnorm_fwd_cfg.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, _f32, _f32,
+                                           _cfgp, _vp]
+_lib.rmsnorm_vjp_workspace_bytes.argtypes = [_i64, _i64, _int]
+_lib.rmsnorm_vjp_workspace_bytes.restype = _sz
+_lib.rmsnorm_vjp.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _int, _f32, _f32, _vp]
+_lib.rmsnorm_vjp_cfg.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _int, _f32, _f32,
+                                 _cfgp, _vp]
+_lib.rmsn_query_config.argtypes = [_int, _i64, _i64, _int, _int, _cfgp]
+_lib.rmsn_status_str.argtypes = [_int]
+_lib.rmsn_status_str.restype = ctypes.c_char_p
+for _name in ("rmsnorm_fwd", "rmsnorm_fwd_cfg", "fused_add_rmsnorm_fwd", "fused_add_rmsnorm_fwd_cfg",
+              "rmsnorm_vjp", "rmsnorm_vjp_cfg", "rmsn_query_config"):
+    getattr(_lib, _name).restype = _int
+
+raw = _lib  # the C functions themselves (pointer-level access for tests)
+
+
+class RMSNormError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} "
+                         f"({_lib.rmsn_status_str(status).decode()})")
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise RMSNormError(status, where)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _rows_d(x: torch.Tensor) -> Tuple[int, int]:
+    if x.dim() < 1:
+        raise ValueError("expected a tensor whose last axis is normalised")
+    D = x.shape[-1]
+    rows = x.numel() // D if D else 0
+    return rows, D
+
+
+def _req(t: torch.Tensor, name: str, dtype, device, numel=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+
+
+def _cfg(cfg) -> Optional[ctypes.pointer]:
+    if cfg is None:
+        return None
+    if isinstance(cfg, dict):
+        cfg = Config(**cfg)
+    return ctypes.pointer(cfg)
+
+
+def _dt(x: torch.Tensor) -> int:
+    if x.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    return _DT[x.dtype]
+
+
+def rmsnorm_fwd(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-5, weight_bias: float = 0.0,
+                out: Optional[torch.Tensor] = None, cfg=None) -> torch.Tensor:
+    """y = x * rsqrt(mean(x^2, -1) + eps) * (weight_bias + w)."""
+    dt = _dt(x)
+    rows, D = _rows_d(x)
+    _req(x, "x", x.dtype, x.device)
+    _req(w, "w", x.dtype, x.device, D)
+    if out is None:
+        out = torch.empty_like(x)
+    _req(out, "out", x.dtype, x.device, x.numel())
+    if cfg is None:
+        st = _lib.rmsnorm_fwd(x.data_ptr(), w.data_ptr(), out.data_ptr(), rows, D, dt,
+                              float(eps), float(weight_bias), _stream(x))
+    else:
+        st = _lib.rmsnorm_fwd_cfg(x.data_ptr(), w.data_ptr(), out.data_ptr(), rows, D, dt,
+                                  float(eps), float(weight_bias), _cfg(cfg), _stream(x))
+    _check(st, "rmsnorm_fwd")
+    return out
+
+
+def fused_add_rmsnorm_fwd(x: torch.Tensor, residual: torch.Tensor, w: torch.Tensor,
+                          eps: float = 1e-6, weight_bias: float = 0.0,
+                          normed: Optional[torch.Tensor] = None,
+                          new_residual: Optional[torch.Tensor] = None,
+                          cfg=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """new_residual = x + residual; normed = rmsnorm(x + residual) * (weight_bias + w)."""
+    dt = _dt(x)
+    rows, D = _rows_d(x)
+    _req(x, "x", x.dtype, x.device)
+    _req(residual, "residual", x.dtype, x.device, x.numel())
+    _req(w, "w", x.dtype, x.device, D)
+    if normed is None:
+        normed = torch.empty_like(x)
+    if new_residual is None:
+        new_residual = torch.empty_like(x)
+    _req(normed, "normed", x.dtype, x.device, x.numel())
+    _req(new_residual, "new_residual", x.dtype, x.device, x.numel())
+    args = (x.data_ptr(), residual.data_ptr(), w.data_ptr(), normed.data_ptr(),
+            new_residual.data_ptr(), rows, D, dt, float(eps), float(weight_bias))
+    if cfg is None:
+        st = _lib.fused_add_rmsnorm_fwd(*args, _stream(x))
+    else:
+        st = _lib.fused_add_rmsnorm_fwd_cfg(*args, _cfg(cfg), _stream(x))
+    _check(st, "fused_add_rmsnorm_fwd")
+    return normed, new_residual
+
+
+def rmsnorm_vjp_workspace_bytes(rows: int, D: int, dtype: torch.dtype) -> int:
+    n = _lib.rmsnorm_vjp_workspace_bytes(int(rows), int(D), _DT[dtype])
+    if n == 0:
+        raise ValueError("invalid shape for rmsnorm_vjp_workspace_bytes")
+    return int(n)
+
+
+def workspace_for(rows: int, D: int, dtype: torch.dtype, device, cfg=None) -> torch.Tensor:
+    """A device workspace large enough for rmsnorm_vjp on this shape (and for
+    `cfg`'s grid when one is given)."""
+    n = rmsnorm_vjp_workspace_bytes(rows, D, dtype)
+    if cfg is not None:
+        c = cfg if isinstance(cfg, dict) else cfg.as_dict()
+        nb = c.get("num_blocks", 0) or 2048
+        n = max(n, nb * D * 4)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def rmsnorm_vjp(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, eps: float = 1e-5,
+                weight_bias: float = 0.0, dx: Optional[torch.Tensor] = None,
+                dw: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                cfg=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Returns (dx, dw): dx in x's dtype, dw fp32 summed over every row."""
+    dt = _dt(x)
+    rows, D = _rows_d(x)
+    _req(x, "x", x.dtype, x.device)
+    _req(w, "w", x.dtype, x.device, D)
+    _req(dy, "dy", x.dtype, x.device, x.numel())
+    if dx is None:
+        dx = torch.empty_like(x)
+    if dw is None:
+        dw = torch.empty(D, dtype=torch.float32, device=x.device)
+    _req(dx, "dx", x.dtype, x.device, x.numel())
+    _req(dw, "dw", torch.float32, x.device, D)
+    if workspace is None:
+        workspace = workspace_for(rows, D, x.dtype, x.device, cfg)
+    _req(workspace, "workspace", workspace.dtype, x.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    args = (x.data_ptr(), w.data_ptr(), dy.data_ptr(), dx.data_ptr(), dw.data_ptr(),
+            workspace.data_ptr(), nbytes, rows, D, dt, float(eps), float(weight_bias))
+    if cfg is None:
+        st = _lib.rmsnorm_vjp(*args, _stream(x))
+    else:
+        st = _lib.rmsnorm_vjp_cfg(*args, _cfg(cfg), _stream(x))
+    _check(st, "rmsnorm_vjp")
+    return dx, dw
+
+
+def query_config(op: int, rows: int, D: int, dtype: torch.dtype, align_bytes: int = 16) -> dict:
+    """The configuration the automatic choice makes for this shape."""
+    c = Config()
+    _check(_lib.rmsn_query_config(op, int(rows), int(D), _DT[dtype], int(align_bytes),
+                                  ctypes.byref(c)), "rmsn_query_config")
+    return c.as_dict()

@@ -1,0 +1,422 @@
+// rmsn_api.hip -- the C ABI declared in include/rmsnorm_mi355x.h: argument
+// checks, the per-shape kernel plan (load width, threads per row, vectors
+// per thread, block, grid) and the launches.  Host code only; the kernels
+// live in rmsn_fwd.hip / rmsn_vjp.hip.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "rmsn_device.hpp"
+#include "rmsn_launch.hpp"
+#include "rmsnorm_mi355x.h"
+
+namespace {
+
+using rmsn::RowArgs;
+
+constexpr int kMaxDevices = 64;
+constexpr int kMaxPartialRows = 2048;   // bound on dw partial rows (workspace)
+std::atomic<int> g_cu_count[kMaxDevices];
+
+// Compute units of the current device (cached per device; the cache is the
+// library's only global state).
+int cu_count(int* out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return RMSN_E_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return RMSN_E_HIP;
+    int n = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return RMSN_E_HIP;
+        g_cu_count[dev].store(n, std::memory_order_relaxed);
+    }
+    *out = n;
+    return RMSN_OK;
+}
+
+int itemsize(int dt) { return dt == RMSN_F32 ? 4 : 2; }
+
+// Largest power of two dividing the address, capped at 16.
+int ptr_align(const void* p) {
+    const uintptr_t u = reinterpret_cast<uintptr_t>(p);
+    if (u == 0) return 16;
+    const uintptr_t low = u & (~u + 1);
+    return low >= 16 ? 16 : static_cast<int>(low);
+}
+
+int next_pow2(int64_t v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+int log2i(int v) {
+    int l = 0;
+    while ((1 << l) < v) ++l;
+    return l;
+}
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+struct Plan {
+    int nv = 1;       // elements per load
+    int nvec = 1;     // D / nv
+    int k = 1;        // vectors per lane; -1 = streaming kernel
+    int lanes = 1;    // threads per row
+    int block = 256;
+    int64_t grid = 1;
+    size_t shmem = 0;
+};
+
+// The kernel plan for one call.  `align` is the largest power of two (<= 16)
+// dividing every pointer the kernels read or write row-wise.
+int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_config_t* cfg,
+              Plan* p) {
+    const int s = itemsize(dt);
+    int cus = 0;
+    int st = cu_count(&cus);
+    if (st != RMSN_OK) return st;
+
+    // load width
+    int vb = 0;
+    if (cfg && cfg->vec_bytes) {
+        vb = cfg->vec_bytes;
+        if (vb < s || vb > 16 || !is_pow2(vb) || (D * s) % vb != 0 || align % vb != 0)
+            return RMSN_E_CONFIG;
+    } else {
+        for (int c = 16; c >= s; c >>= 1) {
+            if ((D * s) % c == 0 && align % c == 0) { vb = c; break; }
+        }
+        if (vb == 0) vb = s;
+    }
+    p->nv = vb / s;
+    p->nvec = static_cast<int>(D / p->nv);
+
+    const int req_k = cfg ? cfg->vecs_per_lane : 0;
+    const int req_l = cfg ? cfg->lanes_per_row : 0;
+    const int req_b = cfg ? cfg->block_threads : 0;
+    bool looped = req_k == -1 || (req_k == 0 && req_l == 0 && p->nvec > 1024 * 8);
+
+    if (!looped) {
+        int lanes = req_l;
+        int k = req_k;
+        if (lanes == 0 && k == 0) {
+            lanes = std::min(1024, next_pow2((p->nvec + 1) / 2));
+            k = next_pow2((p->nvec + lanes - 1) / lanes);
+        } else if (lanes == 0) {
+            lanes = std::min(1024, next_pow2((p->nvec + k - 1) / k));
+        } else if (k == 0) {
+            k = next_pow2((p->nvec + lanes - 1) / lanes);
+            if (k > 8) return RMSN_E_CONFIG;
+        }
+        if (!is_pow2(lanes) || lanes > 1024) return RMSN_E_CONFIG;
+        if (k != 1 && k != 2 && k != 4 && k != 8) return RMSN_E_CONFIG;
+        if ((int64_t)lanes * k < p->nvec) return RMSN_E_CONFIG;
+        const int maxb = rmsn::max_block_threads(op, k, p->nv, s);
+        if (lanes > maxb) {
+            if (req_l || req_k) return RMSN_E_CONFIG;
+            looped = true;  // automatic choice: fall back to the streaming kernel
+        } else {
+            int block = req_b;
+            if (block == 0) {
+                block = (op == RMSN_OP_VJP) ? maxb : std::max(lanes, std::min(256, maxb));
+                block = std::max(block, 64);
+            }
+            if (block < 64 || block > maxb || block % 64 != 0 || block % lanes != 0 || !is_pow2(block))
+                return RMSN_E_CONFIG;
+            p->lanes = lanes;
+            p->k = k;
+            p->block = block;
+            const int nslots = block / lanes;
+            const int64_t groups = (rows + nslots - 1) / nslots;
+            int64_t grid;
+            if (cfg && cfg->num_blocks) {
+                grid = cfg->num_blocks;
+            } else if (op == RMSN_OP_VJP) {
+                const int64_t per_cu = std::max(1, 1024 / block);
+                grid = std::min<int64_t>(groups, std::min<int64_t>(kMaxPartialRows, cus * per_cu));
+            } else {
+                grid = std::min<int64_t>(groups, (int64_t)1 << 20);
+            }
+            if (grid < 1 || grid > ((int64_t)1 << 30)) return RMSN_E_CONFIG;
+            if (op == RMSN_OP_VJP && grid > kMaxPartialRows) return RMSN_E_CONFIG;
+            p->grid = grid;
+            p->shmem = (op == RMSN_OP_VJP && nslots > 1) ? (size_t)block * p->nv * sizeof(float) : 0;
+            return RMSN_OK;
+        }
+    }
+
+    // streaming kernel: one block per row
+    int block = req_b ? req_b : 1024;
+    if (block < 64 || block > 1024 || block % 64 != 0) return RMSN_E_CONFIG;
+    p->k = -1;
+    p->lanes = block;
+    p->block = block;
+    int64_t grid;
+    if (cfg && cfg->num_blocks) {
+        grid = cfg->num_blocks;
+        if (grid > rows && rows > 0) return RMSN_E_CONFIG;  // every block must own a row
+    } else if (op == RMSN_OP_VJP) {
+        grid = std::min<int64_t>(rows, std::min<int64_t>(kMaxPartialRows, cus * std::max(1, 2048 / block)));
+    } else {
+        grid = std::min<int64_t>(rows, (int64_t)1 << 20);
+    }
+    if (grid < 1) grid = 1;
+    if (op == RMSN_OP_VJP && grid > kMaxPartialRows) return RMSN_E_CONFIG;
+    p->grid = grid;
+    p->shmem = 0;
+    return RMSN_OK;
+}
+
+struct Range {
+    uintptr_t lo, hi;
+};
+
+Range range_of(const void* p, int64_t bytes) {
+    const uintptr_t u = reinterpret_cast<uintptr_t>(p);
+    return Range{u, u + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlaps(Range a, Range b) {
+    return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+int check_common(int64_t rows, int64_t D, int dt) {
+    if (dt != RMSN_F32 && dt != RMSN_F16 && dt != RMSN_BF16) return RMSN_E_DTYPE;
+    if (rows < 0 || D < 1 || D > RMSN_MAX_D) return RMSN_E_SHAPE;
+    const int64_t s = itemsize(dt);
+    if (rows > 0 && rows > INT64_MAX / (D * s)) return RMSN_E_SHAPE;
+    return RMSN_OK;
+}
+
+bool elem_aligned(const void* p, int s) {
+    return reinterpret_cast<uintptr_t>(p) % static_cast<uintptr_t>(s) == 0;
+}
+
+int launch(const void* fn, const Plan& p, RowArgs& a, hipStream_t stream) {
+    a.lanes = p.lanes;
+    a.lshift = log2i(p.lanes);
+    a.nvec = p.nvec;
+    void* args[] = {&a};
+    if (hipLaunchKernel(fn, dim3(static_cast<unsigned>(p.grid)), dim3(p.block), args, p.shmem, stream) !=
+        hipSuccess)
+        return RMSN_E_HIP;
+    return RMSN_OK;
+}
+
+int fwd_impl(bool fused, const void* x, const void* res, const void* w, void* y, void* newres,
+             int64_t rows, int64_t D, int dt, float eps, float wb, const rmsn_config_t* cfg,
+             void* stream) {
+    int st = check_common(rows, D, dt);
+    if (st != RMSN_OK) return st;
+    if (rows == 0) return RMSN_OK;
+    if (!x || !w || !y || (fused && (!res || !newres))) return RMSN_E_NULLPTR;
+    const int s = itemsize(dt);
+    if (!elem_aligned(x, s) || !elem_aligned(w, s) || !elem_aligned(y, s) ||
+        (fused && (!elem_aligned(res, s) || !elem_aligned(newres, s))))
+        return RMSN_E_ALIGN;
+    const int64_t tb = rows * D * s;
+    const Range rx = range_of(x, tb), rw = range_of(w, D * s), ry = range_of(y, tb);
+    if (fused) {
+        const Range rr = range_of(res, tb), rn = range_of(newres, tb);
+        const Range outs[2] = {ry, rn};
+        const Range ins[3] = {rx, rr, rw};
+        for (const Range& o : outs)
+            for (const Range& i : ins)
+                if (overlaps(o, i)) return RMSN_E_OVERLAP;
+        if (overlaps(ry, rn)) return RMSN_E_OVERLAP;
+    } else {
+        if (overlaps(ry, rx) || overlaps(ry, rw)) return RMSN_E_OVERLAP;
+    }
+    int align = std::min(std::min(ptr_align(x), ptr_align(w)), ptr_align(y));
+    if (fused) align = std::min(align, std::min(ptr_align(res), ptr_align(newres)));
+
+    Plan p;
+    st = make_plan(fused ? RMSN_OP_FUSED : RMSN_OP_FWD, rows, D, dt, align, cfg, &p);
+    if (st != RMSN_OK) return st;
+    const void* fn = rmsn::fwd_kernel(dt, p.nv, p.k, fused);
+    if (!fn) return RMSN_E_CONFIG;
+
+    RowArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.x = x;
+    a.res = res;
+    a.w = w;
+    a.y = y;
+    a.newres = newres;
+    a.rows = rows;
+    a.D = static_cast<int32_t>(D);
+    a.eps = eps;
+    a.wb = wb;
+    return launch(fn, p, a, static_cast<hipStream_t>(stream));
+}
+
+// Workspace bytes for a plan (fp32 partial rows when the grid has > 1 block).
+size_t ws_bytes(const Plan& p, int64_t D) {
+    return p.grid > 1 ? static_cast<size_t>(p.grid) * static_cast<size_t>(D) * sizeof(float) : 0;
+}
+
+int vjp_impl(const void* x, const void* w, const void* dy, void* dx, float* dw, void* ws,
+             size_t ws_size, int64_t rows, int64_t D, int dt, float eps, float wb,
+             const rmsn_config_t* cfg, void* stream) {
+    int st = check_common(rows, D, dt);
+    if (st != RMSN_OK) return st;
+    if (!dw) return RMSN_E_NULLPTR;
+    if (!elem_aligned(dw, 4)) return RMSN_E_ALIGN;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (rows == 0) {
+        void* args[] = {&dw, &D};
+        const unsigned g = static_cast<unsigned>(std::min<int64_t>((D + 255) / 256, 1024));
+        if (hipLaunchKernel(rmsn::zero_kernel(), dim3(g), dim3(256), args, 0, hs) != hipSuccess)
+            return RMSN_E_HIP;
+        return RMSN_OK;
+    }
+    if (!x || !w || !dy || !dx) return RMSN_E_NULLPTR;
+    const int s = itemsize(dt);
+    if (!elem_aligned(x, s) || !elem_aligned(w, s) || !elem_aligned(dy, s) || !elem_aligned(dx, s))
+        return RMSN_E_ALIGN;
+    const int64_t tb = rows * D * s;
+    const Range rx = range_of(x, tb), rw = range_of(w, D * s), rd = range_of(dy, tb),
+                rdx = range_of(dx, tb), rdw = range_of(dw, D * 4);
+    {
+        const Range ins[3] = {rx, rw, rd};
+        for (const Range& i : ins)
+            if (overlaps(rdx, i) || overlaps(rdw, i)) return RMSN_E_OVERLAP;
+        if (overlaps(rdx, rdw)) return RMSN_E_OVERLAP;
+    }
+    const int align =
+        std::min(std::min(ptr_align(x), ptr_align(w)), std::min(ptr_align(dy), ptr_align(dx)));
+    Plan p;
+    st = make_plan(RMSN_OP_VJP, rows, D, dt, align, cfg, &p);
+    if (st != RMSN_OK) return st;
+    const size_t need = ws_bytes(p, D);
+    if (need > 0) {
+        if (!ws || ws_size < need) return RMSN_E_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(ws) % 16 != 0) return RMSN_E_ALIGN;
+        const Range rws = range_of(ws, static_cast<int64_t>(need));
+        const Range all[5] = {rx, rw, rd, rdx, rdw};
+        for (const Range& o : all)
+            if (overlaps(rws, o)) return RMSN_E_OVERLAP;
+    }
+    const void* fn = rmsn::vjp_kernel(dt, p.nv, p.k);
+    if (!fn) return RMSN_E_CONFIG;
+
+    RowArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.x = x;
+    a.w = w;
+    a.dy = dy;
+    a.dx = dx;
+    a.partial = static_cast<float*>(ws);
+    a.dw = dw;
+    a.rows = rows;
+    a.D = static_cast<int32_t>(D);
+    a.eps = eps;
+    a.wb = wb;
+    st = launch(fn, p, a, hs);
+    if (st != RMSN_OK || p.grid == 1) return st;
+
+    const float* partial = static_cast<const float*>(ws);
+    int nb = static_cast<int>(p.grid);
+    int d32 = static_cast<int>(D);
+    void* cargs[] = {&partial, &dw, &nb, &d32};
+    const unsigned cg = static_cast<unsigned>((D + 15) / 16);
+    if (hipLaunchKernel(rmsn::dw_combine_kernel(), dim3(cg), dim3(256), cargs, 0, hs) != hipSuccess)
+        return RMSN_E_HIP;
+    return RMSN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rmsnorm_fwd(const void* x, const void* w, void* y, int64_t rows, int64_t D, int dt, float eps,
+                float weight_bias, void* hip_stream) {
+    return fwd_impl(false, x, nullptr, w, y, nullptr, rows, D, dt, eps, weight_bias, nullptr,
+                    hip_stream);
+}
+
+int rmsnorm_fwd_cfg(const void* x, const void* w, void* y, int64_t rows, int64_t D, int dt,
+                    float eps, float weight_bias, const rmsn_config_t* cfg, void* hip_stream) {
+    return fwd_impl(false, x, nullptr, w, y, nullptr, rows, D, dt, eps, weight_bias, cfg,
+                    hip_stream);
+}
+
+int fused_add_rmsnorm_fwd(const void* x, const void* residual, const void* w, void* normed,
+                          void* new_residual, int64_t rows, int64_t D, int dt, float eps,
+                          float weight_bias, void* hip_stream) {
+    return fwd_impl(true, x, residual, w, normed, new_residual, rows, D, dt, eps, weight_bias,
+                    nullptr, hip_stream);
+}
+
+int fused_add_rmsnorm_fwd_cfg(const void* x, const void* residual, const void* w, void* normed,
+                              void* new_residual, int64_t rows, int64_t D, int dt, float eps,
+                              float weight_bias, const rmsn_config_t* cfg, void* hip_stream) {
+    return fwd_impl(true, x, residual, w, normed, new_residual, rows, D, dt, eps, weight_bias, cfg,
+                    hip_stream);
+}
+
+size_t rmsnorm_vjp_workspace_bytes(int64_t rows, int64_t D, int dt) {
+    if (check_common(rows, D, dt) != RMSN_OK) return 0;
+    size_t best = 0;
+    if (rows > 0) {
+        // The plan depends on pointer alignment; size for the largest.
+        for (int align = 16; align >= itemsize(dt); align >>= 1) {
+            Plan p;
+            if (make_plan(RMSN_OP_VJP, rows, D, dt, align, nullptr, &p) != RMSN_OK) return 0;
+            best = std::max(best, ws_bytes(p, D));
+        }
+    }
+    return std::max<size_t>(best, 256);
+}
+
+int rmsnorm_vjp(const void* x, const void* w, const void* dy, void* dx, float* dw, void* workspace,
+                size_t workspace_bytes, int64_t rows, int64_t D, int dt, float eps, float weight_bias,
+                void* hip_stream) {
+    return vjp_impl(x, w, dy, dx, dw, workspace, workspace_bytes, rows, D, dt, eps, weight_bias,
+                    nullptr, hip_stream);
+}
+
+int rmsnorm_vjp_cfg(const void* x, const void* w, const void* dy, void* dx, float* dw,
+                    void* workspace, size_t workspace_bytes, int64_t rows, int64_t D, int dt,
+                    float eps, float weight_bias, const rmsn_config_t* cfg, void* hip_stream) {
+    return vjp_impl(x, w, dy, dx, dw, workspace, workspace_bytes, rows, D, dt, eps, weight_bias, cfg,
+                    hip_stream);
+}
+
+int rmsn_query_config(int op, int64_t rows, int64_t D, int dt, int align_bytes, rmsn_config_t* out) {
+    if (!out) return RMSN_E_NULLPTR;
+    if (op != RMSN_OP_FWD && op != RMSN_OP_FUSED && op != RMSN_OP_VJP) return RMSN_E_CONFIG;
+    int st = check_common(rows, D, dt);
+    if (st != RMSN_OK) return st;
+    if (align_bytes <= 0 || !is_pow2(align_bytes)) return RMSN_E_ALIGN;
+    Plan p;
+    st = make_plan(op, std::max<int64_t>(rows, 1), D, dt, std::min(align_bytes, 16), nullptr, &p);
+    if (st != RMSN_OK) return st;
+    out->lanes_per_row = p.k < 0 ? 0 : p.lanes;
+    out->vecs_per_lane = p.k;
+    out->vec_bytes = p.nv * itemsize(dt);
+    out->block_threads = p.block;
+    out->num_blocks = static_cast<int32_t>(p.grid);
+    return RMSN_OK;
+}
+
+const char* rmsn_status_str(int status) {
+    switch (status) {
+        case RMSN_OK: return "ok";
+        case RMSN_E_NULLPTR: return "a required pointer is NULL";
+        case RMSN_E_SHAPE: return "invalid shape (rows < 0, D < 1 or D too large)";
+        case RMSN_E_DTYPE: return "unknown dtype";
+        case RMSN_E_WORKSPACE: return "workspace missing or too small";
+        case RMSN_E_OVERLAP: return "an output overlaps another argument";
+        case RMSN_E_HIP: return "HIP runtime error";
+        case RMSN_E_ALIGN: return "pointer not aligned to its element size";
+        case RMSN_E_CONFIG: return "kernel configuration cannot serve this shape";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

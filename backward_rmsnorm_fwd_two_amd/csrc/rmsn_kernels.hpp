@@ -1,0 +1,404 @@
+// rmsn_kernels.hpp -- RMSNorm forward, fused add+RMSNorm and VJP kernels
+// for gfx950 (wave64, CDNA4).  All arithmetic is fp32; storage is fp32, fp16
+// or bf16, rounded to nearest-even once on store.
+//
+// Row geometry (register-resident kernels): `lanes` consecutive threads own
+// one row; lane l holds vectors v = k * lanes + l (k < K) of NV elements,
+// i.e. columns [v * NV, v * NV + NV).  A block of blockDim.x threads works on
+// blockDim.x / lanes rows at a time and strides over row groups with the
+// grid.  Row sums reduce within the lane group by DPP / permlane swaps; when
+// a row spans several waves (lanes > 64) the wave totals meet in LDS.
+//
+// The streaming kernel (rows_looped) serves any D: one block per row, two
+// passes over the row (sums, then outputs), re-reading the row.
+#pragma once
+
+#include "rmsn_device.hpp"
+#include "rmsn_launch.hpp"
+
+namespace rmsn {
+
+// Per-lane column bookkeeping shared by the register-resident kernels.
+// A lane's vector k covers columns [v * NV, v * NV + NV), v = k * lanes +
+// lane; vectors at or past nvec are masked.  Loads are issued
+// unconditionally from a clamped (always valid) offset so that every load
+// of a row is in flight at once; masked data is zeroed after arrival.
+template <int K>
+struct Cols {
+    int64_t off[K];
+    bool ok[K];
+    __device__ __forceinline__ Cols(int lanes, int lane, int nvec, int nv) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int v = k * lanes + lane;
+            ok[k] = v < nvec;
+            off[k] = ok[k] ? (int64_t)v * nv : 0;
+        }
+    }
+};
+
+template <typename T, int NV, int K>
+__device__ __forceinline__ void issue_row(const T* __restrict__ p, int64_t base, const Cols<K>& c,
+                                          Raw<T, NV> (&dst)[K]) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) dst[k] = load_raw<T, NV>(p + base + c.off[k]);
+}
+
+template <typename T, int NV, int K>
+__device__ __forceinline__ void mask_cols(const Cols<K>& c, Raw<T, NV> (&d)[K]) {
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int i = 0; i < Raw<T, NV>::kWords; ++i) d[k].w[i] = c.ok[k] ? d[k].w[i] : 0u;
+}
+
+// ------------------------------------------------------------ forward
+// y = x * rsqrt(mean(x^2) + eps) * (wb + w)   (FUSED: x := x + residual,
+// which is also stored rounded as new_residual; the unrounded fp32 sum is
+// what is normalised).  Every load of a row group is issued before the
+// first use; latency is hidden by the other waves resident on the CU.
+template <typename T, int NV, int K, bool FUSED>
+struct FwdRow {
+    Raw<T, NV> x[K];
+    Raw<T, NV> r[K];
+};
+
+template <typename T, int NV, int K, bool FUSED>
+__device__ __forceinline__ void fwd_issue(const RowArgs& a, int64_t row0, int slot, const Cols<K>& c,
+                                          FwdRow<T, NV, K, FUSED>& d) {
+    const int64_t row = row0 + slot;
+    const int64_t base = row < a.rows ? row * a.D : 0;
+    issue_row<T, NV, K>(static_cast<const T*>(a.x), base, c, d.x);
+    if constexpr (FUSED) issue_row<T, NV, K>(static_cast<const T*>(a.res), base, c, d.r);
+}
+
+template <typename T, int NV, int K, bool FUSED>
+__device__ __forceinline__ void fwd_process(const RowArgs& a, int64_t row0, int slot, int lanes,
+                                            const Cols<K>& c, const float (&g)[K][NV],
+                                            FwdRow<T, NV, K, FUSED>& d, float* red, int& parity) {
+    const int64_t row = row0 + slot;
+    const bool rok = row < a.rows;
+    const int64_t base = row * a.D;
+    mask_cols<T, NV, K>(c, d.x);
+    if constexpr (FUSED) mask_cols<T, NV, K>(c, d.r);
+
+    float h[K][NV];
+    float ss = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+#pragma unroll
+        for (int e = 0; e < NV; ++e) {
+            float hv = elem(d.x[k], e);
+            if constexpr (FUSED) hv += elem(d.r[k], e);
+            h[k][e] = hv;
+            ss = __builtin_fmaf(hv, hv, ss);
+        }
+    }
+    if constexpr (FUSED) {
+        T* __restrict__ newres = static_cast<T*>(a.newres);
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            if (rok && c.ok[k]) store_f32<T, NV>(newres + base + c.off[k], h[k]);
+    }
+
+    ss = group_sum(ss, lanes < 64 ? lanes : 64);
+    if (lanes > 64) {
+        float t[1] = {ss};
+        cross_wave_sum<1>(t, lanes >> 6, red, parity);
+        ss = t[0];
+        parity ^= 1;
+    }
+    const float r = rsqrtf(ss / static_cast<float>(a.D) + a.eps);
+
+    T* __restrict__ y = static_cast<T*>(a.y);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        if (rok && c.ok[k]) {
+            float o[NV];
+#pragma unroll
+            for (int e = 0; e < NV; ++e) o[e] = h[k][e] * r * g[k][e];
+            store_f32<T, NV>(y + base + c.off[k], o);
+        }
+    }
+}
+
+template <typename T, int NV, int K, bool FUSED>
+__global__ __launch_bounds__(max_block_threads(FUSED ? 1 : 0, K, NV, sizeof(T))) void fwd_rows(RowArgs a) {
+    __shared__ float red[2 * 16];
+    const int lanes = a.lanes;
+    const int lane = threadIdx.x & (lanes - 1);
+    const int slot = threadIdx.x >> a.lshift;
+    const int nslots = blockDim.x >> a.lshift;
+    const Cols<K> c(lanes, lane, a.nvec, NV);
+    const int64_t step = (int64_t)gridDim.x * nslots;
+    int64_t row0 = (int64_t)blockIdx.x * nslots;
+    if (row0 >= a.rows) return;  // whole block
+
+    float g[K][NV];
+    {
+        Raw<T, NV> pw[K];
+        issue_row<T, NV, K>(static_cast<const T*>(a.w), 0, c, pw);
+        mask_cols<T, NV, K>(c, pw);
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+#pragma unroll
+            for (int e = 0; e < NV; ++e) g[k][e] = a.wb + elem(pw[k], e);
+    }
+    int parity = 0;
+    for (; row0 < a.rows; row0 += step) {
+        FwdRow<T, NV, K, FUSED> d;
+        fwd_issue<T, NV, K, FUSED>(a, row0, slot, c, d);
+        fwd_process<T, NV, K, FUSED>(a, row0, slot, lanes, c, g, d, red, parity);
+    }
+}
+
+// ---------------------------------------------------------------- VJP
+// dx = r g dy - x r^3 S / D,  S = sum(dy g x);  the dw partial over this
+// block's rows is accumulated in registers, combined over the block's row
+// slots in LDS (fixed tree order), and written to partial[blockIdx.x, :]
+// (or to dw when the grid is a single block).  `dyn` LDS: blockDim.x * NV
+// floats when the block holds more than one row slot.
+template <typename T, int NV, int K>
+struct VjpRow {
+    Raw<T, NV> x[K];
+    Raw<T, NV> dy[K];
+};
+
+template <typename T, int NV, int K>
+__device__ __forceinline__ void vjp_issue(const RowArgs& a, int64_t row0, int slot, const Cols<K>& c,
+                                          VjpRow<T, NV, K>& d) {
+    const int64_t row = row0 + slot;
+    const int64_t base = row < a.rows ? row * a.D : 0;
+    issue_row<T, NV, K>(static_cast<const T*>(a.x), base, c, d.x);
+    issue_row<T, NV, K>(static_cast<const T*>(a.dy), base, c, d.dy);
+}
+
+template <typename T, int NV, int K>
+__device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int slot, int lanes,
+                                            const Cols<K>& c, const float (&g)[K][NV],
+                                            float (&acc)[K][NV], VjpRow<T, NV, K>& d, float* red,
+                                            int& parity) {
+    const int64_t row = row0 + slot;
+    const bool rok = row < a.rows;
+    const int64_t base = row * a.D;
+    mask_cols<T, NV, K>(c, d.x);
+    mask_cols<T, NV, K>(c, d.dy);
+
+    float s2[2] = {0.0f, 0.0f};  // sum x^2, sum dy g x
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+#pragma unroll
+        for (int e = 0; e < NV; ++e) {
+            const float xv = elem(d.x[k], e);
+            const float dv = elem(d.dy[k], e);
+            s2[0] = __builtin_fmaf(xv, xv, s2[0]);
+            s2[1] = __builtin_fmaf(dv * g[k][e], xv, s2[1]);
+        }
+    }
+    const int gl = lanes < 64 ? lanes : 64;
+    s2[0] = group_sum(s2[0], gl);
+    s2[1] = group_sum(s2[1], gl);
+    if (lanes > 64) {
+        cross_wave_sum<2>(s2, lanes >> 6, red, parity);
+        parity ^= 1;
+    }
+    const float inv_d = 1.0f / static_cast<float>(a.D);
+    const float r = rsqrtf(s2[0] * inv_d + a.eps);
+    const float cc = r * r * r * s2[1] * inv_d;
+
+    if (rok) {
+        T* __restrict__ dx = static_cast<T*>(a.dx);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            float o[NV];
+#pragma unroll
+            for (int e = 0; e < NV; ++e) {
+                const float xv = elem(d.x[k], e);
+                const float dv = elem(d.dy[k], e);
+                o[e] = r * g[k][e] * dv - xv * cc;
+                acc[k][e] = __builtin_fmaf(dv * xv, r, acc[k][e]);
+            }
+            if (c.ok[k]) store_f32<T, NV>(dx + base + c.off[k], o);
+        }
+    }
+}
+
+template <typename T, int NV, int K>
+__global__ __launch_bounds__(max_block_threads(2, K, NV, sizeof(T))) void vjp_rows(RowArgs a) {
+    extern __shared__ float dyn[];
+    __shared__ float red[2 * 16 * 2];
+    const int lanes = a.lanes;
+    const int lane = threadIdx.x & (lanes - 1);
+    const int slot = threadIdx.x >> a.lshift;
+    const int nslots = blockDim.x >> a.lshift;
+    const Cols<K> c(lanes, lane, a.nvec, NV);
+    const int64_t step = (int64_t)gridDim.x * nslots;
+    int64_t row0 = (int64_t)blockIdx.x * nslots;
+
+    float acc[K][NV];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int e = 0; e < NV; ++e) acc[k][e] = 0.0f;
+
+    if (row0 < a.rows) {  // block-uniform
+        float g[K][NV];
+        {
+            Raw<T, NV> pw[K];
+            issue_row<T, NV, K>(static_cast<const T*>(a.w), 0, c, pw);
+            mask_cols<T, NV, K>(c, pw);
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+#pragma unroll
+                for (int e = 0; e < NV; ++e) g[k][e] = a.wb + elem(pw[k], e);
+        }
+        int parity = 0;
+        for (; row0 < a.rows; row0 += step) {
+            VjpRow<T, NV, K> d;
+            vjp_issue<T, NV, K>(a, row0, slot, c, d);
+            vjp_process<T, NV, K>(a, row0, slot, lanes, c, g, acc, d, red, parity);
+        }
+    }
+
+    // Join the row slots' accumulators (fixed tree order) and write this
+    // block's dw row.  A block without rows writes zeros.
+    float* dst = (gridDim.x == 1) ? a.dw : a.partial + (int64_t)blockIdx.x * a.D;
+    const bool vec_ok = (reinterpret_cast<uintptr_t>(dst) % (NV * sizeof(float))) == 0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        if (nslots > 1) {
+            float* mine = dyn + (int64_t)threadIdx.x * NV;
+#pragma unroll
+            for (int e = 0; e < NV; ++e) mine[e] = acc[k][e];
+            lds_barrier();
+            for (int s = nslots >> 1; s >= 1; s >>= 1) {
+                if (slot < s) {
+                    const float* other = mine + (int64_t)s * lanes * NV;
+#pragma unroll
+                    for (int e = 0; e < NV; ++e) mine[e] += other[e];
+                }
+                lds_barrier();
+            }
+            if (slot == 0) {
+#pragma unroll
+                for (int e = 0; e < NV; ++e) acc[k][e] = mine[e];
+            }
+            lds_barrier();
+        }
+        if (slot == 0 && c.ok[k]) {
+            float* out = dst + c.off[k];
+            if (vec_ok) {
+                store_f32<float, NV>(out, acc[k]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < NV; ++e) out[e] = acc[k][e];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------- streaming kernel
+// Any D.  One row per block iteration, threads stride over the row's
+// vectors.  OP 0: forward, 1: fused add + forward, 2: VJP (dw accumulated
+// into this block's partial row in global memory: written on the block's
+// first row, read-modify-written after; each column belongs to one thread).
+template <int NV>
+__device__ __forceinline__ void block_sum(float (&v)[NV], float* red, int& parity) {
+#pragma unroll
+    for (int n = 0; n < NV; ++n) v[n] = wave_sum(v[n]);
+    if (blockDim.x > 64) {
+        cross_wave_sum<NV>(v, blockDim.x >> 6, red, parity);
+        parity ^= 1;
+    }
+}
+
+template <typename T, int NV, int OP>
+__global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
+    __shared__ float red[2 * 16 * 2];
+    const T* __restrict__ x = static_cast<const T*>(a.x);
+    const T* __restrict__ res = static_cast<const T*>(a.res);
+    const T* __restrict__ w = static_cast<const T*>(a.w);
+    const T* __restrict__ dy = static_cast<const T*>(a.dy);
+    T* __restrict__ y = static_cast<T*>(a.y);
+    T* __restrict__ newres = static_cast<T*>(a.newres);
+    T* __restrict__ dx = static_cast<T*>(a.dx);
+    float* dst = (gridDim.x == 1) ? a.dw : a.partial + (int64_t)blockIdx.x * a.D;
+    const float inv_d = 1.0f / static_cast<float>(a.D);
+    int parity = 0;
+    bool first = true;
+
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        const int64_t base = row * a.D;
+        float s2[2] = {0.0f, 0.0f};
+        for (int v = threadIdx.x; v < a.nvec; v += blockDim.x) {
+            const int64_t off = base + (int64_t)v * NV;
+            const Raw<T, NV> px = load_raw<T, NV>(x + off);
+            if constexpr (OP == 2) {
+                const Raw<T, NV> pd = load_raw<T, NV>(dy + off);
+                const Raw<T, NV> pw = load_raw<T, NV>(w + (int64_t)v * NV);
+#pragma unroll
+                for (int e = 0; e < NV; ++e) {
+                    const float xv = elem(px, e);
+                    s2[0] = __builtin_fmaf(xv, xv, s2[0]);
+                    s2[1] = __builtin_fmaf(elem(pd, e) * (a.wb + elem(pw, e)), xv, s2[1]);
+                }
+            } else {
+                float h[NV];
+#pragma unroll
+                for (int e = 0; e < NV; ++e) h[e] = elem(px, e);
+                if constexpr (OP == 1) {
+                    const Raw<T, NV> pr = load_raw<T, NV>(res + off);
+#pragma unroll
+                    for (int e = 0; e < NV; ++e) h[e] += elem(pr, e);
+                    store_f32<T, NV>(newres + off, h);
+                }
+#pragma unroll
+                for (int e = 0; e < NV; ++e) s2[0] = __builtin_fmaf(h[e], h[e], s2[0]);
+            }
+        }
+        if constexpr (OP == 2) {
+            block_sum<2>(s2, red, parity);
+        } else {
+            float t[1] = {s2[0]};
+            block_sum<1>(t, red, parity);
+            s2[0] = t[0];
+        }
+        const float r = rsqrtf(s2[0] * inv_d + a.eps);
+        const float c = r * r * r * s2[1] * inv_d;
+
+        for (int v = threadIdx.x; v < a.nvec; v += blockDim.x) {
+            const int64_t off = base + (int64_t)v * NV;
+            const Raw<T, NV> px = load_raw<T, NV>(x + off);
+            const Raw<T, NV> pw = load_raw<T, NV>(w + (int64_t)v * NV);
+            float o[NV];
+            if constexpr (OP == 2) {
+                const Raw<T, NV> pd = load_raw<T, NV>(dy + off);
+                float* dcol = dst + (int64_t)v * NV;
+#pragma unroll
+                for (int e = 0; e < NV; ++e) {
+                    const float xv = elem(px, e);
+                    const float dv = elem(pd, e);
+                    o[e] = r * (a.wb + elem(pw, e)) * dv - xv * c;
+                    const float contrib = dv * xv * r;
+                    dcol[e] = first ? contrib : dcol[e] + contrib;
+                }
+                store_f32<T, NV>(dx + off, o);
+            } else {
+                float h[NV];
+#pragma unroll
+                for (int e = 0; e < NV; ++e) h[e] = elem(px, e);
+                if constexpr (OP == 1) {
+                    const Raw<T, NV> pr = load_raw<T, NV>(res + off);
+#pragma unroll
+                    for (int e = 0; e < NV; ++e) h[e] += elem(pr, e);
+                }
+#pragma unroll
+                for (int e = 0; e < NV; ++e) o[e] = h[e] * r * (a.wb + elem(pw, e));
+                store_f32<T, NV>(y + off, o);
+            }
+        }
+        first = false;
+    }
+}
+
+}  // namespace rmsn

@@ -1,0 +1,37 @@
+// rmsn_launch.hpp -- host-side view of the kernel set: which instances
+// exist, how large a block each may take, and the launch helpers that the
+// C-ABI layer calls.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rmsn {
+
+struct RowArgs;
+
+enum Op : int { kOpFwd = 0, kOpFused = 1, kOpVjp = 2 };
+enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+// Largest block a register-resident instance may run with.  Per-thread
+// state grows with the bytes of one row a lane holds (K * NV * itemsize:
+// gain, dw accumulators, two prefetch sets of raw row data), so the wide
+// instances are compiled for fewer threads and more VGPRs per thread
+// (1024 threads: 128 VGPRs, 512: 256, 256: 512).
+constexpr int max_block_threads(int op, int k, int nv, int itemsize) {
+    const int bytes = k * nv * itemsize;
+    const int lim1024 = (op == 0) ? 32 : 16;   // forward carries the least state
+    return bytes <= lim1024 ? 1024 : (bytes <= 2 * lim1024 ? 512 : 256);
+}
+
+inline int dtype_size(int dt) { return dt == kF32 ? 4 : 2; }
+
+// Kernel entry for (op, dtype, NV, K); K == -1 is the streaming kernel.
+// Returns nullptr for a combination that is not compiled.
+const void* fwd_kernel(int dt, int nv, int k, bool fused);
+const void* vjp_kernel(int dt, int nv, int k);
+const void* dw_combine_kernel();
+const void* zero_kernel();
+
+}  // namespace rmsn

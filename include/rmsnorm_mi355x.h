@@ -1,0 +1,150 @@
+/*
+ * rmsnorm_mi355x.h -- C ABI of the MI355X (gfx950) RMSNorm library.
+ *
+ * Operations (all rows are independent; normalisation is over the last axis):
+ *
+ *   rmsnorm_fwd            y = x * rsqrt(mean(x^2) + eps) * (weight_bias + w)
+ *       The reference expression of the MLX pull request "RMSNormVJP backward
+ *       writes a full {n_rows, D} gw_temp intermediate" (section POC), with
+ *       the weight_bias offset of mlxcel issue "Fused residual-add RMSNorm and
+ *       fused RoPE + KV-append decode kernels" (FusedAddRMSNorm bullet):
+ *       weight_bias = 1 gives Gemma's (1 + w) convention, 0 the plain one.
+ *
+ *   fused_add_rmsnorm_fwd  new_residual = x + residual,
+ *                          normed = rmsnorm(x + residual)
+ *       Same mlxcel issue, FusedAddRMSNorm bullet and the paragraph on the
+ *       two-output constraint: two separate outputs, no in-place update.  The
+ *       sum is formed once in fp32 and normalised unrounded; new_residual is
+ *       that sum rounded to the storage dtype.
+ *
+ *   rmsnorm_vjp            dx, dw for an upstream gradient dy of y
+ *       MLX pull request above, sections "Proposed changes" and "POC": the
+ *       backward recomputes the row statistic from x, and the weight gradient
+ *       is summed across rows inside the library, never through an
+ *       intermediate of the input's size.  With g = weight_bias + w,
+ *       r = rsqrt(mean(x^2) + eps), S = sum_j dy_j g_j x_j:
+ *           dx_j = r g_j dy_j - x_j r^3 S / D,     dw_j = sum_rows dy_j x_j r.
+ *
+ * Conventions shared by every entry point:
+ *   - Layout: row-major, contiguous [rows, D] tensors; w is [D].  x,
+ *     residual, w, dy, y, normed, new_residual and dx all have the dtype
+ *     `dt`; dw is always fp32.  Arithmetic is fp32 throughout, rounded once
+ *     (to nearest, ties to even) on store.
+ *   - Pointers: device pointers owned by the caller; the library allocates
+ *     no device memory and keeps no pointer after the call returns.  Each
+ *     pointer must be aligned to its element size; wider alignment (16 B) and
+ *     D * itemsize divisible by 16 select the widest loads.
+ *   - Outputs must not overlap any other argument buffer (RMSN_E_OVERLAP).
+ *   - Execution: asynchronous on `hip_stream` (a hipStream_t; NULL is the
+ *     null stream).  No call synchronises.  The functions are thread-safe;
+ *     one workspace must not serve two calls in flight at once.
+ *   - Errors: a status is returned, nothing is thrown.  Arguments are checked
+ *     before any launch; launch failures return RMSN_E_HIP.
+ *   - rows == 0 is valid: nothing is written, except that rmsnorm_vjp sets
+ *     dw to zero (the empty sum).  Pointers other than w and dw may then be
+ *     NULL.
+ */
+#ifndef RMSNORM_MI355X_H
+#define RMSNORM_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RMSN_F32 = 0,
+    RMSN_F16 = 1,
+    RMSN_BF16 = 2
+} rmsn_dtype_t;
+
+typedef enum {
+    RMSN_OK = 0,
+    RMSN_E_NULLPTR = -1,   /* a required pointer is NULL */
+    RMSN_E_SHAPE = -2,     /* rows < 0, D < 1, or D beyond the supported maximum */
+    RMSN_E_DTYPE = -3,     /* unknown dtype */
+    RMSN_E_WORKSPACE = -4, /* workspace NULL or smaller than required */
+    RMSN_E_OVERLAP = -5,   /* an output range overlaps another argument */
+    RMSN_E_HIP = -6,       /* the HIP runtime reported an error */
+    RMSN_E_ALIGN = -7,     /* a pointer is not aligned to its element size */
+    RMSN_E_CONFIG = -8     /* an explicit kernel configuration cannot serve the shape */
+} rmsn_status_t;
+
+/* Largest D served (elements). */
+#define RMSN_MAX_D ((int64_t)1 << 24)
+
+/* Kernel configuration.  Zero in a field means "choose automatically".
+ * Only the *_cfg entry points take one; the plain entry points always choose
+ * automatically.  An explicit choice that cannot serve the shape returns
+ * RMSN_E_CONFIG. */
+typedef struct {
+    int32_t lanes_per_row;  /* threads cooperating on one row: power of two, 1..1024 */
+    int32_t vecs_per_lane;  /* vectors each thread holds per row: 1, 2, 4 or 8;
+                               -1 selects the streaming (looped) kernel */
+    int32_t vec_bytes;      /* bytes per load/store: 16, 8, 4 or the element size */
+    int32_t block_threads;  /* threads per block: 64..1024, multiple of lanes_per_row */
+    int32_t num_blocks;     /* grid size (for rmsnorm_vjp also the number of dw partial rows) */
+} rmsn_config_t;
+
+/* y[rows, D] = rmsnorm(x) * (weight_bias + w).  See the file header. */
+int rmsnorm_fwd(const void *x, const void *w, void *y,
+                int64_t rows, int64_t D, int dt,
+                float eps, float weight_bias, void *hip_stream);
+
+/* new_residual = x + residual; normed = rmsnorm(x + residual) * (weight_bias + w). */
+int fused_add_rmsnorm_fwd(const void *x, const void *residual, const void *w,
+                          void *normed, void *new_residual,
+                          int64_t rows, int64_t D, int dt,
+                          float eps, float weight_bias, void *hip_stream);
+
+/* Bytes of workspace rmsnorm_vjp needs for this shape on the current device
+ * (fp32 dw partials, [num_blocks, D], num_blocks bounded independently of
+ * rows).  0 for invalid arguments.  Never more than 2048 * D * 4 + 256. */
+size_t rmsnorm_vjp_workspace_bytes(int64_t rows, int64_t D, int dt);
+
+/* dx[rows, D] (dtype dt) and dw[D] (fp32, overwritten).  `workspace` is
+ * device memory of at least rmsnorm_vjp_workspace_bytes(rows, D, dt) bytes,
+ * 256-byte aligned; its contents on entry do not matter and are left
+ * undefined. */
+int rmsnorm_vjp(const void *x, const void *w, const void *dy,
+                void *dx, float *dw, void *workspace, size_t workspace_bytes,
+                int64_t rows, int64_t D, int dt,
+                float eps, float weight_bias, void *hip_stream);
+
+/* The same three operations with an explicit kernel configuration (NULL =
+ * automatic).  For rmsnorm_vjp_cfg the workspace must hold
+ * num_blocks * D * 4 bytes for the configuration actually used. */
+int rmsnorm_fwd_cfg(const void *x, const void *w, void *y,
+                    int64_t rows, int64_t D, int dt, float eps, float weight_bias,
+                    const rmsn_config_t *cfg, void *hip_stream);
+int fused_add_rmsnorm_fwd_cfg(const void *x, const void *residual, const void *w,
+                              void *normed, void *new_residual,
+                              int64_t rows, int64_t D, int dt, float eps, float weight_bias,
+                              const rmsn_config_t *cfg, void *hip_stream);
+int rmsnorm_vjp_cfg(const void *x, const void *w, const void *dy,
+                    void *dx, float *dw, void *workspace, size_t workspace_bytes,
+                    int64_t rows, int64_t D, int dt, float eps, float weight_bias,
+                    const rmsn_config_t *cfg, void *hip_stream);
+
+/* Operation ids for rmsn_query_config. */
+#define RMSN_OP_FWD 0
+#define RMSN_OP_FUSED 1
+#define RMSN_OP_VJP 2
+
+/* Fill *out with the configuration the automatic choice makes for `op` on
+ * this shape, assuming every pointer is 16-byte aligned (`align_bytes` = the
+ * largest power of two dividing every pointer, capped at 16, to model other
+ * alignments).  Returns RMSN_OK or an argument error. */
+int rmsn_query_config(int op, int64_t rows, int64_t D, int dt, int align_bytes,
+                      rmsn_config_t *out);
+
+/* Static text for a status code. */
+const char *rmsn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMSNORM_MI355X_H */
