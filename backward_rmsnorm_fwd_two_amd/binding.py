@@ -223,6 +223,54 @@ def rmsnorm_vjp(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, eps: float =
     return dx, dw
 
 
+def prepare(fn_name: str, *args):
+    """Marshal the arguments of one C entry point once and return a callable
+    that re-issues the call (same tensors, same stream) with no per-call
+    Python checks -- for tight loops where the host must stay ahead of the
+    GPU.  The tensors must stay alive while the callable is used."""
+    fn = getattr(_lib, fn_name)
+    conv = []
+    for a, t in zip(args, fn.argtypes):
+        conv.append(a if isinstance(a, ctypes._SimpleCData) else t(a))
+
+    def call():
+        st = fn(*conv)
+        if st != 0:
+            raise RMSNormError(st, fn_name)
+    return call
+
+
+def prepared_fwd(x, w, out, eps, weight_bias):
+    rows, D = _rows_d(x)
+    _req(x, "x", x.dtype, x.device)
+    _req(w, "w", x.dtype, x.device, D)
+    _req(out, "out", x.dtype, x.device, x.numel())
+    return prepare("rmsnorm_fwd", x.data_ptr(), w.data_ptr(), out.data_ptr(), rows, D, _dt(x),
+                   float(eps), float(weight_bias), _stream(x))
+
+
+def prepared_fused(x, residual, w, normed, new_residual, eps, weight_bias):
+    rows, D = _rows_d(x)
+    for t, n in ((x, "x"), (residual, "residual"), (normed, "normed"), (new_residual, "new_residual")):
+        _req(t, n, x.dtype, x.device, x.numel())
+    _req(w, "w", x.dtype, x.device, D)
+    return prepare("fused_add_rmsnorm_fwd", x.data_ptr(), residual.data_ptr(), w.data_ptr(),
+                   normed.data_ptr(), new_residual.data_ptr(), rows, D, _dt(x), float(eps),
+                   float(weight_bias), _stream(x))
+
+
+def prepared_vjp(x, w, dy, dx, dw, workspace, eps, weight_bias):
+    rows, D = _rows_d(x)
+    for t, n in ((x, "x"), (dy, "dy"), (dx, "dx")):
+        _req(t, n, x.dtype, x.device, x.numel())
+    _req(w, "w", x.dtype, x.device, D)
+    _req(dw, "dw", torch.float32, x.device, D)
+    nbytes = workspace.numel() * workspace.element_size()
+    return prepare("rmsnorm_vjp", x.data_ptr(), w.data_ptr(), dy.data_ptr(), dx.data_ptr(),
+                   dw.data_ptr(), workspace.data_ptr(), nbytes, rows, D, _dt(x), float(eps),
+                   float(weight_bias), _stream(x))
+
+
 def query_config(op: int, rows: int, D: int, dtype: torch.dtype, align_bytes: int = 16) -> dict:
     """The configuration the automatic choice makes for this shape."""
     c = Config()

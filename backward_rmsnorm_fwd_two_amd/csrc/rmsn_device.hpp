@@ -1,5 +1,5 @@
 // rmsn_device.hpp -- gfx950 device helpers shared by the RMSNorm kernels:
-// storage-type conversion, vector loads/stores, wave64 DPP / permlane-swap
+// storage-type conversion, vector loads/stores, wave64 DPP / swizzle / bpermute
 // reductions and the LDS-only workgroup barrier.
 #pragma once
 
@@ -32,21 +32,44 @@ struct Raw {
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Streamed row data may be moved with the non-temporal cache policy.
+#ifndef RMSN_NT
+#define RMSN_NT 0
+#endif
+
+template <typename V>
+__device__ __forceinline__ V ld_stream(const V* p) {
+#if RMSN_NT
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+
+template <typename V>
+__device__ __forceinline__ void st_stream(V* p, V v) {
+#if RMSN_NT
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
 template <typename T, int NV>
 __device__ __forceinline__ Raw<T, NV> load_raw(const T* p) {
     Raw<T, NV> r;
     constexpr int B = Raw<T, NV>::kBytes;
     if constexpr (B == 16) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+        const u32x4 v = ld_stream(reinterpret_cast<const u32x4*>(p));
         r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
     } else if constexpr (B == 8) {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+        const u32x2 v = ld_stream(reinterpret_cast<const u32x2*>(p));
         r.w[0] = v.x; r.w[1] = v.y;
     } else if constexpr (B == 4) {
-        r.w[0] = *reinterpret_cast<const uint32_t*>(p);
+        r.w[0] = ld_stream(reinterpret_cast<const uint32_t*>(p));
     } else {
         static_assert(B == 2, "unsupported vector width");
-        r.w[0] = *reinterpret_cast<const uint16_t*>(p);
+        r.w[0] = ld_stream(reinterpret_cast<const uint16_t*>(p));
     }
     return r;
 }
@@ -74,7 +97,8 @@ __device__ __forceinline__ float elem(const Raw<T, NV>& r, int e) {
     }
 }
 
-// Store NV fp32 values as T (round to nearest even) with one instruction.
+// Store N fp32 values as T (round to nearest even) with one instruction;
+// used for the streamed outputs (y, normed, new_residual, dx).
 template <typename T, int N>
 struct alignas(sizeof(T) * N) Pack {
     T v[N];
@@ -85,15 +109,36 @@ __device__ __forceinline__ void store_f32(T* p, const float (&v)[N]) {
     Pack<T, N> pk;
 #pragma unroll
     for (int i = 0; i < N; ++i) pk.v[i] = from_f32<T>(v[i]);
-    *reinterpret_cast<Pack<T, N>*>(p) = pk;
+    constexpr int B = N * static_cast<int>(sizeof(T));
+    if constexpr (B == 16) {
+        st_stream(reinterpret_cast<u32x4*>(p), __builtin_bit_cast(u32x4, pk));
+    } else if constexpr (B == 8) {
+        st_stream(reinterpret_cast<u32x2*>(p), __builtin_bit_cast(u32x2, pk));
+    } else if constexpr (B == 4) {
+        st_stream(reinterpret_cast<uint32_t*>(p), __builtin_bit_cast(uint32_t, pk));
+    } else {
+        static_assert(B == 2, "unsupported vector width");
+        st_stream(reinterpret_cast<uint16_t*>(p), __builtin_bit_cast(uint16_t, pk));
+    }
+}
+
+// Plain (cached) store of N floats; used for the dw partial rows, which the
+// combine kernel reads back right away.
+template <int N>
+__device__ __forceinline__ void store_floats(float* p, const float (&v)[N]) {
+    Pack<float, N> pk;
+#pragma unroll
+    for (int i = 0; i < N; ++i) pk.v[i] = v[i];
+    *reinterpret_cast<Pack<float, N>*>(p) = pk;
 }
 
 // ------------------------------------------------------- wave reductions
 // All-reduce (sum) over aligned groups of `lanes` consecutive lanes of a
 // wave64 (lanes = 1, 2, 4, ..., 64, wave-uniform).  Butterfly steps: DPP
 // quad permutations for distance 1 and 2, half-row and row mirrors for the
-// 8- and 16-lane groups, then the gfx950 permlane16 / permlane32 swaps to
-// join rows.  Each step adds the partner's value to the lane's own, so every
+// 8- and 16-lane groups, a ds_swizzle (bit mode, xor 16) to join the two
+// rows of each 32-lane half and a ds_bpermute (lane ^ 32) to join the
+// halves.  Each step adds the partner's value to the lane's own, so every
 // lane of a group ends with the bit-identical sum (fp32 addition commutes)
 // in a fixed order.  Every lane of the wave must execute this.
 template <int CTRL>
@@ -102,16 +147,17 @@ __device__ __forceinline__ float dpp_move(float v) {
         0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
-__device__ __forceinline__ float swap16_add(float v) {
-    auto p = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v),
-                                              __builtin_bit_cast(unsigned, v), false, false);
-    return __builtin_bit_cast(float, p[0]) + __builtin_bit_cast(float, p[1]);
+// ds_swizzle offset, bit mode: and_mask 0x1F, or_mask 0, xor_mask 0x10.
+constexpr int kSwizzleXor16 = (0x10 << 10) | 0x1F;
+
+__device__ __forceinline__ float xor16_add(float v) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
+                                                                     kSwizzleXor16));
 }
 
-__device__ __forceinline__ float swap32_add(float v) {
-    auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),
-                                              __builtin_bit_cast(unsigned, v), false, false);
-    return __builtin_bit_cast(float, p[0]) + __builtin_bit_cast(float, p[1]);
+__device__ __forceinline__ float xor32_add(float v) {
+    const int src = static_cast<int>((__lane_id() ^ 32u) << 2);
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, v)));
 }
 
 constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
@@ -127,7 +173,7 @@ __device__ __forceinline__ float group_sum(float v, int lanes) {
     if (lanes > 2) v += dpp_move<kDppXor2>(v);
     if (lanes > 4) v += dpp_move<kDppHalfMirror>(v);
     if (lanes > 8) v += dpp_move<kDppMirror>(v);
-    if (lanes > 16) v = swap16_add(v);
+    if (lanes > 16) v = xor16_add(v);
     return v;
 }
 
@@ -136,8 +182,8 @@ __device__ __forceinline__ float wave_sum(float v) {
     v += dpp_move<kDppXor2>(v);
     v += dpp_move<kDppHalfMirror>(v);
     v += dpp_move<kDppMirror>(v);
-    v = swap16_add(v);
-    return swap32_add(v);
+    v = xor16_add(v);
+    return xor32_add(v);
 }
 
 // Workgroup barrier that orders LDS traffic only: global loads issued

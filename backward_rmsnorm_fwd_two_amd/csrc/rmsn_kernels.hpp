@@ -6,7 +6,7 @@
 // one row; lane l holds vectors v = k * lanes + l (k < K) of NV elements,
 // i.e. columns [v * NV, v * NV + NV).  A block of blockDim.x threads works on
 // blockDim.x / lanes rows at a time and strides over row groups with the
-// grid.  Row sums reduce within the lane group by DPP / permlane swaps; when
+// grid.  Row sums reduce within the lane group by DPP / swizzle / bpermute; when
 // a row spans several waves (lanes > 64) the wave totals meet in LDS.
 //
 // The streaming kernel (rows_looped) serves any D: one block per row, two
@@ -15,6 +15,12 @@
 
 #include "rmsn_device.hpp"
 #include "rmsn_launch.hpp"
+
+// Row groups whose loads are issued together per loop iteration (more
+// bytes in flight per wave without loop-carried registers).
+#ifndef RMSN_UNROLL
+#define RMSN_UNROLL 1
+#endif
 
 namespace rmsn {
 
@@ -134,8 +140,19 @@ __global__ __launch_bounds__(max_block_threads(FUSED ? 1 : 0, K, NV, sizeof(T)))
     int64_t row0 = (int64_t)blockIdx.x * nslots;
     if (row0 >= a.rows) return;  // whole block
 
+    // First iteration: the row loads go out before the gain's, so the two
+    // latencies overlap.  Row groups past the end load a clamped (valid)
+    // group and are not processed.
+    constexpr int U = RMSN_UNROLL;
+    int parity = 0;
     float g[K][NV];
     {
+        FwdRow<T, NV, K, FUSED> d[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t r = row0 + u * step;
+            fwd_issue<T, NV, K, FUSED>(a, r < a.rows ? r : row0, slot, c, d[u]);
+        }
         Raw<T, NV> pw[K];
         issue_row<T, NV, K>(static_cast<const T*>(a.w), 0, c, pw);
         mask_cols<T, NV, K>(c, pw);
@@ -143,12 +160,22 @@ __global__ __launch_bounds__(max_block_threads(FUSED ? 1 : 0, K, NV, sizeof(T)))
         for (int k = 0; k < K; ++k)
 #pragma unroll
             for (int e = 0; e < NV; ++e) g[k][e] = a.wb + elem(pw[k], e);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (row0 + u * step < a.rows)
+                fwd_process<T, NV, K, FUSED>(a, row0 + u * step, slot, lanes, c, g, d[u], red, parity);
     }
-    int parity = 0;
-    for (; row0 < a.rows; row0 += step) {
-        FwdRow<T, NV, K, FUSED> d;
-        fwd_issue<T, NV, K, FUSED>(a, row0, slot, c, d);
-        fwd_process<T, NV, K, FUSED>(a, row0, slot, lanes, c, g, d, red, parity);
+    for (row0 += U * step; row0 < a.rows; row0 += U * step) {
+        FwdRow<T, NV, K, FUSED> d[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t r = row0 + u * step;
+            fwd_issue<T, NV, K, FUSED>(a, r < a.rows ? r : row0, slot, c, d[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (row0 + u * step < a.rows)
+                fwd_process<T, NV, K, FUSED>(a, row0 + u * step, slot, lanes, c, g, d[u], red, parity);
     }
 }
 
@@ -242,8 +269,16 @@ __global__ __launch_bounds__(max_block_threads(2, K, NV, sizeof(T))) void vjp_ro
         for (int e = 0; e < NV; ++e) acc[k][e] = 0.0f;
 
     if (row0 < a.rows) {  // block-uniform
+        constexpr int U = RMSN_UNROLL;
+        int parity = 0;
         float g[K][NV];
         {
+            VjpRow<T, NV, K> d[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t r = row0 + u * step;
+                vjp_issue<T, NV, K>(a, r < a.rows ? r : row0, slot, c, d[u]);
+            }
             Raw<T, NV> pw[K];
             issue_row<T, NV, K>(static_cast<const T*>(a.w), 0, c, pw);
             mask_cols<T, NV, K>(c, pw);
@@ -251,12 +286,22 @@ __global__ __launch_bounds__(max_block_threads(2, K, NV, sizeof(T))) void vjp_ro
             for (int k = 0; k < K; ++k)
 #pragma unroll
                 for (int e = 0; e < NV; ++e) g[k][e] = a.wb + elem(pw[k], e);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (row0 + u * step < a.rows)
+                    vjp_process<T, NV, K>(a, row0 + u * step, slot, lanes, c, g, acc, d[u], red, parity);
         }
-        int parity = 0;
-        for (; row0 < a.rows; row0 += step) {
-            VjpRow<T, NV, K> d;
-            vjp_issue<T, NV, K>(a, row0, slot, c, d);
-            vjp_process<T, NV, K>(a, row0, slot, lanes, c, g, acc, d, red, parity);
+        for (row0 += U * step; row0 < a.rows; row0 += U * step) {
+            VjpRow<T, NV, K> d[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t r = row0 + u * step;
+                vjp_issue<T, NV, K>(a, r < a.rows ? r : row0, slot, c, d[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (row0 + u * step < a.rows)
+                    vjp_process<T, NV, K>(a, row0 + u * step, slot, lanes, c, g, acc, d[u], red, parity);
         }
     }
 
@@ -288,7 +333,7 @@ __global__ __launch_bounds__(max_block_threads(2, K, NV, sizeof(T))) void vjp_ro
         if (slot == 0 && c.ok[k]) {
             float* out = dst + c.off[k];
             if (vec_ok) {
-                store_f32<float, NV>(out, acc[k]);
+                store_floats<NV>(out, acc[k]);
             } else {
 #pragma unroll
                 for (int e = 0; e < NV; ++e) out[e] = acc[k][e];

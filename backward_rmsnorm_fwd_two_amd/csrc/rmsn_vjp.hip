@@ -3,26 +3,59 @@
 
 namespace rmsn {
 
-// dw[j] = sum_b partial[b, j] for b = 0 .. nb-1, in a fixed order: 16 row
-// groups each sum a strided subset, then a fixed LDS tree joins them.
-// Block: 256 threads = 16 columns x 16 row groups.
+// dw[j] = sum_b partial[b, j] for b = 0 .. nb-1, in a fixed order.  Block:
+// 256 threads = 4 column quads (16 columns) x 64 row groups.  Row group g
+// sums rows g, g + 64, g + 128, ... (loads issued 8 at a time, added in row
+// order); a fixed LDS tree then joins the 64 group sums.
+constexpr int kCombineGroups = 64;
+constexpr int kCombineBatch = 8;
+
 __global__ __launch_bounds__(256) void dw_combine(const float* __restrict__ partial,
                                                   float* __restrict__ dw, int nb, int D) {
-    __shared__ float buf[16][17];
-    const int cx = threadIdx.x & 15;
-    const int ry = threadIdx.x >> 4;
-    const int col = blockIdx.x * 16 + cx;
-    float s = 0.0f;
-    if (col < D) {
-        for (int b = ry; b < nb; b += 16) s += partial[(int64_t)b * D + col];
+    __shared__ float buf[kCombineGroups][17];
+    const int cq = threadIdx.x & 3;
+    const int rg = threadIdx.x >> 2;
+    const int col0 = blockIdx.x * 16 + cq * 4;
+    const bool vec = (D & 3) == 0;
+    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int b0 = rg; b0 < nb; b0 += kCombineGroups * kCombineBatch) {
+        float v[kCombineBatch][4];
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u) {
+            const int b = b0 + u * kCombineGroups;
+            const float* row = partial + (int64_t)b * D;
+            if (vec) {
+                if (b < nb && col0 < D) {
+                    const float4 q = *reinterpret_cast<const float4*>(row + col0);
+                    v[u][0] = q.x; v[u][1] = q.y; v[u][2] = q.z; v[u][3] = q.w;
+                } else {
+                    v[u][0] = v[u][1] = v[u][2] = v[u][3] = 0.0f;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[u][e] = (b < nb && col0 + e < D) ? row[col0 + e] : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[e] += v[u][e];
     }
-    buf[ry][cx] = s;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) buf[rg][cq * 4 + e] = s[e];
     __syncthreads();
-    for (int st = 8; st >= 1; st >>= 1) {
-        if (ry < st) buf[ry][cx] += buf[ry + st][cx];
+    for (int st = kCombineGroups / 2; st >= 1; st >>= 1) {
+        if (rg < st) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) buf[rg][cq * 4 + e] += buf[rg + st][cq * 4 + e];
+        }
         __syncthreads();
     }
-    if (ry == 0 && col < D) dw[col] = buf[0][cx];
+    if (rg == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (col0 + e < D) dw[col0 + e] = buf[0][cq * 4 + e];
+    }
 }
 
 __global__ __launch_bounds__(256) void zero_f32(float* __restrict__ p, int64_t n) {

@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Benchmark: RMSNorm forward + VJP on one MI355X through the C ABI.
+
+One step = rmsnorm_fwd + rmsnorm_vjp (dx and the fp32 weight gradient dw)
+over one [8192, 4096] fp16 batch (the tensors of the MLX pull request's POC
+timing script: x, w, dy ~ U(0,1), eps 1e-5, weight_bias 0).  Throughput is
+algorithmic bytes moved per step / time:
+    forward  2*R*D*s + D*s        (read x, write y, read w)
+    VJP      3*R*D*s + D*s + 4*D  (read x and dy, write dx, read w, write dw)
+Inputs are resident in HBM before the timed region.  Calls go straight to
+the C ABI with arguments marshalled once per buffer set.  Consecutive steps use
+different buffer sets (rotating through enough copies that a set is touched
+again only after >= 1 GiB of other traffic), so no step is served from the
+256 MB last-level cache left warm by the step before it.
+
+Prints one JSON line (rank 0).  `--workload prefill` measures the fused
+add+RMSNorm forward + VJP at [32768, 8192] bf16 instead (not the headline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (% of peak) for RMSNorm fwd+VJP, 8192x4096 fp16"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCES = ["rmsn_kernels.hpp", "rmsn_device.hpp", "rmsn_vjp.hip", "rmsn_fwd.hip", "rmsn_api.hip"]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "backward_rmsnorm_fwd_two_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(name: str, src_hash: str):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (scaled by a copy kernel of known size), read from the committed summary
+    profiles/<name>.md -- only if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", name + ".md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel source hash:\s*`?([0-9a-f]{16})", text)
+    m_val = re.search(r"traffic per launch \(bytes\):\s*`?([0-9]+)", text)
+    if not m_hash or not m_val or m_hash.group(1) != src_hash:
+        return None
+    return int(m_val.group(1))
+
+
+def elapsed_ms(a: torch.cuda.Event, b: torch.cuda.Event) -> float:
+    return a.elapsed_time(b)
+
+
+def copy_ceiling(nbytes: int = 256 << 20, reps: int = 20) -> float:
+    """Device-to-device copy throughput (read + write bytes / time), GB/s."""
+    src = torch.empty(nbytes // 2, dtype=torch.float16, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = elapsed_ms(e0, e1) / reps
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def cpu_oracle_baseline(c, rows, D, fwd_bytes, vjp_bytes, fused=False):
+    """The fp64 CPU oracle as it stands (single thread), on a bounded sample
+    of the same workload: the first `sample_rows` rows, repeated until about
+    10 s of CPU work; reported in GB/s on the same algorithmic byte model."""
+    from oracle import oracle as O
+    sample_rows = min(rows, 2048 if fused else 8192)
+    x = c["x"][:sample_rows]
+    dy = c["dy"][:sample_rows]
+    res = c["residual"][:sample_rows] if fused else None
+    per_row_bytes = (fwd_bytes + vjp_bytes) / rows
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        if fused:
+            _, h = O.fused_add_rmsnorm_fwd(x, res, c["w"], c["eps"], c["weight_bias"])
+            O.rmsnorm_vjp(h, c["w"], dy, c["eps"], c["weight_bias"])
+        else:
+            O.rmsnorm_fwd(x, c["w"], c["eps"], c["weight_bias"])
+            O.rmsnorm_vjp(x, c["w"], dy, c["eps"], c["weight_bias"])
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= 10.0 or passes >= 20:
+            break
+    gbps = passes * sample_rows * per_row_bytes / dt / 1e9
+    return {
+        "value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"{passes} pass(es) of fwd+VJP over the first {sample_rows} of {rows} rows "
+                  f"(D={D}), fp64 C oracle incl. widening, {dt:.1f} s",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", choices=["poc", "prefill"], default="poc")
+    ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(rows shard across GPUs with one dw all-reduce; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+
+    import backward_rmsnorm_fwd_two_amd as R
+    from backward_rmsnorm_fwd_two_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    fused = args.workload == "prefill"
+    log(f"generating inputs ({args.workload})")
+    if fused:
+        c = I.prefill()
+        workload = "fused add+RMSNorm fwd + VJP, [32768, 8192] bf16, weight_bias 1, eps 1e-6"
+    else:
+        c = I.poc_8192x4096()
+        workload = "RMSNorm fwd + VJP, [8192, 4096] fp16, x/w/dy ~ U(0,1), eps 1e-5, weight_bias 0"
+    rows, D = c["x"].shape
+    s = c["x"].element_size()
+    eps, wb = c["eps"], c["weight_bias"]
+    if fused:
+        fwd_bytes = 4 * rows * D * s + D * s          # read x, res; write normed, new_residual; read w
+    else:
+        fwd_bytes = 2 * rows * D * s + D * s          # read x; write y; read w
+    vjp_bytes = 3 * rows * D * s + D * s + 4 * D      # read x, dy; write dx; read w; write dw (fp32)
+    step_bytes = fwd_bytes + vjp_bytes
+
+    set_bytes = (4 * rows * D * s) + (2 * rows * D * s if fused else 0)
+    nsets = args.sets or max(1, -(-(1 << 30) // set_bytes) + 1) if set_bytes < (1 << 30) else 1
+    nsets = args.sets or nsets
+    log(f"uploading {nsets} buffer set(s) of {set_bytes / 2**20:.0f} MiB")
+    w = c["w"].to(dev)
+    sets = []
+    for _ in range(nsets):
+        st = {"x": c["x"].to(dev), "dy": c["dy"].to(dev)}
+        if fused:
+            st["res"] = c["residual"].to(dev)
+            st["normed"] = torch.empty_like(st["x"])
+            st["newres"] = torch.empty_like(st["x"])
+        else:
+            st["y"] = torch.empty_like(st["x"])
+        st["dx"] = torch.empty_like(st["x"])
+        sets.append(st)
+    dw = torch.empty(D, dtype=torch.float32, device=dev)
+    ws = R.workspace_for(rows, D, c["x"].dtype, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # Arguments are marshalled once per buffer set (prepared C calls), so
+    # the host enqueues faster than the GPU drains and no step waits on Python.
+    f_calls, v_calls = [], []
+    for st in sets:
+        if fused:
+            f_calls.append(R.prepared_fused(st["x"], st["res"], w, st["normed"], st["newres"], eps, wb))
+        else:
+            f_calls.append(R.prepared_fwd(st["x"], w, st["y"], eps, wb))
+        xin = st["newres"] if fused else st["x"]
+        v_calls.append(R.prepared_vjp(xin, w, st["dy"], st["dx"], dw, ws, eps, wb))
+
+    def step(i, ev=None):
+        k = i % nsets
+        if ev is not None:
+            ev[0].record(stream)
+        f_calls[k]()
+        if ev is not None:
+            ev[1].record(stream)
+        v_calls[k]()
+        if ev is not None:
+            ev[2].record(stream)
+
+    log(f"warmup {args.warmup}")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: exactly `steps` steps, bracketed by device syncs.  Every
+    # SAMPLE-th step also carries HIP events (on the stream the kernels run
+    # on) around its forward and its VJP: an event record costs the GPU a
+    # few microseconds, so recording every step would distort the region.
+    SAMPLE = 10
+    nsamp = (args.steps + SAMPLE - 1) // SAMPLE
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nsamp)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i // SAMPLE] if i % SAMPLE == 0 else None)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = np.array([elapsed_ms(e[0], e[1]) for e in evs])
+    vjp_ms = np.array([elapsed_ms(e[1], e[2]) for e in evs])
+    step_ms = np.array([elapsed_ms(e[0], e[2]) for e in evs])
+    ms_per_step = wall * 1e3 / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # The VJP alone (not preceded by the forward on the same buffers, so
+    # none of x is left in the last-level cache by the forward): reported
+    # beside the in-step figure.
+    iso = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(100)]
+    for i in range(100):
+        iso[i][0].record(stream)
+        v_calls[i % nsets]()
+        iso[i][1].record(stream)
+    torch.cuda.synchronize()
+    vjp_iso_us = float(np.mean([a.elapsed_time(b) for a, b in iso])) * 1e3
+
+    vjp_avg_s = float(vjp_ms.mean()) * 1e-3
+    vjp_gbps = vjp_bytes / vjp_avg_s / 1e9
+    src_hash = kernel_source_hash()
+    prof_name = ("vjp_prefill_32768x8192_bf16" if fused else "vjp_poc_8192x4096_fp16")
+    traffic = stored_traffic(prof_name, src_hash)
+
+    log("copy ceiling")
+    ceiling = copy_ceiling()
+
+    out = {
+        "metric": METRIC if not fused else "achieved HBM GB/s for fused add+RMSNorm fwd + VJP, 32768x8192 bf16",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": workload, "rows": rows, "D": D,
+            "storage_dtype": str(c["x"].dtype).replace("torch.", ""),
+            "bytes_per_step": step_bytes, "buffer_sets": nsets,
+            "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        },
+        "roofline": {
+            "kernel": "rmsnorm_vjp (vjp_rows + dw_combine launches)",
+            "bound": "hbm",
+            "achieved": round(vjp_gbps, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(vjp_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": vjp_bytes,
+            "avg_us": round(vjp_avg_s * 1e6, 3),
+        },
+        "ops_event_us": {
+            "fwd_mean": round(float(fwd_ms.mean()) * 1e3, 3),
+            "fwd_min": round(float(fwd_ms.min()) * 1e3, 3),
+            "vjp_mean": round(float(vjp_ms.mean()) * 1e3, 3),
+            "vjp_min": round(float(vjp_ms.min()) * 1e3, 3),
+            "step_mean": round(float(step_ms.mean()) * 1e3, 3),
+            "sampled_steps": int(len(evs)),
+            "fwd_GBps": round(fwd_bytes / (float(fwd_ms.mean()) * 1e-3) / 1e9, 1),
+            "vjp_alone_mean": round(vjp_iso_us, 3),
+            "vjp_alone_GBps": round(vjp_bytes / (vjp_iso_us * 1e-6) / 1e9, 1),
+        },
+        "copy_ceiling_GBps": round(ceiling, 1),
+        "kernel_source_hash": src_hash,
+        "context": "MLX PR POC, Metal, model not stated: ~1.65 ms per grad call at this shape "
+                   "(= %.0f GB/s on this byte model); not comparable hardware" % (step_bytes / 1.65e-3 / 1e9)
+                   if not fused else None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (fp64 oracle)")
+        out["cpu_baseline"] = cpu_oracle_baseline(c, rows, D, fwd_bytes, vjp_bytes, fused)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

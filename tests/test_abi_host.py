@@ -1,0 +1,82 @@
+"""Host-side checks (no GPU): the C-ABI library loads and exports every
+function include/rmsnorm_mi355x.h declares; the product path and the oracle
+share no code and never import each other."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rmsnorm_mi355x.h")
+PKG = os.path.join(ROOT, "backward_rmsnorm_fwd_two_amd")
+LIB = os.path.join(PKG, "librmsnorm_mi355x.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_three_operations():
+    names = declared_functions()
+    for n in ("rmsnorm_fwd", "fused_add_rmsnorm_fwd", "rmsnorm_vjp", "rmsnorm_vjp_workspace_bytes",
+              "rmsn_status_str"):
+        assert n in names, names
+
+
+def test_library_exports_every_declared_symbol():
+    if not os.path.exists(LIB):
+        from backward_rmsnorm_fwd_two_amd import build
+        build.build(verbose=False)
+    lib = ctypes.CDLL(LIB)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported
+
+
+def test_status_strings_without_gpu():
+    lib = ctypes.CDLL(LIB)
+    lib.rmsn_status_str.restype = ctypes.c_char_p
+    for st in range(-8, 1):
+        s = lib.rmsn_status_str(st).decode()
+        assert s and s != "unknown status"
+    # argument errors are reported before any device call
+    lib.rmsnorm_fwd.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                                        ctypes.c_float, ctypes.c_float, ctypes.c_void_p]
+    assert lib.rmsnorm_fwd(None, None, None, 4, 8, 1, 1e-5, 0.0, None) == -1
+    assert lib.rmsnorm_fwd(None, None, None, 4, 8, 9, 1e-5, 0.0, None) == -3
+    assert lib.rmsnorm_fwd(None, None, None, -1, 8, 1, 1e-5, 0.0, None) == -2
+    assert lib.rmsnorm_fwd(None, None, None, 0, 8, 1, 1e-5, 0.0, None) == 0
+
+
+def _py_sources(d):
+    for base, _, files in os.walk(d):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".c", ".h")):
+                yield os.path.join(base, f)
+
+
+def test_product_never_references_the_oracle():
+    for path in _py_sources(PKG):
+        text = open(path, errors="ignore").read()
+        assert not re.search(r"\boracle\b", text.replace("the oracle", "")), path
+
+
+def test_oracle_never_imports_the_product():
+    for path in _py_sources(os.path.join(ROOT, "oracle")):
+        text = open(path, errors="ignore").read()
+        assert "backward_rmsnorm_fwd_two_amd" not in text, path
+        assert "rmsn_device" not in text and "rmsn_kernels" not in text, path
+
+
+def test_gpu_marker_registered(pytestconfig):
+    markers = pytestconfig.getini("markers")
+    assert any(m.startswith("gpu") for m in markers)
