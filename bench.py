@@ -118,12 +118,61 @@ def cpu_oracle_baseline(c, rows, D, fwd_bytes, vjp_bytes, fused=False):
     }
 
 
+def decode_bench(R, I, dev, args) -> int:
+    """Decode-shaped fused add+RMSNorm: latency per call, fused (one launch)
+    against the unfused composition (torch add, then rmsnorm_fwd) over the
+    (batch, hidden) grid of the fused-kernel microbenchmark; bf16, eps 1e-6,
+    weight_bias 0 and 1.  Per-call time = events around N back-to-back calls
+    / N (launch-bound: the host path is part of the latency)."""
+    N = max(args.steps, 100)
+    rows = []
+    for wb in (0.0, 1.0):
+        for B in (1, 4, 8):
+            for H in (2048, 4096, 8192):
+                c = I.decode(B, H, wb)
+                x, res, w = c["x"].to(dev), c["residual"].to(dev), c["w"].to(dev)
+                normed, newres = torch.empty_like(x), torch.empty_like(x)
+                tmp, y = torch.empty_like(x), torch.empty_like(x)
+                fused = R.prepared_fused(x, res, w, normed, newres, c["eps"], wb)
+                fwd = R.prepared_fwd(tmp, w, y, c["eps"], wb)
+
+                def unfused():
+                    torch.add(x, res, out=tmp)
+                    fwd()
+
+                out = {}
+                for name, fn in (("fused", fused), ("unfused", unfused)):
+                    for _ in range(20):
+                        fn()
+                    torch.cuda.synchronize()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for _ in range(N):
+                        fn()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    out[name] = e0.elapsed_time(e1) * 1e3 / N
+                rows.append({"B": B, "H": H, "weight_bias": wb, "fused_us": round(out["fused"], 3),
+                             "unfused_us": round(out["unfused"], 3),
+                             "speedup": round(out["unfused"] / out["fused"], 3)})
+                log(f"decode B={B} H={H} wb={wb}: fused {out['fused']:.2f} us, unfused {out['unfused']:.2f} us")
+    mean_fused = float(np.mean([r["fused_us"] for r in rows]))
+    print(json.dumps({
+        "metric": "fused add+RMSNorm decode latency per call (bf16)", "value": round(mean_fused, 3),
+        "unit": "us", "n_gpus": 1, "steps": N, "warmup": 20, "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "decode fused add+RMSNorm, B in {1,4,8} x H in {2048,4096,8192}, "
+                               "weight_bias in {0,1}", "grid": rows},
+    }), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", choices=["poc", "prefill"], default="poc")
+    ap.add_argument("--workload", choices=["poc", "prefill", "decode"], default="poc")
     ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -141,6 +190,8 @@ def main() -> int:
     from backward_rmsnorm_fwd_two_amd import inputs as I
 
     dev = torch.device("cuda:0")
+    if args.workload == "decode":
+        return decode_bench(R, I, dev, args)
     fused = args.workload == "prefill"
     log(f"generating inputs ({args.workload})")
     if fused:

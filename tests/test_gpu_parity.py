@@ -352,3 +352,49 @@ def test_error_codes(R):
     assert lib.rmsnorm_vjp(p(x2), p(w), p(x2), p(dx2), p(dw), p(tiny), 8, 8192, 64, 1,
                            1e-5, 0.0, s) == -4
     torch.cuda.synchronize()
+
+
+def test_prefill_fused_then_vjp_bf16_full_size(R):
+    # [32768, 8192] bf16, weight_bias 1 (Gemma), in the launch configuration
+    # the benchmark times.  Outputs are checked on sampled rows (the oracle
+    # computes rows one by one); new_residual on the sampled rows bit-exactly;
+    # dw over every row, streaming the oracle in row chunks (dw is additive
+    # over row splits).  The VJP runs on the GPU's new_residual, itself
+    # checked first.
+    _say("prefill 32768x8192 bf16: generating")
+    c = I.prefill()
+    rows, D = c["x"].shape
+    x, res, w, dy = _gpu(c["x"]), _gpu(c["residual"]), _gpu(c["w"]), _gpu(c["dy"])
+    normed, newres = R.fused_add_rmsnorm_fwd(x, res, w, c["eps"], c["weight_bias"])
+    dx, dw = R.rmsnorm_vjp(newres, w, dy, c["eps"], c["weight_bias"])
+    torch.cuda.synchronize()
+    del x, res
+    rng = np.random.default_rng(5)
+    sample = np.unique(np.concatenate([[0, 1, rows - 1], rng.integers(0, rows, 61)]))
+    idx = torch.as_tensor(sample)
+    xs, rs, dys = c["x"][idx], c["residual"][idx], c["dy"][idx]
+    nref, href = O.fused_add_rmsnorm_fwd(xs, rs, c["w"], c["eps"], c["weight_bias"])
+    assert_close(normed[idx.to(DEV)], nref, "normed (sampled rows)")
+    nr_s = newres[idx.to(DEV)].cpu()
+    np.testing.assert_array_equal(to64(nr_s), O.round_to(href, "bfloat16"))
+    dxref, _ = O.rmsnorm_vjp(nr_s, c["w"], dys, c["eps"], c["weight_bias"])
+    assert_close(dx[idx.to(DEV)], dxref, "dx (sampled rows)")
+    _say("prefill: dw over all rows")
+    dwref = np.zeros(D)
+    CH = 2048
+    for r0 in range(0, rows, CH):
+        _, part = O.rmsnorm_vjp(newres[r0:r0 + CH].cpu(), c["w"], c["dy"][r0:r0 + CH], c["eps"],
+                                c["weight_bias"])
+        dwref += part
+    assert_dw_close(dw, dwref, "dw (all rows)")
+
+
+def test_max_D_and_beyond(R):
+    Dmax = R.RMSN_MAX_D
+    c = I.generic(2, Dmax, "float16", seed=1)
+    check_fwd_vjp(R, c["x"], c["w"], c["dy"], c["eps"], 0.0, "D=2^24")
+    x = torch.zeros(1, Dmax + 1, dtype=torch.float16, device=DEV)
+    w = torch.zeros(Dmax + 1, dtype=torch.float16, device=DEV)
+    with pytest.raises(R.RMSNormError) as ei:
+        R.rmsnorm_fwd(x, w)
+    assert ei.value.status == -2
