@@ -26,7 +26,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 RMSN_F32, RMSN_F16, RMSN_BF16 = 0, 1, 2
-RMSN_OP_FWD, RMSN_OP_FUSED, RMSN_OP_VJP = 0, 1, 2
+RMSN_OP_FWD, RMSN_OP_FUSED, RMSN_OP_VJP, RMSN_OP_GRAD = 0, 1, 2, 3
 RMSN_MAX_D = 1 << 24
 
 STATUS = {
@@ -65,11 +65,16 @@ _lib.rmsnorm_vjp_workspace_bytes.restype = _sz
 _lib.rmsnorm_vjp.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _int, _f32, _f32, _vp]
 _lib.rmsnorm_vjp_cfg.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _int, _f32, _f32,
                                  _cfgp, _vp]
+_lib.rmsnorm_fwd_vjp.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _int, _f32, _f32,
+                                 _vp]
+_lib.rmsnorm_fwd_vjp_cfg.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _int, _f32,
+                                     _f32, _cfgp, _vp]
 _lib.rmsn_query_config.argtypes = [_int, _i64, _i64, _int, _int, _cfgp]
 _lib.rmsn_status_str.argtypes = [_int]
 _lib.rmsn_status_str.restype = ctypes.c_char_p
 for _name in ("rmsnorm_fwd", "rmsnorm_fwd_cfg", "fused_add_rmsnorm_fwd", "fused_add_rmsnorm_fwd_cfg",
-              "rmsnorm_vjp", "rmsnorm_vjp_cfg", "rmsn_query_config"):
+              "rmsnorm_vjp", "rmsnorm_vjp_cfg", "rmsnorm_fwd_vjp", "rmsnorm_fwd_vjp_cfg",
+              "rmsn_query_config"):
     getattr(_lib, _name).restype = _int
 
 raw = _lib  # the C functions themselves (pointer-level access for tests)
@@ -269,6 +274,48 @@ def prepared_vjp(x, w, dy, dx, dw, workspace, eps, weight_bias):
     return prepare("rmsnorm_vjp", x.data_ptr(), w.data_ptr(), dy.data_ptr(), dx.data_ptr(),
                    dw.data_ptr(), workspace.data_ptr(), nbytes, rows, D, _dt(x), float(eps),
                    float(weight_bias), _stream(x))
+
+
+def rmsnorm_fwd_vjp(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, eps: float = 1e-5,
+                    weight_bias: float = 0.0, y: Optional[torch.Tensor] = None,
+                    dx: Optional[torch.Tensor] = None, dw: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None,
+                    cfg=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Grad call in one pass: returns (y, dx, dw)."""
+    dt = _dt(x)
+    rows, D = _rows_d(x)
+    _req(x, "x", x.dtype, x.device)
+    _req(w, "w", x.dtype, x.device, D)
+    _req(dy, "dy", x.dtype, x.device, x.numel())
+    y = torch.empty_like(x) if y is None else y
+    dx = torch.empty_like(x) if dx is None else dx
+    dw = torch.empty(D, dtype=torch.float32, device=x.device) if dw is None else dw
+    _req(y, "y", x.dtype, x.device, x.numel())
+    _req(dx, "dx", x.dtype, x.device, x.numel())
+    _req(dw, "dw", torch.float32, x.device, D)
+    if workspace is None:
+        workspace = workspace_for(rows, D, x.dtype, x.device, cfg)
+    nbytes = workspace.numel() * workspace.element_size()
+    args = (x.data_ptr(), w.data_ptr(), dy.data_ptr(), y.data_ptr(), dx.data_ptr(), dw.data_ptr(),
+            workspace.data_ptr(), nbytes, rows, D, dt, float(eps), float(weight_bias))
+    if cfg is None:
+        st = _lib.rmsnorm_fwd_vjp(*args, _stream(x))
+    else:
+        st = _lib.rmsnorm_fwd_vjp_cfg(*args, _cfg(cfg), _stream(x))
+    _check(st, "rmsnorm_fwd_vjp")
+    return y, dx, dw
+
+
+def prepared_grad(x, w, dy, y, dx, dw, workspace, eps, weight_bias):
+    rows, D = _rows_d(x)
+    for t, n in ((x, "x"), (dy, "dy"), (y, "y"), (dx, "dx")):
+        _req(t, n, x.dtype, x.device, x.numel())
+    _req(w, "w", x.dtype, x.device, D)
+    _req(dw, "dw", torch.float32, x.device, D)
+    nbytes = workspace.numel() * workspace.element_size()
+    return prepare("rmsnorm_fwd_vjp", x.data_ptr(), w.data_ptr(), dy.data_ptr(), y.data_ptr(),
+                   dx.data_ptr(), dw.data_ptr(), workspace.data_ptr(), nbytes, rows, D, _dt(x),
+                   float(eps), float(weight_bias), _stream(x))
 
 
 def query_config(op: int, rows: int, D: int, dtype: torch.dtype, align_bytes: int = 16) -> dict:

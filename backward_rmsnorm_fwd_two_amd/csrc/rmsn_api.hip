@@ -122,8 +122,9 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
         } else {
             int block = req_b;
             if (block == 0) {
-                block = (op == RMSN_OP_VJP) ? maxb : std::max(lanes, std::min(256, maxb));
-                block = std::max(block, 64);
+                // Small blocks: a block-wide barrier per row group holds fewer
+                // waves in lock step (measured fastest for both kernels).
+                block = std::max(std::max(lanes, 64), std::min(256, maxb));
             }
             if (block < 64 || block > maxb || block % 64 != 0 || block % lanes != 0 || !is_pow2(block))
                 return RMSN_E_CONFIG;
@@ -136,8 +137,9 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
             if (cfg && cfg->num_blocks) {
                 grid = cfg->num_blocks;
             } else if (op == RMSN_OP_VJP) {
-                const int64_t per_cu = std::max(1, 1024 / block);
-                grid = std::min<int64_t>(groups, std::min<int64_t>(kMaxPartialRows, cus * per_cu));
+                // Two persistent blocks per CU: every extra partial row costs
+                // D * 4 bytes written and re-read by the combine.
+                grid = std::min<int64_t>(groups, std::min<int64_t>(kMaxPartialRows, 2 * cus));
             } else {
                 grid = std::min<int64_t>(groups, (int64_t)1 << 20);
             }
@@ -259,7 +261,8 @@ size_t ws_bytes(const Plan& p, int64_t D) {
     return p.grid > 1 ? static_cast<size_t>(p.grid) * static_cast<size_t>(D) * sizeof(float) : 0;
 }
 
-int vjp_impl(const void* x, const void* w, const void* dy, void* dx, float* dw, void* ws,
+// y == nullptr: the VJP; y != nullptr: the grad call (forward output too).
+int vjp_impl(const void* x, const void* w, const void* dy, void* y, void* dx, float* dw, void* ws,
              size_t ws_size, int64_t rows, int64_t D, int dt, float eps, float wb,
              const rmsn_config_t* cfg, void* stream) {
     int st = check_common(rows, D, dt);
@@ -275,20 +278,24 @@ int vjp_impl(const void* x, const void* w, const void* dy, void* dx, float* dw, 
         return RMSN_OK;
     }
     if (!x || !w || !dy || !dx) return RMSN_E_NULLPTR;
+    const bool grad = y != nullptr;
     const int s = itemsize(dt);
-    if (!elem_aligned(x, s) || !elem_aligned(w, s) || !elem_aligned(dy, s) || !elem_aligned(dx, s))
+    if (!elem_aligned(x, s) || !elem_aligned(w, s) || !elem_aligned(dy, s) || !elem_aligned(dx, s) ||
+        (grad && !elem_aligned(y, s)))
         return RMSN_E_ALIGN;
     const int64_t tb = rows * D * s;
     const Range rx = range_of(x, tb), rw = range_of(w, D * s), rd = range_of(dy, tb),
-                rdx = range_of(dx, tb), rdw = range_of(dw, D * 4);
+                rdx = range_of(dx, tb), rdw = range_of(dw, D * 4),
+                ry = grad ? range_of(y, tb) : Range{0, 0};
     {
         const Range ins[3] = {rx, rw, rd};
         for (const Range& i : ins)
-            if (overlaps(rdx, i) || overlaps(rdw, i)) return RMSN_E_OVERLAP;
-        if (overlaps(rdx, rdw)) return RMSN_E_OVERLAP;
+            if (overlaps(rdx, i) || overlaps(rdw, i) || overlaps(ry, i)) return RMSN_E_OVERLAP;
+        if (overlaps(rdx, rdw) || overlaps(ry, rdx) || overlaps(ry, rdw)) return RMSN_E_OVERLAP;
     }
-    const int align =
+    int align =
         std::min(std::min(ptr_align(x), ptr_align(w)), std::min(ptr_align(dy), ptr_align(dx)));
+    if (grad) align = std::min(align, ptr_align(y));
     Plan p;
     st = make_plan(RMSN_OP_VJP, rows, D, dt, align, cfg, &p);
     if (st != RMSN_OK) return st;
@@ -297,11 +304,11 @@ int vjp_impl(const void* x, const void* w, const void* dy, void* dx, float* dw, 
         if (!ws || ws_size < need) return RMSN_E_WORKSPACE;
         if (reinterpret_cast<uintptr_t>(ws) % 16 != 0) return RMSN_E_ALIGN;
         const Range rws = range_of(ws, static_cast<int64_t>(need));
-        const Range all[5] = {rx, rw, rd, rdx, rdw};
+        const Range all[6] = {rx, rw, rd, rdx, rdw, ry};
         for (const Range& o : all)
             if (overlaps(rws, o)) return RMSN_E_OVERLAP;
     }
-    const void* fn = rmsn::vjp_kernel(dt, p.nv, p.k);
+    const void* fn = rmsn::vjp_kernel(dt, p.nv, p.k, grad);
     if (!fn) return RMSN_E_CONFIG;
 
     RowArgs a;
@@ -309,6 +316,7 @@ int vjp_impl(const void* x, const void* w, const void* dy, void* dx, float* dw, 
     a.x = x;
     a.w = w;
     a.dy = dy;
+    a.y = y;
     a.dx = dx;
     a.partial = static_cast<float*>(ws);
     a.dw = dw;
@@ -376,20 +384,38 @@ size_t rmsnorm_vjp_workspace_bytes(int64_t rows, int64_t D, int dt) {
 int rmsnorm_vjp(const void* x, const void* w, const void* dy, void* dx, float* dw, void* workspace,
                 size_t workspace_bytes, int64_t rows, int64_t D, int dt, float eps, float weight_bias,
                 void* hip_stream) {
-    return vjp_impl(x, w, dy, dx, dw, workspace, workspace_bytes, rows, D, dt, eps, weight_bias,
-                    nullptr, hip_stream);
+    return vjp_impl(x, w, dy, nullptr, dx, dw, workspace, workspace_bytes, rows, D, dt, eps,
+                    weight_bias, nullptr, hip_stream);
+}
+
+int rmsnorm_fwd_vjp(const void* x, const void* w, const void* dy, void* y, void* dx, float* dw,
+                    void* workspace, size_t workspace_bytes, int64_t rows, int64_t D, int dt,
+                    float eps, float weight_bias, void* hip_stream) {
+    if (rows > 0 && !y) return RMSN_E_NULLPTR;
+    return vjp_impl(x, w, dy, rows > 0 ? y : nullptr, dx, dw, workspace, workspace_bytes, rows, D,
+                    dt, eps, weight_bias, nullptr, hip_stream);
+}
+
+int rmsnorm_fwd_vjp_cfg(const void* x, const void* w, const void* dy, void* y, void* dx, float* dw,
+                        void* workspace, size_t workspace_bytes, int64_t rows, int64_t D, int dt,
+                        float eps, float weight_bias, const rmsn_config_t* cfg, void* hip_stream) {
+    if (rows > 0 && !y) return RMSN_E_NULLPTR;
+    return vjp_impl(x, w, dy, rows > 0 ? y : nullptr, dx, dw, workspace, workspace_bytes, rows, D,
+                    dt, eps, weight_bias, cfg, hip_stream);
 }
 
 int rmsnorm_vjp_cfg(const void* x, const void* w, const void* dy, void* dx, float* dw,
                     void* workspace, size_t workspace_bytes, int64_t rows, int64_t D, int dt,
                     float eps, float weight_bias, const rmsn_config_t* cfg, void* hip_stream) {
-    return vjp_impl(x, w, dy, dx, dw, workspace, workspace_bytes, rows, D, dt, eps, weight_bias, cfg,
-                    hip_stream);
+    return vjp_impl(x, w, dy, nullptr, dx, dw, workspace, workspace_bytes, rows, D, dt, eps,
+                    weight_bias, cfg, hip_stream);
 }
 
 int rmsn_query_config(int op, int64_t rows, int64_t D, int dt, int align_bytes, rmsn_config_t* out) {
     if (!out) return RMSN_E_NULLPTR;
-    if (op != RMSN_OP_FWD && op != RMSN_OP_FUSED && op != RMSN_OP_VJP) return RMSN_E_CONFIG;
+    if (op != RMSN_OP_FWD && op != RMSN_OP_FUSED && op != RMSN_OP_VJP && op != RMSN_OP_GRAD)
+        return RMSN_E_CONFIG;
+    if (op == RMSN_OP_GRAD) op = RMSN_OP_VJP;  // same plan
     int st = check_common(rows, D, dt);
     if (st != RMSN_OK) return st;
     if (align_bytes <= 0 || !is_pow2(align_bytes)) return RMSN_E_ALIGN;

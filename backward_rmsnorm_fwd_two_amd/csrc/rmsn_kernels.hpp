@@ -180,7 +180,8 @@ __global__ __launch_bounds__(max_block_threads(FUSED ? 1 : 0, K, NV, sizeof(T)))
 }
 
 // ---------------------------------------------------------------- VJP
-// dx = r g dy - x r^3 S / D,  S = sum(dy g x);  the dw partial over this
+// dx = r g dy - x r^3 S / D,  S = sum(dy g x)  (WY: also y = x r g, the
+// grad call's forward output from the same pass);  the dw partial over this
 // block's rows is accumulated in registers, combined over the block's row
 // slots in LDS (fixed tree order), and written to partial[blockIdx.x, :]
 // (or to dw when the grid is a single block).  `dyn` LDS: blockDim.x * NV
@@ -200,7 +201,7 @@ __device__ __forceinline__ void vjp_issue(const RowArgs& a, int64_t row0, int sl
     issue_row<T, NV, K>(static_cast<const T*>(a.dy), base, c, d.dy);
 }
 
-template <typename T, int NV, int K>
+template <typename T, int NV, int K, bool WY>
 __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int slot, int lanes,
                                             const Cols<K>& c, const float (&g)[K][NV],
                                             float (&acc)[K][NV], VjpRow<T, NV, K>& d, float* red,
@@ -242,15 +243,28 @@ __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int 
             for (int e = 0; e < NV; ++e) {
                 const float xv = elem(d.x[k], e);
                 const float dv = elem(d.dy[k], e);
-                o[e] = r * g[k][e] * dv - xv * cc;
+                // fixed evaluation order (explicit fma), so every instance
+                // that computes dx rounds it identically
+                o[e] = __builtin_fmaf(-xv, cc, (r * g[k][e]) * dv);
                 acc[k][e] = __builtin_fmaf(dv * xv, r, acc[k][e]);
             }
             if (c.ok[k]) store_f32<T, NV>(dx + base + c.off[k], o);
         }
+        if constexpr (WY) {
+            // grad call: the forward output from the same pass over x
+            T* __restrict__ y = static_cast<T*>(a.y);
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                float o[NV];
+#pragma unroll
+                for (int e = 0; e < NV; ++e) o[e] = elem(d.x[k], e) * r * g[k][e];
+                if (c.ok[k]) store_f32<T, NV>(y + base + c.off[k], o);
+            }
+        }
     }
 }
 
-template <typename T, int NV, int K>
+template <typename T, int NV, int K, bool WY>
 __global__ __launch_bounds__(max_block_threads(2, K, NV, sizeof(T))) void vjp_rows(RowArgs a) {
     extern __shared__ float dyn[];
     __shared__ float red[2 * 16 * 2];
@@ -289,7 +303,7 @@ __global__ __launch_bounds__(max_block_threads(2, K, NV, sizeof(T))) void vjp_ro
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 if (row0 + u * step < a.rows)
-                    vjp_process<T, NV, K>(a, row0 + u * step, slot, lanes, c, g, acc, d[u], red, parity);
+                    vjp_process<T, NV, K, WY>(a, row0 + u * step, slot, lanes, c, g, acc, d[u], red, parity);
         }
         for (row0 += U * step; row0 < a.rows; row0 += U * step) {
             VjpRow<T, NV, K> d[U];
@@ -301,7 +315,7 @@ __global__ __launch_bounds__(max_block_threads(2, K, NV, sizeof(T))) void vjp_ro
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 if (row0 + u * step < a.rows)
-                    vjp_process<T, NV, K>(a, row0 + u * step, slot, lanes, c, g, acc, d[u], red, parity);
+                    vjp_process<T, NV, K, WY>(a, row0 + u * step, slot, lanes, c, g, acc, d[u], red, parity);
         }
     }
 
@@ -344,7 +358,8 @@ __global__ __launch_bounds__(max_block_threads(2, K, NV, sizeof(T))) void vjp_ro
 
 // ---------------------------------------------------- streaming kernel
 // Any D.  One row per block iteration, threads stride over the row's
-// vectors.  OP 0: forward, 1: fused add + forward, 2: VJP (dw accumulated
+// vectors.  OP 0: forward, 1: fused add + forward, 2: VJP, 3: VJP that also
+// writes the forward output y (grad call) (dw accumulated
 // into this block's partial row in global memory: written on the block's
 // first row, read-modify-written after; each column belongs to one thread).
 template <int NV>
@@ -378,7 +393,7 @@ __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
         for (int v = threadIdx.x; v < a.nvec; v += blockDim.x) {
             const int64_t off = base + (int64_t)v * NV;
             const Raw<T, NV> px = load_raw<T, NV>(x + off);
-            if constexpr (OP == 2) {
+            if constexpr (OP >= 2) {
                 const Raw<T, NV> pd = load_raw<T, NV>(dy + off);
                 const Raw<T, NV> pw = load_raw<T, NV>(w + (int64_t)v * NV);
 #pragma unroll
@@ -401,7 +416,7 @@ __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
                 for (int e = 0; e < NV; ++e) s2[0] = __builtin_fmaf(h[e], h[e], s2[0]);
             }
         }
-        if constexpr (OP == 2) {
+        if constexpr (OP >= 2) {
             block_sum<2>(s2, red, parity);
         } else {
             float t[1] = {s2[0]};
@@ -416,18 +431,23 @@ __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
             const Raw<T, NV> px = load_raw<T, NV>(x + off);
             const Raw<T, NV> pw = load_raw<T, NV>(w + (int64_t)v * NV);
             float o[NV];
-            if constexpr (OP == 2) {
+            if constexpr (OP >= 2) {
                 const Raw<T, NV> pd = load_raw<T, NV>(dy + off);
                 float* dcol = dst + (int64_t)v * NV;
 #pragma unroll
                 for (int e = 0; e < NV; ++e) {
                     const float xv = elem(px, e);
                     const float dv = elem(pd, e);
-                    o[e] = r * (a.wb + elem(pw, e)) * dv - xv * c;
+                    o[e] = __builtin_fmaf(-xv, c, (r * (a.wb + elem(pw, e))) * dv);
                     const float contrib = dv * xv * r;
                     dcol[e] = first ? contrib : dcol[e] + contrib;
                 }
                 store_f32<T, NV>(dx + off, o);
+                if constexpr (OP == 3) {
+#pragma unroll
+                    for (int e = 0; e < NV; ++e) o[e] = elem(px, e) * r * (a.wb + elem(pw, e));
+                    store_f32<T, NV>(y + off, o);
+                }
             } else {
                 float h[NV];
 #pragma unroll

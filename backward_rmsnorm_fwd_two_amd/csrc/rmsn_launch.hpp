@@ -11,7 +11,7 @@ namespace rmsn {
 
 struct RowArgs;
 
-enum Op : int { kOpFwd = 0, kOpFused = 1, kOpVjp = 2 };
+enum Op : int { kOpFwd = 0, kOpFused = 1, kOpVjp = 2, kOpGrad = 3 };
 enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
 // Largest block a register-resident instance may run with.  Per-thread
@@ -21,7 +21,8 @@ enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 // (1024 threads: 128 VGPRs, 512: 256, 256: 512).
 constexpr int max_block_threads(int op, int k, int nv, int itemsize) {
     const int bytes = k * nv * itemsize;
-    const int lim1024 = (op == 0) ? 32 : 16;   // forward carries the least state
+    // the fused forward and many-vector instances carry the most state
+    const int lim1024 = (op == 1 || k > 4) ? 16 : 32;
     return bytes <= lim1024 ? 1024 : (bytes <= 2 * lim1024 ? 512 : 256);
 }
 
@@ -30,7 +31,7 @@ inline int dtype_size(int dt) { return dt == kF32 ? 4 : 2; }
 // Kernel entry for (op, dtype, NV, K); K == -1 is the streaming kernel.
 // Returns nullptr for a combination that is not compiled.
 const void* fwd_kernel(int dt, int nv, int k, bool fused);
-const void* vjp_kernel(int dt, int nv, int k);
+const void* vjp_kernel(int dt, int nv, int k, bool write_y);
 const void* dw_combine_kernel();
 const void* zero_kernel();
 

@@ -66,40 +66,45 @@ __global__ __launch_bounds__(256) void zero_f32(float* __restrict__ p, int64_t n
 
 namespace {
 
-template <typename T, int NV>
+template <typename T, int NV, bool WY>
 const void* pick_vjp(int k) {
     switch (k) {
-        case -1: return reinterpret_cast<const void*>(&rows_looped<T, NV, 2>);
-        case 1: return reinterpret_cast<const void*>(&vjp_rows<T, NV, 1>);
-        case 2: return reinterpret_cast<const void*>(&vjp_rows<T, NV, 2>);
-        case 4: return reinterpret_cast<const void*>(&vjp_rows<T, NV, 4>);
-        case 8: return reinterpret_cast<const void*>(&vjp_rows<T, NV, 8>);
+        case -1: return reinterpret_cast<const void*>(&rows_looped<T, NV, WY ? 3 : 2>);
+        case 1: return reinterpret_cast<const void*>(&vjp_rows<T, NV, 1, WY>);
+        case 2: return reinterpret_cast<const void*>(&vjp_rows<T, NV, 2, WY>);
+        case 4: return reinterpret_cast<const void*>(&vjp_rows<T, NV, 4, WY>);
+        case 8: return reinterpret_cast<const void*>(&vjp_rows<T, NV, 8, WY>);
         default: return nullptr;
     }
 }
 
-template <typename T>
+template <typename T, bool WY>
 const void* pick_vjp_nv(int nv, int k) {
     switch (nv) {
-        case 1: return pick_vjp<T, 1>(k);
-        case 2: return pick_vjp<T, 2>(k);
-        case 4: return pick_vjp<T, 4>(k);
+        case 1: return pick_vjp<T, 1, WY>(k);
+        case 2: return pick_vjp<T, 2, WY>(k);
+        case 4: return pick_vjp<T, 4, WY>(k);
         case 8:
-            if constexpr (sizeof(T) == 2) return pick_vjp<T, 8>(k);
+            if constexpr (sizeof(T) == 2) return pick_vjp<T, 8, WY>(k);
             return nullptr;
+        default: return nullptr;
+    }
+}
+
+template <bool WY>
+const void* pick_vjp_dt(int dt, int nv, int k) {
+    switch (dt) {
+        case kF32: return pick_vjp_nv<float, WY>(nv, k);
+        case kF16: return pick_vjp_nv<_Float16, WY>(nv, k);
+        case kBF16: return pick_vjp_nv<__bf16, WY>(nv, k);
         default: return nullptr;
     }
 }
 
 }  // namespace
 
-const void* vjp_kernel(int dt, int nv, int k) {
-    switch (dt) {
-        case kF32: return pick_vjp_nv<float>(nv, k);
-        case kF16: return pick_vjp_nv<_Float16>(nv, k);
-        case kBF16: return pick_vjp_nv<__bf16>(nv, k);
-        default: return nullptr;
-    }
+const void* vjp_kernel(int dt, int nv, int k, bool write_y) {
+    return write_y ? pick_vjp_dt<true>(dt, nv, k) : pick_vjp_dt<false>(dt, nv, k);
 }
 
 const void* dw_combine_kernel() { return reinterpret_cast<const void*>(&dw_combine); }

@@ -118,6 +118,55 @@ def cpu_oracle_baseline(c, rows, D, fwd_bytes, vjp_bytes, fused=False):
     }
 
 
+def grad_bench(R, I, dev, args) -> int:
+    """The grad call in one launch (rmsnorm_fwd_vjp: y, dx, dw from one pass
+    over x and dy) on the [8192, 4096] fp16 POC tensors.  Its HBM bytes:
+    read x, dy; write y, dx (4*R*D*s) + w + fp32 dw.  Also reported: the
+    same work done as rmsnorm_fwd + rmsnorm_vjp, timed the same way."""
+    c = I.poc_8192x4096()
+    rows, D = c["x"].shape
+    s = c["x"].element_size()
+    grad_bytes = 4 * rows * D * s + D * s + 4 * D
+    sep_bytes = 5 * rows * D * s + 2 * D * s + 4 * D
+    set_bytes = 4 * rows * D * s
+    nsets = args.sets or (-(-(1 << 30) // set_bytes) + 1)
+    w = c["w"].to(dev)
+    dw = torch.empty(D, dtype=torch.float32, device=dev)
+    ws = R.workspace_for(rows, D, c["x"].dtype, dev)
+    sets = [{"x": c["x"].to(dev), "dy": c["dy"].to(dev), "y": torch.empty(rows, D, dtype=c["x"].dtype, device=dev),
+             "dx": torch.empty(rows, D, dtype=c["x"].dtype, device=dev)} for _ in range(nsets)]
+    g_calls = [R.prepared_grad(st["x"], w, st["dy"], st["y"], st["dx"], dw, ws, c["eps"], c["weight_bias"])
+               for st in sets]
+    f_calls = [R.prepared_fwd(st["x"], w, st["y"], c["eps"], c["weight_bias"]) for st in sets]
+    v_calls = [R.prepared_vjp(st["x"], w, st["dy"], st["dx"], dw, ws, c["eps"], c["weight_bias"]) for st in sets]
+
+    def run(fn, K, W):
+        for i in range(W):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / K
+
+    t_grad = run(lambda i: g_calls[i % nsets](), args.steps, args.warmup)
+    t_sep = run(lambda i: (f_calls[i % nsets](), v_calls[i % nsets]()), args.steps, args.warmup)
+    value = grad_bytes / t_grad / 1e9
+    print(json.dumps({
+        "metric": "achieved HBM GB/s for the one-launch RMSNorm grad call (y, dx, dw), 8192x4096 fp16",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(t_grad * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "grad call rmsnorm_fwd_vjp, [8192, 4096] fp16, U(0,1), eps 1e-5",
+                   "bytes_per_step": grad_bytes, "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+                   "separate_fwd_plus_vjp_us": round(t_sep * 1e6, 3),
+                   "separate_GBps_on_their_bytes": round(sep_bytes / t_sep / 1e9, 1),
+                   "grad_call_us": round(t_grad * 1e6, 3)},
+    }), flush=True)
+    return 0
+
+
 def decode_bench(R, I, dev, args) -> int:
     """Decode-shaped fused add+RMSNorm: latency per call, fused (one launch)
     against the unfused composition (torch add, then rmsnorm_fwd) over the
@@ -172,7 +221,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", choices=["poc", "prefill", "decode"], default="poc")
+    ap.add_argument("--workload", choices=["poc", "prefill", "decode", "grad"], default="poc")
     ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -192,6 +241,8 @@ def main() -> int:
     dev = torch.device("cuda:0")
     if args.workload == "decode":
         return decode_bench(R, I, dev, args)
+    if args.workload == "grad":
+        return grad_bench(R, I, dev, args)
     fused = args.workload == "prefill"
     log(f"generating inputs ({args.workload})")
     if fused:

@@ -25,6 +25,11 @@
  *       r = rsqrt(mean(x^2) + eps), S = sum_j dy_j g_j x_j:
  *           dx_j = r g_j dy_j - x_j r^3 S / D,     dw_j = sum_rows dy_j x_j r.
  *
+ *   rmsnorm_fwd_vjp        y, dx and dw from one pass over x and dy
+ *       The grad call the MLX pull request's POC times (section POC: a
+ *       gradient evaluation is the forward recompute plus the VJP), done in
+ *       one launch: x and dy are read once, y and dx written once.
+ *
  * Conventions shared by every entry point:
  *   - Layout: row-major, contiguous [rows, D] tensors; w is [D].  x,
  *     residual, w, dy, y, normed, new_residual and dx all have the dtype
@@ -113,7 +118,15 @@ int rmsnorm_vjp(const void *x, const void *w, const void *dy,
                 int64_t rows, int64_t D, int dt,
                 float eps, float weight_bias, void *hip_stream);
 
-/* The same three operations with an explicit kernel configuration (NULL =
+/* Grad call: y (as rmsnorm_fwd), dx and dw (as rmsnorm_vjp) from one pass
+ * over x and dy.  Same workspace rule as rmsnorm_vjp; y must not overlap any
+ * other argument. */
+int rmsnorm_fwd_vjp(const void *x, const void *w, const void *dy,
+                    void *y, void *dx, float *dw, void *workspace, size_t workspace_bytes,
+                    int64_t rows, int64_t D, int dt,
+                    float eps, float weight_bias, void *hip_stream);
+
+/* The same operations with an explicit kernel configuration (NULL =
  * automatic).  For rmsnorm_vjp_cfg the workspace must hold
  * num_blocks * D * 4 bytes for the configuration actually used. */
 int rmsnorm_fwd_cfg(const void *x, const void *w, void *y,
@@ -127,11 +140,16 @@ int rmsnorm_vjp_cfg(const void *x, const void *w, const void *dy,
                     void *dx, float *dw, void *workspace, size_t workspace_bytes,
                     int64_t rows, int64_t D, int dt, float eps, float weight_bias,
                     const rmsn_config_t *cfg, void *hip_stream);
+int rmsnorm_fwd_vjp_cfg(const void *x, const void *w, const void *dy,
+                        void *y, void *dx, float *dw, void *workspace, size_t workspace_bytes,
+                        int64_t rows, int64_t D, int dt, float eps, float weight_bias,
+                        const rmsn_config_t *cfg, void *hip_stream);
 
 /* Operation ids for rmsn_query_config. */
 #define RMSN_OP_FWD 0
 #define RMSN_OP_FUSED 1
 #define RMSN_OP_VJP 2
+#define RMSN_OP_GRAD 3
 
 /* Fill *out with the configuration the automatic choice makes for `op` on
  * this shape, assuming every pointer is 16-byte aligned (`align_bytes` = the

@@ -183,7 +183,7 @@ def _legal_configs(op, D, itemsize):
         nvec = D // nv
         for k in (1, 2, 4, 8):
             bytes_ = k * nv * itemsize
-            lim = 32 if op == 0 else 16
+            lim = 16 if (op == 1 or k > 4) else 32   # mirrors the library's register budget
             maxb = 1024 if bytes_ <= lim else (512 if bytes_ <= 2 * lim else 256)
             for lanes in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024):
                 if lanes * k < nvec or lanes > maxb:
@@ -398,3 +398,67 @@ def test_max_D_and_beyond(R):
     with pytest.raises(R.RMSNormError) as ei:
         R.rmsnorm_fwd(x, w)
     assert ei.value.status == -2
+
+
+# ------------------------------------------------------------- grad call
+
+def check_grad(R, x, w, dy, eps, wb, what, cfg=None):
+    xg, wg, dyg = _gpu(x), _gpu(w), _gpu(dy)
+    y, dx, dw = R.rmsnorm_fwd_vjp(xg, wg, dyg, eps, wb, cfg=cfg)
+    torch.cuda.synchronize()
+    yref, _ = O.rmsnorm_fwd(x, w, eps, wb)
+    dxref, dwref = O.rmsnorm_vjp(x, w, dy, eps, wb)
+    assert_close(y, yref, f"{what} grad y")
+    assert_close(dx, dxref, f"{what} grad dx")
+    assert_dw_close(dw, dwref, f"{what} grad dw")
+    return y, dx, dw
+
+
+def test_grad_call_poc_small_and_8192x4096(R):
+    c = I.poc_small()
+    check_grad(R, c["x"], c["w"], c["dy"], c["eps"], c["weight_bias"], "poc_small")
+    c = I.poc_8192x4096()
+    _, dx, dw = check_grad(R, c["x"], c["w"], c["dy"], c["eps"], c["weight_bias"], "poc")
+    # the grad call's dx and dw are the VJP's, bit for bit (same plan, same arithmetic)
+    dx2, dw2 = R.rmsnorm_vjp(_gpu(c["x"]), _gpu(c["w"]), _gpu(c["dy"]), c["eps"], c["weight_bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(dx.view(torch.int16), dx2.view(torch.int16))
+    assert torch.equal(dw.view(torch.int32), dw2.view(torch.int32))
+
+
+@pytest.mark.parametrize("D", AXIS_LIST + [4096, 8192, 70001])
+@pytest.mark.parametrize("dtype", ["float16", "bfloat16", "float32"])
+def test_grad_call_axis_sweep(R, D, dtype):
+    rows = 1024 if D <= 8192 else 3
+    c = I.generic(rows, D, dtype, seed=D)
+    check_grad(R, c["x"], c["w"], c["dy"], c["eps"], 1.0, f"{dtype} D={D}")
+
+
+@pytest.mark.parametrize("dtype,D", [("float16", 512), ("bfloat16", 500), ("float32", 97)])
+def test_grad_call_forced_configs(R, dtype, D):
+    rows = 77
+    c = I.generic(rows, D, dtype, seed=D)
+    s = 4 if dtype == "float32" else 2
+    for cfg in _legal_configs(2, D, s):
+        for nb in (0, 3):
+            check_grad(R, c["x"], c["w"], c["dy"], c["eps"], 0.5, f"{cfg}", cfg=dict(cfg, num_blocks=nb))
+
+
+def test_grad_call_rows_zero_and_errors(R):
+    import ctypes
+    x = torch.empty(0, 64, dtype=torch.float16, device=DEV)
+    w = torch.ones(64, dtype=torch.float16, device=DEV)
+    dw = torch.full((64,), float("nan"), device=DEV)
+    R.rmsnorm_fwd_vjp(x, w, x, dw=dw)
+    torch.cuda.synchronize()
+    assert torch.all(dw == 0)
+    x = torch.zeros(4, 64, dtype=torch.float16, device=DEV)
+    dx = torch.empty_like(x)
+    dwv = torch.empty(64, dtype=torch.float32, device=DEV)
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    p = lambda t: t.data_ptr()
+    lib = R.raw
+    assert lib.rmsnorm_fwd_vjp(p(x), p(w), p(x), None, p(dx), p(dwv), None, 0, 4, 64, 1, 1e-5, 0.0, s) == -1
+    assert lib.rmsnorm_fwd_vjp(p(x), p(w), p(x), p(dx), p(dx), p(dwv), None, 0, 4, 64, 1, 1e-5, 0.0, s) == -5
+    assert lib.rmsnorm_fwd_vjp(p(x), p(w), p(x), p(x), p(dx), p(dwv), None, 0, 4, 64, 1, 1e-5, 0.0, s) == -5
+    torch.cuda.synchronize()
