@@ -45,12 +45,13 @@ def _bind(path: str):
     lib.orc_rmsnorm_fwd.argtypes = [i64, i64, _dp, _dp, dbl, dbl, _dp, _dp]
     lib.orc_fused_add_rmsnorm_fwd.argtypes = [i64, i64, _dp, _dp, _dp, dbl, dbl, _dp, _dp]
     lib.orc_rmsnorm_vjp.argtypes = [i64, i64, _dp, _dp, _dp, dbl, dbl, _dp, _dp]
+    lib.orc_fused_add_rmsnorm_vjp.argtypes = [i64, i64, _dp, _dp, _dp, _dp, dbl, dbl, _dp, _dp]
     lib.orc_round_array.argtypes = [ctypes.c_int, i64, _dp, _dp]
     for name in ("orc_round_f16", "orc_round_bf16", "orc_round_f32"):
         getattr(lib, name).argtypes = [dbl]
         getattr(lib, name).restype = dbl
     for name in ("orc_rmsnorm_fwd", "orc_fused_add_rmsnorm_fwd", "orc_rmsnorm_vjp",
-                 "orc_round_array"):
+                 "orc_fused_add_rmsnorm_vjp", "orc_round_array"):
         getattr(lib, name).restype = None
     return lib
 
@@ -139,6 +140,21 @@ def rmsnorm_vjp(x, w, dy, eps: float, weight_bias: float):
     _load().orc_rmsnorm_vjp(rows, D, _p(x), _p(w), _p(dy), float(np.float32(eps)),
                             float(np.float32(weight_bias)), _p(dx), _p(dw))
     return dx, dw
+
+
+def fused_add_rmsnorm_vjp(h, w, dy, d_new_residual, eps: float, weight_bias: float):
+    """Backward of the fused form: returns (dh, dw) in fp64, where dh is the
+    gradient reaching h = x + residual (and so both x and residual)."""
+    h = widen(h)
+    w = widen(w)
+    dy = widen(dy)
+    dr = widen(d_new_residual)
+    rows, D = _check2d(h)
+    dh = np.empty_like(h)
+    dw = np.empty(D, dtype=np.float64)
+    _load().orc_fused_add_rmsnorm_vjp(rows, D, _p(h), _p(w), _p(dy), _p(dr), float(np.float32(eps)),
+                                      float(np.float32(weight_bias)), _p(dh), _p(dw))
+    return dh, dw
 
 
 _KIND = {"float32": 0, "float16": 1, "bfloat16": 2}

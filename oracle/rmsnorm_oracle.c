@@ -107,6 +107,21 @@ void orc_rmsnorm_vjp(int64_t rows, int64_t D, const double *x, const double *w,
     }
 }
 
+/* Backward of [FA]'s fused form for training: with h = x + residual (the
+ * saved new_residual) feeding both normed = rmsnorm(h) * g and the next
+ * residual stream, the gradient reaching h -- and through the sum both x
+ * and residual -- is the RMSNorm VJP for dy plus the residual-stream
+ * gradient d_new_residual.  dw is the VJP's.  The row statistic is
+ * recomputed from h as given. */
+void orc_fused_add_rmsnorm_vjp(int64_t rows, int64_t D, const double *h, const double *w,
+                               const double *dy, const double *d_new_residual, double eps,
+                               double weight_bias, double *dh, double *dw)
+{
+    orc_rmsnorm_vjp(rows, D, h, w, dy, eps, weight_bias, dh, dw);
+    for (int64_t i = 0; i < rows * D; ++i)
+        dh[i] += d_new_residual[i];
+}
+
 /* ------------------------------------------------------------------------
  * Round-to-nearest-even from fp64 straight to a binary format with
  * `mant` stored mantissa bits and exponent range [emin, emax], returning the

@@ -255,3 +255,51 @@ def test_oracle_widening_is_exact():
     np.testing.assert_array_equal(O.widen(t), t.double().numpy())
     b = torch.tensor([1.0 + 2 ** -7, -3.140625, 1e-38, 3.3e38], dtype=torch.bfloat16)
     np.testing.assert_array_equal(O.widen(b), b.double().numpy())
+
+
+# ------------------------------------------- fused backward (residual grad)
+
+@pytest.mark.parametrize("rows,D", [(1, 1), (2, 3), (3, 8), (2, 17)])
+@pytest.mark.parametrize("wb", [0.0, 1.0])
+def test_fused_vjp_finite_differences(rows, D, wb):
+    # L = sum(dy * normed(x + res)) + sum(dr * (x + res)); dL/dx = dL/dres = dh.
+    r = _rng(20 + D)
+    x = r.standard_normal((rows, D))
+    res = r.standard_normal((rows, D))
+    w = r.uniform(0.5, 1.5, D)
+    dy = r.standard_normal((rows, D))
+    dr = r.standard_normal((rows, D))
+    eps = 2.0 ** -8
+
+    def loss(xx, rr, ww):
+        normed, h = O.fused_add_rmsnorm_fwd(xx, rr, ww, eps, wb)
+        return float(np.sum(dy * normed) + np.sum(dr * h))
+
+    dh, dw = O.fused_add_rmsnorm_vjp(x + res, w, dy, dr, eps, wb)
+    hstep = 1e-6
+    for i in range(rows):
+        for j in range(D):
+            for which in (0, 1):
+                xp, xm, rp, rm = x.copy(), x.copy(), res.copy(), res.copy()
+                if which == 0:
+                    xp[i, j] += hstep
+                    xm[i, j] -= hstep
+                else:
+                    rp[i, j] += hstep
+                    rm[i, j] -= hstep
+                fd = (loss(xp, rp, w) - loss(xm, rm, w)) / (2 * hstep)
+                assert abs(fd - dh[i, j]) <= 1e-7 * max(1.0, abs(dh[i, j]))
+    for j in range(D):
+        wp, wm = w.copy(), w.copy()
+        wp[j] += hstep
+        wm[j] -= hstep
+        fd = (loss(x, res, wp) - loss(x, res, wm)) / (2 * hstep)
+        assert abs(fd - dw[j]) <= 1e-7 * max(1.0, abs(dw[j]))
+
+
+def test_fused_vjp_zero_residual_grad_is_the_vjp():
+    x, w, dy = _case(5, 33, seed=21)
+    dh, dw = O.fused_add_rmsnorm_vjp(x, w, dy, np.zeros_like(x), 1e-5, 1.0)
+    dx, dw2 = O.rmsnorm_vjp(x, w, dy, 1e-5, 1.0)
+    np.testing.assert_array_equal(dh, dx)
+    np.testing.assert_array_equal(dw, dw2)
