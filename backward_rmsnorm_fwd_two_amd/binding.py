@@ -26,7 +26,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 RMSN_F32, RMSN_F16, RMSN_BF16 = 0, 1, 2
-RMSN_OP_FWD, RMSN_OP_FUSED, RMSN_OP_VJP, RMSN_OP_GRAD = 0, 1, 2, 3
+RMSN_OP_FWD, RMSN_OP_FUSED, RMSN_OP_VJP, RMSN_OP_GRAD, RMSN_OP_FUSED_VJP = 0, 1, 2, 3, 4
 RMSN_MAX_D = 1 << 24
 
 STATUS = {
@@ -69,12 +69,16 @@ _lib.rmsnorm_fwd_vjp.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _
                                  _vp]
 _lib.rmsnorm_fwd_vjp_cfg.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _int, _f32,
                                      _f32, _cfgp, _vp]
+_lib.fused_add_rmsnorm_vjp.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _int, _f32,
+                                       _f32, _vp]
+_lib.fused_add_rmsnorm_vjp_cfg.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _int,
+                                           _f32, _f32, _cfgp, _vp]
 _lib.rmsn_query_config.argtypes = [_int, _i64, _i64, _int, _int, _cfgp]
 _lib.rmsn_status_str.argtypes = [_int]
 _lib.rmsn_status_str.restype = ctypes.c_char_p
 for _name in ("rmsnorm_fwd", "rmsnorm_fwd_cfg", "fused_add_rmsnorm_fwd", "fused_add_rmsnorm_fwd_cfg",
               "rmsnorm_vjp", "rmsnorm_vjp_cfg", "rmsnorm_fwd_vjp", "rmsnorm_fwd_vjp_cfg",
-              "rmsn_query_config"):
+              "fused_add_rmsnorm_vjp", "fused_add_rmsnorm_vjp_cfg", "rmsn_query_config"):
     getattr(_lib, _name).restype = _int
 
 raw = _lib  # the C functions themselves (pointer-level access for tests)
@@ -304,6 +308,48 @@ def rmsnorm_fwd_vjp(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, eps: flo
         st = _lib.rmsnorm_fwd_vjp_cfg(*args, _cfg(cfg), _stream(x))
     _check(st, "rmsnorm_fwd_vjp")
     return y, dx, dw
+
+
+def fused_add_rmsnorm_vjp(h: torch.Tensor, w: torch.Tensor, dy: torch.Tensor,
+                          d_new_residual: torch.Tensor, eps: float = 1e-6, weight_bias: float = 0.0,
+                          dh: Optional[torch.Tensor] = None, dw: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None,
+                          cfg=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Backward of fused_add_rmsnorm_fwd at h = new_residual: returns (dh, dw);
+    dh is the gradient of both x and residual."""
+    dt = _dt(h)
+    rows, D = _rows_d(h)
+    _req(h, "h", h.dtype, h.device)
+    _req(w, "w", h.dtype, h.device, D)
+    _req(dy, "dy", h.dtype, h.device, h.numel())
+    _req(d_new_residual, "d_new_residual", h.dtype, h.device, h.numel())
+    dh = torch.empty_like(h) if dh is None else dh
+    dw = torch.empty(D, dtype=torch.float32, device=h.device) if dw is None else dw
+    _req(dh, "dh", h.dtype, h.device, h.numel())
+    _req(dw, "dw", torch.float32, h.device, D)
+    if workspace is None:
+        workspace = workspace_for(rows, D, h.dtype, h.device, cfg)
+    nbytes = workspace.numel() * workspace.element_size()
+    args = (h.data_ptr(), w.data_ptr(), dy.data_ptr(), d_new_residual.data_ptr(), dh.data_ptr(),
+            dw.data_ptr(), workspace.data_ptr(), nbytes, rows, D, dt, float(eps), float(weight_bias))
+    if cfg is None:
+        st = _lib.fused_add_rmsnorm_vjp(*args, _stream(h))
+    else:
+        st = _lib.fused_add_rmsnorm_vjp_cfg(*args, _cfg(cfg), _stream(h))
+    _check(st, "fused_add_rmsnorm_vjp")
+    return dh, dw
+
+
+def prepared_fused_vjp(h, w, dy, d_new_residual, dh, dw, workspace, eps, weight_bias):
+    rows, D = _rows_d(h)
+    for t, n in ((h, "h"), (dy, "dy"), (d_new_residual, "d_new_residual"), (dh, "dh")):
+        _req(t, n, h.dtype, h.device, h.numel())
+    _req(w, "w", h.dtype, h.device, D)
+    _req(dw, "dw", torch.float32, h.device, D)
+    nbytes = workspace.numel() * workspace.element_size()
+    return prepare("fused_add_rmsnorm_vjp", h.data_ptr(), w.data_ptr(), dy.data_ptr(),
+                   d_new_residual.data_ptr(), dh.data_ptr(), dw.data_ptr(), workspace.data_ptr(),
+                   nbytes, rows, D, _dt(h), float(eps), float(weight_bias), _stream(h))
 
 
 def prepared_grad(x, w, dy, y, dx, dw, workspace, eps, weight_bias):

@@ -261,10 +261,11 @@ size_t ws_bytes(const Plan& p, int64_t D) {
     return p.grid > 1 ? static_cast<size_t>(p.grid) * static_cast<size_t>(D) * sizeof(float) : 0;
 }
 
-// y == nullptr: the VJP; y != nullptr: the grad call (forward output too).
-int vjp_impl(const void* x, const void* w, const void* dy, void* y, void* dx, float* dw, void* ws,
-             size_t ws_size, int64_t rows, int64_t D, int dt, float eps, float wb,
-             const rmsn_config_t* cfg, void* stream) {
+// y != nullptr: the grad call (forward output too); dres != nullptr: the
+// fused backward (dx += d_new_residual); neither: the VJP.
+int vjp_impl(const void* x, const void* w, const void* dy, void* y, const void* dres, void* dx,
+             float* dw, void* ws, size_t ws_size, int64_t rows, int64_t D, int dt, float eps,
+             float wb, const rmsn_config_t* cfg, void* stream) {
     int st = check_common(rows, D, dt);
     if (st != RMSN_OK) return st;
     if (!dw) return RMSN_E_NULLPTR;
@@ -279,16 +280,18 @@ int vjp_impl(const void* x, const void* w, const void* dy, void* y, void* dx, fl
     }
     if (!x || !w || !dy || !dx) return RMSN_E_NULLPTR;
     const bool grad = y != nullptr;
+    const bool resgrad = dres != nullptr;
     const int s = itemsize(dt);
     if (!elem_aligned(x, s) || !elem_aligned(w, s) || !elem_aligned(dy, s) || !elem_aligned(dx, s) ||
-        (grad && !elem_aligned(y, s)))
+        (grad && !elem_aligned(y, s)) || (resgrad && !elem_aligned(dres, s)))
         return RMSN_E_ALIGN;
     const int64_t tb = rows * D * s;
     const Range rx = range_of(x, tb), rw = range_of(w, D * s), rd = range_of(dy, tb),
                 rdx = range_of(dx, tb), rdw = range_of(dw, D * 4),
-                ry = grad ? range_of(y, tb) : Range{0, 0};
+                ry = grad ? range_of(y, tb) : Range{0, 0},
+                rr = resgrad ? range_of(dres, tb) : Range{0, 0};
     {
-        const Range ins[3] = {rx, rw, rd};
+        const Range ins[4] = {rx, rw, rd, rr};
         for (const Range& i : ins)
             if (overlaps(rdx, i) || overlaps(rdw, i) || overlaps(ry, i)) return RMSN_E_OVERLAP;
         if (overlaps(rdx, rdw) || overlaps(ry, rdx) || overlaps(ry, rdw)) return RMSN_E_OVERLAP;
@@ -296,6 +299,7 @@ int vjp_impl(const void* x, const void* w, const void* dy, void* y, void* dx, fl
     int align =
         std::min(std::min(ptr_align(x), ptr_align(w)), std::min(ptr_align(dy), ptr_align(dx)));
     if (grad) align = std::min(align, ptr_align(y));
+    if (resgrad) align = std::min(align, ptr_align(dres));
     Plan p;
     st = make_plan(RMSN_OP_VJP, rows, D, dt, align, cfg, &p);
     if (st != RMSN_OK) return st;
@@ -304,11 +308,11 @@ int vjp_impl(const void* x, const void* w, const void* dy, void* y, void* dx, fl
         if (!ws || ws_size < need) return RMSN_E_WORKSPACE;
         if (reinterpret_cast<uintptr_t>(ws) % 16 != 0) return RMSN_E_ALIGN;
         const Range rws = range_of(ws, static_cast<int64_t>(need));
-        const Range all[6] = {rx, rw, rd, rdx, rdw, ry};
+        const Range all[7] = {rx, rw, rd, rdx, rdw, ry, rr};
         for (const Range& o : all)
             if (overlaps(rws, o)) return RMSN_E_OVERLAP;
     }
-    const void* fn = rmsn::vjp_kernel(dt, p.nv, p.k, grad);
+    const void* fn = rmsn::vjp_kernel(dt, p.nv, p.k, grad ? 1 : resgrad ? 2 : 0);
     if (!fn) return RMSN_E_CONFIG;
 
     RowArgs a;
@@ -317,6 +321,7 @@ int vjp_impl(const void* x, const void* w, const void* dy, void* y, void* dx, fl
     a.w = w;
     a.dy = dy;
     a.y = y;
+    a.res = dres;
     a.dx = dx;
     a.partial = static_cast<float*>(ws);
     a.dw = dw;
@@ -384,7 +389,7 @@ size_t rmsnorm_vjp_workspace_bytes(int64_t rows, int64_t D, int dt) {
 int rmsnorm_vjp(const void* x, const void* w, const void* dy, void* dx, float* dw, void* workspace,
                 size_t workspace_bytes, int64_t rows, int64_t D, int dt, float eps, float weight_bias,
                 void* hip_stream) {
-    return vjp_impl(x, w, dy, nullptr, dx, dw, workspace, workspace_bytes, rows, D, dt, eps,
+    return vjp_impl(x, w, dy, nullptr, nullptr, dx, dw, workspace, workspace_bytes, rows, D, dt, eps,
                     weight_bias, nullptr, hip_stream);
 }
 
@@ -392,7 +397,7 @@ int rmsnorm_fwd_vjp(const void* x, const void* w, const void* dy, void* y, void*
                     void* workspace, size_t workspace_bytes, int64_t rows, int64_t D, int dt,
                     float eps, float weight_bias, void* hip_stream) {
     if (rows > 0 && !y) return RMSN_E_NULLPTR;
-    return vjp_impl(x, w, dy, rows > 0 ? y : nullptr, dx, dw, workspace, workspace_bytes, rows, D,
+    return vjp_impl(x, w, dy, rows > 0 ? y : nullptr, nullptr, dx, dw, workspace, workspace_bytes, rows, D,
                     dt, eps, weight_bias, nullptr, hip_stream);
 }
 
@@ -400,22 +405,38 @@ int rmsnorm_fwd_vjp_cfg(const void* x, const void* w, const void* dy, void* y, v
                         void* workspace, size_t workspace_bytes, int64_t rows, int64_t D, int dt,
                         float eps, float weight_bias, const rmsn_config_t* cfg, void* hip_stream) {
     if (rows > 0 && !y) return RMSN_E_NULLPTR;
-    return vjp_impl(x, w, dy, rows > 0 ? y : nullptr, dx, dw, workspace, workspace_bytes, rows, D,
+    return vjp_impl(x, w, dy, rows > 0 ? y : nullptr, nullptr, dx, dw, workspace, workspace_bytes, rows, D,
                     dt, eps, weight_bias, cfg, hip_stream);
 }
 
 int rmsnorm_vjp_cfg(const void* x, const void* w, const void* dy, void* dx, float* dw,
                     void* workspace, size_t workspace_bytes, int64_t rows, int64_t D, int dt,
                     float eps, float weight_bias, const rmsn_config_t* cfg, void* hip_stream) {
-    return vjp_impl(x, w, dy, nullptr, dx, dw, workspace, workspace_bytes, rows, D, dt, eps,
+    return vjp_impl(x, w, dy, nullptr, nullptr, dx, dw, workspace, workspace_bytes, rows, D, dt, eps,
                     weight_bias, cfg, hip_stream);
+}
+
+int fused_add_rmsnorm_vjp(const void* h, const void* w, const void* dy, const void* d_new_residual,
+                          void* dh, float* dw, void* workspace, size_t workspace_bytes, int64_t rows,
+                          int64_t D, int dt, float eps, float weight_bias, void* hip_stream) {
+    if (rows > 0 && !d_new_residual) return RMSN_E_NULLPTR;
+    return vjp_impl(h, w, dy, nullptr, rows > 0 ? d_new_residual : nullptr, dh, dw, workspace,
+                    workspace_bytes, rows, D, dt, eps, weight_bias, nullptr, hip_stream);
+}
+
+int fused_add_rmsnorm_vjp_cfg(const void* h, const void* w, const void* dy,
+                              const void* d_new_residual, void* dh, float* dw, void* workspace,
+                              size_t workspace_bytes, int64_t rows, int64_t D, int dt, float eps,
+                              float weight_bias, const rmsn_config_t* cfg, void* hip_stream) {
+    if (rows > 0 && !d_new_residual) return RMSN_E_NULLPTR;
+    return vjp_impl(h, w, dy, nullptr, rows > 0 ? d_new_residual : nullptr, dh, dw, workspace,
+                    workspace_bytes, rows, D, dt, eps, weight_bias, cfg, hip_stream);
 }
 
 int rmsn_query_config(int op, int64_t rows, int64_t D, int dt, int align_bytes, rmsn_config_t* out) {
     if (!out) return RMSN_E_NULLPTR;
-    if (op != RMSN_OP_FWD && op != RMSN_OP_FUSED && op != RMSN_OP_VJP && op != RMSN_OP_GRAD)
-        return RMSN_E_CONFIG;
-    if (op == RMSN_OP_GRAD) op = RMSN_OP_VJP;  // same plan
+    if (op < RMSN_OP_FWD || op > RMSN_OP_FUSED_VJP) return RMSN_E_CONFIG;
+    if (op == RMSN_OP_GRAD || op == RMSN_OP_FUSED_VJP) op = RMSN_OP_VJP;  // same plan
     int st = check_common(rows, D, dt);
     if (st != RMSN_OK) return st;
     if (align_bytes <= 0 || !is_pow2(align_bytes)) return RMSN_E_ALIGN;

@@ -180,28 +180,36 @@ __global__ __launch_bounds__(max_block_threads(FUSED ? 1 : 0, K, NV, sizeof(T)))
 }
 
 // ---------------------------------------------------------------- VJP
-// dx = r g dy - x r^3 S / D,  S = sum(dy g x)  (WY: also y = x r g, the
-// grad call's forward output from the same pass);  the dw partial over this
+// dx = r g dy - x r^3 S / D,  S = sum(dy g x)  (kGrad: also y = x r g, the
+// grad call's forward output from the same pass; kResGrad: dx plus the
+// residual-stream gradient, the backward of the fused add form);  the dw partial over this
 // block's rows is accumulated in registers, combined over the block's row
 // slots in LDS (fixed tree order), and written to partial[blockIdx.x, :]
 // (or to dw when the grid is a single block).  `dyn` LDS: blockDim.x * NV
 // floats when the block holds more than one row slot.
+// VJP row kernel modes.
+constexpr int kVjp = 0;       // dx, dw
+constexpr int kGrad = 1;      // also y = x r g (grad call)
+constexpr int kResGrad = 2;   // dx + d_new_residual (backward of the fused add form)
+
 template <typename T, int NV, int K>
 struct VjpRow {
     Raw<T, NV> x[K];
     Raw<T, NV> dy[K];
+    Raw<T, NV> dr[K];   // d_new_residual (kResGrad only)
 };
 
-template <typename T, int NV, int K>
+template <typename T, int NV, int K, int MODE>
 __device__ __forceinline__ void vjp_issue(const RowArgs& a, int64_t row0, int slot, const Cols<K>& c,
                                           VjpRow<T, NV, K>& d) {
     const int64_t row = row0 + slot;
     const int64_t base = row < a.rows ? row * a.D : 0;
     issue_row<T, NV, K>(static_cast<const T*>(a.x), base, c, d.x);
     issue_row<T, NV, K>(static_cast<const T*>(a.dy), base, c, d.dy);
+    if constexpr (MODE == kResGrad) issue_row<T, NV, K>(static_cast<const T*>(a.res), base, c, d.dr);
 }
 
-template <typename T, int NV, int K, bool WY>
+template <typename T, int NV, int K, int MODE>
 __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int slot, int lanes,
                                             const Cols<K>& c, const float (&g)[K][NV],
                                             float (&acc)[K][NV], VjpRow<T, NV, K>& d, float* red,
@@ -246,11 +254,12 @@ __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int 
                 // fixed evaluation order (explicit fma), so every instance
                 // that computes dx rounds it identically
                 o[e] = __builtin_fmaf(-xv, cc, (r * g[k][e]) * dv);
+                if constexpr (MODE == kResGrad) o[e] += elem(d.dr[k], e);
                 acc[k][e] = __builtin_fmaf(dv * xv, r, acc[k][e]);
             }
             if (c.ok[k]) store_f32<T, NV>(dx + base + c.off[k], o);
         }
-        if constexpr (WY) {
+        if constexpr (MODE == kGrad) {
             // grad call: the forward output from the same pass over x
             T* __restrict__ y = static_cast<T*>(a.y);
 #pragma unroll
@@ -264,7 +273,7 @@ __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int 
     }
 }
 
-template <typename T, int NV, int K, bool WY>
+template <typename T, int NV, int K, int MODE>
 __global__ __launch_bounds__(max_block_threads(2, K, NV, sizeof(T))) void vjp_rows(RowArgs a) {
     extern __shared__ float dyn[];
     __shared__ float red[2 * 16 * 2];
@@ -291,7 +300,7 @@ __global__ __launch_bounds__(max_block_threads(2, K, NV, sizeof(T))) void vjp_ro
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int64_t r = row0 + u * step;
-                vjp_issue<T, NV, K>(a, r < a.rows ? r : row0, slot, c, d[u]);
+                vjp_issue<T, NV, K, MODE>(a, r < a.rows ? r : row0, slot, c, d[u]);
             }
             Raw<T, NV> pw[K];
             issue_row<T, NV, K>(static_cast<const T*>(a.w), 0, c, pw);
@@ -303,19 +312,19 @@ __global__ __launch_bounds__(max_block_threads(2, K, NV, sizeof(T))) void vjp_ro
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 if (row0 + u * step < a.rows)
-                    vjp_process<T, NV, K, WY>(a, row0 + u * step, slot, lanes, c, g, acc, d[u], red, parity);
+                    vjp_process<T, NV, K, MODE>(a, row0 + u * step, slot, lanes, c, g, acc, d[u], red, parity);
         }
         for (row0 += U * step; row0 < a.rows; row0 += U * step) {
             VjpRow<T, NV, K> d[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int64_t r = row0 + u * step;
-                vjp_issue<T, NV, K>(a, r < a.rows ? r : row0, slot, c, d[u]);
+                vjp_issue<T, NV, K, MODE>(a, r < a.rows ? r : row0, slot, c, d[u]);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 if (row0 + u * step < a.rows)
-                    vjp_process<T, NV, K, WY>(a, row0 + u * step, slot, lanes, c, g, acc, d[u], red, parity);
+                    vjp_process<T, NV, K, MODE>(a, row0 + u * step, slot, lanes, c, g, acc, d[u], red, parity);
         }
     }
 
@@ -359,7 +368,8 @@ __global__ __launch_bounds__(max_block_threads(2, K, NV, sizeof(T))) void vjp_ro
 // ---------------------------------------------------- streaming kernel
 // Any D.  One row per block iteration, threads stride over the row's
 // vectors.  OP 0: forward, 1: fused add + forward, 2: VJP, 3: VJP that also
-// writes the forward output y (grad call) (dw accumulated
+// writes the forward output y (grad call), 4: VJP plus the residual-stream
+// gradient (fused backward) (dw accumulated
 // into this block's partial row in global memory: written on the block's
 // first row, read-modify-written after; each column belongs to one thread).
 template <int NV>
@@ -441,6 +451,11 @@ __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
                     o[e] = __builtin_fmaf(-xv, c, (r * (a.wb + elem(pw, e))) * dv);
                     const float contrib = dv * xv * r;
                     dcol[e] = first ? contrib : dcol[e] + contrib;
+                }
+                if constexpr (OP == 4) {
+                    const Raw<T, NV> pr = load_raw<T, NV>(res + off);
+#pragma unroll
+                    for (int e = 0; e < NV; ++e) o[e] += elem(pr, e);
                 }
                 store_f32<T, NV>(dx + off, o);
                 if constexpr (OP == 3) {

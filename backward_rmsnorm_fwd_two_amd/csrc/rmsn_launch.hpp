@@ -11,7 +11,7 @@ namespace rmsn {
 
 struct RowArgs;
 
-enum Op : int { kOpFwd = 0, kOpFused = 1, kOpVjp = 2, kOpGrad = 3 };
+enum Op : int { kOpFwd = 0, kOpFused = 1, kOpVjp = 2, kOpGrad = 3, kOpFusedVjp = 4 };
 enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
 // Largest block a register-resident instance may run with.  Per-thread
@@ -31,7 +31,9 @@ inline int dtype_size(int dt) { return dt == kF32 ? 4 : 2; }
 // Kernel entry for (op, dtype, NV, K); K == -1 is the streaming kernel.
 // Returns nullptr for a combination that is not compiled.
 const void* fwd_kernel(int dt, int nv, int k, bool fused);
-const void* vjp_kernel(int dt, int nv, int k, bool write_y);
+// mode: 0 VJP, 1 grad call (also writes y), 2 fused backward (adds the
+// residual-stream gradient).
+const void* vjp_kernel(int dt, int nv, int k, int mode);
 const void* dw_combine_kernel();
 const void* zero_kernel();
 

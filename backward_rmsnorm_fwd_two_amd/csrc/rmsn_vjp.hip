@@ -66,45 +66,50 @@ __global__ __launch_bounds__(256) void zero_f32(float* __restrict__ p, int64_t n
 
 namespace {
 
-template <typename T, int NV, bool WY>
+template <typename T, int NV, int MODE>
 const void* pick_vjp(int k) {
     switch (k) {
-        case -1: return reinterpret_cast<const void*>(&rows_looped<T, NV, WY ? 3 : 2>);
-        case 1: return reinterpret_cast<const void*>(&vjp_rows<T, NV, 1, WY>);
-        case 2: return reinterpret_cast<const void*>(&vjp_rows<T, NV, 2, WY>);
-        case 4: return reinterpret_cast<const void*>(&vjp_rows<T, NV, 4, WY>);
-        case 8: return reinterpret_cast<const void*>(&vjp_rows<T, NV, 8, WY>);
+        case -1: return reinterpret_cast<const void*>(&rows_looped<T, NV, 2 + (MODE == kGrad ? 1 : MODE == kResGrad ? 2 : 0)>);
+        case 1: return reinterpret_cast<const void*>(&vjp_rows<T, NV, 1, MODE>);
+        case 2: return reinterpret_cast<const void*>(&vjp_rows<T, NV, 2, MODE>);
+        case 4: return reinterpret_cast<const void*>(&vjp_rows<T, NV, 4, MODE>);
+        case 8: return reinterpret_cast<const void*>(&vjp_rows<T, NV, 8, MODE>);
         default: return nullptr;
     }
 }
 
-template <typename T, bool WY>
+template <typename T, int MODE>
 const void* pick_vjp_nv(int nv, int k) {
     switch (nv) {
-        case 1: return pick_vjp<T, 1, WY>(k);
-        case 2: return pick_vjp<T, 2, WY>(k);
-        case 4: return pick_vjp<T, 4, WY>(k);
+        case 1: return pick_vjp<T, 1, MODE>(k);
+        case 2: return pick_vjp<T, 2, MODE>(k);
+        case 4: return pick_vjp<T, 4, MODE>(k);
         case 8:
-            if constexpr (sizeof(T) == 2) return pick_vjp<T, 8, WY>(k);
+            if constexpr (sizeof(T) == 2) return pick_vjp<T, 8, MODE>(k);
             return nullptr;
         default: return nullptr;
     }
 }
 
-template <bool WY>
+template <int MODE>
 const void* pick_vjp_dt(int dt, int nv, int k) {
     switch (dt) {
-        case kF32: return pick_vjp_nv<float, WY>(nv, k);
-        case kF16: return pick_vjp_nv<_Float16, WY>(nv, k);
-        case kBF16: return pick_vjp_nv<__bf16, WY>(nv, k);
+        case kF32: return pick_vjp_nv<float, MODE>(nv, k);
+        case kF16: return pick_vjp_nv<_Float16, MODE>(nv, k);
+        case kBF16: return pick_vjp_nv<__bf16, MODE>(nv, k);
         default: return nullptr;
     }
 }
 
 }  // namespace
 
-const void* vjp_kernel(int dt, int nv, int k, bool write_y) {
-    return write_y ? pick_vjp_dt<true>(dt, nv, k) : pick_vjp_dt<false>(dt, nv, k);
+const void* vjp_kernel(int dt, int nv, int k, int mode) {
+    switch (mode) {
+        case kVjp: return pick_vjp_dt<kVjp>(dt, nv, k);
+        case kGrad: return pick_vjp_dt<kGrad>(dt, nv, k);
+        case kResGrad: return pick_vjp_dt<kResGrad>(dt, nv, k);
+        default: return nullptr;
+    }
 }
 
 const void* dw_combine_kernel() { return reinterpret_cast<const void*>(&dw_combine); }

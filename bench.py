@@ -328,6 +328,27 @@ def main() -> int:
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
+    extra = {}
+    if fused:
+        # The backward of the fused form with a residual-stream gradient
+        # (fused_add_rmsnorm_vjp): reads h, dy and d_new_residual, writes dh.
+        dr = torch.empty_like(sets[0]["x"]).normal_(0.0, 0.01)
+        rg = R.prepared_fused_vjp(sets[0]["newres"], w, sets[0]["dy"], dr, sets[0]["dx"], dw, ws, eps, wb)
+        for _ in range(3):
+            rg()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            rg()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_rg = e0.elapsed_time(e1) / 10 * 1e-3
+        rg_bytes = 4 * rows * D * s + D * s + 4 * D
+        extra = {"fused_vjp_with_residual_grad_us": round(t_rg * 1e6, 2),
+                 "fused_vjp_with_residual_grad_GBps": round(rg_bytes / t_rg / 1e9, 1)}
+        del dr
+
     # The VJP alone (not preceded by the forward on the same buffers, so
     # none of x is left in the last-level cache by the forward): reported
     # beside the in-step figure.
@@ -390,6 +411,7 @@ def main() -> int:
             "vjp_alone_GBps": round(vjp_bytes / (vjp_iso_us * 1e-6) / 1e9, 1),
         },
         "copy_ceiling_GBps": round(ceiling, 1),
+        **extra,
         "kernel_source_hash": src_hash,
         "context": "MLX PR POC, Metal, model not stated: ~1.65 ms per grad call at this shape "
                    "(= %.0f GB/s on this byte model); not comparable hardware" % (step_bytes / 1.65e-3 / 1e9)

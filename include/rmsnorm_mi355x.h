@@ -25,6 +25,12 @@
  *       r = rsqrt(mean(x^2) + eps), S = sum_j dy_j g_j x_j:
  *           dx_j = r g_j dy_j - x_j r^3 S / D,     dw_j = sum_rows dy_j x_j r.
  *
+ *   fused_add_rmsnorm_vjp  dh = VJP(h; dy) + d_new_residual, dw
+ *       Training-side backward of the fused form: h = x + residual (the saved
+ *       new_residual) feeds both the normalised output and the next residual
+ *       stream, so the gradient reaching h -- and through the sum both x and
+ *       residual -- is the VJP for dy plus the residual-stream gradient.
+ *
  *   rmsnorm_fwd_vjp        y, dx and dw from one pass over x and dy
  *       The grad call the MLX pull request's POC times (section POC: a
  *       gradient evaluation is the forward recompute plus the VJP), done in
@@ -45,8 +51,8 @@
  *     one workspace must not serve two calls in flight at once.
  *   - Errors: a status is returned, nothing is thrown.  Arguments are checked
  *     before any launch; launch failures return RMSN_E_HIP.
- *   - rows == 0 is valid: nothing is written, except that rmsnorm_vjp sets
- *     dw to zero (the empty sum).  Pointers other than w and dw may then be
+ *   - rows == 0 is valid: nothing is written, except that the backward
+ *     entry points set dw to zero (the empty sum).  Pointers other than w and dw may then be
  *     NULL.
  */
 #ifndef RMSNORM_MI355X_H
@@ -126,6 +132,15 @@ int rmsnorm_fwd_vjp(const void *x, const void *w, const void *dy,
                     int64_t rows, int64_t D, int dt,
                     float eps, float weight_bias, void *hip_stream);
 
+/* Backward of fused_add_rmsnorm_fwd: dh[rows, D] = VJP of rmsnorm at h (the
+ * new_residual the forward returned) for dy, plus d_new_residual; dw as
+ * rmsnorm_vjp.  dh is the gradient of both x and residual.  Same workspace
+ * rule as rmsnorm_vjp. */
+int fused_add_rmsnorm_vjp(const void *h, const void *w, const void *dy, const void *d_new_residual,
+                          void *dh, float *dw, void *workspace, size_t workspace_bytes,
+                          int64_t rows, int64_t D, int dt,
+                          float eps, float weight_bias, void *hip_stream);
+
 /* The same operations with an explicit kernel configuration (NULL =
  * automatic).  For rmsnorm_vjp_cfg the workspace must hold
  * num_blocks * D * 4 bytes for the configuration actually used. */
@@ -144,12 +159,18 @@ int rmsnorm_fwd_vjp_cfg(const void *x, const void *w, const void *dy,
                         void *y, void *dx, float *dw, void *workspace, size_t workspace_bytes,
                         int64_t rows, int64_t D, int dt, float eps, float weight_bias,
                         const rmsn_config_t *cfg, void *hip_stream);
+int fused_add_rmsnorm_vjp_cfg(const void *h, const void *w, const void *dy,
+                              const void *d_new_residual, void *dh, float *dw,
+                              void *workspace, size_t workspace_bytes,
+                              int64_t rows, int64_t D, int dt, float eps, float weight_bias,
+                              const rmsn_config_t *cfg, void *hip_stream);
 
 /* Operation ids for rmsn_query_config. */
 #define RMSN_OP_FWD 0
 #define RMSN_OP_FUSED 1
 #define RMSN_OP_VJP 2
 #define RMSN_OP_GRAD 3
+#define RMSN_OP_FUSED_VJP 4
 
 /* Fill *out with the configuration the automatic choice makes for `op` on
  * this shape, assuming every pointer is 16-byte aligned (`align_bytes` = the

@@ -462,3 +462,69 @@ def test_grad_call_rows_zero_and_errors(R):
     assert lib.rmsnorm_fwd_vjp(p(x), p(w), p(x), p(dx), p(dx), p(dwv), None, 0, 4, 64, 1, 1e-5, 0.0, s) == -5
     assert lib.rmsnorm_fwd_vjp(p(x), p(w), p(x), p(x), p(dx), p(dwv), None, 0, 4, 64, 1, 1e-5, 0.0, s) == -5
     torch.cuda.synchronize()
+
+
+# -------------------------------------- fused backward (residual gradient)
+
+def check_fused_vjp(R, h, w, dy, dr, eps, wb, what, cfg=None):
+    hg, wg, dyg, drg = _gpu(h), _gpu(w), _gpu(dy), _gpu(dr)
+    dh, dw = R.fused_add_rmsnorm_vjp(hg, wg, dyg, drg, eps, wb, cfg=cfg)
+    torch.cuda.synchronize()
+    dhref, dwref = O.fused_add_rmsnorm_vjp(h, w, dy, dr, eps, wb)
+    assert_close(dh, dhref, f"{what} dh")
+    assert_dw_close(dw, dwref, f"{what} dw")
+    return dh, dw
+
+
+@pytest.mark.parametrize("dtype", ["bfloat16", "float16", "float32"])
+@pytest.mark.parametrize("rows,D", [(1, 2048), (8, 4096), (512, 8192), (300, 512), (77, 513), (5, 70001)])
+def test_fused_vjp_parity(R, dtype, rows, D):
+    c = I.generic(rows, D, dtype, seed=rows + D)
+    rng = np.random.default_rng(D)
+    dr = I.normal(rng, (rows, D), 0.0, 0.5, dtype)
+    check_fused_vjp(R, c["x"], c["w"], c["dy"], dr, c["eps"], 1.0, f"{dtype} {rows}x{D}")
+
+
+def test_fused_vjp_zero_residual_grad_equals_vjp_bitwise(R):
+    c = I.generic(1000, 4096, "bfloat16", seed=3)
+    hg, wg, dyg = _gpu(c["x"]), _gpu(c["w"]), _gpu(c["dy"])
+    dh, dw = R.fused_add_rmsnorm_vjp(hg, wg, dyg, torch.zeros_like(hg), c["eps"], 1.0)
+    dx, dw2 = R.rmsnorm_vjp(hg, wg, dyg, c["eps"], 1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(dh.view(torch.int16), dx.view(torch.int16))
+    assert torch.equal(dw.view(torch.int32), dw2.view(torch.int32))
+
+
+@pytest.mark.parametrize("dtype,D", [("bfloat16", 512), ("float16", 500), ("float32", 97)])
+def test_fused_vjp_forced_configs(R, dtype, D):
+    rows = 53
+    c = I.generic(rows, D, dtype, seed=D)
+    dr = I.normal(np.random.default_rng(1), (rows, D), 0.0, 1.0, dtype)
+    s = 4 if dtype == "float32" else 2
+    for cfg in _legal_configs(2, D, s):
+        check_fused_vjp(R, c["x"], c["w"], c["dy"], dr, c["eps"], 0.0, f"{cfg}", cfg=dict(cfg, num_blocks=3))
+
+
+def test_prefill_full_training_step_bf16(R):
+    # The prefill workload end to end: fused forward, then its backward with a
+    # residual-stream gradient (seeded N(0, 0.01)); sampled rows against the
+    # oracle, dw over every row.
+    _say("prefill training step 32768x8192 bf16")
+    c = I.prefill()
+    rows, D = c["x"].shape
+    dr_cpu = I.normal(np.random.default_rng(11), (rows, D), 0.0, 0.01, "bfloat16")
+    x, res, w, dy = _gpu(c["x"]), _gpu(c["residual"]), _gpu(c["w"]), _gpu(c["dy"])
+    normed, h = R.fused_add_rmsnorm_fwd(x, res, w, c["eps"], c["weight_bias"])
+    del x, res, normed
+    dr = _gpu(dr_cpu)
+    dh, dw = R.fused_add_rmsnorm_vjp(h, w, dy, dr, c["eps"], c["weight_bias"])
+    torch.cuda.synchronize()
+    sample = torch.as_tensor(np.unique(np.concatenate([[0, rows - 1], np.random.default_rng(6).integers(0, rows, 62)])))
+    hs = h[sample.to(DEV)].cpu()
+    dhref, _ = O.fused_add_rmsnorm_vjp(hs, c["w"], c["dy"][sample], dr_cpu[sample], c["eps"], c["weight_bias"])
+    assert_close(dh[sample.to(DEV)], dhref, "dh (sampled rows)")
+    dwref = np.zeros(D)
+    for r0 in range(0, rows, 2048):
+        _, part = O.rmsnorm_vjp(h[r0:r0 + 2048].cpu(), c["w"], c["dy"][r0:r0 + 2048], c["eps"], c["weight_bias"])
+        dwref += part
+    assert_dw_close(dw, dwref, "dw (all rows)")
