@@ -118,6 +118,33 @@ def cpu_oracle_baseline(c, rows, D, fwd_bytes, vjp_bytes, fused=False):
     }
 
 
+def ceiling_bench() -> int:
+    """HBM throughput of trivial streaming kernels for each traffic mix the
+    RMSNorm kernels have (the `stream_ceiling` tool built with the library):
+    the practical ceiling each kernel is measured against."""
+    import subprocess
+    exe = os.path.join(ROOT, "backward_rmsnorm_fwd_two_amd", "stream_ceiling")
+    if not os.path.exists(exe):
+        print(f"{exe} is not built; run __graft_entry__.build()", file=sys.stderr)
+        return 2
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=240)
+    if out.returncode != 0:
+        print(out.stdout + out.stderr, file=sys.stderr)
+        return out.returncode
+    best = {}
+    for line in out.stdout.splitlines():
+        f = dict(kv.split("=") for kv in line.split())
+        key = (f["mix"], int(f["stream_MiB"]))
+        best[key] = max(best.get(key, 0.0), float(f["GBps_med"]))
+        log(line)
+    grid = [{"mix": m, "stream_MiB": s, "median_GBps_best_grid": v} for (m, s), v in sorted(best.items())]
+    cold = max(v for (m, s), v in best.items() if s == 512 and m == "1R1W")
+    print(json.dumps({"metric": "HBM ceiling of trivial streaming kernels (1R1W, 512 MiB streams)",
+                      "value": cold, "unit": "GB/s", "n_gpus": 1, "higher_is_better": True,
+                      "data": "synthetic", "config": {"workload": "stream ceiling", "grid": grid}}))
+    return 0
+
+
 def grad_bench(R, I, dev, args) -> int:
     """The grad call in one launch (rmsnorm_fwd_vjp: y, dx, dw from one pass
     over x and dy) on the [8192, 4096] fp16 POC tensors.  Its HBM bytes:
@@ -221,7 +248,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", choices=["poc", "prefill", "decode", "grad"], default="poc")
+    ap.add_argument("--workload", choices=["poc", "prefill", "decode", "grad", "ceiling"], default="poc")
     ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -231,6 +258,8 @@ def main() -> int:
               "(rows shard across GPUs with one dw all-reduce; see the design notes). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
+    if args.workload == "ceiling":
+        return ceiling_bench()
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
