@@ -528,3 +528,60 @@ def test_prefill_full_training_step_bf16(R):
         _, part = O.rmsnorm_vjp(h[r0:r0 + 2048].cpu(), c["w"], c["dy"][r0:r0 + 2048], c["eps"], c["weight_bias"])
         dwref += part
     assert_dw_close(dw, dwref, "dw (all rows)")
+
+
+# ------------------------------------------------- fused forward coverage
+
+def check_fused(R, x, res, w, eps, wb, what, cfg=None, out=None):
+    xg, rg, wg = _gpu(x), _gpu(res), _gpu(w)
+    if out is None:
+        normed, newres = R.fused_add_rmsnorm_fwd(xg, rg, wg, eps, wb, cfg=cfg)
+    else:
+        normed, newres = R.fused_add_rmsnorm_fwd(xg, rg, wg, eps, wb, normed=out[0], new_residual=out[1], cfg=cfg)
+    torch.cuda.synchronize()
+    nref, href = O.fused_add_rmsnorm_fwd(x, res, w, eps, wb)
+    assert_close(normed, nref, f"{what} normed")
+    np.testing.assert_array_equal(to64(newres).reshape(href.shape),
+                                  O.round_to(href, str(x.dtype).replace("torch.", "")), err_msg=f"{what} new_residual")
+
+
+@pytest.mark.parametrize("dtype", ["float32", "float16", "bfloat16"])
+def test_fused_every_D_1_to_700(R, dtype):
+    for D in range(1, 701):
+        c = I.generic(3, D, dtype, seed=D)
+        check_fused(R, c["x"], c["residual"], c["w"], c["eps"], 1.0, f"{dtype} D={D}")
+
+
+@pytest.mark.parametrize("dtype,D", [("bfloat16", 512), ("float16", 500), ("float32", 97), ("bfloat16", 8192)])
+def test_fused_forced_configs(R, dtype, D):
+    rows = 37
+    c = I.generic(rows, D, dtype, seed=D)
+    s = 4 if dtype == "float32" else 2
+    cfgs = _legal_configs(1, D, s)
+    _say(f"fused forced configs {dtype} D={D}: {len(cfgs)}")
+    for cfg in cfgs:
+        check_fused(R, c["x"], c["residual"], c["w"], c["eps"], 0.0, f"{cfg}", cfg=cfg)
+
+
+@pytest.mark.parametrize("dtype", ["float32", "float16", "bfloat16"])
+@pytest.mark.parametrize("offset", [1, 3, 5])
+def test_fused_misaligned(R, dtype, offset):
+    rows, D = 21, 1024
+    c = I.generic(rows, D, dtype, seed=offset)
+    td = I.torch_dtype(dtype)
+    n = rows * D
+
+    def shifted(t, off):
+        buf = torch.empty(t.numel() + 16, dtype=td, device=DEV)
+        v = buf[off:off + t.numel()]
+        v.copy_(_gpu(t).reshape(-1))
+        return v.view(t.shape)
+
+    x, res, w = shifted(c["x"], offset), shifted(c["residual"], (offset + 2) % 8), shifted(c["w"], 0)
+    normed = torch.empty(n + 16, dtype=td, device=DEV)[offset:offset + n].view(rows, D)
+    newres = torch.empty(n + 16, dtype=td, device=DEV)[7 - offset:7 - offset + n].view(rows, D)
+    R.fused_add_rmsnorm_fwd(x, res, w, c["eps"], 1.0, normed=normed, new_residual=newres)
+    torch.cuda.synchronize()
+    nref, href = O.fused_add_rmsnorm_fwd(c["x"], c["residual"], c["w"], c["eps"], 1.0)
+    assert_close(normed, nref, "normed")
+    np.testing.assert_array_equal(to64(newres), O.round_to(href, dtype))
