@@ -46,12 +46,13 @@ def _bind(path: str):
     lib.orc_fused_add_rmsnorm_fwd.argtypes = [i64, i64, _dp, _dp, _dp, dbl, dbl, _dp, _dp]
     lib.orc_rmsnorm_vjp.argtypes = [i64, i64, _dp, _dp, _dp, dbl, dbl, _dp, _dp]
     lib.orc_fused_add_rmsnorm_vjp.argtypes = [i64, i64, _dp, _dp, _dp, _dp, dbl, dbl, _dp, _dp]
+    lib.orc_silu_gate.argtypes = [i64, i64, _dp, _dp]
     lib.orc_round_array.argtypes = [ctypes.c_int, i64, _dp, _dp]
     for name in ("orc_round_f16", "orc_round_bf16", "orc_round_f32"):
         getattr(lib, name).argtypes = [dbl]
         getattr(lib, name).restype = dbl
     for name in ("orc_rmsnorm_fwd", "orc_fused_add_rmsnorm_fwd", "orc_rmsnorm_vjp",
-                 "orc_fused_add_rmsnorm_vjp", "orc_round_array"):
+                 "orc_fused_add_rmsnorm_vjp", "orc_silu_gate", "orc_round_array"):
         getattr(lib, name).restype = None
     return lib
 
@@ -155,6 +156,18 @@ def fused_add_rmsnorm_vjp(h, w, dy, d_new_residual, eps: float, weight_bias: flo
     _load().orc_fused_add_rmsnorm_vjp(rows, D, _p(h), _p(w), _p(dy), _p(dr), float(np.float32(eps)),
                                       float(np.float32(weight_bias)), _p(dh), _p(dw))
     return dh, dw
+
+
+def silu_gate(x):
+    """y = silu(x[:, :d]) * x[:, d:2d] for x of shape [rows, 2d]; fp64."""
+    x = widen(x)
+    rows, two_d = _check2d(x)
+    if two_d % 2:
+        raise ValueError("last axis must be even (2d)")
+    d = two_d // 2
+    y = np.empty((rows, d), dtype=np.float64)
+    _load().orc_silu_gate(rows, d, _p(x), _p(y))
+    return y
 
 
 _KIND = {"float32": 0, "float16": 1, "bfloat16": 2}

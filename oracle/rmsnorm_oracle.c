@@ -16,7 +16,9 @@
  *         KV-append decode kernels" -- the FusedAddRMSNorm bullet of the
  *         candidate-fusion list (new residual = input + residual, output =
  *         rmsnorm(new residual) * (weight_bias + weight), rsqrt(mean + eps),
- *         fp32 sum kept once) and "Regression guard" (Gemma 1+w case).
+ *         fp32 sum kept once), "Regression guard" (Gemma 1+w case), and the
+ *         gated-activation bullet (silu of the first half of a row times its
+ *         second half).
  *
  * Every routine computes in IEEE fp64 with plain loops in row order; there is
  * no blocking, fusion or reordering beyond the definition.  Inputs are the
@@ -120,6 +122,19 @@ void orc_fused_add_rmsnorm_vjp(int64_t rows, int64_t D, const double *h, const d
     orc_rmsnorm_vjp(rows, D, h, w, dy, eps, weight_bias, dh, dw);
     for (int64_t i = 0; i < rows * D; ++i)
         dh[i] += d_new_residual[i];
+}
+
+/* [FA] gated activation: x is [rows, 2d]; with a = x[:, :d], b = x[:, d:2d],
+ *   y = silu(a) * b,   silu(a) = a * sigmoid(a) = a / (1 + exp(-a)).
+ * y is [rows, d]. */
+void orc_silu_gate(int64_t rows, int64_t d, const double *x, double *y)
+{
+    for (int64_t i = 0; i < rows; ++i) {
+        const double *a = x + i * 2 * d;
+        const double *b = a + d;
+        for (int64_t j = 0; j < d; ++j)
+            y[i * d + j] = a[j] / (1.0 + exp(-a[j])) * b[j];
+    }
 }
 
 /* ------------------------------------------------------------------------

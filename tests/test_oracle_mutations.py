@@ -39,6 +39,8 @@ MUTATIONS = [
      "new_residual[i * D + j] = (double)(float)(x[i * D + j] + residual[i * D + j]) + 1e-3;"),
     ("fused_vjp_drops_residual_grad", "        dh[i] += d_new_residual[i];", "        dh[i] += 0.0 * d_new_residual[i];"),
     ("fused_vjp_subtracts_residual_grad", "        dh[i] += d_new_residual[i];", "        dh[i] -= d_new_residual[i];"),
+    ("gate_sigmoid_sign", "y[i * d + j] = a[j] / (1.0 + exp(-a[j])) * b[j];", "y[i * d + j] = a[j] / (1.0 + exp(a[j])) * b[j];"),
+    ("gate_swapped_halves", "y[i * d + j] = a[j] / (1.0 + exp(-a[j])) * b[j];", "y[i * d + j] = b[j] / (1.0 + exp(-b[j])) * a[j];"),
     ("f16_one_bit_short", "return rne_to_format(v, 10, -14, 15);", "return rne_to_format(v, 9, -14, 15);"),
     ("f16_wrong_emin", "return rne_to_format(v, 10, -14, 15);", "return rne_to_format(v, 10, -15, 15);"),
     ("bf16_truncates", "double n = nearbyint(q);", "double n = trunc(q);"),
@@ -60,6 +62,8 @@ CHECKS = [
     P.test_vjp_D1_and_zero_row,
     P.test_dw_independent_of_weight,
     lambda: [P.test_fused_vjp_finite_differences(r, d, wb) for (r, d) in ((1, 1), (2, 3)) for wb in (0.0, 1.0)],
+    P.test_silu_gate_odd_part_identity,
+    P.test_silu_gate_special_values_and_torch,
     R.test_f16_exhaustive_round_trip,
     R.test_f16_midpoints_and_random_match_numpy,
     R.test_bf16_matches_brute_force_nearest,

@@ -303,3 +303,32 @@ def test_fused_vjp_zero_residual_grad_is_the_vjp():
     dx, dw2 = O.rmsnorm_vjp(x, w, dy, 1e-5, 1.0)
     np.testing.assert_array_equal(dh, dx)
     np.testing.assert_array_equal(dw, dw2)
+
+
+# ---------------------------------------------------------- gated activation
+
+def test_silu_gate_odd_part_identity():
+    # silu(a) - silu(-a) = a, so y(a, b) - y(-a, b) = a * b exactly in the
+    # mathematics (to rounding in fp64).
+    r = _rng(30)
+    a = r.standard_normal((7, 33)) * 4
+    b = r.standard_normal((7, 33))
+    y1 = O.silu_gate(np.concatenate([a, b], axis=1))
+    y2 = O.silu_gate(np.concatenate([-a, b], axis=1))
+    np.testing.assert_allclose(y1 - y2, a * b, rtol=1e-12, atol=1e-14)
+
+
+def test_silu_gate_special_values_and_torch():
+    a = np.array([[0.0, 1.0, -1.0, 30.0, -30.0, 800.0, -800.0]])
+    b = np.ones_like(a)
+    y = O.silu_gate(np.concatenate([a, b], axis=1))[0]
+    assert y[0] == 0.0
+    np.testing.assert_allclose(y[1], 1.0 / (1.0 + np.exp(-1.0)), rtol=1e-15)
+    np.testing.assert_allclose(y[3], 30.0, rtol=1e-12)      # ~a for large a
+    assert abs(y[4]) < 1e-11                                  # ~0 for very negative a
+    assert y[5] == 800.0 and y[6] == 0.0
+    # library cross-check: torch's silu in fp64
+    r = _rng(31)
+    x = r.standard_normal((5, 2 * 40)) * 3
+    ref = (torch.nn.functional.silu(torch.tensor(x[:, :40])) * torch.tensor(x[:, 40:])).numpy()
+    np.testing.assert_allclose(O.silu_gate(x), ref, rtol=1e-13, atol=1e-15)
