@@ -26,8 +26,9 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 RMSN_F32, RMSN_F16, RMSN_BF16 = 0, 1, 2
-RMSN_OP_FWD, RMSN_OP_FUSED, RMSN_OP_VJP, RMSN_OP_GRAD, RMSN_OP_FUSED_VJP = 0, 1, 2, 3, 4
+RMSN_OP_FWD, RMSN_OP_FUSED, RMSN_OP_VJP, RMSN_OP_GRAD, RMSN_OP_FUSED_VJP, RMSN_OP_GATE = 0, 1, 2, 3, 4, 5
 RMSN_MAX_D = 1 << 24
+RMSN_MAX_GATE_D = 1 << 28
 
 STATUS = {
     0: "RMSN_OK", -1: "RMSN_E_NULLPTR", -2: "RMSN_E_SHAPE", -3: "RMSN_E_DTYPE",
@@ -73,12 +74,15 @@ _lib.fused_add_rmsnorm_vjp.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _
                                        _f32, _vp]
 _lib.fused_add_rmsnorm_vjp_cfg.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _int,
                                            _f32, _f32, _cfgp, _vp]
+_lib.silu_gate.argtypes = [_vp, _vp, _i64, _i64, _int, _vp]
+_lib.silu_gate_cfg.argtypes = [_vp, _vp, _i64, _i64, _int, _cfgp, _vp]
 _lib.rmsn_query_config.argtypes = [_int, _i64, _i64, _int, _int, _cfgp]
 _lib.rmsn_status_str.argtypes = [_int]
 _lib.rmsn_status_str.restype = ctypes.c_char_p
 for _name in ("rmsnorm_fwd", "rmsnorm_fwd_cfg", "fused_add_rmsnorm_fwd", "fused_add_rmsnorm_fwd_cfg",
               "rmsnorm_vjp", "rmsnorm_vjp_cfg", "rmsnorm_fwd_vjp", "rmsnorm_fwd_vjp_cfg",
-              "fused_add_rmsnorm_vjp", "fused_add_rmsnorm_vjp_cfg", "rmsn_query_config"):
+              "fused_add_rmsnorm_vjp", "fused_add_rmsnorm_vjp_cfg", "silu_gate", "silu_gate_cfg",
+              "rmsn_query_config"):
     getattr(_lib, _name).restype = _int
 
 raw = _lib  # the C functions themselves (pointer-level access for tests)
@@ -362,6 +366,32 @@ def prepared_grad(x, w, dy, y, dx, dw, workspace, eps, weight_bias):
     return prepare("rmsnorm_fwd_vjp", x.data_ptr(), w.data_ptr(), dy.data_ptr(), y.data_ptr(),
                    dx.data_ptr(), dw.data_ptr(), workspace.data_ptr(), nbytes, rows, D, _dt(x),
                    float(eps), float(weight_bias), _stream(x))
+
+
+def silu_gate(x: torch.Tensor, out: Optional[torch.Tensor] = None, cfg=None) -> torch.Tensor:
+    """y = silu(x[..., :d]) * x[..., d:2d] for x of last axis 2d; y has last axis d."""
+    dt = _dt(x)
+    rows, two_d = _rows_d(x)
+    if two_d % 2:
+        raise ValueError("the last axis of x must be even (2d)")
+    d = two_d // 2
+    _req(x, "x", x.dtype, x.device)
+    if out is None:
+        out = torch.empty(tuple(x.shape[:-1]) + (d,), dtype=x.dtype, device=x.device)
+    _req(out, "out", x.dtype, x.device, rows * d)
+    if cfg is None:
+        st = _lib.silu_gate(x.data_ptr(), out.data_ptr(), rows, d, dt, _stream(x))
+    else:
+        st = _lib.silu_gate_cfg(x.data_ptr(), out.data_ptr(), rows, d, dt, _cfg(cfg), _stream(x))
+    _check(st, "silu_gate")
+    return out
+
+
+def prepared_gate(x, out):
+    rows, two_d = _rows_d(x)
+    _req(x, "x", x.dtype, x.device)
+    _req(out, "out", x.dtype, x.device, rows * (two_d // 2))
+    return prepare("silu_gate", x.data_ptr(), out.data_ptr(), rows, two_d // 2, _dt(x), _stream(x))
 
 
 def query_config(op: int, rows: int, D: int, dtype: torch.dtype, align_bytes: int = 16) -> dict:

@@ -1,7 +1,7 @@
 // rmsn_api.hip -- the C ABI declared in include/rmsnorm_mi355x.h: argument
 // checks, the per-shape kernel plan (load width, threads per row, vectors
 // per thread, block, grid) and the launches.  Host code only; the kernels
-// live in rmsn_fwd.hip / rmsn_vjp.hip.
+// live in rmsn_fwd.hip / rmsn_vjp.hip / rmsn_gate.hip.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -342,9 +342,101 @@ int vjp_impl(const void* x, const void* w, const void* dy, void* y, const void* 
     return RMSN_OK;
 }
 
+// ------------------------------------------------------ gated activation
+
+struct GatePlan {
+    int nv = 1;        // elements per load
+    int64_t nvec = 1;  // d / nv
+    int u = 1;         // output vectors per thread per chunk
+    int block = 256;
+    int64_t nchunks = 1;
+    int64_t grid = 1;
+};
+
+int check_gate(int64_t rows, int64_t d, int dt) {
+    if (dt != RMSN_F32 && dt != RMSN_F16 && dt != RMSN_BF16) return RMSN_E_DTYPE;
+    if (rows < 0 || d < 1 || d > RMSN_MAX_GATE_D) return RMSN_E_SHAPE;
+    if (rows > 0 && rows > INT64_MAX / (2 * d * itemsize(dt))) return RMSN_E_SHAPE;
+    return RMSN_OK;
+}
+
+int make_gate_plan(int64_t rows, int64_t d, int dt, int align, const rmsn_config_t* cfg,
+                   GatePlan* p) {
+    const int s = itemsize(dt);
+    if (cfg && (cfg->lanes_per_row != 0 || cfg->vecs_per_lane < 0)) return RMSN_E_CONFIG;
+    int vb = 0;
+    if (cfg && cfg->vec_bytes) {
+        vb = cfg->vec_bytes;
+        if (vb < s || vb > 16 || !is_pow2(vb) || (d * s) % vb != 0 || align % vb != 0)
+            return RMSN_E_CONFIG;
+    } else {
+        for (int c = 16; c >= s; c >>= 1) {
+            if ((d * s) % c == 0 && align % c == 0) { vb = c; break; }
+        }
+        if (vb == 0) vb = s;
+    }
+    p->nv = vb / s;
+    p->nvec = d / p->nv;
+    // Default: one-wave blocks, 16 bytes of each half of x per thread in
+    // flight (measured fastest on the prefill-scale MLP shape: many small
+    // blocks keep every CU's wave slots refilled as soon as a wave retires).
+    int u = cfg && cfg->vecs_per_lane ? cfg->vecs_per_lane : std::min(8, std::max(1, 16 / vb));
+    if (u != 1 && u != 2 && u != 4 && u != 8) return RMSN_E_CONFIG;
+    const int block = cfg && cfg->block_threads ? cfg->block_threads : 64;
+    if (block < 64 || block > 1024 || block % 64 != 0) return RMSN_E_CONFIG;
+    p->u = u;
+    p->block = block;
+    const int64_t chunk = static_cast<int64_t>(block) * u;
+    const int64_t total = rows * p->nvec;
+    p->nchunks = (total + chunk - 1) / chunk;
+    // the kernel locates rows with an fp64 estimate that needs chunk starts < 2^52
+    if (p->nchunks > ((int64_t)1 << 52) / chunk) return RMSN_E_SHAPE;
+    const int64_t max_grid = ((int64_t)1 << 32) / block - 1;  // work-items per dimension < 2^32
+    int64_t grid = cfg && cfg->num_blocks ? cfg->num_blocks : std::min<int64_t>(p->nchunks, (int64_t)1 << 20);
+    if (grid < 1 || grid > max_grid) return RMSN_E_CONFIG;
+    p->grid = grid;
+    return RMSN_OK;
+}
+
+int gate_impl(const void* x, void* y, int64_t rows, int64_t d, int dt, const rmsn_config_t* cfg,
+              void* stream) {
+    int st = check_gate(rows, d, dt);
+    if (st != RMSN_OK) return st;
+    if (rows == 0) return RMSN_OK;
+    if (!x || !y) return RMSN_E_NULLPTR;
+    const int s = itemsize(dt);
+    if (!elem_aligned(x, s) || !elem_aligned(y, s)) return RMSN_E_ALIGN;
+    if (overlaps(range_of(y, rows * d * s), range_of(x, rows * 2 * d * s))) return RMSN_E_OVERLAP;
+    GatePlan p;
+    st = make_gate_plan(rows, d, dt, std::min(ptr_align(x), ptr_align(y)), cfg, &p);
+    if (st != RMSN_OK) return st;
+    const void* fn = rmsn::gate_kernel(dt, p.nv, p.u);
+    if (!fn) return RMSN_E_CONFIG;
+    int64_t total = rows * p.nvec;
+    int64_t nvec = p.nvec;
+    // ceil(2^32 / nvec); exact row offsets for the small quotients inside a chunk
+    uint32_t recip = nvec > 1 ? static_cast<uint32_t>((((uint64_t)1 << 32) + nvec - 1) / nvec) : 0u;
+    double inv = 1.0 / static_cast<double>(nvec);
+    int64_t nchunks = p.nchunks;
+    void* args[] = {&x, &y, &total, &nvec, &recip, &inv, &nchunks};
+    if (hipLaunchKernel(fn, dim3(static_cast<unsigned>(p.grid)), dim3(p.block), args, 0,
+                        static_cast<hipStream_t>(stream)) != hipSuccess)
+        return RMSN_E_HIP;
+    return RMSN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int silu_gate(const void* x, void* y, int64_t rows, int64_t d, int dt, void* hip_stream) {
+    return gate_impl(x, y, rows, d, dt, nullptr, hip_stream);
+}
+
+int silu_gate_cfg(const void* x, void* y, int64_t rows, int64_t d, int dt, const rmsn_config_t* cfg,
+                  void* hip_stream) {
+    return gate_impl(x, y, rows, d, dt, cfg, hip_stream);
+}
 
 int rmsnorm_fwd(const void* x, const void* w, void* y, int64_t rows, int64_t D, int dt, float eps,
                 float weight_bias, void* hip_stream) {
@@ -435,6 +527,20 @@ int fused_add_rmsnorm_vjp_cfg(const void* h, const void* w, const void* dy,
 
 int rmsn_query_config(int op, int64_t rows, int64_t D, int dt, int align_bytes, rmsn_config_t* out) {
     if (!out) return RMSN_E_NULLPTR;
+    if (op == RMSN_OP_GATE) {
+        int st = check_gate(rows, D, dt);
+        if (st != RMSN_OK) return st;
+        if (align_bytes <= 0 || !is_pow2(align_bytes)) return RMSN_E_ALIGN;
+        GatePlan g;
+        st = make_gate_plan(std::max<int64_t>(rows, 1), D, dt, std::min(align_bytes, 16), nullptr, &g);
+        if (st != RMSN_OK) return st;
+        out->lanes_per_row = 0;
+        out->vecs_per_lane = g.u;
+        out->vec_bytes = g.nv * itemsize(dt);
+        out->block_threads = g.block;
+        out->num_blocks = static_cast<int32_t>(g.grid);
+        return RMSN_OK;
+    }
     if (op < RMSN_OP_FWD || op > RMSN_OP_FUSED_VJP) return RMSN_E_CONFIG;
     if (op == RMSN_OP_GRAD || op == RMSN_OP_FUSED_VJP) op = RMSN_OP_VJP;  // same plan
     int st = check_common(rows, D, dt);

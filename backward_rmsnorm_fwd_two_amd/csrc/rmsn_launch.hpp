@@ -35,6 +35,9 @@ const void* fwd_kernel(int dt, int nv, int k, bool fused);
 // residual-stream gradient).
 const void* vjp_kernel(int dt, int nv, int k, int mode);
 const void* dw_combine_kernel();
+// Gated activation silu(x[:, :d]) * x[:, d:2d]: NV elements per load, U
+// output vectors per thread per chunk.
+const void* gate_kernel(int dt, int nv, int u);
 const void* zero_kernel();
 
 }  // namespace rmsn

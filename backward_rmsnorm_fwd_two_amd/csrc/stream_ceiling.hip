@@ -7,7 +7,7 @@
 // of a 4 GiB pool, and each launch moves on to the next chunks, so a chunk is
 // touched again only after >= 1 GiB of other traffic (nothing is served from
 // the 256 MB last-level cache).  Prints one line per (mix, stream size,
-// grid): best and median of 14 timed launches.
+// block, grid): best and median of 14 timed launches.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -62,8 +62,10 @@ int main() {
     for (int64_t bytes : {64LL << 20, 512LL << 20}) {
         const int64_t n = bytes / 16;
         const int64_t chunks = kPool / bytes;
-        for (int grid : {2048, 8192, 0}) {
-            const int bs = 256;
+        // (block, grid): grid 0 = one 16-byte element per thread
+        const int shapes[5][2] = {{256, 2048}, {256, 8192}, {256, 0}, {64, 0}, {1024, 0}};
+        for (const auto& sh : shapes) {
+            const int bs = sh[0], grid = sh[1];
             const int g = grid ? grid : (int)((n + bs - 1) / bs);
             for (int mix = 0; mix < 4; ++mix) {
                 std::vector<float> t;
@@ -84,8 +86,8 @@ int main() {
                 }
                 std::sort(t.begin(), t.end());
                 const double best = t.front(), med = t[t.size() / 2];
-                std::printf("mix=%s stream_MiB=%lld grid=%d best_us=%.2f med_us=%.2f GBps=%.0f GBps_med=%.0f\n",
-                            names[mix], (long long)(bytes >> 20), g, best * 1e3, med * 1e3,
+                std::printf("mix=%s stream_MiB=%lld block=%d grid=%d best_us=%.2f med_us=%.2f GBps=%.0f GBps_med=%.0f\n",
+                            names[mix], (long long)(bytes >> 20), bs, g, best * 1e3, med * 1e3,
                             streams[mix] * (double)bytes / (best * 1e-3) / 1e9,
                             streams[mix] * (double)bytes / (med * 1e-3) / 1e9);
             }

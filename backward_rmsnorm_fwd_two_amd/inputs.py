@@ -25,6 +25,10 @@ Workloads (shapes and distributions of the pages' benchmarks):
   * ``prefill``      bf16 x, residual [R,D] ~ N(0,1), dy ~ N(0,0.01),
     w ~ N(0,0.1), weight_bias 1.0, eps 1e-6 -- prefill-scale fused add+norm
     followed by the backward pass
+  * ``gate``         x[rows, 2d] ~ N(0,2) (both halves) -- the gated
+    activation silu(x[:, :d]) * x[:, d:2d]; d = 14336 is the MLP width of
+    the Llama-3 8B model (the decoder family the fused-kernel issue adopts
+    first), rows 8192 (prefill chunk) or 1 / 4 / 8 (decode batch)
 """
 from __future__ import annotations
 
@@ -127,3 +131,9 @@ def generic(rows: int, D: int, dtype: str, seed: int = 0, dist: str = "normal"):
     res = normal(rng, (rows, D), 0.0, 1.0, dtype)
     w = uniform(rng, (D,), 0.5, 1.5, dtype)
     return dict(x=x, dy=dy, residual=res, w=w, eps=1e-6, weight_bias=0.0, dtype=dtype)
+
+
+def gate(rows: int, d: int, dtype: str = "bfloat16", seed: int = 0, std: float = 2.0):
+    rng = np.random.default_rng(seed)
+    x = normal(rng, (rows, 2 * d), 0.0, std, dtype)
+    return dict(x=x, d=d, dtype=dtype)

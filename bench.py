@@ -14,7 +14,9 @@ again only after >= 1 GiB of other traffic), so no step is served from the
 256 MB last-level cache left warm by the step before it.
 
 Prints one JSON line (rank 0).  `--workload prefill` measures the fused
-add+RMSNorm forward + VJP at [32768, 8192] bf16 instead (not the headline).
+add+RMSNorm forward + VJP at [32768, 8192] bf16 instead (not the headline);
+`--workload gate` the gated activation silu(x[:, :d]) * x[:, d:2d] at the
+Llama-3 8B MLP width (d = 14336) in bf16, prefill chunk and decode batches.
 """
 from __future__ import annotations
 
@@ -36,15 +38,16 @@ if ROOT not in sys.path:
 METRIC = "achieved HBM GB/s (% of peak) for RMSNorm fwd+VJP, 8192x4096 fp16"
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SOURCES = ["rmsn_kernels.hpp", "rmsn_device.hpp", "rmsn_vjp.hip", "rmsn_fwd.hip", "rmsn_api.hip"]
+GATE_SOURCES = ["rmsn_gate.hip", "rmsn_device.hpp", "rmsn_api.hip"]
 
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(files=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "backward_rmsnorm_fwd_two_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -243,12 +246,110 @@ def decode_bench(R, I, dev, args) -> int:
     return 0
 
 
+def gate_bench(R, I, dev, args) -> int:
+    """Gated activation y = silu(x[:, :d]) * x[:, d:2d], bf16, d = 14336 (the
+    Llama-3 8B MLP width), x ~ N(0, 2).  Headline: the [8192, 2d] prefill
+    chunk (x 448 MiB, y 224 MiB; algorithmic bytes 3 * rows * d * s, two
+    reads and one write per output element), rotating buffer sets so that
+    each call reads cold data.  Also: per-call latency at decode batches 1,
+    4 and 8 (back-to-back prepared calls)."""
+    rows, d = 8192, 14336
+    c = I.gate(rows, d, "bfloat16")
+    s = 2
+    nbytes = 3 * rows * d * s
+    set_bytes = 3 * rows * d * s
+    nsets = args.sets or (-(-(1 << 30) // set_bytes) + 1)
+    log(f"uploading {nsets} buffer set(s) of {set_bytes / 2**20:.0f} MiB")
+    xs = [c["x"].to(dev) for _ in range(nsets)]
+    ys = [torch.empty(rows, d, dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
+    calls = [R.prepared_gate(x, y) for x, y in zip(xs, ys)]
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        calls[i % nsets]()
+    torch.cuda.synchronize()
+    SAMPLE = 10
+    nsamp = (args.steps + SAMPLE - 1) // SAMPLE
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nsamp)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev = evs[i // SAMPLE] if i % SAMPLE == 0 else None
+        if ev:
+            ev[0].record(stream)
+        calls[i % nsets]()
+        if ev:
+            ev[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    ms_per_step = wall * 1e3 / args.steps
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (k_us * 1e-6) / 1e9
+    src_hash = kernel_source_hash(GATE_SOURCES)
+    traffic = stored_traffic("gate_8192x14336_bf16", src_hash)
+    del xs, ys, calls
+
+    decode = []
+    N = max(args.steps, 200)
+    for B in (1, 4, 8):
+        cb = I.gate(B, d, "bfloat16", seed=B)
+        x = cb["x"].to(dev)
+        y = torch.empty(B, d, dtype=torch.bfloat16, device=dev)
+        fn = R.prepared_gate(x, y)
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(N):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        decode.append({"B": B, "us_per_call": round(e0.elapsed_time(e1) * 1e3 / N, 3)})
+        log(f"decode B={B}: {decode[-1]['us_per_call']} us per call")
+
+    out = {
+        "metric": "achieved HBM GB/s for the gated activation silu(x[:, :d]) * x[:, d:2d], 8192x14336 bf16",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "silu gate, x [8192, 28672] bf16 ~ N(0,2) -> y [8192, 14336]",
+                   "rows": rows, "d": d, "bytes_per_step": nbytes, "buffer_sets": nsets,
+                   "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2), "decode": decode},
+        "roofline": {"kernel": "silu_gate_kernel", "bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes": nbytes, "avg_us": round(k_us, 3)},
+        "kernel_source_hash": src_hash,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        sample = 512
+        xs_cpu = c["x"][:sample]
+        t0 = time.perf_counter()
+        passes = 0
+        while True:
+            O.silu_gate(xs_cpu)
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= 10.0 or passes >= 20:
+                break
+        out["cpu_baseline"] = {
+            "value": round(passes * 3 * sample * d * s / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{passes} pass(es) over the first {sample} of {rows} rows (d={d}), "
+                      f"fp64 C oracle incl. widening, {dt:.1f} s"}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", choices=["poc", "prefill", "decode", "grad", "ceiling"], default="poc")
+    ap.add_argument("--workload", choices=["poc", "prefill", "decode", "grad", "gate", "ceiling"],
+                    default="poc")
     ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -272,6 +373,8 @@ def main() -> int:
         return decode_bench(R, I, dev, args)
     if args.workload == "grad":
         return grad_bench(R, I, dev, args)
+    if args.workload == "gate":
+        return gate_bench(R, I, dev, args)
     fused = args.workload == "prefill"
     log(f"generating inputs ({args.workload})")
     if fused:

@@ -36,6 +36,11 @@
  *       gradient evaluation is the forward recompute plus the VJP), done in
  *       one launch: x and dy are read once, y and dx written once.
  *
+ *   silu_gate              y = silu(x[:, :d]) * x[:, d:2d],  silu(a) = a / (1 + e^-a)
+ *       The gated activation of the same mlxcel issue's candidate-fusion
+ *       list, with 16-byte loads: x is [rows, 2d] (the two halves of each row
+ *       side by side), y is [rows, d].  fp32 arithmetic, one rounding.
+ *
  * Conventions shared by every entry point:
  *   - Layout: row-major, contiguous [rows, D] tensors; w is [D].  x,
  *     residual, w, dy, y, normed, new_residual and dx all have the dtype
@@ -85,6 +90,8 @@ typedef enum {
 
 /* Largest D served (elements). */
 #define RMSN_MAX_D ((int64_t)1 << 24)
+/* Largest half width d served by silu_gate (elements). */
+#define RMSN_MAX_GATE_D ((int64_t)1 << 28)
 
 /* Kernel configuration.  Zero in a field means "choose automatically".
  * Only the *_cfg entry points take one; the plain entry points always choose
@@ -141,6 +148,13 @@ int fused_add_rmsnorm_vjp(const void *h, const void *w, const void *dy, const vo
                           int64_t rows, int64_t D, int dt,
                           float eps, float weight_bias, void *hip_stream);
 
+/* Gated activation: y[rows, d] = silu(x[:, :d]) * x[:, d:2d] for x[rows, 2d]
+ * (x and y of dtype dt, row-major, contiguous).  y must not overlap x.  No
+ * workspace.  Errors: RMSN_E_SHAPE for rows < 0, d < 1, d > RMSN_MAX_GATE_D
+ * or a size that overflows; the usual pointer, alignment and dtype codes.
+ * First-half elements below -88.7 give silu = -0 (true magnitude < 6e-37). */
+int silu_gate(const void *x, void *y, int64_t rows, int64_t d, int dt, void *hip_stream);
+
 /* The same operations with an explicit kernel configuration (NULL =
  * automatic).  For rmsnorm_vjp_cfg the workspace must hold
  * num_blocks * D * 4 bytes for the configuration actually used. */
@@ -164,6 +178,12 @@ int fused_add_rmsnorm_vjp_cfg(const void *h, const void *w, const void *dy,
                               void *workspace, size_t workspace_bytes,
                               int64_t rows, int64_t D, int dt, float eps, float weight_bias,
                               const rmsn_config_t *cfg, void *hip_stream);
+/* For silu_gate_cfg: lanes_per_row must be 0; vecs_per_lane (1, 2, 4, 8) is
+ * the number of output vectors each thread handles per chunk; num_blocks is
+ * the grid (the kernel loops over chunks of block_threads * vecs_per_lane
+ * output vectors). */
+int silu_gate_cfg(const void *x, void *y, int64_t rows, int64_t d, int dt,
+                  const rmsn_config_t *cfg, void *hip_stream);
 
 /* Operation ids for rmsn_query_config. */
 #define RMSN_OP_FWD 0
@@ -171,6 +191,7 @@ int fused_add_rmsnorm_vjp_cfg(const void *h, const void *w, const void *dy,
 #define RMSN_OP_VJP 2
 #define RMSN_OP_GRAD 3
 #define RMSN_OP_FUSED_VJP 4
+#define RMSN_OP_GATE 5      /* D is the half width d */
 
 /* Fill *out with the configuration the automatic choice makes for `op` on
  * this shape, assuming every pointer is 16-byte aligned (`align_bytes` = the

@@ -80,3 +80,35 @@ def test_oracle_never_imports_the_product():
 def test_gpu_marker_registered(pytestconfig):
     markers = pytestconfig.getini("markers")
     assert any(m.startswith("gpu") for m in markers)
+
+
+def test_gate_argument_errors_and_plan_without_gpu():
+    lib = ctypes.CDLL(LIB)
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.silu_gate.argtypes = [vp, vp, i64, i64, ctypes.c_int, vp]
+    assert lib.silu_gate(None, None, 4, 8, 2, None) == -1
+    assert lib.silu_gate(None, None, 4, 8, 9, None) == -3
+    assert lib.silu_gate(None, None, 4, 0, 2, None) == -2
+    assert lib.silu_gate(None, None, 4, (1 << 28) + 1, 2, None) == -2
+    assert lib.silu_gate(None, None, 0, 8, 2, None) == 0
+
+    class Cfg(ctypes.Structure):
+        _fields_ = [(n, ctypes.c_int32) for n in
+                    ("lanes_per_row", "vecs_per_lane", "vec_bytes", "block_threads", "num_blocks")]
+
+    lib.rmsn_query_config.argtypes = [ctypes.c_int, i64, i64, ctypes.c_int, ctypes.c_int,
+                                      ctypes.POINTER(Cfg)]
+
+    def plan(rows, d, dt, align=16):
+        c = Cfg()
+        st = lib.rmsn_query_config(5, rows, d, dt, align, ctypes.byref(c))
+        assert st == 0, st
+        return (c.lanes_per_row, c.vecs_per_lane, c.vec_bytes, c.block_threads, c.num_blocks)
+
+    # Llama-3 8B MLP width, bf16: 16-byte loads, one vector per thread,
+    # 14336 * 2 / 16 = 1792 vectors per row, 64 per chunk (one-wave blocks)
+    assert plan(8192, 14336, 2) == (0, 1, 16, 64, 8192 * 1792 // 64)
+    assert plan(1, 14336, 2) == (0, 1, 16, 64, 28)
+    # odd d in bf16: element loads; fp32 with 8-byte alignment
+    assert plan(3, 1001, 2)[2] == 2 and plan(3, 1001, 2)[1] == 8
+    assert plan(3, 1000, 0, align=8)[2] == 8
