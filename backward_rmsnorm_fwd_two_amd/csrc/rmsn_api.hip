@@ -186,6 +186,12 @@ bool overlaps(Range a, Range b) {
     return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
 }
 
+// A row output may be the very buffer of a row input (in place: same start,
+// same extent); any other overlap is refused.
+bool bad_alias(Range out, Range in) {
+    return overlaps(out, in) && !(out.lo == in.lo && out.hi == in.hi);
+}
+
 int check_common(int64_t rows, int64_t D, int dt) {
     if (dt != RMSN_F32 && dt != RMSN_F16 && dt != RMSN_BF16) return RMSN_E_DTYPE;
     if (rows < 0 || D < 1 || D > RMSN_MAX_D) return RMSN_E_SHAPE;
@@ -225,13 +231,11 @@ int fwd_impl(bool fused, const void* x, const void* res, const void* w, void* y,
     if (fused) {
         const Range rr = range_of(res, tb), rn = range_of(newres, tb);
         const Range outs[2] = {ry, rn};
-        const Range ins[3] = {rx, rr, rw};
         for (const Range& o : outs)
-            for (const Range& i : ins)
-                if (overlaps(o, i)) return RMSN_E_OVERLAP;
+            if (bad_alias(o, rx) || bad_alias(o, rr) || overlaps(o, rw)) return RMSN_E_OVERLAP;
         if (overlaps(ry, rn)) return RMSN_E_OVERLAP;
     } else {
-        if (overlaps(ry, rx) || overlaps(ry, rw)) return RMSN_E_OVERLAP;
+        if (bad_alias(ry, rx) || overlaps(ry, rw)) return RMSN_E_OVERLAP;
     }
     int align = std::min(std::min(ptr_align(x), ptr_align(w)), ptr_align(y));
     if (fused) align = std::min(align, std::min(ptr_align(res), ptr_align(newres)));
@@ -291,9 +295,12 @@ int vjp_impl(const void* x, const void* w, const void* dy, void* y, const void* 
                 ry = grad ? range_of(y, tb) : Range{0, 0},
                 rr = resgrad ? range_of(dres, tb) : Range{0, 0};
     {
-        const Range ins[4] = {rx, rw, rd, rr};
-        for (const Range& i : ins)
-            if (overlaps(rdx, i) || overlaps(rdw, i) || overlaps(ry, i)) return RMSN_E_OVERLAP;
+        // dx and y may each be exactly one of the row inputs (x, dy,
+        // d_new_residual); dw overlaps nothing
+        const Range row_ins[3] = {rx, rd, rr};
+        for (const Range& i : row_ins)
+            if (bad_alias(rdx, i) || bad_alias(ry, i) || overlaps(rdw, i)) return RMSN_E_OVERLAP;
+        if (overlaps(rdx, rw) || overlaps(ry, rw) || overlaps(rdw, rw)) return RMSN_E_OVERLAP;
         if (overlaps(rdx, rdw) || overlaps(ry, rdx) || overlaps(ry, rdw)) return RMSN_E_OVERLAP;
     }
     int align =

@@ -11,6 +11,12 @@
 //
 // The streaming kernel (rows_looped) serves any D: one block per row, two
 // passes over the row (sums, then outputs), re-reading the row.
+//
+// In place: an output may be the very buffer of a row input (y over x, dx
+// over dy, new_residual over residual, ...).  Every kernel reads all inputs
+// of an element before it writes that element's outputs, from the same
+// thread, and the first pass of rows_looped writes nothing; row pointers
+// are therefore not declared __restrict__.
 #pragma once
 
 #include "rmsn_device.hpp"
@@ -44,7 +50,7 @@ struct Cols {
 };
 
 template <typename T, int NV, int K>
-__device__ __forceinline__ void issue_row(const T* __restrict__ p, int64_t base, const Cols<K>& c,
+__device__ __forceinline__ void issue_row(const T* p, int64_t base, const Cols<K>& c,
                                           Raw<T, NV> (&dst)[K]) {
 #pragma unroll
     for (int k = 0; k < K; ++k) dst[k] = load_raw<T, NV>(p + base + c.off[k]);
@@ -101,7 +107,7 @@ __device__ __forceinline__ void fwd_process(const RowArgs& a, int64_t row0, int 
         }
     }
     if constexpr (FUSED) {
-        T* __restrict__ newres = static_cast<T*>(a.newres);
+        T* newres = static_cast<T*>(a.newres);
 #pragma unroll
         for (int k = 0; k < K; ++k)
             if (rok && c.ok[k]) store_f32<T, NV>(newres + base + c.off[k], h[k]);
@@ -116,7 +122,7 @@ __device__ __forceinline__ void fwd_process(const RowArgs& a, int64_t row0, int 
     }
     const float r = rsqrtf(ss / static_cast<float>(a.D) + a.eps);
 
-    T* __restrict__ y = static_cast<T*>(a.y);
+    T* y = static_cast<T*>(a.y);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         if (rok && c.ok[k]) {
@@ -243,7 +249,7 @@ __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int 
     const float cc = r * r * r * s2[1] * inv_d;
 
     if (rok) {
-        T* __restrict__ dx = static_cast<T*>(a.dx);
+        T* dx = static_cast<T*>(a.dx);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             float o[NV];
@@ -261,7 +267,7 @@ __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int 
         }
         if constexpr (MODE == kGrad) {
             // grad call: the forward output from the same pass over x
-            T* __restrict__ y = static_cast<T*>(a.y);
+            T* y = static_cast<T*>(a.y);
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 float o[NV];
@@ -385,13 +391,13 @@ __device__ __forceinline__ void block_sum(float (&v)[NV], float* red, int& parit
 template <typename T, int NV, int OP>
 __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
     __shared__ float red[2 * 16 * 2];
-    const T* __restrict__ x = static_cast<const T*>(a.x);
-    const T* __restrict__ res = static_cast<const T*>(a.res);
-    const T* __restrict__ w = static_cast<const T*>(a.w);
-    const T* __restrict__ dy = static_cast<const T*>(a.dy);
-    T* __restrict__ y = static_cast<T*>(a.y);
-    T* __restrict__ newres = static_cast<T*>(a.newres);
-    T* __restrict__ dx = static_cast<T*>(a.dx);
+    const T* x = static_cast<const T*>(a.x);
+    const T* res = static_cast<const T*>(a.res);
+    const T* w = static_cast<const T*>(a.w);
+    const T* dy = static_cast<const T*>(a.dy);
+    T* y = static_cast<T*>(a.y);
+    T* newres = static_cast<T*>(a.newres);
+    T* dx = static_cast<T*>(a.dx);
     float* dst = (gridDim.x == 1) ? a.dw : a.partial + (int64_t)blockIdx.x * a.D;
     const float inv_d = 1.0f / static_cast<float>(a.D);
     int parity = 0;
@@ -420,7 +426,6 @@ __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
                     const Raw<T, NV> pr = load_raw<T, NV>(res + off);
 #pragma unroll
                     for (int e = 0; e < NV; ++e) h[e] += elem(pr, e);
-                    store_f32<T, NV>(newres + off, h);
                 }
 #pragma unroll
                 for (int e = 0; e < NV; ++e) s2[0] = __builtin_fmaf(h[e], h[e], s2[0]);
@@ -474,6 +479,8 @@ __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
                 }
 #pragma unroll
                 for (int e = 0; e < NV; ++e) o[e] = h[e] * r * (a.wb + elem(pw, e));
+                // both outputs after both loads: x or residual may be overwritten
+                if constexpr (OP == 1) store_f32<T, NV>(newres + off, h);
                 store_f32<T, NV>(y + off, o);
             }
         }

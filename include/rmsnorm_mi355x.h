@@ -50,7 +50,12 @@
  *     no device memory and keeps no pointer after the call returns.  Each
  *     pointer must be aligned to its element size; wider alignment (16 B) and
  *     D * itemsize divisible by 16 select the widest loads.
- *   - Outputs must not overlap any other argument buffer (RMSN_E_OVERLAP).
+ *   - In place: a [rows, D] output may be the very buffer of a [rows, D]
+ *     input of the same call (same address, same extent) -- y over x;
+ *     normed or new_residual over x or residual; dx (dh) or y over x (h), dy
+ *     or d_new_residual.  Any other overlap -- partial, between two outputs,
+ *     with w, dw or the workspace, or any overlap for silu_gate -- returns
+ *     RMSN_E_OVERLAP.
  *   - Execution: asynchronous on `hip_stream` (a hipStream_t; NULL is the
  *     null stream).  No call synchronises.  The functions are thread-safe;
  *     one workspace must not serve two calls in flight at once.
@@ -132,8 +137,8 @@ int rmsnorm_vjp(const void *x, const void *w, const void *dy,
                 float eps, float weight_bias, void *hip_stream);
 
 /* Grad call: y (as rmsnorm_fwd), dx and dw (as rmsnorm_vjp) from one pass
- * over x and dy.  Same workspace rule as rmsnorm_vjp; y must not overlap any
- * other argument. */
+ * over x and dy.  Same workspace rule as rmsnorm_vjp; y may be x or dy in
+ * place (not dx), like dx. */
 int rmsnorm_fwd_vjp(const void *x, const void *w, const void *dy,
                     void *y, void *dx, float *dw, void *workspace, size_t workspace_bytes,
                     int64_t rows, int64_t D, int dt,

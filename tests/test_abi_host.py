@@ -112,3 +112,41 @@ def test_gate_argument_errors_and_plan_without_gpu():
     # odd d in bf16: element loads; fp32 with 8-byte alignment
     assert plan(3, 1001, 2)[2] == 2 and plan(3, 1001, 2)[1] == 8
     assert plan(3, 1000, 0, align=8)[2] == 8
+
+
+def test_in_place_alias_rules_without_gpu():
+    """Argument checks run before any device call: without a GPU, a call that
+    passes them fails at the first HIP call (-6); an overlap the rules refuse
+    returns -5.  Pointers are fake addresses (never dereferenced)."""
+    lib = ctypes.CDLL(LIB)
+    vp, i64, f32, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    lib.rmsnorm_fwd.argtypes = [vp, vp, vp, i64, i64, ci, f32, f32, vp]
+    lib.fused_add_rmsnorm_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, ci, f32, f32, vp]
+    lib.rmsnorm_fwd_vjp.argtypes = [vp] * 7 + [ctypes.c_size_t, i64, i64, ci, f32, f32, vp]
+    lib.fused_add_rmsnorm_vjp.argtypes = [vp] * 7 + [ctypes.c_size_t, i64, i64, ci, f32, f32, vp]
+    R, D = 4, 64
+    tb = R * D * 2                                   # fp16 [4, 64]
+    X, RES, W, DY, OUT, OUT2, DW, WS = (0x100000 * (i + 1) for i in range(8))
+    HIP, OVL = -6, -5
+    # forward: y over x allowed; y one row into x, or over w, refused
+    assert lib.rmsnorm_fwd(X, W, X, R, D, 1, 1e-5, 0.0, None) == HIP
+    assert lib.rmsnorm_fwd(X, W, X + 2 * D, R, D, 1, 1e-5, 0.0, None) == OVL
+    assert lib.rmsnorm_fwd(X, W, W, 1, D, 1, 1e-5, 0.0, None) == OVL
+    # fused: each output over x or residual; outputs never over each other
+    for normed, newres in ((X, RES), (RES, X), (X, OUT), (OUT, RES)):
+        assert lib.fused_add_rmsnorm_fwd(X, RES, W, normed, newres, R, D, 1, 1e-5, 0.0, None) == HIP
+    assert lib.fused_add_rmsnorm_fwd(X, RES, W, X, X, R, D, 1, 1e-5, 0.0, None) == OVL
+    assert lib.fused_add_rmsnorm_fwd(X, RES, W, OUT, OUT, R, D, 1, 1e-5, 0.0, None) == OVL
+    assert lib.fused_add_rmsnorm_fwd(X, RES, W, RES + 2, OUT, R, D, 1, 1e-5, 0.0, None) == OVL
+    # grad call: y and dx each over x or dy, not over each other, not partial
+    ws_bytes = 1 << 20
+    for y, dx in ((X, DY), (DY, X), (OUT, X), (DY, OUT2)):
+        assert lib.rmsnorm_fwd_vjp(X, W, DY, y, dx, DW, WS, ws_bytes, R, D, 1, 1e-5, 0.0, None) == HIP
+    assert lib.rmsnorm_fwd_vjp(X, W, DY, X, X, DW, WS, ws_bytes, R, D, 1, 1e-5, 0.0, None) == OVL
+    assert lib.rmsnorm_fwd_vjp(X, W, DY, OUT, DY + tb // 2, DW, WS, ws_bytes, R, D, 1, 1e-5, 0.0, None) == OVL
+    # dw never overlaps a row buffer
+    assert lib.rmsnorm_fwd_vjp(X, W, DY, OUT, OUT2, X, WS, ws_bytes, R, D, 1, 1e-5, 0.0, None) == OVL
+    # fused backward: dh over h, dy or d_new_residual
+    for dh in (X, DY, RES, OUT):
+        assert lib.fused_add_rmsnorm_vjp(X, W, DY, RES, dh, DW, WS, ws_bytes, R, D, 1, 1e-5, 0.0, None) == HIP
+    assert lib.fused_add_rmsnorm_vjp(X, W, DY, RES, RES + 64, DW, WS, ws_bytes, R, D, 1, 1e-5, 0.0, None) == OVL

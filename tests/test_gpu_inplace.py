@@ -1,0 +1,162 @@
+"""GPU: in-place calls.  An output may be the very buffer of a row input of
+the same call (y over x; normed / new_residual over x or residual; dx, dh
+and the grad call's y over x, dy or d_new_residual).  Each in-place result
+must be bit-identical to the out-of-place call on the same inputs (and that
+one is checked against the fp64 oracle), on the register kernels with one
+and several row slots per block, the streaming kernel, and small VJP grids."""
+import sys
+
+import pytest
+import torch
+
+from _parity import assert_close, assert_dw_close
+from backward_rmsnorm_fwd_two_amd import inputs as I
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+# (rows, D, dtype, cfg): auto register path, several row slots per block,
+# fp32, forced streaming kernel, automatic streaming kernel (large D)
+CASES = [
+    (37, 4096, "bfloat16", None),
+    (29, 128, "float16", dict(lanes_per_row=16, vecs_per_lane=1, vec_bytes=16, block_threads=256)),
+    (5, 1000, "float32", None),
+    (6, 5000, "bfloat16", dict(vecs_per_lane=-1, block_threads=256)),
+    (2, 70000, "bfloat16", None),
+]
+VJP_GRIDS = [None, 1, 3]
+
+
+@pytest.fixture(scope="module")
+def R():
+    import backward_rmsnorm_fwd_two_amd as pkg
+    return pkg
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _cfg(cfg, grid=None):
+    if cfg is None and grid is None:
+        return None
+    c = dict(cfg or {})
+    if grid is not None:
+        c["num_blocks"] = grid
+    return c
+
+
+def _grid(grid, rows):
+    # the streaming kernel needs a row for every block
+    return None if grid is None else min(grid, rows)
+
+
+def _case_id(c):
+    return f"{c[0]}x{c[1]}-{c[2]}-{'auto' if c[3] is None else 'forced'}"
+
+
+@pytest.mark.parametrize("case", CASES, ids=_case_id)
+def test_fwd_in_place(R, case):
+    rows, D, dtype, cfg = case
+    _say(f"in-place fwd {rows}x{D} {dtype} cfg={cfg}")
+    c = I.generic(rows, D, dtype, seed=rows + D)
+    x, w = c["x"].to(DEV), c["w"].to(DEV)
+    y = R.rmsnorm_fwd(x, w, c["eps"], 0.0, cfg=cfg)
+    xi = x.clone()
+    R.rmsnorm_fwd(xi, w, c["eps"], 0.0, out=xi, cfg=cfg)
+    torch.cuda.synchronize()
+    assert torch.equal(xi, y)
+    assert_close(y, O.rmsnorm_fwd(c["x"], c["w"], c["eps"], 0.0)[0], "y")
+
+
+@pytest.mark.parametrize("case", CASES, ids=_case_id)
+@pytest.mark.parametrize("alias", ["normed=x,newres=res", "normed=res,newres=x", "normed=x",
+                                   "newres=res", "newres=x"])
+def test_fused_in_place(R, case, alias):
+    rows, D, dtype, cfg = case
+    _say(f"in-place fused {alias} {rows}x{D} {dtype} cfg={cfg}")
+    c = I.generic(rows, D, dtype, seed=rows * 3 + D)
+    x, res, w = c["x"].to(DEV), c["residual"].to(DEV), c["w"].to(DEV)
+    normed, newres = R.fused_add_rmsnorm_fwd(x, res, w, c["eps"], 1.0, cfg=cfg)
+    xi, ri = x.clone(), res.clone()
+    bufs = {"x": xi, "res": ri}
+    outs = dict(kv.split("=") for kv in alias.split(","))
+    n_out = bufs[outs["normed"]] if "normed" in outs else torch.empty_like(x)
+    r_out = bufs[outs["newres"]] if "newres" in outs else torch.empty_like(x)
+    R.fused_add_rmsnorm_fwd(xi, ri, w, c["eps"], 1.0, normed=n_out, new_residual=r_out, cfg=cfg)
+    torch.cuda.synchronize()
+    assert torch.equal(n_out, normed), "normed differs from the out-of-place call"
+    assert torch.equal(r_out, newres), "new_residual differs from the out-of-place call"
+    nref, href = O.fused_add_rmsnorm_fwd(c["x"], c["residual"], c["w"], c["eps"], 1.0)
+    assert_close(normed, nref, "normed")
+
+
+@pytest.mark.parametrize("case", CASES, ids=_case_id)
+@pytest.mark.parametrize("grid", VJP_GRIDS)
+@pytest.mark.parametrize("alias", ["dx=x", "dx=dy"])
+def test_vjp_in_place(R, case, grid, alias):
+    rows, D, dtype, cfg = case
+    _say(f"in-place vjp {alias} grid={grid} {rows}x{D} {dtype} cfg={cfg}")
+    c = I.generic(rows, D, dtype, seed=rows * 5 + D)
+    x, w, dy = c["x"].to(DEV), c["w"].to(DEV), c["dy"].to(DEV)
+    cf = _cfg(cfg, _grid(grid, rows))
+    dx, dw = R.rmsnorm_vjp(x, w, dy, c["eps"], 0.0, cfg=cf)
+    xi, dyi = x.clone(), dy.clone()
+    out = xi if alias == "dx=x" else dyi
+    _, dwi = R.rmsnorm_vjp(xi, w, dyi, c["eps"], 0.0, dx=out, cfg=cf)
+    torch.cuda.synchronize()
+    assert torch.equal(out, dx)
+    assert torch.equal(dwi, dw)
+    dxref, dwref = O.rmsnorm_vjp(c["x"], c["w"], c["dy"], c["eps"], 0.0)
+    assert_close(dx, dxref, "dx")
+    assert_dw_close(dw, dwref)
+
+
+@pytest.mark.parametrize("case", CASES, ids=_case_id)
+@pytest.mark.parametrize("alias", ["y=x,dx=dy", "y=dy,dx=x", "y=x", "dx=dy"])
+def test_grad_call_in_place(R, case, alias):
+    rows, D, dtype, cfg = case
+    _say(f"in-place grad call {alias} {rows}x{D} {dtype} cfg={cfg}")
+    c = I.generic(rows, D, dtype, seed=rows * 7 + D)
+    x, w, dy = c["x"].to(DEV), c["w"].to(DEV), c["dy"].to(DEV)
+    y, dx, dw = R.rmsnorm_fwd_vjp(x, w, dy, c["eps"], 0.0, cfg=cfg)
+    xi, dyi = x.clone(), dy.clone()
+    bufs = {"x": xi, "dy": dyi}
+    outs = dict(kv.split("=") for kv in alias.split(","))
+    y_out = bufs[outs["y"]] if "y" in outs else torch.empty_like(x)
+    dx_out = bufs[outs["dx"]] if "dx" in outs else torch.empty_like(x)
+    _, _, dwi = R.rmsnorm_fwd_vjp(xi, w, dyi, c["eps"], 0.0, y=y_out, dx=dx_out, cfg=cfg)
+    torch.cuda.synchronize()
+    assert torch.equal(y_out, y) and torch.equal(dx_out, dx) and torch.equal(dwi, dw)
+
+
+@pytest.mark.parametrize("case", CASES, ids=_case_id)
+@pytest.mark.parametrize("alias", ["dh=h", "dh=dy", "dh=dnr"])
+def test_fused_vjp_in_place(R, case, alias):
+    rows, D, dtype, cfg = case
+    _say(f"in-place fused backward {alias} {rows}x{D} {dtype} cfg={cfg}")
+    c = I.generic(rows, D, dtype, seed=rows * 11 + D)
+    h, w, dy = c["x"].to(DEV), c["w"].to(DEV), c["dy"].to(DEV)
+    dnr = c["residual"].to(DEV)
+    dh, dw = R.fused_add_rmsnorm_vjp(h, w, dy, dnr, c["eps"], 1.0, cfg=cfg)
+    hi, dyi, dnri = h.clone(), dy.clone(), dnr.clone()
+    out = {"dh=h": hi, "dh=dy": dyi, "dh=dnr": dnri}[alias]
+    _, dwi = R.fused_add_rmsnorm_vjp(hi, w, dyi, dnri, c["eps"], 1.0, dh=out, cfg=cfg)
+    torch.cuda.synchronize()
+    assert torch.equal(out, dh) and torch.equal(dwi, dw)
+    dhref, dwref = O.fused_add_rmsnorm_vjp(c["x"], c["w"], c["dy"], c["residual"], c["eps"], 1.0)
+    assert_close(dh, dhref, "dh")
+
+
+def test_partial_overlap_refused(R):
+    x = torch.randn(8, 256, dtype=torch.float16, device=DEV)
+    w = torch.ones(256, dtype=torch.float16, device=DEV)
+    with pytest.raises(R.RMSNormError) as e:
+        R.rmsnorm_fwd(x[:4], w, out=x[1:5])
+    assert e.value.status == -5
+    with pytest.raises(R.RMSNormError) as e:
+        R.fused_add_rmsnorm_fwd(x[:4], x[4:], w, normed=x[:4], new_residual=x[:4])
+    assert e.value.status == -5

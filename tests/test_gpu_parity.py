@@ -335,13 +335,15 @@ def test_error_codes(R):
     assert lib.rmsnorm_fwd(p(x), p(w), p(y), -1, 64, 1, 1e-5, 0.0, s) == -2
     assert lib.rmsnorm_fwd(p(x), p(w), p(y), 4, 0, 1, 1e-5, 0.0, s) == -2
     assert lib.rmsnorm_fwd(p(x), p(w), p(y), 4, 64, 7, 1e-5, 0.0, s) == -3
-    assert lib.rmsnorm_fwd(p(x), p(w), p(x), 4, 64, 1, 1e-5, 0.0, s) == -5
+    # y one row into x: a partial overlap (y == x exactly would be in place)
+    assert lib.rmsnorm_fwd(p(x), p(w), p(x) + 128, 3, 64, 1, 1e-5, 0.0, s) == -5
     assert lib.rmsnorm_fwd(p(x) + 1, p(w), p(y), 2, 64, 1, 1e-5, 0.0, s) == -7
     dx = torch.empty_like(x)
     dw = torch.empty(64, dtype=torch.float32, device=DEV)
     assert lib.rmsnorm_vjp(p(x), p(w), p(x), p(dx), p(dw), None, 0, 4, 64, 1, 1e-5, 0.0, s) == -4 or \
         R.rmsnorm_vjp_workspace_bytes(4, 64, torch.float16) <= 256
-    assert lib.rmsnorm_vjp(p(x), p(w), p(x), p(x), p(dw), None, 0, 4, 64, 1, 1e-5, 0.0, s) == -5
+    assert lib.rmsnorm_vjp(p(x), p(w), p(x), p(x) + 128, p(dw), None, 0, 3, 64, 1, 1e-5, 0.0, s) == -5
+    assert lib.rmsnorm_vjp(p(x), p(w), p(x), p(dx), p(x), None, 0, 4, 64, 1, 1e-5, 0.0, s) == -5
     assert lib.rmsnorm_vjp(p(x), p(w), p(x), p(dx), None, None, 0, 4, 64, 1, 1e-5, 0.0, s) == -1
     # a workspace smaller than the plan needs is refused before any launch
     x2 = torch.zeros(8192, 64, dtype=torch.float16, device=DEV)
@@ -460,7 +462,7 @@ def test_grad_call_rows_zero_and_errors(R):
     lib = R.raw
     assert lib.rmsnorm_fwd_vjp(p(x), p(w), p(x), None, p(dx), p(dwv), None, 0, 4, 64, 1, 1e-5, 0.0, s) == -1
     assert lib.rmsnorm_fwd_vjp(p(x), p(w), p(x), p(dx), p(dx), p(dwv), None, 0, 4, 64, 1, 1e-5, 0.0, s) == -5
-    assert lib.rmsnorm_fwd_vjp(p(x), p(w), p(x), p(x), p(dx), p(dwv), None, 0, 4, 64, 1, 1e-5, 0.0, s) == -5
+    assert lib.rmsnorm_fwd_vjp(p(x), p(w), p(x), p(x) + 128, p(dx), p(dwv), None, 0, 3, 64, 1, 1e-5, 0.0, s) == -5
     torch.cuda.synchronize()
 
 
