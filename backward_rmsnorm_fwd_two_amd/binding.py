@@ -74,6 +74,8 @@ _lib.fused_add_rmsnorm_vjp.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _
                                        _f32, _vp]
 _lib.fused_add_rmsnorm_vjp_cfg.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _int,
                                            _f32, _f32, _cfgp, _vp]
+_lib.rmsnorm_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _sz, _i64, _i64, _int,
+                                  _f32, _f32, _cfgp, _vp]
 _lib.silu_gate.argtypes = [_vp, _vp, _i64, _i64, _int, _vp]
 _lib.silu_gate_cfg.argtypes = [_vp, _vp, _i64, _i64, _int, _cfgp, _vp]
 _lib.rmsn_query_config.argtypes = [_int, _i64, _i64, _int, _int, _cfgp]
@@ -82,7 +84,7 @@ _lib.rmsn_status_str.restype = ctypes.c_char_p
 for _name in ("rmsnorm_fwd", "rmsnorm_fwd_cfg", "fused_add_rmsnorm_fwd", "fused_add_rmsnorm_fwd_cfg",
               "rmsnorm_vjp", "rmsnorm_vjp_cfg", "rmsnorm_fwd_vjp", "rmsnorm_fwd_vjp_cfg",
               "fused_add_rmsnorm_vjp", "fused_add_rmsnorm_vjp_cfg", "silu_gate", "silu_gate_cfg",
-              "rmsn_query_config"):
+              "rmsnorm_backward", "rmsn_query_config"):
     getattr(_lib, _name).restype = _int
 
 raw = _lib  # the C functions themselves (pointer-level access for tests)
@@ -366,6 +368,48 @@ def prepared_grad(x, w, dy, y, dx, dw, workspace, eps, weight_bias):
     return prepare("rmsnorm_fwd_vjp", x.data_ptr(), w.data_ptr(), dy.data_ptr(), y.data_ptr(),
                    dx.data_ptr(), dw.data_ptr(), workspace.data_ptr(), nbytes, rows, D, _dt(x),
                    float(eps), float(weight_bias), _stream(x))
+
+
+def rmsnorm_backward(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, eps: float = 1e-5,
+                     weight_bias: float = 0.0, d_new_residual: Optional[torch.Tensor] = None,
+                     y: Optional[torch.Tensor] = None, dx: Optional[torch.Tensor] = None,
+                     dw: Optional[torch.Tensor] = None, dw_dtype: Optional[torch.dtype] = None,
+                     want_y: bool = False, workspace: Optional[torch.Tensor] = None,
+                     cfg=None) -> Tuple[Optional[torch.Tensor], torch.Tensor, torch.Tensor]:
+    """The general backward: returns (y or None, dx, dw).  `d_new_residual`
+    selects the fused backward (x is then h), `y` / `want_y` the grad call;
+    `dw_dtype` is torch.float32 (default) or x's dtype."""
+    dt = _dt(x)
+    rows, D = _rows_d(x)
+    dw_dtype = torch.float32 if dw_dtype is None else dw_dtype
+    if dw_dtype not in (torch.float32, x.dtype):
+        raise ValueError(f"dw_dtype must be torch.float32 or {x.dtype}")
+    _req(x, "x", x.dtype, x.device)
+    _req(w, "w", x.dtype, x.device, D)
+    _req(dy, "dy", x.dtype, x.device, x.numel())
+    if d_new_residual is not None:
+        _req(d_new_residual, "d_new_residual", x.dtype, x.device, x.numel())
+    if y is None and want_y:
+        y = torch.empty_like(x)
+    if y is not None:
+        _req(y, "y", x.dtype, x.device, x.numel())
+    if dx is None:
+        dx = torch.empty_like(x)
+    if dw is None:
+        dw = torch.empty(D, dtype=dw_dtype, device=x.device)
+    _req(dx, "dx", x.dtype, x.device, x.numel())
+    _req(dw, "dw", dw_dtype, x.device, D)
+    if workspace is None:
+        workspace = workspace_for(rows, D, x.dtype, x.device, cfg)
+    _req(workspace, "workspace", workspace.dtype, x.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = _lib.rmsnorm_backward(x.data_ptr(), w.data_ptr(), dy.data_ptr(),
+                               None if d_new_residual is None else d_new_residual.data_ptr(),
+                               None if y is None else y.data_ptr(), dx.data_ptr(), dw.data_ptr(),
+                               _DT[dw_dtype], workspace.data_ptr(), nbytes, rows, D, dt, float(eps),
+                               float(weight_bias), _cfg(cfg), _stream(x))
+    _check(st, "rmsnorm_backward")
+    return y, dx, dw
 
 
 def silu_gate(x: torch.Tensor, out: Optional[torch.Tensor] = None, cfg=None) -> torch.Tensor:

@@ -260,25 +260,32 @@ int fwd_impl(bool fused, const void* x, const void* res, const void* w, void* y,
     return launch(fn, p, a, static_cast<hipStream_t>(stream));
 }
 
-// Workspace bytes for a plan (fp32 partial rows when the grid has > 1 block).
-size_t ws_bytes(const Plan& p, int64_t D) {
-    return p.grid > 1 ? static_cast<size_t>(p.grid) * static_cast<size_t>(D) * sizeof(float) : 0;
+// Workspace bytes for a plan: fp32 partial rows when the grid has > 1
+// block; with dw in the weight dtype also for a one-block grid (the fp32
+// sum is staged there and rounded by the combine).
+size_t ws_bytes(const Plan& p, int64_t D, bool typed_dw = false) {
+    const int64_t nrows = p.grid > 1 ? p.grid : (typed_dw ? 1 : 0);
+    return static_cast<size_t>(nrows) * static_cast<size_t>(D) * sizeof(float);
 }
 
 // y != nullptr: the grad call (forward output too); dres != nullptr: the
-// fused backward (dx += d_new_residual); neither: the VJP.
+// fused backward (dx += d_new_residual); neither: the VJP.  dw has dtype
+// dw_dt: fp32, or dt (rounded once from the fp32 sum).
 int vjp_impl(const void* x, const void* w, const void* dy, void* y, const void* dres, void* dx,
-             float* dw, void* ws, size_t ws_size, int64_t rows, int64_t D, int dt, float eps,
-             float wb, const rmsn_config_t* cfg, void* stream) {
+             void* dw, int dw_dt, void* ws, size_t ws_size, int64_t rows, int64_t D, int dt,
+             float eps, float wb, const rmsn_config_t* cfg, void* stream) {
     int st = check_common(rows, D, dt);
     if (st != RMSN_OK) return st;
+    if (dw_dt != RMSN_F32 && dw_dt != dt) return RMSN_E_DTYPE;
+    const bool typed_dw = dw_dt != RMSN_F32;
+    const int dws = itemsize(dw_dt);
     if (!dw) return RMSN_E_NULLPTR;
-    if (!elem_aligned(dw, 4)) return RMSN_E_ALIGN;
+    if (!elem_aligned(dw, dws)) return RMSN_E_ALIGN;
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     if (rows == 0) {
         void* args[] = {&dw, &D};
         const unsigned g = static_cast<unsigned>(std::min<int64_t>((D + 255) / 256, 1024));
-        if (hipLaunchKernel(rmsn::zero_kernel(), dim3(g), dim3(256), args, 0, hs) != hipSuccess)
+        if (hipLaunchKernel(rmsn::zero_kernel(dw_dt), dim3(g), dim3(256), args, 0, hs) != hipSuccess)
             return RMSN_E_HIP;
         return RMSN_OK;
     }
@@ -291,7 +298,7 @@ int vjp_impl(const void* x, const void* w, const void* dy, void* y, const void* 
         return RMSN_E_ALIGN;
     const int64_t tb = rows * D * s;
     const Range rx = range_of(x, tb), rw = range_of(w, D * s), rd = range_of(dy, tb),
-                rdx = range_of(dx, tb), rdw = range_of(dw, D * 4),
+                rdx = range_of(dx, tb), rdw = range_of(dw, D * dws),
                 ry = grad ? range_of(y, tb) : Range{0, 0},
                 rr = resgrad ? range_of(dres, tb) : Range{0, 0};
     {
@@ -310,7 +317,7 @@ int vjp_impl(const void* x, const void* w, const void* dy, void* y, const void* 
     Plan p;
     st = make_plan(RMSN_OP_VJP, rows, D, dt, align, cfg, &p);
     if (st != RMSN_OK) return st;
-    const size_t need = ws_bytes(p, D);
+    const size_t need = ws_bytes(p, D, typed_dw);
     if (need > 0) {
         if (!ws || ws_size < need) return RMSN_E_WORKSPACE;
         if (reinterpret_cast<uintptr_t>(ws) % 16 != 0) return RMSN_E_ALIGN;
@@ -331,20 +338,22 @@ int vjp_impl(const void* x, const void* w, const void* dy, void* y, const void* 
     a.res = dres;
     a.dx = dx;
     a.partial = static_cast<float*>(ws);
-    a.dw = dw;
+    // a one-block grid writes the fp32 sum straight to dw, or, for a dw in
+    // the weight dtype, to the workspace for the combine to round
+    a.dw = typed_dw ? static_cast<float*>(ws) : static_cast<float*>(dw);
     a.rows = rows;
     a.D = static_cast<int32_t>(D);
     a.eps = eps;
     a.wb = wb;
     st = launch(fn, p, a, hs);
-    if (st != RMSN_OK || p.grid == 1) return st;
+    if (st != RMSN_OK || (p.grid == 1 && !typed_dw)) return st;
 
     const float* partial = static_cast<const float*>(ws);
     int nb = static_cast<int>(p.grid);
     int d32 = static_cast<int>(D);
     void* cargs[] = {&partial, &dw, &nb, &d32};
     const unsigned cg = static_cast<unsigned>((D + 15) / 16);
-    if (hipLaunchKernel(rmsn::dw_combine_kernel(), dim3(cg), dim3(256), cargs, 0, hs) != hipSuccess)
+    if (hipLaunchKernel(rmsn::dw_combine_kernel(dw_dt), dim3(cg), dim3(256), cargs, 0, hs) != hipSuccess)
         return RMSN_E_HIP;
     return RMSN_OK;
 }
@@ -479,7 +488,7 @@ size_t rmsnorm_vjp_workspace_bytes(int64_t rows, int64_t D, int dt) {
         for (int align = 16; align >= itemsize(dt); align >>= 1) {
             Plan p;
             if (make_plan(RMSN_OP_VJP, rows, D, dt, align, nullptr, &p) != RMSN_OK) return 0;
-            best = std::max(best, ws_bytes(p, D));
+            best = std::max(best, ws_bytes(p, D, /*typed_dw=*/true));
         }
     }
     return std::max<size_t>(best, 256);
@@ -488,7 +497,7 @@ size_t rmsnorm_vjp_workspace_bytes(int64_t rows, int64_t D, int dt) {
 int rmsnorm_vjp(const void* x, const void* w, const void* dy, void* dx, float* dw, void* workspace,
                 size_t workspace_bytes, int64_t rows, int64_t D, int dt, float eps, float weight_bias,
                 void* hip_stream) {
-    return vjp_impl(x, w, dy, nullptr, nullptr, dx, dw, workspace, workspace_bytes, rows, D, dt, eps,
+    return vjp_impl(x, w, dy, nullptr, nullptr, dx, dw, RMSN_F32, workspace, workspace_bytes, rows, D, dt, eps,
                     weight_bias, nullptr, hip_stream);
 }
 
@@ -496,7 +505,7 @@ int rmsnorm_fwd_vjp(const void* x, const void* w, const void* dy, void* y, void*
                     void* workspace, size_t workspace_bytes, int64_t rows, int64_t D, int dt,
                     float eps, float weight_bias, void* hip_stream) {
     if (rows > 0 && !y) return RMSN_E_NULLPTR;
-    return vjp_impl(x, w, dy, rows > 0 ? y : nullptr, nullptr, dx, dw, workspace, workspace_bytes, rows, D,
+    return vjp_impl(x, w, dy, rows > 0 ? y : nullptr, nullptr, dx, dw, RMSN_F32, workspace, workspace_bytes, rows, D,
                     dt, eps, weight_bias, nullptr, hip_stream);
 }
 
@@ -504,14 +513,14 @@ int rmsnorm_fwd_vjp_cfg(const void* x, const void* w, const void* dy, void* y, v
                         void* workspace, size_t workspace_bytes, int64_t rows, int64_t D, int dt,
                         float eps, float weight_bias, const rmsn_config_t* cfg, void* hip_stream) {
     if (rows > 0 && !y) return RMSN_E_NULLPTR;
-    return vjp_impl(x, w, dy, rows > 0 ? y : nullptr, nullptr, dx, dw, workspace, workspace_bytes, rows, D,
+    return vjp_impl(x, w, dy, rows > 0 ? y : nullptr, nullptr, dx, dw, RMSN_F32, workspace, workspace_bytes, rows, D,
                     dt, eps, weight_bias, cfg, hip_stream);
 }
 
 int rmsnorm_vjp_cfg(const void* x, const void* w, const void* dy, void* dx, float* dw,
                     void* workspace, size_t workspace_bytes, int64_t rows, int64_t D, int dt,
                     float eps, float weight_bias, const rmsn_config_t* cfg, void* hip_stream) {
-    return vjp_impl(x, w, dy, nullptr, nullptr, dx, dw, workspace, workspace_bytes, rows, D, dt, eps,
+    return vjp_impl(x, w, dy, nullptr, nullptr, dx, dw, RMSN_F32, workspace, workspace_bytes, rows, D, dt, eps,
                     weight_bias, cfg, hip_stream);
 }
 
@@ -519,7 +528,7 @@ int fused_add_rmsnorm_vjp(const void* h, const void* w, const void* dy, const vo
                           void* dh, float* dw, void* workspace, size_t workspace_bytes, int64_t rows,
                           int64_t D, int dt, float eps, float weight_bias, void* hip_stream) {
     if (rows > 0 && !d_new_residual) return RMSN_E_NULLPTR;
-    return vjp_impl(h, w, dy, nullptr, rows > 0 ? d_new_residual : nullptr, dh, dw, workspace,
+    return vjp_impl(h, w, dy, nullptr, rows > 0 ? d_new_residual : nullptr, dh, dw, RMSN_F32, workspace,
                     workspace_bytes, rows, D, dt, eps, weight_bias, nullptr, hip_stream);
 }
 
@@ -528,8 +537,17 @@ int fused_add_rmsnorm_vjp_cfg(const void* h, const void* w, const void* dy,
                               size_t workspace_bytes, int64_t rows, int64_t D, int dt, float eps,
                               float weight_bias, const rmsn_config_t* cfg, void* hip_stream) {
     if (rows > 0 && !d_new_residual) return RMSN_E_NULLPTR;
-    return vjp_impl(h, w, dy, nullptr, rows > 0 ? d_new_residual : nullptr, dh, dw, workspace,
+    return vjp_impl(h, w, dy, nullptr, rows > 0 ? d_new_residual : nullptr, dh, dw, RMSN_F32, workspace,
                     workspace_bytes, rows, D, dt, eps, weight_bias, cfg, hip_stream);
+}
+
+int rmsnorm_backward(const void* x, const void* w, const void* dy, const void* d_new_residual,
+                     void* y, void* dx, void* dw, int dw_dt, void* workspace,
+                     size_t workspace_bytes, int64_t rows, int64_t D, int dt, float eps,
+                     float weight_bias, const rmsn_config_t* cfg, void* hip_stream) {
+    if (y && d_new_residual) return RMSN_E_CONFIG;  // no kernel computes both
+    return vjp_impl(x, w, dy, rows > 0 ? y : nullptr, rows > 0 ? d_new_residual : nullptr, dx, dw,
+                    dw_dt, workspace, workspace_bytes, rows, D, dt, eps, weight_bias, cfg, hip_stream);
 }
 
 int rmsn_query_config(int op, int64_t rows, int64_t D, int dt, int align_bytes, rmsn_config_t* out) {

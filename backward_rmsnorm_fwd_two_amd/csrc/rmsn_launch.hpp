@@ -34,10 +34,11 @@ const void* fwd_kernel(int dt, int nv, int k, bool fused);
 // mode: 0 VJP, 1 grad call (also writes y), 2 fused backward (adds the
 // residual-stream gradient).
 const void* vjp_kernel(int dt, int nv, int k, int mode);
-const void* dw_combine_kernel();
+// dw_dt: dtype of dw (fp32, or the weight dtype).
+const void* dw_combine_kernel(int dw_dt);
 // Gated activation silu(x[:, :d]) * x[:, d:2d]: NV elements per load, U
 // output vectors per thread per chunk.
 const void* gate_kernel(int dt, int nv, int u);
-const void* zero_kernel();
+const void* zero_kernel(int dw_dt);
 
 }  // namespace rmsn

@@ -3,15 +3,17 @@
 
 namespace rmsn {
 
-// dw[j] = sum_b partial[b, j] for b = 0 .. nb-1, in a fixed order.  Block:
-// 256 threads = 4 column quads (16 columns) x 64 row groups.  Row group g
-// sums rows g, g + 64, g + 128, ... (loads issued 8 at a time, added in row
-// order); a fixed LDS tree then joins the 64 group sums.
+// dw[j] = sum_b partial[b, j] for b = 0 .. nb-1, in a fixed order, stored
+// as TO (fp32, or the weight dtype rounded once).  Block: 256 threads = 4
+// column quads (16 columns) x 64 row groups.  Row group g sums rows g,
+// g + 64, g + 128, ... (loads issued 8 at a time, added in row order); a
+// fixed LDS tree then joins the 64 group sums.
 constexpr int kCombineGroups = 64;
 constexpr int kCombineBatch = 8;
 
+template <typename TO>
 __global__ __launch_bounds__(256) void dw_combine(const float* __restrict__ partial,
-                                                  float* __restrict__ dw, int nb, int D) {
+                                                  TO* __restrict__ dw, int nb, int D) {
     __shared__ float buf[kCombineGroups][17];
     const int cq = threadIdx.x & 3;
     const int rg = threadIdx.x >> 2;
@@ -54,14 +56,15 @@ __global__ __launch_bounds__(256) void dw_combine(const float* __restrict__ part
     if (rg == 0) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            if (col0 + e < D) dw[col0 + e] = buf[0][cq * 4 + e];
+            if (col0 + e < D) dw[col0 + e] = from_f32<TO>(buf[0][cq * 4 + e]);
     }
 }
 
-__global__ __launch_bounds__(256) void zero_f32(float* __restrict__ p, int64_t n) {
+template <typename TO>
+__global__ __launch_bounds__(256) void zero_fill(TO* __restrict__ p, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = 0.0f;
+        p[i] = from_f32<TO>(0.0f);
 }
 
 namespace {
@@ -112,7 +115,22 @@ const void* vjp_kernel(int dt, int nv, int k, int mode) {
     }
 }
 
-const void* dw_combine_kernel() { return reinterpret_cast<const void*>(&dw_combine); }
-const void* zero_kernel() { return reinterpret_cast<const void*>(&zero_f32); }
+const void* dw_combine_kernel(int dw_dt) {
+    switch (dw_dt) {
+        case kF32: return reinterpret_cast<const void*>(&dw_combine<float>);
+        case kF16: return reinterpret_cast<const void*>(&dw_combine<_Float16>);
+        case kBF16: return reinterpret_cast<const void*>(&dw_combine<__bf16>);
+        default: return nullptr;
+    }
+}
+
+const void* zero_kernel(int dw_dt) {
+    switch (dw_dt) {
+        case kF32: return reinterpret_cast<const void*>(&zero_fill<float>);
+        case kF16: return reinterpret_cast<const void*>(&zero_fill<_Float16>);
+        case kBF16: return reinterpret_cast<const void*>(&zero_fill<__bf16>);
+        default: return nullptr;
+    }
+}
 
 }  // namespace rmsn

@@ -122,9 +122,11 @@ int fused_add_rmsnorm_fwd(const void *x, const void *residual, const void *w,
                           int64_t rows, int64_t D, int dt,
                           float eps, float weight_bias, void *hip_stream);
 
-/* Bytes of workspace rmsnorm_vjp needs for this shape on the current device
- * (fp32 dw partials, [num_blocks, D], num_blocks bounded independently of
- * rows).  0 for invalid arguments.  Never more than 2048 * D * 4 + 256. */
+/* Bytes of workspace rmsnorm_vjp (and every backward entry point, including
+ * rmsnorm_backward with dw in the weight dtype) needs for this shape on the
+ * current device: fp32 dw partials, [num_blocks, D] with num_blocks bounded
+ * independently of rows (at least one row).  0 for invalid arguments.  Never
+ * more than 2048 * D * 4 + 256. */
 size_t rmsnorm_vjp_workspace_bytes(int64_t rows, int64_t D, int dt);
 
 /* dx[rows, D] (dtype dt) and dw[D] (fp32, overwritten).  `workspace` is
@@ -159,6 +161,24 @@ int fused_add_rmsnorm_vjp(const void *h, const void *w, const void *dy, const vo
  * or a size that overflows; the usual pointer, alignment and dtype codes.
  * First-half elements below -88.7 give silu = -0 (true magnitude < 6e-37). */
 int silu_gate(const void *x, void *y, int64_t rows, int64_t d, int dt, void *hip_stream);
+
+/* General backward, one entry point for the three backward forms and the
+ * weight-gradient dtype: the VJP (y and d_new_residual NULL), the grad call
+ * (y non-NULL, as rmsnorm_fwd_vjp) or the fused backward (d_new_residual
+ * non-NULL, as fused_add_rmsnorm_vjp; x is then h).  dw has dtype dw_dt:
+ * RMSN_F32, or dt -- the weight's dtype, the fp32 sum rounded once to
+ * nearest even (the MLX pull request above prices its gw temporary at the
+ * input's itemsize in "Proposed changes", i.e. its gw is in the storage
+ * dtype).  y and d_new_residual together return
+ * RMSN_E_CONFIG; another dw_dt returns RMSN_E_DTYPE.  Workspace: at least
+ * rmsnorm_vjp_workspace_bytes(rows, D, dt) (or, with cfg, num_blocks * D * 4,
+ * and D * 4 for a one-block grid with dw in the weight dtype).  cfg may be
+ * NULL. */
+int rmsnorm_backward(const void *x, const void *w, const void *dy, const void *d_new_residual,
+                     void *y, void *dx, void *dw, int dw_dt,
+                     void *workspace, size_t workspace_bytes,
+                     int64_t rows, int64_t D, int dt, float eps, float weight_bias,
+                     const rmsn_config_t *cfg, void *hip_stream);
 
 /* The same operations with an explicit kernel configuration (NULL =
  * automatic).  For rmsnorm_vjp_cfg the workspace must hold
