@@ -164,6 +164,8 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8
 constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16
+constexpr int kDppRowRor4 = 0x124;    // rotate right by 4 within 16
+constexpr int kDppRowRor8 = 0x128;    // rotate right by 8 within 16
 
 __device__ __forceinline__ float wave_sum(float v);
 

@@ -6,17 +6,19 @@ namespace rmsn {
 // dw[j] = sum_b partial[b, j] for b = 0 .. nb-1, in a fixed order, stored
 // as TO (fp32, or the weight dtype rounded once).  Block: 256 threads = 4
 // column quads (16 columns) x 64 row groups.  Row group g sums rows g,
-// g + 64, g + 128, ... (loads issued 8 at a time, added in row order); a
-// fixed LDS tree then joins the 64 group sums.
+// g + 64, g + 128, ... (loads issued 8 at a time, added in row order); the
+// 16 row groups of a wave are joined with DPP row rotations, a swizzle and a
+// bpermute, and the four wave sums through LDS behind one barrier.
 constexpr int kCombineGroups = 64;
 constexpr int kCombineBatch = 8;
 
 template <typename TO>
 __global__ __launch_bounds__(256) void dw_combine(const float* __restrict__ partial,
                                                   TO* __restrict__ dw, int nb, int D) {
-    __shared__ float buf[kCombineGroups][17];
+    __shared__ float buf[4][16];
     const int cq = threadIdx.x & 3;
     const int rg = threadIdx.x >> 2;
+    const int wave = threadIdx.x >> 6;
     const int col0 = blockIdx.x * 16 + cq * 4;
     const bool vec = (D & 3) == 0;
     float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -43,20 +45,24 @@ __global__ __launch_bounds__(256) void dw_combine(const float* __restrict__ part
 #pragma unroll
             for (int e = 0; e < 4; ++e) s[e] += v[u][e];
     }
+    // the wave's 16 row groups: lanes l, l+4, l+8, l+12 of each 16-lane row
+    // (DPP rotations), then the four rows of the wave
 #pragma unroll
-    for (int e = 0; e < 4; ++e) buf[rg][cq * 4 + e] = s[e];
-    __syncthreads();
-    for (int st = kCombineGroups / 2; st >= 1; st >>= 1) {
-        if (rg < st) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) buf[rg][cq * 4 + e] += buf[rg + st][cq * 4 + e];
-        }
-        __syncthreads();
+    for (int e = 0; e < 4; ++e) {
+        s[e] += dpp_move<kDppRowRor4>(s[e]);
+        s[e] += dpp_move<kDppRowRor8>(s[e]);
+        s[e] = xor16_add(s[e]);
+        s[e] = xor32_add(s[e]);
     }
-    if (rg == 0) {
+    if ((threadIdx.x & 63) < 4) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (col0 + e < D) dw[col0 + e] = from_f32<TO>(buf[0][cq * 4 + e]);
+        for (int e = 0; e < 4; ++e) buf[wave][cq * 4 + e] = s[e];
+    }
+    __syncthreads();
+    if (threadIdx.x < 16) {
+        const int col = blockIdx.x * 16 + threadIdx.x;
+        const float t = (buf[0][threadIdx.x] + buf[1][threadIdx.x]) + (buf[2][threadIdx.x] + buf[3][threadIdx.x]);
+        if (col < D) dw[col] = from_f32<TO>(t);
     }
 }
 
