@@ -267,20 +267,18 @@ def gate_bench(R, I, dev, args) -> int:
     for i in range(args.warmup):
         calls[i % nsets]()
     torch.cuda.synchronize()
-    SAMPLE = 10
-    nsamp = (args.steps + SAMPLE - 1) // SAMPLE
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nsamp)]
+    # the timed region holds only gate launches: one event pair around it
+    # (on the launch stream) gives the kernel's average launch duration
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
+    g0.record(stream)
     for i in range(args.steps):
-        ev = evs[i // SAMPLE] if i % SAMPLE == 0 else None
-        if ev:
-            ev[0].record(stream)
         calls[i % nsets]()
-        if ev:
-            ev[1].record(stream)
+    g1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    k_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    k_us = g0.elapsed_time(g1) * 1e3 / args.steps
     ms_per_step = wall * 1e3 / args.steps
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (k_us * 1e-6) / 1e9
@@ -317,7 +315,8 @@ def gate_bench(R, I, dev, args) -> int:
                    "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2), "decode": decode},
         "roofline": {"kernel": "silu_gate_kernel", "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "algorithmic_bytes": nbytes, "avg_us": round(k_us, 3)},
+                     "traffic": traffic, "algorithmic_bytes": nbytes, "avg_us": round(k_us, 3),
+                     "method": "events around the whole timed region / steps"},
         "kernel_source_hash": src_hash,
     }
     if not args.no_cpu_baseline:
@@ -481,18 +480,24 @@ def main() -> int:
                  "fused_vjp_with_residual_grad_GBps": round(rg_bytes / t_rg / 1e9, 1)}
         del dr
 
-    # The VJP alone (not preceded by the forward on the same buffers, so
-    # none of x is left in the last-level cache by the forward): reported
-    # beside the in-step figure.
-    iso = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(100)]
-    for i in range(100):
-        iso[i][0].record(stream)
+    # The VJP's launch duration for the roofline: one event pair (on the
+    # stream the kernels run on) around 100 back-to-back VJP calls that
+    # rotate through the buffer sets like the timed steps.  Per-call event
+    # records cost the GPU a few microseconds each, so the sampled in-step
+    # figures above run high; this one agrees with the kernel trace's
+    # vjp_rows + dw_combine averages.
+    NB = 100
+    for i in range(3):
         v_calls[i % nsets]()
-        iso[i][1].record(stream)
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b0.record(stream)
+    for i in range(NB):
+        v_calls[i % nsets]()
+    b1.record(stream)
     torch.cuda.synchronize()
-    vjp_iso_us = float(np.mean([a.elapsed_time(b) for a, b in iso])) * 1e3
+    vjp_b2b_us = b0.elapsed_time(b1) * 1e3 / NB
 
-    vjp_avg_s = float(vjp_ms.mean()) * 1e-3
+    vjp_avg_s = vjp_b2b_us * 1e-6
     vjp_gbps = vjp_bytes / vjp_avg_s / 1e9
     src_hash = kernel_source_hash()
     prof_name = ("vjp_prefill_32768x8192_bf16" if fused else "vjp_poc_8192x4096_fp16")
@@ -530,6 +535,7 @@ def main() -> int:
             "traffic": traffic,
             "algorithmic_bytes": vjp_bytes,
             "avg_us": round(vjp_avg_s * 1e6, 3),
+            "method": "events around 100 back-to-back VJP calls on the bench stream, after the timed region",
         },
         "ops_event_us": {
             "fwd_mean": round(float(fwd_ms.mean()) * 1e3, 3),
@@ -539,8 +545,8 @@ def main() -> int:
             "step_mean": round(float(step_ms.mean()) * 1e3, 3),
             "sampled_steps": int(len(evs)),
             "fwd_GBps": round(fwd_bytes / (float(fwd_ms.mean()) * 1e-3) / 1e9, 1),
-            "vjp_alone_mean": round(vjp_iso_us, 3),
-            "vjp_alone_GBps": round(vjp_bytes / (vjp_iso_us * 1e-6) / 1e9, 1),
+            "vjp_back_to_back": round(vjp_b2b_us, 3),
+            "note": "fwd_*/vjp_*/step_* carry per-call event overhead; the roofline uses vjp_back_to_back",
         },
         "copy_ceiling_GBps": round(ceiling, 1),
         **extra,
