@@ -354,8 +354,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(rows shard across GPUs with one dw all-reduce; see the design notes). "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(rows would shard across GPUs with one all-reduce of dw). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
     if args.workload == "ceiling":
