@@ -586,8 +586,8 @@ const char* rmsn_status_str(int status) {
     switch (status) {
         case RMSN_OK: return "ok";
         case RMSN_E_NULLPTR: return "a required pointer is NULL";
-        case RMSN_E_SHAPE: return "invalid shape (rows < 0, D < 1 or D too large)";
-        case RMSN_E_DTYPE: return "unknown dtype";
+        case RMSN_E_SHAPE: return "invalid shape (rows < 0, D < 1, D too large or sizes overflow)";
+        case RMSN_E_DTYPE: return "unknown dtype, or a dw dtype other than fp32 and the storage dtype";
         case RMSN_E_WORKSPACE: return "workspace missing or too small";
         case RMSN_E_OVERLAP: return "an output overlaps another argument";
         case RMSN_E_HIP: return "HIP runtime error";

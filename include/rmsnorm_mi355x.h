@@ -13,9 +13,10 @@
  *   fused_add_rmsnorm_fwd  new_residual = x + residual,
  *                          normed = rmsnorm(x + residual)
  *       Same mlxcel issue, FusedAddRMSNorm bullet and the paragraph on the
- *       two-output constraint: two separate outputs, no in-place update.  The
- *       sum is formed once in fp32 and normalised unrounded; new_residual is
- *       that sum rounded to the storage dtype.
+ *       two-output constraint: two separate outputs (which may also be placed
+ *       over the inputs, see "In place" below).  The sum is formed once in
+ *       fp32 and normalised unrounded; new_residual is that sum rounded to the
+ *       storage dtype.
  *
  *   rmsnorm_vjp            dx, dw for an upstream gradient dy of y
  *       MLX pull request above, sections "Proposed changes" and "POC": the
@@ -36,6 +37,9 @@
  *       gradient evaluation is the forward recompute plus the VJP), done in
  *       one launch: x and dy are read once, y and dx written once.
  *
+ *   rmsnorm_backward       the three backward forms above through one call,
+ *                          with dw in fp32 or in the weight dtype
+ *
  *   silu_gate              y = silu(x[:, :d]) * x[:, d:2d],  silu(a) = a / (1 + e^-a)
  *       The gated activation of the same mlxcel issue's candidate-fusion
  *       list, with 16-byte loads: x is [rows, 2d] (the two halves of each row
@@ -44,8 +48,9 @@
  * Conventions shared by every entry point:
  *   - Layout: row-major, contiguous [rows, D] tensors; w is [D].  x,
  *     residual, w, dy, y, normed, new_residual and dx all have the dtype
- *     `dt`; dw is always fp32.  Arithmetic is fp32 throughout, rounded once
- *     (to nearest, ties to even) on store.
+ *     `dt`; dw is fp32 (rmsnorm_backward can also return it in `dt`).
+ *     Arithmetic is fp32 throughout, rounded once (to nearest, ties to even)
+ *     on store.
  *   - Pointers: device pointers owned by the caller; the library allocates
  *     no device memory and keeps no pointer after the call returns.  Each
  *     pointer must be aligned to its element size; wider alignment (16 B) and
@@ -62,8 +67,8 @@
  *   - Errors: a status is returned, nothing is thrown.  Arguments are checked
  *     before any launch; launch failures return RMSN_E_HIP.
  *   - rows == 0 is valid: nothing is written, except that the backward
- *     entry points set dw to zero (the empty sum).  Pointers other than w and dw may then be
- *     NULL.
+ *     entry points set dw to zero (the empty sum).  Pointers other than w
+ *     and dw may then be NULL.
  */
 #ifndef RMSNORM_MI355X_H
 #define RMSNORM_MI355X_H
@@ -84,8 +89,8 @@ typedef enum {
 typedef enum {
     RMSN_OK = 0,
     RMSN_E_NULLPTR = -1,   /* a required pointer is NULL */
-    RMSN_E_SHAPE = -2,     /* rows < 0, D < 1, or D beyond the supported maximum */
-    RMSN_E_DTYPE = -3,     /* unknown dtype */
+    RMSN_E_SHAPE = -2,     /* rows < 0, D (or d) < 1, beyond its maximum, or sizes overflow */
+    RMSN_E_DTYPE = -3,     /* unknown dtype, or a dw dtype other than fp32 and dt */
     RMSN_E_WORKSPACE = -4, /* workspace NULL or smaller than required */
     RMSN_E_OVERLAP = -5,   /* an output range overlaps another argument */
     RMSN_E_HIP = -6,       /* the HIP runtime reported an error */
@@ -131,8 +136,8 @@ size_t rmsnorm_vjp_workspace_bytes(int64_t rows, int64_t D, int dt);
 
 /* dx[rows, D] (dtype dt) and dw[D] (fp32, overwritten).  `workspace` is
  * device memory of at least rmsnorm_vjp_workspace_bytes(rows, D, dt) bytes,
- * 256-byte aligned; its contents on entry do not matter and are left
- * undefined. */
+ * 16-byte aligned (RMSN_E_ALIGN otherwise); its contents on entry do not
+ * matter and are left undefined. */
 int rmsnorm_vjp(const void *x, const void *w, const void *dy,
                 void *dx, float *dw, void *workspace, size_t workspace_bytes,
                 int64_t rows, int64_t D, int dt,
