@@ -66,6 +66,7 @@ struct Plan {
     int nvec = 1;     // D / nv
     int k = 1;        // vectors per lane; -1 = streaming kernel
     int lanes = 1;    // threads per row
+    int jreg = 0;     // streaming VJP: dw vectors per thread in registers (0: in memory)
     int block = 256;
     int64_t grid = 1;
     size_t shmem = 0;
@@ -104,7 +105,12 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
         int lanes = req_l;
         int k = req_k;
         if (lanes == 0 && k == 0) {
-            lanes = std::min(1024, next_pow2((p->nvec + 1) / 2));
+            // About 32 bytes of each row tensor per lane: 2 vectors of 16
+            // bytes, up to 8 of a narrower width (narrow loads on fewer
+            // lanes keep more rows in flight per wave; measured 1.4-2.5x
+            // faster than 2 narrow vectors per lane at D = 257..513 fp16)
+            const int kt = std::min(8, std::max(1, 32 / vb));
+            lanes = std::min(1024, next_pow2((p->nvec + kt - 1) / kt));
             k = next_pow2((p->nvec + lanes - 1) / lanes);
         } else if (lanes == 0) {
             lanes = std::min(1024, next_pow2((p->nvec + k - 1) / k));
@@ -123,8 +129,12 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
             int block = req_b;
             if (block == 0) {
                 // Small blocks: a block-wide barrier per row group holds fewer
-                // waves in lock step (measured fastest for both kernels).
-                block = std::max(std::max(lanes, 64), std::min(256, maxb));
+                // waves in lock step (measured fastest for both kernels) --
+                // except the persistent VJP on narrow loads, whose 512-block
+                // grid then needs 512-thread blocks to keep enough waves
+                // resident (measured 10-25 % faster at D = 257..513).
+                const int cap = (op == RMSN_OP_VJP && vb <= 4) ? 512 : 256;
+                block = std::max(std::max(lanes, 64), std::min(cap, maxb));
             }
             if (block < 64 || block > maxb || block % 64 != 0 || block % lanes != 0 || !is_pow2(block))
                 return RMSN_E_CONFIG;
@@ -157,6 +167,12 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
     p->k = -1;
     p->lanes = block;
     p->block = block;
+    // streaming VJP: dw in registers when every thread owns at most 32
+    // columns (j vectors of nv), else a partial row in memory
+    p->jreg = 0;
+    for (int j = 1; j <= 8 && j * p->nv <= 32; j <<= 1) {
+        if ((int64_t)j * block >= p->nvec) { p->jreg = j; break; }
+    }
     int64_t grid;
     if (cfg && cfg->num_blocks) {
         grid = cfg->num_blocks;
@@ -326,7 +342,7 @@ int vjp_impl(const void* x, const void* w, const void* dy, void* y, const void* 
         for (const Range& o : all)
             if (overlaps(rws, o)) return RMSN_E_OVERLAP;
     }
-    const void* fn = rmsn::vjp_kernel(dt, p.nv, p.k, grad ? 1 : resgrad ? 2 : 0);
+    const void* fn = rmsn::vjp_kernel(dt, p.nv, p.k, grad ? 1 : resgrad ? 2 : 0, p.jreg);
     if (!fn) return RMSN_E_CONFIG;
 
     RowArgs a;

@@ -375,9 +375,13 @@ __global__ __launch_bounds__(max_block_threads(2, K, NV, sizeof(T))) void vjp_ro
 // Any D.  One row per block iteration, threads stride over the row's
 // vectors.  OP 0: forward, 1: fused add + forward, 2: VJP, 3: VJP that also
 // writes the forward output y (grad call), 4: VJP plus the residual-stream
-// gradient (fused backward) (dw accumulated
-// into this block's partial row in global memory: written on the block's
-// first row, read-modify-written after; each column belongs to one thread).
+// gradient (fused backward).  dw (OP >= 2): with J > 0 every thread owns at
+// most J vectors of columns (v = threadIdx.x + j * blockDim.x) and sums
+// their dw in registers over the block's rows, writing this block's partial
+// row once at the end; with J == 0 (rows wider than 8 vectors per thread)
+// the partial row in global memory is written on the block's first row and
+// read-modify-written after.  Either way each column belongs to one thread
+// and is summed in row order.
 template <int NV>
 __device__ __forceinline__ void block_sum(float (&v)[NV], float* red, int& parity) {
 #pragma unroll
@@ -388,7 +392,7 @@ __device__ __forceinline__ void block_sum(float (&v)[NV], float* red, int& parit
     }
 }
 
-template <typename T, int NV, int OP>
+template <typename T, int NV, int OP, int J = 0>
 __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
     __shared__ float red[2 * 16 * 2];
     const T* x = static_cast<const T*>(a.x);
@@ -402,6 +406,12 @@ __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
     const float inv_d = 1.0f / static_cast<float>(a.D);
     int parity = 0;
     bool first = true;
+    constexpr int JA = J > 0 ? J : 1;
+    float acc[JA][NV];
+#pragma unroll
+    for (int j = 0; j < JA; ++j)
+#pragma unroll
+        for (int e = 0; e < NV; ++e) acc[j][e] = 0.0f;
 
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
         const int64_t base = row * a.D;
@@ -441,6 +451,38 @@ __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
         const float r = rsqrtf(s2[0] * inv_d + a.eps);
         const float c = r * r * r * s2[1] * inv_d;
 
+        if constexpr (OP >= 2 && J > 0) {
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int v = threadIdx.x + j * static_cast<int>(blockDim.x);
+                if (v < a.nvec) {
+                    const int64_t off = base + (int64_t)v * NV;
+                    const Raw<T, NV> px = load_raw<T, NV>(x + off);
+                    const Raw<T, NV> pw = load_raw<T, NV>(w + (int64_t)v * NV);
+                    const Raw<T, NV> pd = load_raw<T, NV>(dy + off);
+                    float o[NV];
+#pragma unroll
+                    for (int e = 0; e < NV; ++e) {
+                        const float xv = elem(px, e);
+                        const float dv = elem(pd, e);
+                        o[e] = __builtin_fmaf(-xv, c, (r * (a.wb + elem(pw, e))) * dv);
+                        acc[j][e] += dv * xv * r;
+                    }
+                    if constexpr (OP == 4) {
+                        const Raw<T, NV> pr = load_raw<T, NV>(res + off);
+#pragma unroll
+                        for (int e = 0; e < NV; ++e) o[e] += elem(pr, e);
+                    }
+                    store_f32<T, NV>(dx + off, o);
+                    if constexpr (OP == 3) {
+#pragma unroll
+                        for (int e = 0; e < NV; ++e) o[e] = elem(px, e) * r * (a.wb + elem(pw, e));
+                        store_f32<T, NV>(y + off, o);
+                    }
+                }
+            }
+            continue;
+        }
         for (int v = threadIdx.x; v < a.nvec; v += blockDim.x) {
             const int64_t off = base + (int64_t)v * NV;
             const Raw<T, NV> px = load_raw<T, NV>(x + off);
@@ -485,6 +527,17 @@ __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
             }
         }
         first = false;
+    }
+    if constexpr (OP >= 2 && J > 0) {
+        // this block's dw partial row (zeros for a block without rows)
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int v = threadIdx.x + j * static_cast<int>(blockDim.x);
+            if (v < a.nvec) {
+#pragma unroll
+                for (int e = 0; e < NV; ++e) dst[(int64_t)v * NV + e] = acc[j][e];
+            }
+        }
     }
 }
 

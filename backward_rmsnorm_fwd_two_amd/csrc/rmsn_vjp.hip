@@ -76,9 +76,25 @@ __global__ __launch_bounds__(256) void zero_fill(TO* __restrict__ p, int64_t n) 
 namespace {
 
 template <typename T, int NV, int MODE>
-const void* pick_vjp(int k) {
+const void* pick_looped(int jreg) {
+    constexpr int OP = 2 + (MODE == kGrad ? 1 : MODE == kResGrad ? 2 : 0);
+    switch (jreg) {
+        case 0: return reinterpret_cast<const void*>(&rows_looped<T, NV, OP, 0>);
+        case 1: return reinterpret_cast<const void*>(&rows_looped<T, NV, OP, 1>);
+        case 2: return reinterpret_cast<const void*>(&rows_looped<T, NV, OP, 2>);
+        case 4: return reinterpret_cast<const void*>(&rows_looped<T, NV, OP, 4>);
+        case 8:
+            // at most 32 dw floats per thread (128 VGPRs at 1024 threads)
+            if constexpr (NV <= 4) return reinterpret_cast<const void*>(&rows_looped<T, NV, OP, 8>);
+            return nullptr;
+        default: return nullptr;
+    }
+}
+
+template <typename T, int NV, int MODE>
+const void* pick_vjp(int k, int jreg) {
     switch (k) {
-        case -1: return reinterpret_cast<const void*>(&rows_looped<T, NV, 2 + (MODE == kGrad ? 1 : MODE == kResGrad ? 2 : 0)>);
+        case -1: return pick_looped<T, NV, MODE>(jreg);
         case 1: return reinterpret_cast<const void*>(&vjp_rows<T, NV, 1, MODE>);
         case 2: return reinterpret_cast<const void*>(&vjp_rows<T, NV, 2, MODE>);
         case 4: return reinterpret_cast<const void*>(&vjp_rows<T, NV, 4, MODE>);
@@ -88,35 +104,35 @@ const void* pick_vjp(int k) {
 }
 
 template <typename T, int MODE>
-const void* pick_vjp_nv(int nv, int k) {
+const void* pick_vjp_nv(int nv, int k, int jreg) {
     switch (nv) {
-        case 1: return pick_vjp<T, 1, MODE>(k);
-        case 2: return pick_vjp<T, 2, MODE>(k);
-        case 4: return pick_vjp<T, 4, MODE>(k);
+        case 1: return pick_vjp<T, 1, MODE>(k, jreg);
+        case 2: return pick_vjp<T, 2, MODE>(k, jreg);
+        case 4: return pick_vjp<T, 4, MODE>(k, jreg);
         case 8:
-            if constexpr (sizeof(T) == 2) return pick_vjp<T, 8, MODE>(k);
+            if constexpr (sizeof(T) == 2) return pick_vjp<T, 8, MODE>(k, jreg);
             return nullptr;
         default: return nullptr;
     }
 }
 
 template <int MODE>
-const void* pick_vjp_dt(int dt, int nv, int k) {
+const void* pick_vjp_dt(int dt, int nv, int k, int jreg) {
     switch (dt) {
-        case kF32: return pick_vjp_nv<float, MODE>(nv, k);
-        case kF16: return pick_vjp_nv<_Float16, MODE>(nv, k);
-        case kBF16: return pick_vjp_nv<__bf16, MODE>(nv, k);
+        case kF32: return pick_vjp_nv<float, MODE>(nv, k, jreg);
+        case kF16: return pick_vjp_nv<_Float16, MODE>(nv, k, jreg);
+        case kBF16: return pick_vjp_nv<__bf16, MODE>(nv, k, jreg);
         default: return nullptr;
     }
 }
 
 }  // namespace
 
-const void* vjp_kernel(int dt, int nv, int k, int mode) {
+const void* vjp_kernel(int dt, int nv, int k, int mode, int jreg) {
     switch (mode) {
-        case kVjp: return pick_vjp_dt<kVjp>(dt, nv, k);
-        case kGrad: return pick_vjp_dt<kGrad>(dt, nv, k);
-        case kResGrad: return pick_vjp_dt<kResGrad>(dt, nv, k);
+        case kVjp: return pick_vjp_dt<kVjp>(dt, nv, k, jreg);
+        case kGrad: return pick_vjp_dt<kGrad>(dt, nv, k, jreg);
+        case kResGrad: return pick_vjp_dt<kResGrad>(dt, nv, k, jreg);
         default: return nullptr;
     }
 }

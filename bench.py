@@ -342,12 +342,77 @@ def gate_bench(R, I, dev, args) -> int:
     return 0
 
 
+def sweep_bench(R, I, dev, args) -> int:
+    """The small-axis dispatch sweep and the small fp32 case: fwd + VJP per
+    call at 16384 rows x D for the D list of the CUDA regression report's
+    band (fp16; the tensors fit in the 256 MB last-level cache, so the GB/s
+    are effective, not HBM), the same D at rows = 1 (latency), and the
+    [64, 512] fp32 POC case (latency).  Back-to-back prepared calls between
+    one event pair per measurement."""
+    stream = torch.cuda.current_stream(dev)
+    N = max(50, min(args.steps, 400))
+
+    def timed(fn):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(N):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / N
+
+    def fwd_vjp_calls(c):
+        x, w, dy = c["x"].to(dev), c["w"].to(dev), c["dy"].to(dev)
+        rows, D = x.shape
+        y, dx = torch.empty_like(x), torch.empty_like(x)
+        dw = torch.empty(D, dtype=torch.float32, device=dev)
+        ws = R.workspace_for(rows, D, x.dtype, dev)
+        f = R.prepared_fwd(x, w, y, c["eps"], c["weight_bias"])
+        v = R.prepared_vjp(x, w, dy, dx, dw, ws, c["eps"], c["weight_bias"])
+        keep = (x, w, dy, y, dx, dw, ws)
+
+        def step():
+            f()
+            v()
+        return step, keep
+
+    grid = []
+    for D in (128, 256, 257, 320, 384, 448, 500, 511, 512, 513, 1024):
+        c = I.axis_sweep(16384, D)
+        step, keep = fwd_vjp_calls(c)
+        us = timed(step)
+        nbytes = 5 * 16384 * D * 2 + 2 * D * 2 + 4 * D
+        c1 = I.axis_sweep(1, D)
+        step1, keep1 = fwd_vjp_calls(c1)
+        us1 = timed(step1)
+        grid.append({"D": D, "rows16384_us": round(us, 3), "effective_GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "rows1_us": round(us1, 3)})
+        log(f"D={D}: {us:.2f} us ({grid[-1]['effective_GBps']} GB/s effective), rows=1 {us1:.2f} us")
+        del keep, keep1
+    cs = I.poc_small()
+    step, keep = fwd_vjp_calls(cs)
+    small_us = timed(step)
+    worst = min(g["effective_GBps"] for g in grid)
+    print(json.dumps({
+        "metric": "RMSNorm fwd+VJP over the small-axis D list, 16384 rows fp16 (effective, cache-resident)",
+        "value": worst, "unit": "GB/s", "n_gpus": 1, "steps": N, "warmup": 5, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "axis sweep fp16 16384 x D (value = the worst D) and rows = 1; "
+                               "POC small case fp32 64 x 512", "grid": grid,
+                   "poc_small_fp32_fwd_plus_vjp_us": round(small_us, 3)},
+    }), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", choices=["poc", "prefill", "decode", "grad", "gate", "ceiling"],
+    ap.add_argument("--workload", choices=["poc", "prefill", "decode", "grad", "gate", "sweep", "ceiling"],
                     default="poc")
     ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -374,6 +439,8 @@ def main() -> int:
         return grad_bench(R, I, dev, args)
     if args.workload == "gate":
         return gate_bench(R, I, dev, args)
+    if args.workload == "sweep":
+        return sweep_bench(R, I, dev, args)
     fused = args.workload == "prefill"
     log(f"generating inputs ({args.workload})")
     if fused:

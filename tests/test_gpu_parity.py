@@ -182,9 +182,9 @@ def _legal_configs(op, D, itemsize):
         nv = vb // itemsize
         nvec = D // nv
         for k in (1, 2, 4, 8):
-            bytes_ = k * nv * itemsize
-            lim = 16 if (op == 1 or k > 4) else 32   # mirrors the library's register budget
-            maxb = 1024 if bytes_ <= lim else (512 if bytes_ <= 2 * lim else 256)
+            elems = k * nv
+            lim = 8 if (op == 1 or k > 4) else 16   # mirrors the library's register budget
+            maxb = 1024 if elems <= lim else (512 if elems <= 2 * lim else 256)
             for lanes in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024):
                 if lanes * k < nvec or lanes > maxb:
                     continue
