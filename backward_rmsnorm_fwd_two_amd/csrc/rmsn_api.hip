@@ -178,7 +178,11 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
         grid = cfg->num_blocks;
         if (grid > rows && rows > 0) return RMSN_E_CONFIG;  // every block must own a row
     } else if (op == RMSN_OP_VJP) {
-        grid = std::min<int64_t>(rows, std::min<int64_t>(kMaxPartialRows, cus * std::max(1, 2048 / block)));
+        // rows past the register dw (row-batched kernel): one block per CU,
+        // since every partial row there is D * 4 bytes written and re-read
+        // (measured best from 40000 to 262144 columns)
+        const int per_cu = p->jreg == 0 ? 1 : std::max(1, 2048 / block);
+        grid = std::min<int64_t>(rows, std::min<int64_t>(kMaxPartialRows, (int64_t)cus * per_cu));
     } else {
         grid = std::min<int64_t>(rows, (int64_t)1 << 20);
     }

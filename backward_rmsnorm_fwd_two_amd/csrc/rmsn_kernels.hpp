@@ -375,13 +375,10 @@ __global__ __launch_bounds__(max_block_threads(2, K, NV, sizeof(T))) void vjp_ro
 // Any D.  One row per block iteration, threads stride over the row's
 // vectors.  OP 0: forward, 1: fused add + forward, 2: VJP, 3: VJP that also
 // writes the forward output y (grad call), 4: VJP plus the residual-stream
-// gradient (fused backward).  dw (OP >= 2): with J > 0 every thread owns at
-// most J vectors of columns (v = threadIdx.x + j * blockDim.x) and sums
-// their dw in registers over the block's rows, writing this block's partial
-// row once at the end; with J == 0 (rows wider than 8 vectors per thread)
-// the partial row in global memory is written on the block's first row and
-// read-modify-written after.  Either way each column belongs to one thread
-// and is summed in row order.
+// gradient (fused backward).  dw (OP >= 2): every thread owns at most J
+// vectors of columns (v = threadIdx.x + j * blockDim.x) and sums their dw in
+// registers over the block's rows, in row order, writing this block's
+// partial row once at the end (rows wider than that take rows_batched_vjp).
 template <int NV>
 __device__ __forceinline__ void block_sum(float (&v)[NV], float* red, int& parity) {
 #pragma unroll
@@ -394,6 +391,7 @@ __device__ __forceinline__ void block_sum(float (&v)[NV], float* red, int& parit
 
 template <typename T, int NV, int OP, int J = 0>
 __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
+    static_assert(OP < 2 || J > 0, "the streaming VJP keeps dw in registers");
     __shared__ float red[2 * 16 * 2];
     const T* x = static_cast<const T*>(a.x);
     const T* res = static_cast<const T*>(a.res);
@@ -402,10 +400,8 @@ __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
     T* y = static_cast<T*>(a.y);
     T* newres = static_cast<T*>(a.newres);
     T* dx = static_cast<T*>(a.dx);
-    float* dst = (gridDim.x == 1) ? a.dw : a.partial + (int64_t)blockIdx.x * a.D;
     const float inv_d = 1.0f / static_cast<float>(a.D);
     int parity = 0;
-    bool first = true;
     constexpr int JA = J > 0 ? J : 1;
     float acc[JA][NV];
 #pragma unroll
@@ -451,7 +447,7 @@ __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
         const float r = rsqrtf(s2[0] * inv_d + a.eps);
         const float c = r * r * r * s2[1] * inv_d;
 
-        if constexpr (OP >= 2 && J > 0) {
+        if constexpr (OP >= 2) {
 #pragma unroll
             for (int j = 0; j < J; ++j) {
                 const int v = threadIdx.x + j * static_cast<int>(blockDim.x);
@@ -481,37 +477,12 @@ __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
                     }
                 }
             }
-            continue;
-        }
-        for (int v = threadIdx.x; v < a.nvec; v += blockDim.x) {
-            const int64_t off = base + (int64_t)v * NV;
-            const Raw<T, NV> px = load_raw<T, NV>(x + off);
-            const Raw<T, NV> pw = load_raw<T, NV>(w + (int64_t)v * NV);
-            float o[NV];
-            if constexpr (OP >= 2) {
-                const Raw<T, NV> pd = load_raw<T, NV>(dy + off);
-                float* dcol = dst + (int64_t)v * NV;
-#pragma unroll
-                for (int e = 0; e < NV; ++e) {
-                    const float xv = elem(px, e);
-                    const float dv = elem(pd, e);
-                    o[e] = __builtin_fmaf(-xv, c, (r * (a.wb + elem(pw, e))) * dv);
-                    const float contrib = dv * xv * r;
-                    dcol[e] = first ? contrib : dcol[e] + contrib;
-                }
-                if constexpr (OP == 4) {
-                    const Raw<T, NV> pr = load_raw<T, NV>(res + off);
-#pragma unroll
-                    for (int e = 0; e < NV; ++e) o[e] += elem(pr, e);
-                }
-                store_f32<T, NV>(dx + off, o);
-                if constexpr (OP == 3) {
-#pragma unroll
-                    for (int e = 0; e < NV; ++e) o[e] = elem(px, e) * r * (a.wb + elem(pw, e));
-                    store_f32<T, NV>(y + off, o);
-                }
-            } else {
-                float h[NV];
+        } else {
+            for (int v = threadIdx.x; v < a.nvec; v += blockDim.x) {
+                const int64_t off = base + (int64_t)v * NV;
+                const Raw<T, NV> px = load_raw<T, NV>(x + off);
+                const Raw<T, NV> pw = load_raw<T, NV>(w + (int64_t)v * NV);
+                float h[NV], o[NV];
 #pragma unroll
                 for (int e = 0; e < NV; ++e) h[e] = elem(px, e);
                 if constexpr (OP == 1) {
@@ -526,10 +497,10 @@ __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
                 store_f32<T, NV>(y + off, o);
             }
         }
-        first = false;
     }
-    if constexpr (OP >= 2 && J > 0) {
+    if constexpr (OP >= 2) {
         // this block's dw partial row (zeros for a block without rows)
+        float* dst = (gridDim.x == 1) ? a.dw : a.partial + (int64_t)blockIdx.x * a.D;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const int v = threadIdx.x + j * static_cast<int>(blockDim.x);
@@ -538,6 +509,100 @@ __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
                 for (int e = 0; e < NV; ++e) dst[(int64_t)v * NV + e] = acc[j][e];
             }
         }
+    }
+}
+
+// Streaming VJP for rows wider than the register dw (more than 32 columns
+// per thread).  Rows are taken RB at a time (rows row0, row0 + gridDim.x,
+// ...): the first pass computes each row's statistics (one block-wide
+// reduction per row), the second walks the block's columns once for all RB
+// rows, so the block's dw partial row is read-modify-written once per RB
+// rows instead of once per row.  OP: 2 VJP, 3 grad call, 4 fused backward.
+#ifndef RMSN_VJP_BATCH
+#define RMSN_VJP_BATCH 8
+#endif
+
+template <typename T, int NV, int OP, int RB>
+__global__ __launch_bounds__(1024) void rows_batched_vjp(RowArgs a) {
+    static_assert(OP >= 2 && OP <= 4, "backward ops only");
+    __shared__ float red[2 * 16 * 2];
+    const T* x = static_cast<const T*>(a.x);
+    const T* res = static_cast<const T*>(a.res);
+    const T* w = static_cast<const T*>(a.w);
+    const T* dy = static_cast<const T*>(a.dy);
+    T* y = static_cast<T*>(a.y);
+    T* dx = static_cast<T*>(a.dx);
+    float* dst = (gridDim.x == 1) ? a.dw : a.partial + (int64_t)blockIdx.x * a.D;
+    const float inv_d = 1.0f / static_cast<float>(a.D);
+    const int64_t stride = gridDim.x;
+    int parity = 0;
+    bool first = true;
+
+    for (int64_t row0 = blockIdx.x; row0 < a.rows; row0 += RB * stride) {
+        float rr[RB], cc[RB];
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+            const int64_t row = row0 + b * stride;
+            rr[b] = 0.0f;
+            cc[b] = 0.0f;
+            if (row < a.rows) {  // block-uniform
+                const int64_t base = row * a.D;
+                float s2[2] = {0.0f, 0.0f};
+                for (int v = threadIdx.x; v < a.nvec; v += blockDim.x) {
+                    const int64_t off = base + (int64_t)v * NV;
+                    const Raw<T, NV> px = load_raw<T, NV>(x + off);
+                    const Raw<T, NV> pd = load_raw<T, NV>(dy + off);
+                    const Raw<T, NV> pw = load_raw<T, NV>(w + (int64_t)v * NV);
+#pragma unroll
+                    for (int e = 0; e < NV; ++e) {
+                        const float xv = elem(px, e);
+                        s2[0] = __builtin_fmaf(xv, xv, s2[0]);
+                        s2[1] = __builtin_fmaf(elem(pd, e) * (a.wb + elem(pw, e)), xv, s2[1]);
+                    }
+                }
+                block_sum<2>(s2, red, parity);
+                rr[b] = rsqrtf(s2[0] * inv_d + a.eps);
+                cc[b] = rr[b] * rr[b] * rr[b] * s2[1] * inv_d;
+            }
+        }
+        for (int v = threadIdx.x; v < a.nvec; v += blockDim.x) {
+            const Raw<T, NV> pw = load_raw<T, NV>(w + (int64_t)v * NV);
+            float acc[NV];
+#pragma unroll
+            for (int e = 0; e < NV; ++e) acc[e] = 0.0f;
+#pragma unroll
+            for (int b = 0; b < RB; ++b) {
+                const int64_t row = row0 + b * stride;
+                if (row < a.rows) {
+                    const int64_t off = row * a.D + (int64_t)v * NV;
+                    const Raw<T, NV> px = load_raw<T, NV>(x + off);
+                    const Raw<T, NV> pd = load_raw<T, NV>(dy + off);
+                    float o[NV];
+#pragma unroll
+                    for (int e = 0; e < NV; ++e) {
+                        const float xv = elem(px, e);
+                        const float dv = elem(pd, e);
+                        o[e] = __builtin_fmaf(-xv, cc[b], (rr[b] * (a.wb + elem(pw, e))) * dv);
+                        acc[e] += dv * xv * rr[b];
+                    }
+                    if constexpr (OP == 4) {
+                        const Raw<T, NV> pr = load_raw<T, NV>(res + off);
+#pragma unroll
+                        for (int e = 0; e < NV; ++e) o[e] += elem(pr, e);
+                    }
+                    store_f32<T, NV>(dx + off, o);
+                    if constexpr (OP == 3) {
+#pragma unroll
+                        for (int e = 0; e < NV; ++e) o[e] = elem(px, e) * rr[b] * (a.wb + elem(pw, e));
+                        store_f32<T, NV>(y + off, o);
+                    }
+                }
+            }
+            float* dcol = dst + (int64_t)v * NV;
+#pragma unroll
+            for (int e = 0; e < NV; ++e) dcol[e] = first ? acc[e] : dcol[e] + acc[e];
+        }
+        first = false;
     }
 }
 

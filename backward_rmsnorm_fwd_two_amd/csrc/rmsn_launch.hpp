@@ -36,8 +36,8 @@ inline int dtype_size(int dt) { return dt == kF32 ? 4 : 2; }
 const void* fwd_kernel(int dt, int nv, int k, bool fused);
 // mode: 0 VJP, 1 grad call (also writes y), 2 fused backward (adds the
 // residual-stream gradient).  jreg (streaming kernel only): vectors of dw
-// columns each thread keeps in registers (1, 2, 4, 8), or 0 for a partial
-// row read-modify-written in memory.
+// columns each thread keeps in registers (1, 2, 4, 8), or 0 for rows wider
+// than that (the row-batched streaming VJP).
 const void* vjp_kernel(int dt, int nv, int k, int mode, int jreg);
 // dw_dt: dtype of dw (fp32, or the weight dtype).
 const void* dw_combine_kernel(int dw_dt);

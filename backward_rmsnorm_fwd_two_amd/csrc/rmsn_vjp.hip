@@ -79,7 +79,7 @@ template <typename T, int NV, int MODE>
 const void* pick_looped(int jreg) {
     constexpr int OP = 2 + (MODE == kGrad ? 1 : MODE == kResGrad ? 2 : 0);
     switch (jreg) {
-        case 0: return reinterpret_cast<const void*>(&rows_looped<T, NV, OP, 0>);
+        case 0: return reinterpret_cast<const void*>(&rows_batched_vjp<T, NV, OP, RMSN_VJP_BATCH>);
         case 1: return reinterpret_cast<const void*>(&rows_looped<T, NV, OP, 1>);
         case 2: return reinterpret_cast<const void*>(&rows_looped<T, NV, OP, 2>);
         case 4: return reinterpret_cast<const void*>(&rows_looped<T, NV, OP, 4>);
