@@ -24,8 +24,9 @@ enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 constexpr int max_block_threads(int op, int k, int nv, int itemsize) {
     (void)itemsize;
     const int elems = k * nv;
-    // the fused forward and many-vector instances carry the most state
-    const int lim1024 = (op == 1 || k > 4) ? 8 : 16;
+    // per-element state: forward < fused forward < VJP (two row tensors, the
+    // dw accumulators); many-vector instances add per-vector offsets
+    const int lim1024 = op == 0 ? 32 : op == 1 ? (k > 4 ? 16 : 32) : (k > 4 ? 8 : 16);
     return elems <= lim1024 ? 1024 : (elems <= 2 * lim1024 ? 512 : 256);
 }
 

@@ -184,7 +184,8 @@ def _legal_configs(op, D, itemsize):
         nvec = D // nv
         for k in (1, 2, 4, 8):
             elems = k * nv
-            lim = 8 if (op == 1 or k > 4) else 16   # mirrors the library's register budget
+            # mirrors the library's register budget
+            lim = 32 if op == 0 else ((16 if k > 4 else 32) if op == 1 else (8 if k > 4 else 16))
             maxb = 1024 if elems <= lim else (512 if elems <= 2 * lim else 256)
             for lanes in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024):
                 if lanes * k < nvec or lanes > maxb:
