@@ -1,5 +1,6 @@
 """MI355X-native RMSNorm: forward, fused residual-add + RMSNorm, and VJP;
-plus the gated activation silu(x[:, :d]) * x[:, d:2d].
+plus the gated activation silu(x[:, :d]) * x[:, d:2d].  `rms_norm`,
+`fused_add_rms_norm` and `RMSNorm` wire them into torch autograd.
 
 The computation runs in hand-written gfx950 HIP kernels behind a C ABI
 (``include/rmsnorm_mi355x.h``); this package is the thin binding over it.
@@ -18,11 +19,16 @@ _BINDING_NAMES = {
     "RMSN_MAX_D", "STATUS",
 }
 
-__all__ = sorted(_BINDING_NAMES)
+_AUTOGRAD_NAMES = {"rms_norm", "fused_add_rms_norm", "RMSNorm"}
+
+__all__ = sorted(_BINDING_NAMES | _AUTOGRAD_NAMES)
 
 
 def __getattr__(name):
     if name in _BINDING_NAMES:
         from . import binding
         return getattr(binding, name)
+    if name in _AUTOGRAD_NAMES:
+        from . import autograd
+        return getattr(autograd, name)
     raise AttributeError(name)
