@@ -53,3 +53,25 @@ def assert_dw_close(dw_t: torch.Tensor, ref: np.ndarray, what: str = "dw", tol: 
     err = float(np.max(np.abs(dw[fin] - ref[fin]))) if fin.any() else 0.0
     assert err <= tol * max(scale, 1e-30), f"{what}: max |err| {err:.3e} > {tol:.0e} * {scale:.3e}"
     return err / max(scale, 1e-30)
+
+
+def ulp_report(out_t: torch.Tensor, ref: np.ndarray, rounded: np.ndarray) -> dict:
+    """Informational: how many outputs differ from the round-to-nearest-even
+    of the reference (`rounded`, the oracle's own rounding), and by how many
+    units in the last place at most (ulps counted on the storage format's bit
+    patterns; fp16/bf16/fp32 are sign-magnitude, so patterns are mapped to a
+    monotone integer line first)."""
+    out = out_t.detach().cpu().contiguous()
+    bits = {torch.float16: torch.int16, torch.bfloat16: torch.int16, torch.float32: torch.int32}[out.dtype]
+    ro = torch.from_numpy(np.ascontiguousarray(rounded)).to(out.dtype)
+
+    def line(t):
+        i = t.view(bits).to(torch.int64)
+        sign_bit = 1 << (8 * t.element_size() - 1)
+        mag = i & (sign_bit - 1)
+        return torch.where(i < 0, -mag, mag)
+
+    d = (line(out) - line(ro)).abs().reshape(-1)
+    fin = torch.from_numpy(np.isfinite(ref).reshape(-1))
+    d = d[fin]
+    return {"n": int(d.numel()), "differ": int((d != 0).sum()), "max_ulp": int(d.max()) if d.numel() else 0}
