@@ -47,12 +47,13 @@ def _bind(path: str):
     lib.orc_rmsnorm_vjp.argtypes = [i64, i64, _dp, _dp, _dp, dbl, dbl, _dp, _dp]
     lib.orc_fused_add_rmsnorm_vjp.argtypes = [i64, i64, _dp, _dp, _dp, _dp, dbl, dbl, _dp, _dp]
     lib.orc_silu_gate.argtypes = [i64, i64, _dp, _dp]
+    lib.orc_silu_gate_vjp.argtypes = [i64, i64, _dp, _dp, _dp]
     lib.orc_round_array.argtypes = [ctypes.c_int, i64, _dp, _dp]
     for name in ("orc_round_f16", "orc_round_bf16", "orc_round_f32"):
         getattr(lib, name).argtypes = [dbl]
         getattr(lib, name).restype = dbl
     for name in ("orc_rmsnorm_fwd", "orc_fused_add_rmsnorm_fwd", "orc_rmsnorm_vjp",
-                 "orc_fused_add_rmsnorm_vjp", "orc_silu_gate", "orc_round_array"):
+                 "orc_fused_add_rmsnorm_vjp", "orc_silu_gate", "orc_silu_gate_vjp", "orc_round_array"):
         getattr(lib, name).restype = None
     return lib
 
@@ -168,6 +169,17 @@ def silu_gate(x):
     y = np.empty((rows, d), dtype=np.float64)
     _load().orc_silu_gate(rows, d, _p(x), _p(y))
     return y
+
+
+def silu_gate_vjp(x, dy):
+    """Gradient [rows, 2d] of sum(dy * silu_gate(x)) with respect to x; fp64."""
+    x, dy = widen(x), widen(dy)
+    rows, two_d = _check2d(x)
+    if two_d % 2 or dy.shape != (rows, two_d // 2):
+        raise ValueError("x must be [rows, 2d] and dy [rows, d]")
+    dx = np.empty((rows, two_d), dtype=np.float64)
+    _load().orc_silu_gate_vjp(rows, two_d // 2, _p(x), _p(dy), _p(dx))
+    return dx
 
 
 _KIND = {"float32": 0, "float16": 1, "bfloat16": 2}

@@ -137,6 +137,27 @@ void orc_silu_gate(int64_t rows, int64_t d, const double *x, double *y)
     }
 }
 
+/* Backward of the gated activation for an upstream gradient dy [rows, d]:
+ * with s = sigmoid(a) = 1 / (1 + exp(-a)),
+ *   d/db = dy * a * s,   d/da = dy * b * s * (1 + a * (1 - s))
+ * (the derivative of a * s is s + a * s * (1 - s)).  dx is [rows, 2d]: the
+ * gradient of the first half, then of the second. */
+void orc_silu_gate_vjp(int64_t rows, int64_t d, const double *x, const double *dy, double *dx)
+{
+    for (int64_t i = 0; i < rows; ++i) {
+        const double *a = x + i * 2 * d;
+        const double *b = a + d;
+        double *da = dx + i * 2 * d;
+        double *db = da + d;
+        for (int64_t j = 0; j < d; ++j) {
+            const double g = dy[i * d + j];
+            const double sg = 1.0 / (1.0 + exp(-a[j]));
+            db[j] = g * a[j] * sg;
+            da[j] = g * b[j] * sg * (1.0 + a[j] * (1.0 - sg));
+        }
+    }
+}
+
 /* ------------------------------------------------------------------------
  * Round-to-nearest-even from fp64 straight to a binary format with
  * `mant` stored mantissa bits and exponent range [emin, emax], returning the

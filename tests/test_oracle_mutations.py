@@ -41,6 +41,8 @@ MUTATIONS = [
     ("fused_vjp_subtracts_residual_grad", "        dh[i] += d_new_residual[i];", "        dh[i] -= d_new_residual[i];"),
     ("gate_sigmoid_sign", "y[i * d + j] = a[j] / (1.0 + exp(-a[j])) * b[j];", "y[i * d + j] = a[j] / (1.0 + exp(a[j])) * b[j];"),
     ("gate_swapped_halves", "y[i * d + j] = a[j] / (1.0 + exp(-a[j])) * b[j];", "y[i * d + j] = b[j] / (1.0 + exp(-b[j])) * a[j];"),
+    ("gate_vjp_drop_sigmoid_slope", "da[j] = g * b[j] * sg * (1.0 + a[j] * (1.0 - sg));", "da[j] = g * b[j] * sg;"),
+    ("gate_vjp_db_without_a", "db[j] = g * a[j] * sg;", "db[j] = g * sg;"),
     ("f16_one_bit_short", "return rne_to_format(v, 10, -14, 15);", "return rne_to_format(v, 9, -14, 15);"),
     ("f16_wrong_emin", "return rne_to_format(v, 10, -14, 15);", "return rne_to_format(v, 10, -15, 15);"),
     ("bf16_truncates", "double n = nearbyint(q);", "double n = trunc(q);"),
@@ -64,6 +66,8 @@ CHECKS = [
     lambda: [P.test_fused_vjp_finite_differences(r, d, wb) for (r, d) in ((1, 1), (2, 3)) for wb in (0.0, 1.0)],
     P.test_silu_gate_odd_part_identity,
     P.test_silu_gate_special_values_and_torch,
+    P.test_silu_gate_vjp_finite_differences,
+    P.test_silu_gate_vjp_torch_and_special_values,
     R.test_f16_exhaustive_round_trip,
     R.test_f16_midpoints_and_random_match_numpy,
     R.test_bf16_matches_brute_force_nearest,

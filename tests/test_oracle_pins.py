@@ -332,3 +332,35 @@ def test_silu_gate_special_values_and_torch():
     x = r.standard_normal((5, 2 * 40)) * 3
     ref = (torch.nn.functional.silu(torch.tensor(x[:, :40])) * torch.tensor(x[:, 40:])).numpy()
     np.testing.assert_allclose(O.silu_gate(x), ref, rtol=1e-13, atol=1e-15)
+
+
+def test_silu_gate_vjp_finite_differences():
+    # central differences of L = sum(dy * y) with respect to every element of x
+    r = _rng(32)
+    rows, d = 3, 5
+    x = r.standard_normal((rows, 2 * d)) * 3
+    dy = r.standard_normal((rows, d))
+    g = O.silu_gate_vjp(x, dy)
+    h = 1e-6
+    fd = np.empty_like(x)
+    for i in range(rows):
+        for j in range(2 * d):
+            xp, xm = x.copy(), x.copy()
+            xp[i, j] += h
+            xm[i, j] -= h
+            fd[i, j] = (np.sum(dy * O.silu_gate(xp)) - np.sum(dy * O.silu_gate(xm))) / (2 * h)
+    np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-8)
+
+
+def test_silu_gate_vjp_torch_and_special_values():
+    r = _rng(33)
+    x = r.standard_normal((4, 2 * 24)) * 4
+    dy = r.standard_normal((4, 24))
+    xt = torch.tensor(x, requires_grad=True)
+    y = torch.nn.functional.silu(xt[:, :24]) * xt[:, 24:]
+    y.backward(torch.tensor(dy))
+    np.testing.assert_allclose(O.silu_gate_vjp(x, dy), xt.grad.numpy(), rtol=1e-12, atol=1e-14)
+    # a = 0: silu'(0) = 1/2 and silu(0) = 0
+    x0 = np.array([[0.0, 0.0, 3.0, -5.0]])
+    g0 = O.silu_gate_vjp(x0, np.array([[2.0, 1.0]]))[0]
+    assert g0[0] == 3.0 and g0[1] == -2.5 and g0[2] == 0.0 and g0[3] == 0.0
