@@ -12,14 +12,14 @@ the library.  A missing library raises ImportError -- there is no fallback.
 _BINDING_NAMES = {
     "rmsnorm_fwd", "fused_add_rmsnorm_fwd", "rmsnorm_vjp", "rmsnorm_fwd_vjp", "prepared_grad",
     "rmsnorm_vjp_workspace_bytes", "RMSN_OP_GRAD", "fused_add_rmsnorm_vjp", "prepared_fused_vjp",
-    "RMSN_OP_FUSED_VJP", "silu_gate", "prepared_gate", "rmsnorm_backward", "RMSN_OP_GATE", "RMSN_MAX_GATE_D",
+    "RMSN_OP_FUSED_VJP", "silu_gate", "prepared_gate", "rmsnorm_backward", "silu_gate_vjp", "prepared_gate_vjp", "RMSN_OP_GATE", "RMSN_MAX_GATE_D",
     "workspace_for", "query_config", "prepare", "prepared_fwd", "prepared_fused", "prepared_vjp",
     "Config", "RMSNormError", "LIB_PATH", "raw",
     "RMSN_F32", "RMSN_F16", "RMSN_BF16", "RMSN_OP_FWD", "RMSN_OP_FUSED", "RMSN_OP_VJP",
     "RMSN_MAX_D", "STATUS",
 }
 
-_AUTOGRAD_NAMES = {"rms_norm", "fused_add_rms_norm", "RMSNorm"}
+_AUTOGRAD_NAMES = {"rms_norm", "fused_add_rms_norm", "RMSNorm", "silu_gate_op"}
 
 __all__ = sorted(_BINDING_NAMES | _AUTOGRAD_NAMES)
 

@@ -7,7 +7,8 @@ MLX pull request "RMSNormVJP backward writes a full {n_rows, D} gw_temp
 intermediate", with the weight gradient summed over rows inside the library
 and returned in the weight's dtype).  Every arithmetic step runs in the HIP
 kernels; this module only saves tensors for the backward and routes
-gradients.  `RMSNorm` is a module holding the weight.
+gradients.  `RMSNorm` is a module holding the weight; `silu_gate_op` is the
+differentiable gated activation (backward: `silu_gate_vjp`).
 """
 from __future__ import annotations
 
@@ -57,6 +58,24 @@ class _FusedAddRMSNormFn(torch.autograd.Function):
                                        d_new_residual=_c(d_new_residual), dw_dtype=w.dtype)
         # h = x + residual: the same gradient reaches both
         return dh, dh, dw, None, None
+
+
+class _SiluGateFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x):
+        x = x.contiguous()
+        ctx.save_for_backward(x)
+        return B.silu_gate(x)
+
+    @staticmethod
+    def backward(ctx, dy):
+        (x,) = ctx.saved_tensors
+        return B.silu_gate_vjp(x, dy.contiguous())
+
+
+def silu_gate_op(x: torch.Tensor) -> torch.Tensor:
+    """Differentiable silu(x[..., :d]) * x[..., d:2d]."""
+    return _SiluGateFn.apply(x)
 
 
 def rms_norm(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-5,

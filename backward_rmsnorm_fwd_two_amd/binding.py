@@ -78,13 +78,15 @@ _lib.rmsnorm_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, 
                                   _f32, _f32, _cfgp, _vp]
 _lib.silu_gate.argtypes = [_vp, _vp, _i64, _i64, _int, _vp]
 _lib.silu_gate_cfg.argtypes = [_vp, _vp, _i64, _i64, _int, _cfgp, _vp]
+_lib.silu_gate_vjp.argtypes = [_vp, _vp, _vp, _i64, _i64, _int, _vp]
+_lib.silu_gate_vjp_cfg.argtypes = [_vp, _vp, _vp, _i64, _i64, _int, _cfgp, _vp]
 _lib.rmsn_query_config.argtypes = [_int, _i64, _i64, _int, _int, _cfgp]
 _lib.rmsn_status_str.argtypes = [_int]
 _lib.rmsn_status_str.restype = ctypes.c_char_p
 for _name in ("rmsnorm_fwd", "rmsnorm_fwd_cfg", "fused_add_rmsnorm_fwd", "fused_add_rmsnorm_fwd_cfg",
               "rmsnorm_vjp", "rmsnorm_vjp_cfg", "rmsnorm_fwd_vjp", "rmsnorm_fwd_vjp_cfg",
               "fused_add_rmsnorm_vjp", "fused_add_rmsnorm_vjp_cfg", "silu_gate", "silu_gate_cfg",
-              "rmsnorm_backward", "rmsn_query_config"):
+              "silu_gate_vjp", "silu_gate_vjp_cfg", "rmsnorm_backward", "rmsn_query_config"):
     getattr(_lib, _name).restype = _int
 
 raw = _lib  # the C functions themselves (pointer-level access for tests)
@@ -429,6 +431,37 @@ def silu_gate(x: torch.Tensor, out: Optional[torch.Tensor] = None, cfg=None) -> 
         st = _lib.silu_gate_cfg(x.data_ptr(), out.data_ptr(), rows, d, dt, _cfg(cfg), _stream(x))
     _check(st, "silu_gate")
     return out
+
+
+def silu_gate_vjp(x: torch.Tensor, dy: torch.Tensor, out: Optional[torch.Tensor] = None,
+                  cfg=None) -> torch.Tensor:
+    """Gradient of sum(dy * silu_gate(x)) with respect to x (x's shape)."""
+    dt = _dt(x)
+    rows, two_d = _rows_d(x)
+    if two_d % 2:
+        raise ValueError("the last axis of x must be even (2d)")
+    d = two_d // 2
+    _req(x, "x", x.dtype, x.device)
+    _req(dy, "dy", x.dtype, x.device, rows * d)
+    if out is None:
+        out = torch.empty_like(x)
+    _req(out, "out", x.dtype, x.device, x.numel())
+    if cfg is None:
+        st = _lib.silu_gate_vjp(x.data_ptr(), dy.data_ptr(), out.data_ptr(), rows, d, dt, _stream(x))
+    else:
+        st = _lib.silu_gate_vjp_cfg(x.data_ptr(), dy.data_ptr(), out.data_ptr(), rows, d, dt, _cfg(cfg),
+                                    _stream(x))
+    _check(st, "silu_gate_vjp")
+    return out
+
+
+def prepared_gate_vjp(x, dy, out):
+    rows, two_d = _rows_d(x)
+    _req(x, "x", x.dtype, x.device)
+    _req(dy, "dy", x.dtype, x.device, rows * (two_d // 2))
+    _req(out, "out", x.dtype, x.device, x.numel())
+    return prepare("silu_gate_vjp", x.data_ptr(), dy.data_ptr(), out.data_ptr(), rows, two_d // 2, _dt(x),
+                   _stream(x))
 
 
 def prepared_gate(x, out):

@@ -434,19 +434,29 @@ int make_gate_plan(int64_t rows, int64_t d, int dt, int align, const rmsn_config
     return RMSN_OK;
 }
 
-int gate_impl(const void* x, void* y, int64_t rows, int64_t d, int dt, const rmsn_config_t* cfg,
-              void* stream) {
+// Forward (dy == nullptr): out = y [rows, d].  Backward: out = dx [rows, 2d]
+// for the upstream gradient dy [rows, d]; dx may be x itself.
+int gate_impl(bool vjp, const void* x, const void* dy, void* out, int64_t rows, int64_t d, int dt,
+              const rmsn_config_t* cfg, void* stream) {
     int st = check_gate(rows, d, dt);
     if (st != RMSN_OK) return st;
     if (rows == 0) return RMSN_OK;
-    if (!x || !y) return RMSN_E_NULLPTR;
+    if (!x || !out || (vjp && !dy)) return RMSN_E_NULLPTR;
     const int s = itemsize(dt);
-    if (!elem_aligned(x, s) || !elem_aligned(y, s)) return RMSN_E_ALIGN;
-    if (overlaps(range_of(y, rows * d * s), range_of(x, rows * 2 * d * s))) return RMSN_E_OVERLAP;
+    if (!elem_aligned(x, s) || !elem_aligned(out, s) || (vjp && !elem_aligned(dy, s))) return RMSN_E_ALIGN;
+    const Range rx = range_of(x, rows * 2 * d * s);
+    int align = std::min(ptr_align(x), ptr_align(out));
+    if (vjp) {
+        const Range rdx = range_of(out, rows * 2 * d * s), rdy = range_of(dy, rows * d * s);
+        if (bad_alias(rdx, rx) || overlaps(rdx, rdy)) return RMSN_E_OVERLAP;
+        align = std::min(align, ptr_align(dy));
+    } else if (overlaps(range_of(out, rows * d * s), rx)) {
+        return RMSN_E_OVERLAP;
+    }
     GatePlan p;
-    st = make_gate_plan(rows, d, dt, std::min(ptr_align(x), ptr_align(y)), cfg, &p);
+    st = make_gate_plan(rows, d, dt, align, cfg, &p);
     if (st != RMSN_OK) return st;
-    const void* fn = rmsn::gate_kernel(dt, p.nv, p.u);
+    const void* fn = vjp ? rmsn::gate_vjp_kernel(dt, p.nv, p.u) : rmsn::gate_kernel(dt, p.nv, p.u);
     if (!fn) return RMSN_E_CONFIG;
     int64_t total = rows * p.nvec;
     int64_t nvec = p.nvec;
@@ -454,8 +464,9 @@ int gate_impl(const void* x, void* y, int64_t rows, int64_t d, int dt, const rms
     uint32_t recip = nvec > 1 ? static_cast<uint32_t>((((uint64_t)1 << 32) + nvec - 1) / nvec) : 0u;
     double inv = 1.0 / static_cast<double>(nvec);
     int64_t nchunks = p.nchunks;
-    void* args[] = {&x, &y, &total, &nvec, &recip, &inv, &nchunks};
-    if (hipLaunchKernel(fn, dim3(static_cast<unsigned>(p.grid)), dim3(p.block), args, 0,
+    void* fargs[] = {&x, &out, &total, &nvec, &recip, &inv, &nchunks};
+    void* bargs[] = {&x, &dy, &out, &total, &nvec, &recip, &inv, &nchunks};
+    if (hipLaunchKernel(fn, dim3(static_cast<unsigned>(p.grid)), dim3(p.block), vjp ? bargs : fargs, 0,
                         static_cast<hipStream_t>(stream)) != hipSuccess)
         return RMSN_E_HIP;
     return RMSN_OK;
@@ -466,12 +477,22 @@ int gate_impl(const void* x, void* y, int64_t rows, int64_t d, int dt, const rms
 extern "C" {
 
 int silu_gate(const void* x, void* y, int64_t rows, int64_t d, int dt, void* hip_stream) {
-    return gate_impl(x, y, rows, d, dt, nullptr, hip_stream);
+    return gate_impl(false, x, nullptr, y, rows, d, dt, nullptr, hip_stream);
 }
 
 int silu_gate_cfg(const void* x, void* y, int64_t rows, int64_t d, int dt, const rmsn_config_t* cfg,
                   void* hip_stream) {
-    return gate_impl(x, y, rows, d, dt, cfg, hip_stream);
+    return gate_impl(false, x, nullptr, y, rows, d, dt, cfg, hip_stream);
+}
+
+int silu_gate_vjp(const void* x, const void* dy, void* dx, int64_t rows, int64_t d, int dt,
+                  void* hip_stream) {
+    return gate_impl(true, x, dy, dx, rows, d, dt, nullptr, hip_stream);
+}
+
+int silu_gate_vjp_cfg(const void* x, const void* dy, void* dx, int64_t rows, int64_t d, int dt,
+                      const rmsn_config_t* cfg, void* hip_stream) {
+    return gate_impl(true, x, dy, dx, rows, d, dt, cfg, hip_stream);
 }
 
 int rmsnorm_fwd(const void* x, const void* w, void* y, int64_t rows, int64_t D, int dt, float eps,

@@ -45,6 +45,8 @@ const void* dw_combine_kernel(int dw_dt);
 // Gated activation silu(x[:, :d]) * x[:, d:2d]: NV elements per load, U
 // output vectors per thread per chunk.
 const void* gate_kernel(int dt, int nv, int u);
+// Its backward (dx = [da | db] for dy of y's shape), same geometry.
+const void* gate_vjp_kernel(int dt, int nv, int u);
 const void* zero_kernel(int dw_dt);
 
 }  // namespace rmsn

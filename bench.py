@@ -252,7 +252,8 @@ def gate_bench(R, I, dev, args) -> int:
     chunk (x 448 MiB, y 224 MiB; algorithmic bytes 3 * rows * d * s, two
     reads and one write per output element), rotating buffer sets so that
     each call reads cold data.  Also: per-call latency at decode batches 1,
-    4 and 8 (back-to-back prepared calls)."""
+    4 and 8 (back-to-back prepared calls), and the backward dx = [da | db]
+    at the prefill shape (5 * rows * d * s bytes per call)."""
     rows, d = 8192, 14336
     c = I.gate(rows, d, "bfloat16")
     s = 2
@@ -286,6 +287,31 @@ def gate_bench(R, I, dev, args) -> int:
     traffic = stored_traffic("gate_8192x14336_bf16", src_hash)
     del xs, ys, calls
 
+    # backward: dx [rows, 2d] from x and dy [rows, d]; 5 * rows * d * s
+    # algorithmic bytes (reads of x and dy, the write of dx), two rotating
+    # sets of 1.1 GiB each so that every call reads cold data
+    vbytes = 5 * rows * d * s
+    dy_cpu = I.normal(np.random.default_rng(1), (rows, d), 0.0, 1.0, "bfloat16")
+    vx = [c["x"].to(dev) for _ in range(2)]
+    vdy = [dy_cpu.to(dev) for _ in range(2)]
+    vdx = [torch.empty_like(v) for v in vx]
+    vcalls = [R.prepared_gate_vjp(a, b, o) for a, b, o in zip(vx, vdy, vdx)]
+    for i in range(args.warmup):
+        vcalls[i % 2]()
+    torch.cuda.synchronize()
+    v0, v1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    v0.record(stream)
+    for i in range(args.steps):
+        vcalls[i % 2]()
+    v1.record(stream)
+    torch.cuda.synchronize()
+    v_us = v0.elapsed_time(v1) * 1e3 / args.steps
+    vjp = {"kernel": "silu_gate_vjp_kernel", "algorithmic_bytes": vbytes, "avg_us": round(v_us, 3),
+           "achieved_gbps": round(vbytes / (v_us * 1e-6) / 1e9, 2),
+           "frac": round(vbytes / (v_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+    log(f"gate backward: {vjp['avg_us']} us, {vjp['achieved_gbps']} GB/s")
+    del vx, vdy, vdx, vcalls
+
     decode = []
     N = max(args.steps, 200)
     for B in (1, 4, 8):
@@ -312,7 +338,8 @@ def gate_bench(R, I, dev, args) -> int:
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "silu gate, x [8192, 28672] bf16 ~ N(0,2) -> y [8192, 14336]",
                    "rows": rows, "d": d, "bytes_per_step": nbytes, "buffer_sets": nsets,
-                   "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2), "decode": decode},
+                   "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2), "decode": decode,
+                   "backward": vjp},
         "roofline": {"kernel": "silu_gate_kernel", "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes": nbytes, "avg_us": round(k_us, 3),

@@ -45,6 +45,10 @@
  *       list, with 16-byte loads: x is [rows, 2d] (the two halves of each row
  *       side by side), y is [rows, d].  fp32 arithmetic, one rounding.
  *
+ *   silu_gate_vjp          dx = [da | db] for an upstream gradient dy of y:
+ *                          db = dy * a * s,  da = dy * b * s * (1 + a * (1 - s)),
+ *                          s = sigmoid(a) (the derivative of the gate above)
+ *
  * Conventions shared by every entry point:
  *   - Layout: row-major, contiguous [rows, D] tensors; w is [D].  x,
  *     residual, w, dy, y, normed, new_residual and dx all have the dtype
@@ -58,9 +62,9 @@
  *   - In place: a [rows, D] output may be the very buffer of a [rows, D]
  *     input of the same call (same address, same extent) -- y over x;
  *     normed or new_residual over x or residual; dx (dh) or y over x (h), dy
- *     or d_new_residual.  Any other overlap -- partial, between two outputs,
- *     with w, dw or the workspace, or any overlap for silu_gate -- returns
- *     RMSN_E_OVERLAP.
+ *     or d_new_residual; silu_gate_vjp's dx over x.  Any other overlap --
+ *     partial, between two outputs, with w, dw or the workspace, any overlap
+ *     for silu_gate -- returns RMSN_E_OVERLAP.
  *   - Execution: asynchronous on `hip_stream` (a hipStream_t; NULL is the
  *     null stream).  No call synchronises.  The functions are thread-safe;
  *     one workspace must not serve two calls in flight at once.
@@ -167,6 +171,13 @@ int fused_add_rmsnorm_vjp(const void *h, const void *w, const void *dy, const vo
  * First-half elements below -88.7 give silu = -0 (true magnitude < 6e-37). */
 int silu_gate(const void *x, void *y, int64_t rows, int64_t d, int dt, void *hip_stream);
 
+/* Backward of silu_gate: dx[rows, 2d] (gradient of the first half, then of
+ * the second) for x[rows, 2d] and the upstream gradient dy[rows, d], all of
+ * dtype dt.  dx may be x itself (in place); it must not overlap dy.  fp32
+ * arithmetic, one rounding per output; errors as silu_gate. */
+int silu_gate_vjp(const void *x, const void *dy, void *dx, int64_t rows, int64_t d, int dt,
+                  void *hip_stream);
+
 /* General backward, one entry point for the three backward forms and the
  * weight-gradient dtype: the VJP (y and d_new_residual NULL), the grad call
  * (y non-NULL, as rmsnorm_fwd_vjp) or the fused backward (d_new_residual
@@ -214,6 +225,8 @@ int fused_add_rmsnorm_vjp_cfg(const void *h, const void *w, const void *dy,
  * output vectors). */
 int silu_gate_cfg(const void *x, void *y, int64_t rows, int64_t d, int dt,
                   const rmsn_config_t *cfg, void *hip_stream);
+int silu_gate_vjp_cfg(const void *x, const void *dy, void *dx, int64_t rows, int64_t d, int dt,
+                      const rmsn_config_t *cfg, void *hip_stream);
 
 /* Operation ids for rmsn_query_config. */
 #define RMSN_OP_FWD 0

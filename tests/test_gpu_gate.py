@@ -186,3 +186,122 @@ def test_gate_errors(R):
     with pytest.raises(ValueError):
         R.silu_gate(torch.zeros(2, 7, dtype=torch.float32, device=DEV))
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------ backward
+
+def _dy(rows, d, dtype, seed):
+    return I.normal(np.random.default_rng(seed), (rows, d), 0.0, 1.0, dtype)
+
+
+def check_vjp(R, x, dy, what, cfg=None, out=None):
+    g = R.silu_gate_vjp(x.to(DEV), dy.to(DEV), out=out, cfg=cfg)
+    torch.cuda.synchronize()
+    return assert_close(g, O.silu_gate_vjp(x, dy), what)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_gate_vjp_every_d_1_to_300(R, dtype):
+    _say(f"gate vjp every d 1..300 {dtype}")
+    for d in range(1, 301):
+        x = I.gate(3, d, dtype, seed=d)["x"]
+        check_vjp(R, x, _dy(3, d, dtype, d), f"{dtype} d={d}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("rows,d", [(1, MLP_D), (8, MLP_D), (129, 1000), (4097, 8), (2, 100003)])
+def test_gate_vjp_shapes(R, dtype, rows, d):
+    _say(f"gate vjp rows={rows} d={d} {dtype}")
+    x = I.gate(rows, d, dtype, seed=rows + d)["x"]
+    check_vjp(R, x, _dy(rows, d, dtype, rows), f"{dtype} rows={rows} d={d}")
+
+
+def test_gate_vjp_full_prefill_chunk_every_element(R):
+    rows, d = 8192, MLP_D
+    _say(f"gate vjp full size rows={rows} d={d} bfloat16")
+    x = I.gate(rows, d, "bfloat16", seed=1)["x"]
+    dy = _dy(rows, d, "bfloat16", 2)
+    g = R.silu_gate_vjp(x.to(DEV), dy.to(DEV))
+    torch.cuda.synchronize()
+    gc = g.cpu()
+    for r0 in range(0, rows, 512):
+        assert_close(gc[r0:r0 + 512], O.silu_gate_vjp(x[r0:r0 + 512], dy[r0:r0 + 512]), f"rows {r0}..")
+
+
+@pytest.mark.parametrize("dtype,rows,d", [("bfloat16", 5, 1000), ("float32", 7, 520), ("float16", 33, 96)])
+def test_gate_vjp_forced_configs_and_in_place(R, dtype, rows, d):
+    x = I.gate(rows, d, dtype, seed=17)["x"]
+    dy = _dy(rows, d, dtype, 18)
+    ref = O.silu_gate_vjp(x, dy)
+    xg, dyg = x.to(DEV), dy.to(DEV)
+    base = R.silu_gate_vjp(xg, dyg)
+    for cfg in _configs(d, x.element_size()):
+        g = R.silu_gate_vjp(xg, dyg, cfg=cfg)
+        torch.cuda.synchronize()
+        assert_close(g, ref, f"cfg {cfg}")
+    # in place: dx over x, bit-identical to the out-of-place result
+    xi = xg.clone()
+    R.silu_gate_vjp(xi, dyg, out=xi)
+    torch.cuda.synchronize()
+    assert torch.equal(xi, base)
+
+
+@pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
+@pytest.mark.parametrize("xoff,dyoff,dxoff", [(1, 0, 0), (0, 3, 0), (0, 0, 5), (2, 2, 2)])
+def test_gate_vjp_misaligned(R, dtype, xoff, dyoff, dxoff):
+    rows, d = 9, 776
+    x = I.gate(rows, d, dtype, seed=19)["x"]
+    dy = _dy(rows, d, dtype, 20)
+    tdt = I.torch_dtype(dtype)
+
+    def place(t, off):
+        flat = torch.zeros(t.numel() + 16, dtype=tdt, device=DEV)
+        flat[off:off + t.numel()] = t.reshape(-1).to(DEV)
+        return flat, flat[off:off + t.numel()].view(t.shape)
+
+    _, xv = place(x, xoff)
+    _, dyv = place(dy, dyoff)
+    gb = torch.full((rows * 2 * d + 16,), 7.0, dtype=tdt, device=DEV)
+    gv = gb[dxoff:dxoff + rows * 2 * d].view(rows, 2 * d)
+    R.silu_gate_vjp(xv, dyv, out=gv)
+    torch.cuda.synchronize()
+    assert_close(gv, O.silu_gate_vjp(x, dy), "dx")
+    gc = to64(gb)
+    assert np.all(gc[:dxoff] == 7.0) and np.all(gc[dxoff + rows * 2 * d:] == 7.0)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_gate_vjp_special_values(R, dtype):
+    a_vals = [0.0, -0.0, 1.0, -1.0, 5.0, -5.0, 30.0, -30.0, float("inf"), float("-inf"), float("nan")]
+    if dtype != "float16":
+        a_vals += [88.0, -88.0, 100.0, -100.0]
+    b_vals = [1.0, -2.0, 0.0]
+    g_vals = [1.0, -0.5]
+    trip = [(a, b, g) for a in a_vals for b in b_vals for g in g_vals]
+    d = len(trip)
+    x = torch.tensor([[t[0] for t in trip] + [t[1] for t in trip]], dtype=torch.float64).to(I.torch_dtype(dtype))
+    dy = torch.tensor([[t[2] for t in trip]], dtype=torch.float64).to(I.torch_dtype(dtype))
+    check_vjp(R, x, dy, f"{dtype} special values")
+
+
+def test_gate_vjp_errors_and_autograd(R):
+    lib = R.raw
+    x = torch.zeros(4, 16, dtype=torch.bfloat16, device=DEV)
+    dy = torch.zeros(4, 8, dtype=torch.bfloat16, device=DEV)
+    dx = torch.empty_like(x)
+    p = lambda t: t.data_ptr()
+    assert lib.silu_gate_vjp(p(x), p(dy), p(dx), 0, 8, 2, None) == 0
+    assert lib.silu_gate_vjp(p(x), None, p(dx), 4, 8, 2, None) == -1
+    assert lib.silu_gate_vjp(p(x), p(dy), p(x) + 32, 4, 8, 2, None) == -5      # partial overlap with x
+    assert lib.silu_gate_vjp(p(x), p(dy), p(dy), 2, 8, 2, None) == -5          # dx over dy
+    assert lib.silu_gate_vjp(p(x), p(dy), p(x), 4, 8, 2, None) == 0            # in place
+    torch.cuda.synchronize()
+    # autograd through silu_gate_op
+    c = I.gate(16, 512, "float32", seed=21)
+    xg = c["x"].to(DEV).requires_grad_(True)
+    y = R.silu_gate_op(xg)
+    dyc = _dy(16, 512, "float32", 22)
+    y.backward(dyc.to(DEV))
+    torch.cuda.synchronize()
+    assert_close(y.detach(), O.silu_gate(c["x"]), "y")
+    assert_close(xg.grad, O.silu_gate_vjp(c["x"], dyc), "dx")
