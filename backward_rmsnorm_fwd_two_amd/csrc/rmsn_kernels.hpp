@@ -57,6 +57,12 @@ __device__ __forceinline__ void issue_row(const T* p, int64_t base, const Cols<K
 }
 
 template <typename T, int NV, int K>
+__device__ __forceinline__ void issue_w(const T* w, const Cols<K>& c, Raw<T, NV> (&dst)[K]) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) dst[k] = load_w<T, NV>(w + c.off[k]);
+}
+
+template <typename T, int NV, int K>
 __device__ __forceinline__ void mask_cols(const Cols<K>& c, Raw<T, NV> (&d)[K]) {
 #pragma unroll
     for (int k = 0; k < K; ++k)
@@ -160,7 +166,7 @@ __global__ __launch_bounds__(max_block_threads(FUSED ? 1 : 0, K, NV, sizeof(T)))
             fwd_issue<T, NV, K, FUSED>(a, r < a.rows ? r : row0, slot, c, d[u]);
         }
         Raw<T, NV> pw[K];
-        issue_row<T, NV, K>(static_cast<const T*>(a.w), 0, c, pw);
+        issue_w<T, NV, K>(static_cast<const T*>(a.w), c, pw);
         mask_cols<T, NV, K>(c, pw);
 #pragma unroll
         for (int k = 0; k < K; ++k)
@@ -309,7 +315,7 @@ __global__ __launch_bounds__(max_block_threads(2, K, NV, sizeof(T))) void vjp_ro
                 vjp_issue<T, NV, K, MODE>(a, r < a.rows ? r : row0, slot, c, d[u]);
             }
             Raw<T, NV> pw[K];
-            issue_row<T, NV, K>(static_cast<const T*>(a.w), 0, c, pw);
+            issue_w<T, NV, K>(static_cast<const T*>(a.w), c, pw);
             mask_cols<T, NV, K>(c, pw);
 #pragma unroll
             for (int k = 0; k < K; ++k)
@@ -417,7 +423,7 @@ __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
             const Raw<T, NV> px = load_raw<T, NV>(x + off);
             if constexpr (OP >= 2) {
                 const Raw<T, NV> pd = load_raw<T, NV>(dy + off);
-                const Raw<T, NV> pw = load_raw<T, NV>(w + (int64_t)v * NV);
+                const Raw<T, NV> pw = load_w<T, NV>(w + (int64_t)v * NV);
 #pragma unroll
                 for (int e = 0; e < NV; ++e) {
                     const float xv = elem(px, e);
@@ -454,7 +460,7 @@ __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
                 if (v < a.nvec) {
                     const int64_t off = base + (int64_t)v * NV;
                     const Raw<T, NV> px = load_raw<T, NV>(x + off);
-                    const Raw<T, NV> pw = load_raw<T, NV>(w + (int64_t)v * NV);
+                    const Raw<T, NV> pw = load_w<T, NV>(w + (int64_t)v * NV);
                     const Raw<T, NV> pd = load_raw<T, NV>(dy + off);
                     float o[NV];
 #pragma unroll
@@ -481,7 +487,7 @@ __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
             for (int v = threadIdx.x; v < a.nvec; v += blockDim.x) {
                 const int64_t off = base + (int64_t)v * NV;
                 const Raw<T, NV> px = load_raw<T, NV>(x + off);
-                const Raw<T, NV> pw = load_raw<T, NV>(w + (int64_t)v * NV);
+                const Raw<T, NV> pw = load_w<T, NV>(w + (int64_t)v * NV);
                 float h[NV], o[NV];
 #pragma unroll
                 for (int e = 0; e < NV; ++e) h[e] = elem(px, e);
@@ -552,7 +558,7 @@ __global__ __launch_bounds__(1024) void rows_batched_vjp(RowArgs a) {
                     const int64_t off = base + (int64_t)v * NV;
                     const Raw<T, NV> px = load_raw<T, NV>(x + off);
                     const Raw<T, NV> pd = load_raw<T, NV>(dy + off);
-                    const Raw<T, NV> pw = load_raw<T, NV>(w + (int64_t)v * NV);
+                    const Raw<T, NV> pw = load_w<T, NV>(w + (int64_t)v * NV);
 #pragma unroll
                     for (int e = 0; e < NV; ++e) {
                         const float xv = elem(px, e);
@@ -566,7 +572,7 @@ __global__ __launch_bounds__(1024) void rows_batched_vjp(RowArgs a) {
             }
         }
         for (int v = threadIdx.x; v < a.nvec; v += blockDim.x) {
-            const Raw<T, NV> pw = load_raw<T, NV>(w + (int64_t)v * NV);
+            const Raw<T, NV> pw = load_w<T, NV>(w + (int64_t)v * NV);
             float acc[NV];
 #pragma unroll
             for (int e = 0; e < NV; ++e) acc[e] = 0.0f;
