@@ -74,8 +74,12 @@ struct Plan {
 
 // The kernel plan for one call.  `align` is the largest power of two (<= 16)
 // dividing every pointer the kernels read or write row-wise.
+// op: RMSN_OP_FWD, RMSN_OP_FUSED, or one of the backward forms RMSN_OP_VJP,
+// RMSN_OP_GRAD, RMSN_OP_FUSED_VJP (all planned alike).
 int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_config_t* cfg,
               Plan* p) {
+    const bool vjp = op == RMSN_OP_VJP || op == RMSN_OP_GRAD || op == RMSN_OP_FUSED_VJP;
+    const int budget_op = vjp ? 2 : op;
     const int s = itemsize(dt);
     int cus = 0;
     int st = cu_count(&cus);
@@ -121,7 +125,14 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
         if (!is_pow2(lanes) || lanes > 1024) return RMSN_E_CONFIG;
         if (k != 1 && k != 2 && k != 4 && k != 8) return RMSN_E_CONFIG;
         if ((int64_t)lanes * k < p->nvec) return RMSN_E_CONFIG;
-        const int maxb = rmsn::max_block_threads(op, k, p->nv, s);
+        int maxb = rmsn::max_block_threads(budget_op, k, p->nv, s);
+        // automatic choice: more vectors per lane on fewer lanes while the
+        // row does not fit the budget's block
+        while (!req_l && !req_k && lanes > maxb && k < 8 && lanes > 64) {
+            k <<= 1;
+            lanes >>= 1;
+            maxb = rmsn::max_block_threads(budget_op, k, p->nv, s);
+        }
         if (lanes > maxb) {
             if (req_l || req_k) return RMSN_E_CONFIG;
             looped = true;  // automatic choice: fall back to the streaming kernel
@@ -133,7 +144,7 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
                 // except the persistent VJP on narrow loads, whose 512-block
                 // grid then needs 512-thread blocks to keep enough waves
                 // resident (measured 10-25 % faster at D = 257..513).
-                const int cap = (op == RMSN_OP_VJP && vb <= 4) ? 512 : 256;
+                const int cap = (vjp && vb <= 4) ? 512 : 256;
                 block = std::max(std::max(lanes, 64), std::min(cap, maxb));
             }
             if (block < 64 || block > maxb || block % 64 != 0 || block % lanes != 0 || !is_pow2(block))
@@ -146,7 +157,7 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
             int64_t grid;
             if (cfg && cfg->num_blocks) {
                 grid = cfg->num_blocks;
-            } else if (op == RMSN_OP_VJP) {
+            } else if (vjp) {
                 // Two persistent blocks per CU: every extra partial row costs
                 // D * 4 bytes written and re-read by the combine.
                 grid = std::min<int64_t>(groups, std::min<int64_t>(kMaxPartialRows, 2 * cus));
@@ -154,9 +165,9 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
                 grid = std::min<int64_t>(groups, (int64_t)1 << 20);
             }
             if (grid < 1 || grid > ((int64_t)1 << 30)) return RMSN_E_CONFIG;
-            if (op == RMSN_OP_VJP && grid > kMaxPartialRows) return RMSN_E_CONFIG;
+            if (vjp && grid > kMaxPartialRows) return RMSN_E_CONFIG;
             p->grid = grid;
-            p->shmem = (op == RMSN_OP_VJP && nslots > 1) ? (size_t)block * p->nv * sizeof(float) : 0;
+            p->shmem = (vjp && nslots > 1) ? (size_t)block * p->nv * sizeof(float) : 0;
             return RMSN_OK;
         }
     }
@@ -177,7 +188,7 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
     if (cfg && cfg->num_blocks) {
         grid = cfg->num_blocks;
         if (grid > rows && rows > 0) return RMSN_E_CONFIG;  // every block must own a row
-    } else if (op == RMSN_OP_VJP) {
+    } else if (vjp) {
         // rows past the register dw (row-batched kernel): one block per CU,
         // since every partial row there is D * 4 bytes written and re-read
         // (measured best from 40000 to 262144 columns)
@@ -187,7 +198,7 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
         grid = std::min<int64_t>(rows, (int64_t)1 << 20);
     }
     if (grid < 1) grid = 1;
-    if (op == RMSN_OP_VJP && grid > kMaxPartialRows) return RMSN_E_CONFIG;
+    if (vjp && grid > kMaxPartialRows) return RMSN_E_CONFIG;
     p->grid = grid;
     p->shmem = 0;
     return RMSN_OK;
@@ -335,7 +346,7 @@ int vjp_impl(const void* x, const void* w, const void* dy, void* y, const void* 
     if (grad) align = std::min(align, ptr_align(y));
     if (resgrad) align = std::min(align, ptr_align(dres));
     Plan p;
-    st = make_plan(RMSN_OP_VJP, rows, D, dt, align, cfg, &p);
+    st = make_plan(resgrad ? RMSN_OP_FUSED_VJP : (grad ? RMSN_OP_GRAD : RMSN_OP_VJP), rows, D, dt, align, cfg, &p);
     if (st != RMSN_OK) return st;
     const size_t need = ws_bytes(p, D, typed_dw);
     if (need > 0) {
@@ -346,7 +357,8 @@ int vjp_impl(const void* x, const void* w, const void* dy, void* y, const void* 
         for (const Range& o : all)
             if (overlaps(rws, o)) return RMSN_E_OVERLAP;
     }
-    const void* fn = rmsn::vjp_kernel(dt, p.nv, p.k, grad ? 1 : resgrad ? 2 : 0, p.jreg);
+    const bool pipe = p.k > 0 && p.k * p.nv <= rmsn::kVjpPipeElems && p.block <= rmsn::kVjpPipeBlock;
+    const void* fn = rmsn::vjp_kernel(dt, p.nv, p.k, grad ? 1 : resgrad ? 2 : 0, p.jreg, pipe);
     if (!fn) return RMSN_E_CONFIG;
 
     RowArgs a;
@@ -526,10 +538,12 @@ size_t rmsnorm_vjp_workspace_bytes(int64_t rows, int64_t D, int dt) {
     size_t best = 0;
     if (rows > 0) {
         // The plan depends on pointer alignment; size for the largest.
-        for (int align = 16; align >= itemsize(dt); align >>= 1) {
-            Plan p;
-            if (make_plan(RMSN_OP_VJP, rows, D, dt, align, nullptr, &p) != RMSN_OK) return 0;
-            best = std::max(best, ws_bytes(p, D, /*typed_dw=*/true));
+        for (int op : {RMSN_OP_VJP, RMSN_OP_GRAD, RMSN_OP_FUSED_VJP}) {
+            for (int align = 16; align >= itemsize(dt); align >>= 1) {
+                Plan p;
+                if (make_plan(op, rows, D, dt, align, nullptr, &p) != RMSN_OK) return 0;
+                best = std::max(best, ws_bytes(p, D, /*typed_dw=*/true));
+            }
         }
     }
     return std::max<size_t>(best, 256);
@@ -608,7 +622,6 @@ int rmsn_query_config(int op, int64_t rows, int64_t D, int dt, int align_bytes, 
         return RMSN_OK;
     }
     if (op < RMSN_OP_FWD || op > RMSN_OP_FUSED_VJP) return RMSN_E_CONFIG;
-    if (op == RMSN_OP_GRAD || op == RMSN_OP_FUSED_VJP) op = RMSN_OP_VJP;  // same plan
     int st = check_common(rows, D, dt);
     if (st != RMSN_OK) return st;
     if (align_bytes <= 0 || !is_pow2(align_bytes)) return RMSN_E_ALIGN;

@@ -198,7 +198,10 @@ __global__ __launch_bounds__(max_block_threads(FUSED ? 1 : 0, K, NV, sizeof(T)))
 // block's rows is accumulated in registers, combined over the block's row
 // slots in LDS (fixed tree order), and written to partial[blockIdx.x, :]
 // (or to dw when the grid is a single block).  `dyn` LDS: blockDim.x * NV
-// floats when the block holds more than one row slot.
+// floats when the block holds more than one row slot.  The blocks are
+// persistent (a bounded grid strides over the row groups, so that dw has a
+// bounded number of partial rows); PIPE instances overlap each group's
+// loads with the processing of the previous group.
 // VJP row kernel modes.
 constexpr int kVjp = 0;       // dx, dw
 constexpr int kGrad = 1;      // also y = x r g (grad call)
@@ -285,8 +288,9 @@ __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int 
     }
 }
 
-template <typename T, int NV, int K, int MODE>
-__global__ __launch_bounds__(max_block_threads(2, K, NV, sizeof(T))) void vjp_rows(RowArgs a) {
+template <typename T, int NV, int K, int MODE, bool PIPE = false>
+__global__ __launch_bounds__(PIPE ? kVjpPipeBlock : max_block_threads(2, K, NV, sizeof(T))) void vjp_rows(RowArgs a) {
+    static_assert(!PIPE || K * NV <= kVjpPipeElems, "pipelined instances hold two row groups");
     extern __shared__ float dyn[];
     __shared__ float red[2 * 16 * 2];
     const int lanes = a.lanes;
@@ -304,39 +308,67 @@ __global__ __launch_bounds__(max_block_threads(2, K, NV, sizeof(T))) void vjp_ro
         for (int e = 0; e < NV; ++e) acc[k][e] = 0.0f;
 
     if (row0 < a.rows) {  // block-uniform
-        constexpr int U = RMSN_UNROLL;
         int parity = 0;
         float g[K][NV];
-        {
-            VjpRow<T, NV, K> d[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t r = row0 + u * step;
-                vjp_issue<T, NV, K, MODE>(a, r < a.rows ? r : row0, slot, c, d[u]);
-            }
+        if constexpr (PIPE) {
+            // Software pipeline over the block's row groups: the loads of
+            // group i + 1 are issued before group i is processed, so every
+            // wave keeps one group's loads in flight while it reduces,
+            // computes and stores the previous one (a persistent block
+            // otherwise pays one full memory round trip per row group).  Two
+            // register buffers alternate (the loop is unrolled twice): a copy
+            // of loaded data would make the wave wait for the prefetch at the
+            // end of every iteration.  The gain's loads go out first, so that
+            // none of them is still pending when the loop starts.
             Raw<T, NV> pw[K];
             issue_w<T, NV, K>(static_cast<const T*>(a.w), c, pw);
+            VjpRow<T, NV, K> ra, rb;
+            vjp_issue<T, NV, K, MODE>(a, row0, slot, c, ra);
             mask_cols<T, NV, K>(c, pw);
 #pragma unroll
             for (int k = 0; k < K; ++k)
 #pragma unroll
                 for (int e = 0; e < NV; ++e) g[k][e] = a.wb + elem(pw[k], e);
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (row0 + u * step < a.rows)
-                    vjp_process<T, NV, K, MODE>(a, row0 + u * step, slot, lanes, c, g, acc, d[u], red, parity);
-        }
-        for (row0 += U * step; row0 < a.rows; row0 += U * step) {
-            VjpRow<T, NV, K> d[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t r = row0 + u * step;
-                vjp_issue<T, NV, K, MODE>(a, r < a.rows ? r : row0, slot, c, d[u]);
+            int64_t next = row0 + step;
+            for (;;) {  // ra holds group row0
+                if (next >= a.rows) {
+                    vjp_process<T, NV, K, MODE>(a, row0, slot, lanes, c, g, acc, ra, red, parity);
+                    break;
+                }
+                vjp_issue<T, NV, K, MODE>(a, next, slot, c, rb);
+                vjp_process<T, NV, K, MODE>(a, row0, slot, lanes, c, g, acc, ra, red, parity);
+                row0 = next;
+                next += step;
+                // rb holds group row0
+                if (next >= a.rows) {
+                    vjp_process<T, NV, K, MODE>(a, row0, slot, lanes, c, g, acc, rb, red, parity);
+                    break;
+                }
+                vjp_issue<T, NV, K, MODE>(a, next, slot, c, ra);
+                vjp_process<T, NV, K, MODE>(a, row0, slot, lanes, c, g, acc, rb, red, parity);
+                row0 = next;
+                next += step;
             }
+        } else {
+            // one row group in flight: its loads, then (first group only) the
+            // gain's, then the group is processed
+            {
+                VjpRow<T, NV, K> d;
+                vjp_issue<T, NV, K, MODE>(a, row0, slot, c, d);
+                Raw<T, NV> pw[K];
+                issue_w<T, NV, K>(static_cast<const T*>(a.w), c, pw);
+                mask_cols<T, NV, K>(c, pw);
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (row0 + u * step < a.rows)
-                    vjp_process<T, NV, K, MODE>(a, row0 + u * step, slot, lanes, c, g, acc, d[u], red, parity);
+                for (int k = 0; k < K; ++k)
+#pragma unroll
+                    for (int e = 0; e < NV; ++e) g[k][e] = a.wb + elem(pw[k], e);
+                vjp_process<T, NV, K, MODE>(a, row0, slot, lanes, c, g, acc, d, red, parity);
+            }
+            for (row0 += step; row0 < a.rows; row0 += step) {
+                VjpRow<T, NV, K> d;
+                vjp_issue<T, NV, K, MODE>(a, row0, slot, c, d);
+                vjp_process<T, NV, K, MODE>(a, row0, slot, lanes, c, g, acc, d, red, parity);
+            }
         }
     }
 

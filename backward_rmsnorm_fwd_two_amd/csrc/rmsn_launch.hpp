@@ -19,16 +19,25 @@ enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 // dw accumulators and fp32 temporaries per element, raw row words, and a
 // 64-bit offset per vector), so the wide instances are compiled for fewer
 // threads and more VGPRs per thread (1024 threads: 128 VGPRs, 512: 256,
-// 256: 512).  The thresholds keep every instance's measured VGPR count
-// (ISA metadata) within its budget without spills.
+// 256: 512).  The thresholds keep every instance's VGPR count (ISA
+// metadata) within its budget.  op: 0 forward, 1 fused forward, 2 any VJP
+// form.
 constexpr int max_block_threads(int op, int k, int nv, int itemsize) {
     (void)itemsize;
     const int elems = k * nv;
-    // per-element state: forward < fused forward < VJP (two row tensors, the
-    // dw accumulators); many-vector instances add per-vector offsets
     const int lim1024 = op == 0 ? 32 : op == 1 ? (k > 4 ? 16 : 32) : (k > 4 ? 8 : 16);
     return elems <= lim1024 ? 1024 : (elems <= 2 * lim1024 ? 512 : 256);
 }
+
+// The VJP row kernel also comes software-pipelined (the next row group's
+// loads in flight while the current one is processed; two groups of raw data
+// live), for instances with at most this many elements per lane, run in
+// blocks of at most kVjpPipeBlock threads: there a block holds one row of up
+// to four waves, and two blocks per CU leave the registers the second buffer
+// needs.  Wider blocks (rows of eight or more waves) keep the plain loop,
+// whose lower register count lets two blocks share a CU.
+constexpr int kVjpPipeElems = 16;
+constexpr int kVjpPipeBlock = 256;
 
 inline int dtype_size(int dt) { return dt == kF32 ? 4 : 2; }
 
@@ -39,7 +48,9 @@ const void* fwd_kernel(int dt, int nv, int k, bool fused);
 // residual-stream gradient).  jreg (streaming kernel only): vectors of dw
 // columns each thread keeps in registers (1, 2, 4, 8), or 0 for rows wider
 // than that (the row-batched streaming VJP).
-const void* vjp_kernel(int dt, int nv, int k, int mode, int jreg);
+// pipe: the software-pipelined register kernel (k > 0, k * nv <=
+// kVjpPipeElems, block <= kVjpPipeBlock).
+const void* vjp_kernel(int dt, int nv, int k, int mode, int jreg, bool pipe);
 // dw_dt: dtype of dw (fp32, or the weight dtype).
 const void* dw_combine_kernel(int dw_dt);
 // Gated activation silu(x[:, :d]) * x[:, d:2d]: NV elements per load, U

@@ -91,48 +91,58 @@ const void* pick_looped(int jreg) {
     }
 }
 
+template <typename T, int NV, int K, int MODE>
+const void* pick_rows(bool pipe) {
+    if constexpr (K * NV <= kVjpPipeElems) {
+        if (pipe) return reinterpret_cast<const void*>(&vjp_rows<T, NV, K, MODE, true>);
+    } else {
+        if (pipe) return nullptr;
+    }
+    return reinterpret_cast<const void*>(&vjp_rows<T, NV, K, MODE, false>);
+}
+
 template <typename T, int NV, int MODE>
-const void* pick_vjp(int k, int jreg) {
+const void* pick_vjp(int k, int jreg, bool pipe) {
     switch (k) {
-        case -1: return pick_looped<T, NV, MODE>(jreg);
-        case 1: return reinterpret_cast<const void*>(&vjp_rows<T, NV, 1, MODE>);
-        case 2: return reinterpret_cast<const void*>(&vjp_rows<T, NV, 2, MODE>);
-        case 4: return reinterpret_cast<const void*>(&vjp_rows<T, NV, 4, MODE>);
-        case 8: return reinterpret_cast<const void*>(&vjp_rows<T, NV, 8, MODE>);
+        case -1: return pipe ? nullptr : pick_looped<T, NV, MODE>(jreg);
+        case 1: return pick_rows<T, NV, 1, MODE>(pipe);
+        case 2: return pick_rows<T, NV, 2, MODE>(pipe);
+        case 4: return pick_rows<T, NV, 4, MODE>(pipe);
+        case 8: return pick_rows<T, NV, 8, MODE>(pipe);
         default: return nullptr;
     }
 }
 
 template <typename T, int MODE>
-const void* pick_vjp_nv(int nv, int k, int jreg) {
+const void* pick_vjp_nv(int nv, int k, int jreg, bool pipe) {
     switch (nv) {
-        case 1: return pick_vjp<T, 1, MODE>(k, jreg);
-        case 2: return pick_vjp<T, 2, MODE>(k, jreg);
-        case 4: return pick_vjp<T, 4, MODE>(k, jreg);
+        case 1: return pick_vjp<T, 1, MODE>(k, jreg, pipe);
+        case 2: return pick_vjp<T, 2, MODE>(k, jreg, pipe);
+        case 4: return pick_vjp<T, 4, MODE>(k, jreg, pipe);
         case 8:
-            if constexpr (sizeof(T) == 2) return pick_vjp<T, 8, MODE>(k, jreg);
+            if constexpr (sizeof(T) == 2) return pick_vjp<T, 8, MODE>(k, jreg, pipe);
             return nullptr;
         default: return nullptr;
     }
 }
 
 template <int MODE>
-const void* pick_vjp_dt(int dt, int nv, int k, int jreg) {
+const void* pick_vjp_dt(int dt, int nv, int k, int jreg, bool pipe) {
     switch (dt) {
-        case kF32: return pick_vjp_nv<float, MODE>(nv, k, jreg);
-        case kF16: return pick_vjp_nv<_Float16, MODE>(nv, k, jreg);
-        case kBF16: return pick_vjp_nv<__bf16, MODE>(nv, k, jreg);
+        case kF32: return pick_vjp_nv<float, MODE>(nv, k, jreg, pipe);
+        case kF16: return pick_vjp_nv<_Float16, MODE>(nv, k, jreg, pipe);
+        case kBF16: return pick_vjp_nv<__bf16, MODE>(nv, k, jreg, pipe);
         default: return nullptr;
     }
 }
 
 }  // namespace
 
-const void* vjp_kernel(int dt, int nv, int k, int mode, int jreg) {
+const void* vjp_kernel(int dt, int nv, int k, int mode, int jreg, bool pipe) {
     switch (mode) {
-        case kVjp: return pick_vjp_dt<kVjp>(dt, nv, k, jreg);
-        case kGrad: return pick_vjp_dt<kGrad>(dt, nv, k, jreg);
-        case kResGrad: return pick_vjp_dt<kResGrad>(dt, nv, k, jreg);
+        case kVjp: return pick_vjp_dt<kVjp>(dt, nv, k, jreg, pipe);
+        case kGrad: return pick_vjp_dt<kGrad>(dt, nv, k, jreg, pipe);
+        case kResGrad: return pick_vjp_dt<kResGrad>(dt, nv, k, jreg, pipe);
         default: return nullptr;
     }
 }

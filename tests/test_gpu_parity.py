@@ -182,6 +182,14 @@ def test_misaligned_base_pointers(R, dtype, offset):
     assert_dw_close(dw, dwref)
 
 
+def _max_block(op, k, nv, itemsize):
+    """Mirrors the library's register budget (0 forward, 1 fused forward, 2
+    and 3 the VJP forms)."""
+    elems = k * nv
+    lim = 32 if op == 0 else ((16 if k > 4 else 32) if op == 1 else (8 if k > 4 else 16))
+    return 1024 if elems <= lim else (512 if elems <= 2 * lim else 256)
+
+
 def _legal_configs(op, D, itemsize):
     """Every (lanes, K, vec_bytes, block) combination the register kernels
     accept for D, plus the streaming kernel at two block sizes."""
@@ -192,10 +200,7 @@ def _legal_configs(op, D, itemsize):
         nv = vb // itemsize
         nvec = D // nv
         for k in (1, 2, 4, 8):
-            elems = k * nv
-            # mirrors the library's register budget
-            lim = 32 if op == 0 else ((16 if k > 4 else 32) if op == 1 else (8 if k > 4 else 16))
-            maxb = 1024 if elems <= lim else (512 if elems <= 2 * lim else 256)
+            maxb = _max_block(op, k, nv, itemsize)
             for lanes in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024):
                 if lanes * k < nvec or lanes > maxb:
                     continue
@@ -514,7 +519,7 @@ def test_fused_vjp_forced_configs(R, dtype, D):
     c = I.generic(rows, D, dtype, seed=D)
     dr = I.normal(np.random.default_rng(1), (rows, D), 0.0, 1.0, dtype)
     s = 4 if dtype == "float32" else 2
-    for cfg in _legal_configs(2, D, s):
+    for cfg in _legal_configs(3, D, s):
         check_fused_vjp(R, c["x"], c["w"], c["dy"], dr, c["eps"], 0.0, f"{cfg}", cfg=dict(cfg, num_blocks=3))
 
 
