@@ -357,7 +357,13 @@ int vjp_impl(const void* x, const void* w, const void* dy, void* y, const void* 
         for (const Range& o : all)
             if (overlaps(rws, o)) return RMSN_E_OVERLAP;
     }
-    const bool pipe = p.k > 0 && p.k * p.nv <= rmsn::kVjpPipeElems && p.block <= rmsn::kVjpPipeBlock;
+    // the pipelined kernel stores unconditionally: every vector of a row in
+    // range (lanes * k == nvec) and every row slot of every group a real row.
+    // The grad call keeps the plain kernel: pipelined it measured slower
+    // (55.0 vs 53 us at 8192 x 4096 fp16), and its dx then differed from the
+    // VJP's by one fp16 ulp in a few elements of the last row group.
+    const bool pipe = !grad && p.k > 0 && p.k * p.nv <= rmsn::kVjpPipeElems && p.block <= rmsn::kVjpPipeBlock &&
+                      static_cast<int64_t>(p.lanes) * p.k == p.nvec && rows % (p.block / p.lanes) == 0;
     const void* fn = rmsn::vjp_kernel(dt, p.nv, p.k, grad ? 1 : resgrad ? 2 : 0, p.jreg, pipe);
     if (!fn) return RMSN_E_CONFIG;
 

@@ -224,16 +224,23 @@ __device__ __forceinline__ void vjp_issue(const RowArgs& a, int64_t row0, int sl
     if constexpr (MODE == kResGrad) issue_row<T, NV, K>(static_cast<const T*>(a.res), base, c, d.dr);
 }
 
-template <typename T, int NV, int K, int MODE>
+// FULL: every vector of the row is in range and every processed row exists
+// (the plan guarantees it), so no element is masked and every store is
+// unconditional -- which also keeps the wave's count of outstanding memory
+// operations the same on every path (a store skipped on some paths would
+// make later waits for loads wait for everything).
+template <typename T, int NV, int K, int MODE, bool FULL = false>
 __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int slot, int lanes,
                                             const Cols<K>& c, const float (&g)[K][NV],
                                             float (&acc)[K][NV], VjpRow<T, NV, K>& d, float* red,
                                             int& parity) {
     const int64_t row = row0 + slot;
-    const bool rok = row < a.rows;
+    const bool rok = FULL || row < a.rows;
     const int64_t base = row * a.D;
-    mask_cols<T, NV, K>(c, d.x);
-    mask_cols<T, NV, K>(c, d.dy);
+    if constexpr (!FULL) {
+        mask_cols<T, NV, K>(c, d.x);
+        mask_cols<T, NV, K>(c, d.dy);
+    }
 
     float s2[2] = {0.0f, 0.0f};  // sum x^2, sum dy g x
 #pragma unroll
@@ -254,7 +261,10 @@ __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int 
         parity ^= 1;
     }
     const float inv_d = 1.0f / static_cast<float>(a.D);
-    const float r = rsqrtf(s2[0] * inv_d + a.eps);
+    // explicit fma: every instance (VJP, grad call, fused backward, pipelined
+    // or not) rounds the row statistic identically, whatever the compiler
+    // would contract
+    const float r = rsqrtf(__builtin_fmaf(s2[0], inv_d, a.eps));
     const float cc = r * r * r * s2[1] * inv_d;
 
     if (rok) {
@@ -272,7 +282,7 @@ __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int 
                 if constexpr (MODE == kResGrad) o[e] += elem(d.dr[k], e);
                 acc[k][e] = __builtin_fmaf(dv * xv, r, acc[k][e]);
             }
-            if (c.ok[k]) store_f32<T, NV>(dx + base + c.off[k], o);
+            if (FULL || c.ok[k]) store_f32<T, NV>(dx + base + c.off[k], o);
         }
         if constexpr (MODE == kGrad) {
             // grad call: the forward output from the same pass over x
@@ -282,7 +292,7 @@ __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int 
                 float o[NV];
 #pragma unroll
                 for (int e = 0; e < NV; ++e) o[e] = elem(d.x[k], e) * r * g[k][e];
-                if (c.ok[k]) store_f32<T, NV>(y + base + c.off[k], o);
+                if (FULL || c.ok[k]) store_f32<T, NV>(y + base + c.off[k], o);
             }
         }
     }
@@ -319,7 +329,10 @@ __global__ __launch_bounds__(PIPE ? kVjpPipeBlock : max_block_threads(2, K, NV, 
             // register buffers alternate (the loop is unrolled twice): a copy
             // of loaded data would make the wave wait for the prefetch at the
             // end of every iteration.  The gain's loads go out first, so that
-            // none of them is still pending when the loop starts.
+            // none of them is still pending when the loop starts.  Every row
+            // and vector is in range here (the plan selects this kernel only
+            // then), so the processing masks nothing and stores
+            // unconditionally.
             Raw<T, NV> pw[K];
             issue_w<T, NV, K>(static_cast<const T*>(a.w), c, pw);
             VjpRow<T, NV, K> ra, rb;
@@ -332,20 +345,20 @@ __global__ __launch_bounds__(PIPE ? kVjpPipeBlock : max_block_threads(2, K, NV, 
             int64_t next = row0 + step;
             for (;;) {  // ra holds group row0
                 if (next >= a.rows) {
-                    vjp_process<T, NV, K, MODE>(a, row0, slot, lanes, c, g, acc, ra, red, parity);
+                    vjp_process<T, NV, K, MODE, true>(a, row0, slot, lanes, c, g, acc, ra, red, parity);
                     break;
                 }
                 vjp_issue<T, NV, K, MODE>(a, next, slot, c, rb);
-                vjp_process<T, NV, K, MODE>(a, row0, slot, lanes, c, g, acc, ra, red, parity);
+                vjp_process<T, NV, K, MODE, true>(a, row0, slot, lanes, c, g, acc, ra, red, parity);
                 row0 = next;
                 next += step;
                 // rb holds group row0
                 if (next >= a.rows) {
-                    vjp_process<T, NV, K, MODE>(a, row0, slot, lanes, c, g, acc, rb, red, parity);
+                    vjp_process<T, NV, K, MODE, true>(a, row0, slot, lanes, c, g, acc, rb, red, parity);
                     break;
                 }
                 vjp_issue<T, NV, K, MODE>(a, next, slot, c, ra);
-                vjp_process<T, NV, K, MODE>(a, row0, slot, lanes, c, g, acc, rb, red, parity);
+                vjp_process<T, NV, K, MODE, true>(a, row0, slot, lanes, c, g, acc, rb, red, parity);
                 row0 = next;
                 next += step;
             }
@@ -482,7 +495,7 @@ __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
             block_sum<1>(t, red, parity);
             s2[0] = t[0];
         }
-        const float r = rsqrtf(s2[0] * inv_d + a.eps);
+        const float r = rsqrtf(__builtin_fmaf(s2[0], inv_d, a.eps));
         const float c = r * r * r * s2[1] * inv_d;
 
         if constexpr (OP >= 2) {
@@ -599,7 +612,7 @@ __global__ __launch_bounds__(1024) void rows_batched_vjp(RowArgs a) {
                     }
                 }
                 block_sum<2>(s2, red, parity);
-                rr[b] = rsqrtf(s2[0] * inv_d + a.eps);
+                rr[b] = rsqrtf(__builtin_fmaf(s2[0], inv_d, a.eps));
                 cc[b] = rr[b] * rr[b] * rr[b] * s2[1] * inv_d;
             }
         }

@@ -35,7 +35,9 @@ constexpr int max_block_threads(int op, int k, int nv, int itemsize) {
 // blocks of at most kVjpPipeBlock threads: there a block holds one row of up
 // to four waves, and two blocks per CU leave the registers the second buffer
 // needs.  Wider blocks (rows of eight or more waves) keep the plain loop,
-// whose lower register count lets two blocks share a CU.
+// whose lower register count lets two blocks share a CU.  The pipelined
+// kernel masks nothing: it serves rows that are exactly lanes * K vectors
+// and row counts that fill every row slot of the block.
 constexpr int kVjpPipeElems = 16;
 constexpr int kVjpPipeBlock = 256;
 

@@ -93,7 +93,7 @@ const void* pick_looped(int jreg) {
 
 template <typename T, int NV, int K, int MODE>
 const void* pick_rows(bool pipe) {
-    if constexpr (K * NV <= kVjpPipeElems) {
+    if constexpr (K * NV <= kVjpPipeElems && MODE != kGrad) {
         if (pipe) return reinterpret_cast<const void*>(&vjp_rows<T, NV, K, MODE, true>);
     } else {
         if (pipe) return nullptr;
