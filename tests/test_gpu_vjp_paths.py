@@ -1,0 +1,96 @@
+"""GPU: the two VJP row loops.  Blocks of at most 256 threads whose rows are
+exactly lanes x K vectors, with a row count that fills every row slot, run
+the software-pipelined unmasked loop; every other register-resident shape
+runs the plain loop.  Checks, on both sides of that rule: parity with the
+fp64 oracle on the first and the last rows (the last row group of every
+block goes through the loop's exit path) and dw over all rows; and dx of
+the pipelined loop bit-identical to the plain loop's (forced through a
+512-thread block, same row geometry) for the VJP and the fused backward."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from _parity import assert_close, assert_dw_close
+from backward_rmsnorm_fwd_two_amd import inputs as I
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def R():
+    import backward_rmsnorm_fwd_two_amd as pkg
+    return pkg
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _edge_rows(rows, n=48):
+    idx = list(range(min(rows, n))) + list(range(max(n, rows - n), rows))
+    return sorted(set(idx))
+
+
+# (rows, D, dtype): pipelined shapes (rows fill the slots, D tiles exactly)
+# next to plain ones (a ragged last group of slots, or D that does not tile)
+CASES = [
+    (8192, 4096, "float16"),    # pipelined: 256 lanes x 2 vectors, one slot
+    (8191, 4096, "float16"),    # still pipelined (one slot), odd row count
+    (4096, 512, "bfloat16"),    # pipelined: 32 lanes, 8 row slots
+    (4093, 512, "bfloat16"),    # plain: last group of slots is ragged
+    (2048, 1024, "float32"),    # pipelined: 128 lanes x 2 x 4 floats, 2 slots
+    (2047, 1024, "float32"),    # plain: ragged
+    (3000, 3072, "float16"),    # plain: 384 vectors on 256 lanes x 2
+    (1000, 1024, "bfloat16"),   # pipelined: 64 lanes, 4 slots
+]
+
+
+@pytest.mark.parametrize("rows,D,dtype", CASES)
+def test_vjp_paths_match_oracle(R, rows, D, dtype):
+    _say(f"vjp paths rows={rows} D={D} {dtype}")
+    c = I.generic(rows, D, dtype, seed=rows + 7 * D)
+    x, w, dy, dr = (c[k].to(DEV) for k in ("x", "w", "dy", "residual"))
+    dx, dw = R.rmsnorm_vjp(x, w, dy, c["eps"], 0.5)
+    dh, dwf = R.fused_add_rmsnorm_vjp(x, w, dy, dr, c["eps"], 0.5)
+    torch.cuda.synchronize()
+    idx = _edge_rows(rows)
+    dxref, _ = O.rmsnorm_vjp(c["x"][idx], c["w"], c["dy"][idx], c["eps"], 0.5)
+    assert_close(dx[idx], dxref, "dx (edge rows)")
+    dhref, _ = O.fused_add_rmsnorm_vjp(c["x"][idx], c["w"], c["dy"][idx], c["residual"][idx], c["eps"], 0.5)
+    assert_close(dh[idx], dhref, "dh (edge rows)")
+    # dw over every row, in slabs
+    dwref = np.zeros(D)
+    for r0 in range(0, rows, 1024):
+        _, part = O.rmsnorm_vjp(c["x"][r0:r0 + 1024], c["w"], c["dy"][r0:r0 + 1024], c["eps"], 0.5)
+        dwref += part
+    assert_dw_close(dw, dwref, "dw")
+    assert_dw_close(dwf, dwref, "fused dw")
+
+
+@pytest.mark.parametrize("rows,D,dtype", [c for c in CASES if c[1] <= 4096])
+def test_pipelined_dx_equals_plain_loop(R, rows, D, dtype):
+    """dx does not depend on the grid or on which loop ran: forcing 512-thread
+    blocks (same lanes, vectors and load width) selects the plain loop."""
+    c = I.generic(rows, D, dtype, seed=3 * rows + D)
+    x, w, dy, dr = (c[k].to(DEV) for k in ("x", "w", "dy", "residual"))
+    q = R.query_config(2, rows, D, x.dtype)
+    if q["vecs_per_lane"] < 0 or q["lanes_per_row"] > 512:
+        pytest.skip("streaming kernel or rows wider than 512 lanes")
+    plain = dict(lanes_per_row=q["lanes_per_row"], vecs_per_lane=q["vecs_per_lane"],
+                 vec_bytes=q["vec_bytes"], block_threads=512, num_blocks=0)
+    _say(f"pipelined vs plain rows={rows} D={D} {dtype} plan={q}")
+    dx_a, _ = R.rmsnorm_vjp(x, w, dy, c["eps"], 0.0)
+    dx_b, _ = R.rmsnorm_vjp(x, w, dy, c["eps"], 0.0, cfg=plain)
+    dh_a, _ = R.fused_add_rmsnorm_vjp(x, w, dy, dr, c["eps"], 1.0)
+    dh_b, _ = R.fused_add_rmsnorm_vjp(x, w, dy, dr, c["eps"], 1.0, cfg=plain)
+    _, dx_g, _ = R.rmsnorm_fwd_vjp(x, w, dy, c["eps"], 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(dx_a, dx_b)
+    assert torch.equal(dh_a, dh_b)
+    assert torch.equal(dx_g, dx_a)
