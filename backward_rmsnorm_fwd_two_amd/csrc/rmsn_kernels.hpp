@@ -430,6 +430,12 @@ __global__ __launch_bounds__(PIPE ? kVjpPipeBlock : max_block_threads(2, K, NV, 
 // vectors of columns (v = threadIdx.x + j * blockDim.x) and sums their dw in
 // registers over the block's rows, in row order, writing this block's
 // partial row once at the end (rows wider than that take rows_batched_vjp).
+// First-pass loads of the two-pass streaming kernels keep the default cache
+// policy: the second pass re-reads the row and finds it in L2 / the
+// last-level cache (non-temporal first-pass loads measured 15-30 % slower
+// at D = 16392..65536: the re-read went back to HBM).
+constexpr bool kPass1Stream = false;
+
 template <int NV>
 __device__ __forceinline__ void block_sum(float (&v)[NV], float* red, int& parity) {
 #pragma unroll
@@ -465,9 +471,9 @@ __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
         float s2[2] = {0.0f, 0.0f};
         for (int v = threadIdx.x; v < a.nvec; v += blockDim.x) {
             const int64_t off = base + (int64_t)v * NV;
-            const Raw<T, NV> px = load_raw<T, NV>(x + off);
+            const Raw<T, NV> px = load_raw<T, NV, kPass1Stream>(x + off);
             if constexpr (OP >= 2) {
-                const Raw<T, NV> pd = load_raw<T, NV>(dy + off);
+                const Raw<T, NV> pd = load_raw<T, NV, kPass1Stream>(dy + off);
                 const Raw<T, NV> pw = load_w<T, NV>(w + (int64_t)v * NV);
 #pragma unroll
                 for (int e = 0; e < NV; ++e) {
@@ -480,7 +486,7 @@ __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
 #pragma unroll
                 for (int e = 0; e < NV; ++e) h[e] = elem(px, e);
                 if constexpr (OP == 1) {
-                    const Raw<T, NV> pr = load_raw<T, NV>(res + off);
+                    const Raw<T, NV> pr = load_raw<T, NV, kPass1Stream>(res + off);
 #pragma unroll
                     for (int e = 0; e < NV; ++e) h[e] += elem(pr, e);
                 }
@@ -601,8 +607,8 @@ __global__ __launch_bounds__(1024) void rows_batched_vjp(RowArgs a) {
                 float s2[2] = {0.0f, 0.0f};
                 for (int v = threadIdx.x; v < a.nvec; v += blockDim.x) {
                     const int64_t off = base + (int64_t)v * NV;
-                    const Raw<T, NV> px = load_raw<T, NV>(x + off);
-                    const Raw<T, NV> pd = load_raw<T, NV>(dy + off);
+                    const Raw<T, NV> px = load_raw<T, NV, kPass1Stream>(x + off);
+                    const Raw<T, NV> pd = load_raw<T, NV, kPass1Stream>(dy + off);
                     const Raw<T, NV> pw = load_w<T, NV>(w + (int64_t)v * NV);
 #pragma unroll
                     for (int e = 0; e < NV; ++e) {
