@@ -239,7 +239,12 @@ int silu_gate_vjp_cfg(const void *x, const void *dy, void *dx, int64_t rows, int
 /* Fill *out with the configuration the automatic choice makes for `op` on
  * this shape, assuming every pointer is 16-byte aligned (`align_bytes` = the
  * largest power of two dividing every pointer, capped at 16, to model other
- * alignments).  Returns RMSN_OK or an argument error. */
+ * alignments).  Returns RMSN_OK or an argument error.  For the backward forms
+ * the library additionally picks, per call, between two row loops of the same
+ * geometry and arithmetic: a software-pipelined one (blocks of at most 256
+ * threads, rows of exactly lanes_per_row * vecs_per_lane vectors, a row count
+ * that fills every row slot; not for the grad call) and the plain one; the
+ * choice does not change any result. */
 int rmsn_query_config(int op, int64_t rows, int64_t D, int dt, int align_bytes,
                       rmsn_config_t *out);
 
