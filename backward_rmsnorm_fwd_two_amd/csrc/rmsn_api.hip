@@ -70,6 +70,8 @@ struct Plan {
     int block = 256;
     int64_t grid = 1;
     size_t shmem = 0;
+    bool pipe = false;        // backward forms: the software-pipelined row kernel
+    bool fixed_lanes = false; // ... in an instance with the lanes fixed at compile time
 };
 
 // The kernel plan for one call.  `align` is the largest power of two (<= 16)
@@ -164,9 +166,27 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
             p->block = block;
             const int nslots = block / lanes;
             const int64_t groups = (rows + nslots - 1) / nslots;
+            // Backward forms: the software-pipelined kernel stores
+            // unconditionally, so it serves rows that are exactly lanes * k
+            // vectors and row counts that fill every row slot.  The grad
+            // call keeps the plain kernel: pipelined it measured slower (55.0
+            // vs 53 us at 8192 x 4096 fp16), and its dx then differed from
+            // the VJP's by one fp16 ulp in a few elements of the last row
+            // group.
+            p->pipe = vjp && op != RMSN_OP_GRAD && k * p->nv <= rmsn::kVjpPipeElems &&
+                      block <= rmsn::kVjpPipeBlock && (int64_t)lanes * k == p->nvec && rows % nslots == 0;
+            p->fixed_lanes = p->pipe &&
+                             rmsn::vjp_kernel_fixed_lanes(dt, p->nv, k, op == RMSN_OP_FUSED_VJP ? 2 : 0, lanes) != nullptr;
             int64_t grid;
             if (cfg && cfg->num_blocks) {
                 grid = cfg->num_blocks;
+            } else if (p->fixed_lanes) {
+                // one persistent block per CU: with the row width fixed at
+                // compile time the pipelined kernel keeps HBM busy with four
+                // waves per CU, and half the partial rows make the combine
+                // cheaper (8192 x 4096 fp16: VJP 39.2 us vs 40.9 at two
+                // blocks per CU)
+                grid = std::min<int64_t>(groups, std::min<int64_t>(kMaxPartialRows, cus));
             } else if (vjp) {
                 // Two persistent blocks per CU: every extra partial row costs
                 // D * 4 bytes written and re-read by the combine.
@@ -367,14 +387,9 @@ int vjp_impl(const void* x, const void* w, const void* dy, void* y, const void* 
         for (const Range& o : all)
             if (overlaps(rws, o)) return RMSN_E_OVERLAP;
     }
-    // the pipelined kernel stores unconditionally: every vector of a row in
-    // range (lanes * k == nvec) and every row slot of every group a real row.
-    // The grad call keeps the plain kernel: pipelined it measured slower
-    // (55.0 vs 53 us at 8192 x 4096 fp16), and its dx then differed from the
-    // VJP's by one fp16 ulp in a few elements of the last row group.
-    const bool pipe = !grad && p.k > 0 && p.k * p.nv <= rmsn::kVjpPipeElems && p.block <= rmsn::kVjpPipeBlock &&
-                      static_cast<int64_t>(p.lanes) * p.k == p.nvec && rows % (p.block / p.lanes) == 0;
-    const void* fn = rmsn::vjp_kernel(dt, p.nv, p.k, grad ? 1 : resgrad ? 2 : 0, p.jreg, pipe);
+    const int mode = grad ? 1 : resgrad ? 2 : 0;
+    const void* fn = p.fixed_lanes ? rmsn::vjp_kernel_fixed_lanes(dt, p.nv, p.k, mode, p.lanes) : nullptr;
+    if (!fn) fn = rmsn::vjp_kernel(dt, p.nv, p.k, mode, p.jreg, p.pipe);
     if (!fn) return RMSN_E_CONFIG;
 
     RowArgs a;

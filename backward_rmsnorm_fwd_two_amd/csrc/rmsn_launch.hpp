@@ -53,6 +53,9 @@ const void* fwd_kernel(int dt, int nv, int k, bool fused);
 // pipe: the software-pipelined register kernel (k > 0, k * nv <=
 // kVjpPipeElems, block <= kVjpPipeBlock).
 const void* vjp_kernel(int dt, int nv, int k, int mode, int jreg, bool pipe);
+// The pipelined VJP kernel with `lanes` fixed at compile time, or nullptr
+// where no such instance exists (then vjp_kernel(..., pipe = true) serves).
+const void* vjp_kernel_fixed_lanes(int dt, int nv, int k, int mode, int lanes);
 // dw_dt: dtype of dw (fp32, or the weight dtype).
 const void* dw_combine_kernel(int dw_dt);
 // Gated activation silu(x[:, :d]) * x[:, d:2d]: NV elements per load, U

@@ -437,11 +437,14 @@ def test_grad_call_poc_small_and_8192x4096(R):
     check_grad(R, c["x"], c["w"], c["dy"], c["eps"], c["weight_bias"], "poc_small")
     c = I.poc_8192x4096()
     _, dx, dw = check_grad(R, c["x"], c["w"], c["dy"], c["eps"], c["weight_bias"], "poc")
-    # the grad call's dx and dw are the VJP's, bit for bit (same plan, same arithmetic)
+    # the grad call's dx is the VJP's, bit for bit (same row geometry, same
+    # arithmetic); dw too when both use the same grid (the same partial rows)
     dx2, dw2 = R.rmsnorm_vjp(_gpu(c["x"]), _gpu(c["w"]), _gpu(c["dy"]), c["eps"], c["weight_bias"])
     torch.cuda.synchronize()
     assert torch.equal(dx.view(torch.int16), dx2.view(torch.int16))
-    assert torch.equal(dw.view(torch.int32), dw2.view(torch.int32))
+    rows, D = c["x"].shape
+    if R.query_config(3, rows, D, dx.dtype)["num_blocks"] == R.query_config(2, rows, D, dx.dtype)["num_blocks"]:
+        assert torch.equal(dw.view(torch.int32), dw2.view(torch.int32))
 
 
 @pytest.mark.parametrize("D", AXIS_LIST + [4096, 8192, 70001])

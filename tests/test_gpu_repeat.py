@@ -73,9 +73,12 @@ def test_repeat_backward_ops(R, rows, D, dtype):
     _same(vjp, "rmsnorm_vjp")
     _same(grad, "rmsnorm_fwd_vjp")
     _same(fused, "fused_add_rmsnorm_vjp")
-    # the VJP and the grad call share dx and dw bit for bit; the grad call's
-    # y (row sums in the VJP's lane order) is checked against the oracle
-    assert torch.equal(grad[0][1], vjp[0][0]) and torch.equal(grad[0][2], vjp[0][1])
+    # the VJP and the grad call share dx bit for bit, and dw when both use the
+    # same grid; the grad call's y (row sums in the VJP's lane order) is
+    # checked against the oracle
+    assert torch.equal(grad[0][1], vjp[0][0])
+    if R.query_config(3, rows, D, x.dtype)["num_blocks"] == R.query_config(2, rows, D, x.dtype)["num_blocks"]:
+        assert torch.equal(grad[0][2], vjp[0][1])
     n = _lead(rows)
     assert_close(grad[0][0][:n], O.rmsnorm_fwd(c["x"][:n], c["w"], 1e-6, 0.0)[0], "grad y")
     if rows <= 64:
