@@ -173,19 +173,27 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
             // vs 53 us at 8192 x 4096 fp16), and its dx then differed from
             // the VJP's by one fp16 ulp in a few elements of the last row
             // group.
+            // Blocks wider than kVjpPipeBlock are pipelined only as a whole
+            // 512-lane row in an instance with the lanes fixed (the generic
+            // pipelined kernel needs more registers than two such blocks per
+            // CU leave; with the width fixed, one block per CU runs faster).
+            const bool whole_wide_row = lanes == rmsn::kVjpPipeFixedMax && block == lanes;
             p->pipe = vjp && op != RMSN_OP_GRAD && k * p->nv <= rmsn::kVjpPipeElems &&
-                      block <= rmsn::kVjpPipeBlock && (int64_t)lanes * k == p->nvec && rows % nslots == 0;
+                      (block <= rmsn::kVjpPipeBlock || whole_wide_row) && (int64_t)lanes * k == p->nvec &&
+                      rows % nslots == 0;
             p->fixed_lanes = p->pipe &&
                              rmsn::vjp_kernel_fixed_lanes(dt, p->nv, k, op == RMSN_OP_FUSED_VJP ? 2 : 0, lanes) != nullptr;
+            if (p->pipe && !p->fixed_lanes && block > rmsn::kVjpPipeBlock) p->pipe = false;
             int64_t grid;
             if (cfg && cfg->num_blocks) {
                 grid = cfg->num_blocks;
             } else if (p->fixed_lanes) {
                 // one persistent block per CU: with the row width fixed at
                 // compile time the pipelined kernel keeps HBM busy with four
-                // waves per CU, and half the partial rows make the combine
-                // cheaper (8192 x 4096 fp16: VJP 39.2 us vs 40.9 at two
-                // blocks per CU)
+                // (or eight) waves per CU, and half the partial rows make the
+                // combine cheaper (8192 x 4096 fp16: VJP 39.2 us vs 40.9 at
+                // two blocks per CU; 32768 x 8192 bf16: 260 us vs 266 for the
+                // plain loop)
                 grid = std::min<int64_t>(groups, std::min<int64_t>(kMaxPartialRows, cus));
             } else if (vjp) {
                 // Two persistent blocks per CU: every extra partial row costs

@@ -302,13 +302,13 @@ __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int 
 // instances for the common geometries), so the row reductions compile
 // without branches on the row width; 0: taken from the arguments.
 template <typename T, int NV, int K, int MODE, bool PIPE = false, int LANES = 0>
-__global__ __launch_bounds__(PIPE ? kVjpPipeBlock : max_block_threads(2, K, NV, sizeof(T))) void vjp_rows(RowArgs a) {
+__global__ __launch_bounds__(PIPE ? (LANES > kVjpPipeBlock ? LANES : kVjpPipeBlock) : max_block_threads(2, K, NV, sizeof(T))) void vjp_rows(RowArgs a) {
     static_assert(!PIPE || K * NV <= kVjpPipeElems, "pipelined instances hold two row groups");
-    static_assert(LANES == 0 || (PIPE && (LANES & (LANES - 1)) == 0 && LANES <= kVjpPipeBlock),
+    static_assert(LANES == 0 || (PIPE && (LANES & (LANES - 1)) == 0 && LANES <= kVjpPipeFixedMax),
                   "fixed lane counts are pipelined powers of two");
     extern __shared__ float dyn[];
     __shared__ float red[2 * 16 * 2];
-    constexpr int kShift = LANES >= 256 ? 8 : LANES >= 128 ? 7 : LANES >= 64 ? 6 : LANES >= 32 ? 5
+    constexpr int kShift = LANES >= 512 ? 9 : LANES >= 256 ? 8 : LANES >= 128 ? 7 : LANES >= 64 ? 6 : LANES >= 32 ? 5
                          : LANES >= 16 ? 4 : LANES >= 8 ? 3 : LANES >= 4 ? 2 : LANES >= 2 ? 1 : 0;
     const int lanes = LANES > 0 ? LANES : a.lanes;
     const int lshift = LANES > 0 ? kShift : a.lshift;

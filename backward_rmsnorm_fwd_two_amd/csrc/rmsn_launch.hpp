@@ -40,6 +40,10 @@ constexpr int max_block_threads(int op, int k, int nv, int itemsize) {
 // and row counts that fill every row slot of the block.
 constexpr int kVjpPipeElems = 16;
 constexpr int kVjpPipeBlock = 256;
+// Instances with the lanes per row fixed at compile time also exist for rows
+// of up to this many lanes (a 512-lane row runs pipelined in a 512-thread
+// block, one block per CU).
+constexpr int kVjpPipeFixedMax = 512;
 
 inline int dtype_size(int dt) { return dt == kF32 ? 4 : 2; }
 

@@ -18,6 +18,7 @@ const void* pick_lanes(int lanes) {
         case 64: return reinterpret_cast<const void*>(&vjp_rows<T, NV, K, MODE, true, 64>);
         case 128: return reinterpret_cast<const void*>(&vjp_rows<T, NV, K, MODE, true, 128>);
         case 256: return reinterpret_cast<const void*>(&vjp_rows<T, NV, K, MODE, true, 256>);
+        case 512: return reinterpret_cast<const void*>(&vjp_rows<T, NV, K, MODE, true, 512>);
         default: return nullptr;
     }
 }

@@ -1,7 +1,8 @@
-"""GPU: the two VJP row loops.  Blocks of at most 256 threads whose rows are
-exactly lanes x K vectors, with a row count that fills every row slot, run
-the software-pipelined unmasked loop; every other register-resident shape
-runs the plain loop.  Checks, on both sides of that rule: parity with the
+"""GPU: the two VJP row loops.  Blocks of at most 256 threads (or a whole
+512-lane row in a 512-thread block) whose rows are exactly lanes x K
+vectors, with a row count that fills every row slot, run the
+software-pipelined unmasked loop; every other register-resident shape runs
+the plain loop.  Checks, on both sides of that rule: parity with the
 fp64 oracle on the first and the last rows (the last row group of every
 block goes through the loop's exit path) and dw over all rows; and dx of
 the pipelined loop bit-identical to the plain loop's (forced through a
@@ -48,6 +49,9 @@ CASES = [
     (2047, 1024, "float32"),    # plain: ragged
     (3000, 3072, "float16"),    # plain: 384 vectors on 256 lanes x 2
     (1000, 1024, "bfloat16"),   # pipelined: 64 lanes, 4 slots
+    (1024, 8192, "bfloat16"),   # pipelined: a 512-lane row per 512-thread block
+    (1023, 8192, "float16"),    # pipelined, odd row count
+    (512, 4096, "float32"),     # pipelined: 512 lanes x 2 x 4 floats
 ]
 
 
@@ -73,17 +77,20 @@ def test_vjp_paths_match_oracle(R, rows, D, dtype):
     assert_dw_close(dwf, dwref, "fused dw")
 
 
-@pytest.mark.parametrize("rows,D,dtype", [c for c in CASES if c[1] <= 4096])
+@pytest.mark.parametrize("rows,D,dtype", CASES)
 def test_pipelined_dx_equals_plain_loop(R, rows, D, dtype):
-    """dx does not depend on the grid or on which loop ran: forcing 512-thread
-    blocks (same lanes, vectors and load width) selects the plain loop."""
+    """dx does not depend on the grid or on which loop ran: forcing a block
+    with two row slots (same lanes, vectors and load width) selects the plain
+    loop."""
     c = I.generic(rows, D, dtype, seed=3 * rows + D)
     x, w, dy, dr = (c[k].to(DEV) for k in ("x", "w", "dy", "residual"))
     q = R.query_config(2, rows, D, x.dtype)
     if q["vecs_per_lane"] < 0 or q["lanes_per_row"] > 512:
         pytest.skip("streaming kernel or rows wider than 512 lanes")
+    if q["vecs_per_lane"] * q["vec_bytes"] // x.element_size() > 16 and q["lanes_per_row"] == 512:
+        pytest.skip("no 1024-thread instance for this width")
     plain = dict(lanes_per_row=q["lanes_per_row"], vecs_per_lane=q["vecs_per_lane"],
-                 vec_bytes=q["vec_bytes"], block_threads=512, num_blocks=0)
+                 vec_bytes=q["vec_bytes"], block_threads=max(512, 2 * q["lanes_per_row"]), num_blocks=0)
     _say(f"pipelined vs plain rows={rows} D={D} {dtype} plan={q}")
     dx_a, _ = R.rmsnorm_vjp(x, w, dy, c["eps"], 0.0)
     dx_b, _ = R.rmsnorm_vjp(x, w, dy, c["eps"], 0.0, cfg=plain)
