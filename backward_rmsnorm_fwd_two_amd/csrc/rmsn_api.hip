@@ -312,7 +312,8 @@ int fwd_impl(bool fused, const void* x, const void* res, const void* w, void* y,
     Plan p;
     st = make_plan(fused ? RMSN_OP_FUSED : RMSN_OP_FWD, rows, D, dt, align, cfg, &p);
     if (st != RMSN_OK) return st;
-    const void* fn = rmsn::fwd_kernel(dt, p.nv, p.k, fused);
+    const void* fn = p.k > 0 ? rmsn::fwd_kernel_fixed_lanes(dt, p.nv, p.k, fused, p.lanes) : nullptr;
+    if (!fn) fn = rmsn::fwd_kernel(dt, p.nv, p.k, fused);
     if (!fn) return RMSN_E_CONFIG;
 
     RowArgs a;

@@ -39,10 +39,62 @@ const void* pick_fwd_dt(int dt, int nv, int k) {
     }
 }
 
+// 16-byte loads, one or two vectors per lane: the instance with the lanes
+// fixed at compile time -- 32 to 1024 lanes per row for the forward, 32 to
+// 256 for the fused forward (measured on cold data: forward 0.8-3 % faster
+// at every width, e.g. 8192 x 4096 fp16 24.4 vs 25.3 us; fused forward 4 %
+// faster up to 256 lanes, 1-2 % slower at 512 and 1024)
+template <typename T, int K, bool FUSED>
+const void* pick_fixed(int lanes) {
+    constexpr int NV = 16 / static_cast<int>(sizeof(T));
+    if constexpr (FUSED) {
+        switch (lanes) {
+            case 32: return reinterpret_cast<const void*>(&fwd_rows<T, NV, K, FUSED, 32>);
+            case 64: return reinterpret_cast<const void*>(&fwd_rows<T, NV, K, FUSED, 64>);
+            case 128: return reinterpret_cast<const void*>(&fwd_rows<T, NV, K, FUSED, 128>);
+            case 256: return reinterpret_cast<const void*>(&fwd_rows<T, NV, K, FUSED, 256>);
+            default: return nullptr;
+        }
+    }
+    switch (lanes) {
+        case 32: return reinterpret_cast<const void*>(&fwd_rows<T, NV, K, FUSED, 32>);
+        case 64: return reinterpret_cast<const void*>(&fwd_rows<T, NV, K, FUSED, 64>);
+        case 128: return reinterpret_cast<const void*>(&fwd_rows<T, NV, K, FUSED, 128>);
+        case 256: return reinterpret_cast<const void*>(&fwd_rows<T, NV, K, FUSED, 256>);
+        case 512: return reinterpret_cast<const void*>(&fwd_rows<T, NV, K, FUSED, 512>);
+        case 1024: return reinterpret_cast<const void*>(&fwd_rows<T, NV, K, FUSED, 1024>);
+        default: return nullptr;
+    }
+}
+
+template <typename T, bool FUSED>
+const void* pick_fixed_k(int nv, int k, int lanes) {
+    if (nv != 16 / static_cast<int>(sizeof(T))) return nullptr;
+    switch (k) {
+        case 1: return pick_fixed<T, 1, FUSED>(lanes);
+        case 2: return pick_fixed<T, 2, FUSED>(lanes);
+        default: return nullptr;
+    }
+}
+
+template <bool FUSED>
+const void* pick_fixed_dt(int dt, int nv, int k, int lanes) {
+    switch (dt) {
+        case kF32: return pick_fixed_k<float, FUSED>(nv, k, lanes);
+        case kF16: return pick_fixed_k<_Float16, FUSED>(nv, k, lanes);
+        case kBF16: return pick_fixed_k<__bf16, FUSED>(nv, k, lanes);
+        default: return nullptr;
+    }
+}
+
 }  // namespace
 
 const void* fwd_kernel(int dt, int nv, int k, bool fused) {
     return fused ? pick_fwd_dt<true>(dt, nv, k) : pick_fwd_dt<false>(dt, nv, k);
+}
+
+const void* fwd_kernel_fixed_lanes(int dt, int nv, int k, bool fused, int lanes) {
+    return fused ? pick_fixed_dt<true>(dt, nv, k, lanes) : pick_fixed_dt<false>(dt, nv, k, lanes);
 }
 
 }  // namespace rmsn

@@ -140,13 +140,21 @@ __device__ __forceinline__ void fwd_process(const RowArgs& a, int64_t row0, int 
     }
 }
 
-template <typename T, int NV, int K, bool FUSED>
+// LANES > 0: the lanes per row fixed at compile time (instances for the
+// common geometries), so the row reduction compiles without branches on the
+// row width; 0: taken from the arguments.
+template <typename T, int NV, int K, bool FUSED, int LANES = 0>
 __global__ __launch_bounds__(max_block_threads(FUSED ? 1 : 0, K, NV, sizeof(T))) void fwd_rows(RowArgs a) {
+    static_assert(LANES == 0 || ((LANES & (LANES - 1)) == 0 && LANES <= 1024), "lanes: a power of two");
     __shared__ float red[2 * 16];
-    const int lanes = a.lanes;
+    constexpr int kShift = LANES >= 1024 ? 10 : LANES >= 512 ? 9 : LANES >= 256 ? 8 : LANES >= 128 ? 7
+                         : LANES >= 64 ? 6 : LANES >= 32 ? 5 : LANES >= 16 ? 4 : LANES >= 8 ? 3
+                         : LANES >= 4 ? 2 : LANES >= 2 ? 1 : 0;
+    const int lanes = LANES > 0 ? LANES : a.lanes;
+    const int lshift = LANES > 0 ? kShift : a.lshift;
     const int lane = threadIdx.x & (lanes - 1);
-    const int slot = threadIdx.x >> a.lshift;
-    const int nslots = blockDim.x >> a.lshift;
+    const int slot = threadIdx.x >> lshift;
+    const int nslots = blockDim.x >> lshift;
     const Cols<K> c(lanes, lane, a.nvec, NV);
     const int64_t step = (int64_t)gridDim.x * nslots;
     int64_t row0 = (int64_t)blockIdx.x * nslots;

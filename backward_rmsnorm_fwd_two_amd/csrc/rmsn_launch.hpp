@@ -50,6 +50,9 @@ inline int dtype_size(int dt) { return dt == kF32 ? 4 : 2; }
 // Kernel entry for (op, dtype, NV, K); K == -1 is the streaming kernel.
 // Returns nullptr for a combination that is not compiled.
 const void* fwd_kernel(int dt, int nv, int k, bool fused);
+// The register forward kernel with `lanes` fixed at compile time, or nullptr
+// where no such instance exists (then fwd_kernel serves).
+const void* fwd_kernel_fixed_lanes(int dt, int nv, int k, bool fused, int lanes);
 // mode: 0 VJP, 1 grad call (also writes y), 2 fused backward (adds the
 // residual-stream gradient).  jreg (streaming kernel only): vectors of dw
 // columns each thread keeps in registers (1, 2, 4, 8), or 0 for rows wider
