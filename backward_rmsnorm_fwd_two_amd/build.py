@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 # into the library.
 CEILING_SRC = "stream_ceiling.hip"
 CEILING_BIN = os.path.join(HERE, "stream_ceiling")
-SOURCES = ["rmsn_fwd.hip", "rmsn_vjp.hip", "rmsn_vjp_lanes.hip", "rmsn_gate.hip", "rmsn_api.hip"]
+SOURCES = ["rmsn_fwd.hip", "rmsn_fwd_waves.hip", "rmsn_vjp.hip", "rmsn_vjp_lanes.hip", "rmsn_vjp_waves.hip",
+           "rmsn_gate.hip", "rmsn_api.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 instructions are disabled for every HIP translation unit.

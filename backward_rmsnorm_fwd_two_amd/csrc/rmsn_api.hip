@@ -19,6 +19,9 @@ using rmsn::RowArgs;
 
 constexpr int kMaxDevices = 64;
 constexpr int kMaxPartialRows = 2048;   // bound on dw partial rows (workspace)
+// Row data a CU should hold in flight in the wave-row VJP, in units of one
+// wave's 16-byte vector of one row tensor (see make_plan).
+constexpr int kWaveRowsInFlight = 15;
 std::atomic<int> g_cu_count[kMaxDevices];
 
 // Compute units of the current device (cached per device; the cache is the
@@ -111,6 +114,95 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
     if (!looped) {
         int lanes = req_l;
         int k = req_k;
+        // Rows of a whole number of waves that is not a power of two (lanes
+        // = 64 W with one or two 16-byte vectors per lane: D = 3072, 5120,
+        // 6144, 7168 ... in 16-bit storage) are tiled exactly by an instance
+        // with the lanes fixed at compile time -- pipelined and unmasked for
+        // the backward forms -- instead of masking part of a power-of-two
+        // lane group.  The grad call keeps the plain loop.
+        if (op != RMSN_OP_GRAD && vb == 16 && (lanes == 0 ? k == 0 : rmsn::wave_rows(lanes))) {
+            int wl = 0, wk = 0;
+            for (int kk = 2; kk >= 1 && wl == 0; --kk) {
+                if ((k != 0 && kk != k) || p->nvec % kk != 0) continue;
+                const int l = p->nvec / kk;
+                if ((lanes == 0 || l == lanes) && rmsn::wave_rows(l) && rmsn::wave_rows_supported(l)) {
+                    wl = l;
+                    wk = kk;
+                }
+            }
+            // The automatic forward takes wave rows with two vectors per lane
+            // up to 768 lanes; with one vector, or at 896 lanes, the masked
+            // power-of-two layout measured as fast or faster (cold 64 MiB
+            // tensors: D = 5120 bf16 24.5 vs 25.8 us; D = 3584 bf16 25.0 vs
+            // 24.2 us, 14336 bf16 28.2 vs 27.0 us).
+            if (wl && lanes == 0 && !vjp && (wk != 2 || wl > 768)) wl = 0;
+            const void* fn = nullptr;
+            if (wl) {
+                fn = vjp ? rmsn::vjp_kernel_fixed_lanes(dt, p->nv, wk, op == RMSN_OP_FUSED_VJP ? 2 : 0, wl)
+                         : rmsn::fwd_kernel_fixed_lanes(dt, p->nv, wk, op == RMSN_OP_FUSED, wl);
+            }
+            // one, two or four rows per block, as the registers allow
+            const int most = vjp ? rmsn::wave_rows_block_max(wl)
+                                 : (4 * wl <= 1024 ? 4 * wl : 2 * wl <= 1024 ? 2 * wl : wl);
+            const int maxb = fn ? std::min(rmsn::max_block_threads(budget_op, wk, p->nv, s), most) : 0;
+            if (fn && wl <= maxb) {
+                // Rows per block and the persistent grid of the backward
+                // forms: each CU needs enough row data in flight, counted as
+                // waves per row x vectors per lane x row tensors loaded (2;
+                // 3 for the fused backward) x rows per block.  Rows per block
+                // double until that reaches kWaveRowsInFlight (as the
+                // registers allow); if it still falls short, two blocks per
+                // CU.  Cold 64 MiB tensors, VJP: D = 1536 bf16 (3 waves, one
+                // vector) 39.4 us at four rows per block vs 63.3 at one;
+                // 2560 fp16 39.4 vs 48.0 at two; 3072 fp16 40.0 vs 44.6 at
+                // two; 5120 fp16 40.7 at one vs 42.3 at two; 3584 bf16 41.1
+                // at two blocks per CU vs 42.2.  Fused backward: 1536 bf16
+                // 47.1 at two rows vs 63.1 at one, 3072 fp16 48.1 at one vs
+                // 51.6 at two.  The forward (not persistent) runs two
+                // three-wave rows per block (D = 3072 fp16 24.0 vs 24.6 us).
+                const int w_units = (wl / 64) * wk * (op == RMSN_OP_FUSED_VJP ? 3 : 2);
+                int block = req_b;
+                if (!block) {
+                    int slots = 1;
+                    if (vjp) {
+                        while (slots < 4 && w_units * slots < kWaveRowsInFlight && 2 * slots * wl <= maxb &&
+                               rows % (2 * slots) == 0)
+                            slots *= 2;
+                    } else if (wl == 192 && 2 * wl <= maxb) {
+                        slots = 2;
+                    }
+                    block = slots * wl;
+                }
+                if (block != wl && block != 2 * wl && block != 4 * wl) return RMSN_E_CONFIG;
+                if (block > maxb) return RMSN_E_CONFIG;
+                // the pipelined kernel fills every row slot
+                if (vjp && rows % (block / wl) != 0) return RMSN_E_CONFIG;
+                const int nslots = block / wl;
+                const int64_t groups = (rows + nslots - 1) / nslots;
+                int64_t grid;
+                if (cfg && cfg->num_blocks) {
+                    grid = cfg->num_blocks;
+                } else if (vjp) {
+                    // persistent: one block per CU, two where the blocks hold
+                    // too little row data
+                    const int per_cu = w_units * nslots < kWaveRowsInFlight ? 2 : 1;
+                    grid = std::min<int64_t>(groups, std::min<int64_t>(kMaxPartialRows, (int64_t)per_cu * cus));
+                } else {
+                    grid = std::min<int64_t>(groups, (int64_t)1 << 20);
+                }
+                if (grid < 1 || grid > ((int64_t)1 << 30)) return RMSN_E_CONFIG;
+                if (vjp && grid > kMaxPartialRows) return RMSN_E_CONFIG;
+                p->lanes = wl;
+                p->k = wk;
+                p->block = block;
+                p->pipe = vjp;
+                p->fixed_lanes = true;
+                p->grid = grid;
+                p->shmem = (vjp && nslots > 1) ? (size_t)block * p->nv * sizeof(float) : 0;
+                return RMSN_OK;
+            }
+            if (lanes != 0) return RMSN_E_CONFIG;  // requested wave rows that do not apply
+        }
         if (lanes == 0 && k == 0) {
             // About 32 bytes of each row tensor per lane: 2 vectors of 16
             // bytes, up to 8 of a narrower width (narrow loads on fewer
@@ -313,7 +405,7 @@ int fwd_impl(bool fused, const void* x, const void* res, const void* w, void* y,
     st = make_plan(fused ? RMSN_OP_FUSED : RMSN_OP_FWD, rows, D, dt, align, cfg, &p);
     if (st != RMSN_OK) return st;
     const void* fn = p.k > 0 ? rmsn::fwd_kernel_fixed_lanes(dt, p.nv, p.k, fused, p.lanes) : nullptr;
-    if (!fn) fn = rmsn::fwd_kernel(dt, p.nv, p.k, fused);
+    if (!fn && !(p.k > 0 && rmsn::wave_rows(p.lanes))) fn = rmsn::fwd_kernel(dt, p.nv, p.k, fused);
     if (!fn) return RMSN_E_CONFIG;
 
     RowArgs a;
@@ -398,7 +490,7 @@ int vjp_impl(const void* x, const void* w, const void* dy, void* y, const void* 
     }
     const int mode = grad ? 1 : resgrad ? 2 : 0;
     const void* fn = p.fixed_lanes ? rmsn::vjp_kernel_fixed_lanes(dt, p.nv, p.k, mode, p.lanes) : nullptr;
-    if (!fn) fn = rmsn::vjp_kernel(dt, p.nv, p.k, mode, p.jreg, p.pipe);
+    if (!fn && !(p.k > 0 && rmsn::wave_rows(p.lanes))) fn = rmsn::vjp_kernel(dt, p.nv, p.k, mode, p.jreg, p.pipe);
     if (!fn) return RMSN_E_CONFIG;
 
     RowArgs a;

@@ -94,6 +94,7 @@ const void* fwd_kernel(int dt, int nv, int k, bool fused) {
 }
 
 const void* fwd_kernel_fixed_lanes(int dt, int nv, int k, bool fused, int lanes) {
+    if (wave_rows(lanes)) return fwd_kernel_wave_rows(dt, nv, k, fused, lanes);
     return fused ? pick_fixed_dt<true>(dt, nv, k, lanes) : pick_fixed_dt<false>(dt, nv, k, lanes);
 }
 

@@ -70,6 +70,35 @@ __device__ __forceinline__ void mask_cols(const Cols<K>& c, Raw<T, NV> (&d)[K]) 
         for (int i = 0; i < Raw<T, NV>::kWords; ++i) d[k].w[i] = c.ok[k] ? d[k].w[i] : 0u;
 }
 
+// A thread's row slot in its block and its lane in the row.  Power-of-two
+// lane counts split threadIdx.x with a mask and a shift (lshift = log2 of
+// the lanes, from the arguments when LANES is 0); a wave-row instance
+// (LANES = 64 W, W not a power of two) divides by the constant LANES.
+struct RowSlot {
+    int lane;
+    int slot;
+    int nslots;
+};
+
+template <int LANES>
+__device__ __forceinline__ RowSlot row_slot(int lshift_arg) {
+    RowSlot r;
+    if constexpr (wave_rows(LANES)) {
+        r.slot = static_cast<int>(threadIdx.x) / LANES;
+        r.lane = static_cast<int>(threadIdx.x) - r.slot * LANES;
+        r.nslots = static_cast<int>(blockDim.x) / LANES;
+    } else {
+        constexpr int kShift = LANES >= 1024 ? 10 : LANES >= 512 ? 9 : LANES >= 256 ? 8 : LANES >= 128 ? 7
+                             : LANES >= 64 ? 6 : LANES >= 32 ? 5 : LANES >= 16 ? 4 : LANES >= 8 ? 3
+                             : LANES >= 4 ? 2 : LANES >= 2 ? 1 : 0;
+        const int lshift = LANES > 0 ? kShift : lshift_arg;
+        r.lane = static_cast<int>(threadIdx.x) & ((1 << lshift) - 1);
+        r.slot = static_cast<int>(threadIdx.x) >> lshift;
+        r.nslots = static_cast<int>(blockDim.x) >> lshift;
+    }
+    return r;
+}
+
 // ------------------------------------------------------------ forward
 // y = x * rsqrt(mean(x^2) + eps) * (wb + w)   (FUSED: x := x + residual,
 // which is also stored rounded as new_residual; the unrounded fp32 sum is
@@ -145,16 +174,14 @@ __device__ __forceinline__ void fwd_process(const RowArgs& a, int64_t row0, int 
 // row width; 0: taken from the arguments.
 template <typename T, int NV, int K, bool FUSED, int LANES = 0>
 __global__ __launch_bounds__(max_block_threads(FUSED ? 1 : 0, K, NV, sizeof(T))) void fwd_rows(RowArgs a) {
-    static_assert(LANES == 0 || ((LANES & (LANES - 1)) == 0 && LANES <= 1024), "lanes: a power of two");
+    static_assert(LANES == 0 || ((LANES & (LANES - 1)) == 0 && LANES <= 1024) || wave_rows_supported(LANES),
+                  "lanes: a power of two or a supported whole number of waves");
     __shared__ float red[2 * 16];
-    constexpr int kShift = LANES >= 1024 ? 10 : LANES >= 512 ? 9 : LANES >= 256 ? 8 : LANES >= 128 ? 7
-                         : LANES >= 64 ? 6 : LANES >= 32 ? 5 : LANES >= 16 ? 4 : LANES >= 8 ? 3
-                         : LANES >= 4 ? 2 : LANES >= 2 ? 1 : 0;
     const int lanes = LANES > 0 ? LANES : a.lanes;
-    const int lshift = LANES > 0 ? kShift : a.lshift;
-    const int lane = threadIdx.x & (lanes - 1);
-    const int slot = threadIdx.x >> lshift;
-    const int nslots = blockDim.x >> lshift;
+    const RowSlot rs = row_slot<LANES>(a.lshift);
+    const int lane = rs.lane;
+    const int slot = rs.slot;
+    const int nslots = rs.nslots;
     const Cols<K> c(lanes, lane, a.nvec, NV);
     const int64_t step = (int64_t)gridDim.x * nslots;
     int64_t row0 = (int64_t)blockIdx.x * nslots;
@@ -310,19 +337,20 @@ __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int 
 // instances for the common geometries), so the row reductions compile
 // without branches on the row width; 0: taken from the arguments.
 template <typename T, int NV, int K, int MODE, bool PIPE = false, int LANES = 0>
-__global__ __launch_bounds__(PIPE ? (LANES > kVjpPipeBlock ? LANES : kVjpPipeBlock) : max_block_threads(2, K, NV, sizeof(T))) void vjp_rows(RowArgs a) {
+__global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
+                             : wave_rows(LANES) ? wave_rows_block_max(LANES)
+                             : (LANES > kVjpPipeBlock ? LANES : kVjpPipeBlock)) void vjp_rows(RowArgs a) {
     static_assert(!PIPE || K * NV <= kVjpPipeElems, "pipelined instances hold two row groups");
-    static_assert(LANES == 0 || (PIPE && (LANES & (LANES - 1)) == 0 && LANES <= kVjpPipeFixedMax),
-                  "fixed lane counts are pipelined powers of two");
+    static_assert(LANES == 0 || (PIPE && (((LANES & (LANES - 1)) == 0 && LANES <= kVjpPipeFixedMax) ||
+                                          wave_rows_supported(LANES))),
+                  "fixed lane counts are pipelined: powers of two or supported whole numbers of waves");
     extern __shared__ float dyn[];
     __shared__ float red[2 * 16 * 2];
-    constexpr int kShift = LANES >= 512 ? 9 : LANES >= 256 ? 8 : LANES >= 128 ? 7 : LANES >= 64 ? 6 : LANES >= 32 ? 5
-                         : LANES >= 16 ? 4 : LANES >= 8 ? 3 : LANES >= 4 ? 2 : LANES >= 2 ? 1 : 0;
     const int lanes = LANES > 0 ? LANES : a.lanes;
-    const int lshift = LANES > 0 ? kShift : a.lshift;
-    const int lane = threadIdx.x & (lanes - 1);
-    const int slot = threadIdx.x >> lshift;
-    const int nslots = blockDim.x >> lshift;
+    const RowSlot rs = row_slot<LANES>(a.lshift);
+    const int lane = rs.lane;
+    const int slot = rs.slot;
+    const int nslots = rs.nslots;
     const Cols<K> c(lanes, lane, a.nvec, NV);
     const int64_t step = (int64_t)gridDim.x * nslots;
     int64_t row0 = (int64_t)blockIdx.x * nslots;

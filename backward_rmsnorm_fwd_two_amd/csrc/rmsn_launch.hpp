@@ -45,6 +45,29 @@ constexpr int kVjpPipeBlock = 256;
 // block, one block per CU).
 constexpr int kVjpPipeFixedMax = 512;
 
+// Rows of a whole number of waves that is not a power of two (lanes = 64 W,
+// W = 3, 5, 6, 7, 10, 12, 14): D = 3072, 5120, 6144, 7168 ... in 16-bit
+// storage tile such rows exactly, where a power-of-two lane count would leave
+// a quarter to a half of its vectors masked.  Instances exist with the lanes
+// fixed at compile time, in blocks of one or two rows.
+constexpr bool wave_rows(int lanes) { return lanes > 64 && (lanes & (lanes - 1)) != 0; }
+constexpr bool wave_rows_supported(int lanes) {
+    return lanes == 192 || lanes == 320 || lanes == 384 || lanes == 448 || lanes == 640 ||
+           lanes == 768 || lanes == 896;
+}
+// Largest block of a pipelined VJP wave-row instance: up to four rows while
+// they fit 768 threads (the two register buffers need about 90-170 VGPRs;
+// 768 threads leave 170, larger blocks would cap below that).
+constexpr int wave_rows_block_max(int lanes) {
+    return 4 * lanes <= 768 ? 4 * lanes : 2 * lanes <= 768 ? 2 * lanes : lanes;
+}
+// Pipelined VJP wave-row instances that hold their registers without
+// spilling at one row per block: 16-bit rows with two vectors per lane need
+// up to 168 VGPRs, more than rows of 12 or 14 waves leave (170 / 128).
+constexpr bool vjp_wave_rows_fit(int lanes, int k, int itemsize) {
+    return !(itemsize == 2 && k == 2 && lanes > 640);
+}
+
 inline int dtype_size(int dt) { return dt == kF32 ? 4 : 2; }
 
 // Kernel entry for (op, dtype, NV, K); K == -1 is the streaming kernel.
@@ -63,6 +86,9 @@ const void* vjp_kernel(int dt, int nv, int k, int mode, int jreg, bool pipe);
 // The pipelined VJP kernel with `lanes` fixed at compile time, or nullptr
 // where no such instance exists (then vjp_kernel(..., pipe = true) serves).
 const void* vjp_kernel_fixed_lanes(int dt, int nv, int k, int mode, int lanes);
+// The wave-row instances (lanes = 64 W, W not a power of two), or nullptr.
+const void* fwd_kernel_wave_rows(int dt, int nv, int k, bool fused, int lanes);
+const void* vjp_kernel_wave_rows(int dt, int nv, int k, int mode, int lanes);
 // dw_dt: dtype of dw (fp32, or the weight dtype).
 const void* dw_combine_kernel(int dw_dt);
 // Gated activation silu(x[:, :d]) * x[:, d:2d]: NV elements per load, U

@@ -3,7 +3,11 @@ vector slots take the streaming kernel (512-thread blocks); full rows and
 the 4-vector fp32 instance stay in registers.  Checks the automatic plan on
 both sides of that rule and parity of the forward with the fp64 oracle on
 the first and last rows, plus the same rows forced through the register
-kernel."""
+kernel.  Rows of a whole number of waves that is not a power of two (wave
+rows) with two 16-byte vectors per lane take an exact-tiling instance of
+up to 768 lanes (two three-wave rows per block); its plan, parity of the
+forward and the fused forward, forced one-vector and 896-lane instances,
+and outputs bit-identical across rows per block."""
 import sys
 
 import pytest
@@ -25,7 +29,7 @@ def R():
 
 
 # (rows, D, dtype, streamed by the automatic plan)
-CASES = [(600, 8200, "bfloat16", True), (500, 10240, "float16", True), (300, 16392, "bfloat16", True),
+CASES = [(600, 8200, "bfloat16", True), (500, 10248, "float16", True), (300, 16392, "bfloat16", True),
          (700, 4100, "float32", True), (400, 16384, "bfloat16", False), (300, 8200, "float32", False),
          (500, 12288, "bfloat16", False)]
 
@@ -48,3 +52,61 @@ def test_sparse_forward_rows_stream(R, rows, D, dtype, streamed):
     yref, _ = O.rmsnorm_fwd(c["x"][idx], c["w"], c["eps"], 1.0)
     assert_close(y[idx], yref, "y")
     assert_close(y_reg[idx], yref, "y (register kernel)")
+
+
+def _is_pow2(v):
+    return v > 0 and (v & (v - 1)) == 0
+
+
+# (rows, D, dtype, lanes, rows per block) of the automatic forward plan;
+# lanes None: the power-of-two layout
+WAVE = [(4000, 3072, "float16", 192, 2), (4001, 3072, "bfloat16", 192, 2), (1001, 5120, "bfloat16", 320, 1),
+        (700, 6144, "float16", 384, 1), (333, 12288, "bfloat16", 768, 1), (500, 10240, "float16", 640, 1),
+        (700, 3072, "float32", 384, 1), (500, 3584, "bfloat16", None, None), (200, 14336, "bfloat16", None, None)]
+
+
+@pytest.mark.parametrize("rows,D,dtype,lanes,slots", WAVE)
+def test_wave_rows_forward(R, rows, D, dtype, lanes, slots):
+    print(f"forward wave rows rows={rows} D={D} {dtype}", flush=True)
+    sys.stdout.flush()
+    c = I.generic(rows, D, dtype, seed=2 * rows + D)
+    x, w, res = c["x"].to(DEV), c["w"].to(DEV), c["residual"].to(DEV)
+    nvec = D * x.element_size() // 16
+    for op in (0, 1):
+        q = R.query_config(op, rows, D, x.dtype)
+        if lanes is None:
+            assert _is_pow2(q["lanes_per_row"]) or q["vecs_per_lane"] == -1, q
+        else:
+            assert q["lanes_per_row"] == lanes and q["vecs_per_lane"] == 2 and q["vec_bytes"] == 16, q
+            assert q["block_threads"] == slots * lanes and q["num_blocks"] == (rows + slots - 1) // slots, q
+    # the automatic plan, and (power-of-two plans) the wave-row instance the
+    # row also tiles, forced: one vector per lane on 64 W lanes
+    cfgs = [None]
+    if lanes is None:
+        for k in (1, 2):
+            wl = nvec // k
+            if nvec % k == 0 and wl % 64 == 0 and not _is_pow2(wl) and wl <= 1024:
+                cfgs.append(dict(lanes_per_row=wl, vecs_per_lane=k, vec_bytes=16, block_threads=wl, num_blocks=0))
+    else:
+        for s_ in (1, 2, 4):
+            if s_ != slots and s_ * lanes <= 1024:
+                cfgs.append(dict(lanes_per_row=lanes, vecs_per_lane=2, vec_bytes=16, block_threads=s_ * lanes,
+                                 num_blocks=0))
+    assert lanes is not None or len(cfgs) > 1
+    idx = list(range(16)) + list(range(rows - 16, rows))
+    yref, _ = O.rmsnorm_fwd(c["x"][idx], c["w"], c["eps"], 1.0)
+    nref, href = O.fused_add_rmsnorm_fwd(c["x"][idx], c["residual"][idx], c["w"], c["eps"], 1.0)
+    first = None
+    for cfg in cfgs:
+        y = R.rmsnorm_fwd(x, w, c["eps"], 1.0, cfg=cfg)
+        n, h = R.fused_add_rmsnorm_fwd(x, res, w, c["eps"], 1.0, cfg=cfg)
+        torch.cuda.synchronize()
+        assert_close(y[idx], yref, f"y cfg={cfg}")
+        assert_close(n[idx], nref, f"normed cfg={cfg}")
+        assert_close(h[idx], href, f"new_residual cfg={cfg}")
+        if lanes is not None:
+            # same lanes and vectors: rows per block change nothing
+            if first is None:
+                first = (y, n, h)
+            else:
+                assert torch.equal(y, first[0]) and torch.equal(n, first[1]) and torch.equal(h, first[2]), cfg

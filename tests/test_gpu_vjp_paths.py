@@ -1,12 +1,16 @@
 """GPU: the two VJP row loops.  Blocks of at most 256 threads (or a whole
 512-lane row in a 512-thread block) whose rows are exactly lanes x K
 vectors, with a row count that fills every row slot, run the
-software-pipelined unmasked loop; every other register-resident shape runs
+software-pipelined unmasked loop, and so do rows of a whole number of
+waves that is not a power of two (wave rows: 3, 5, 6, 7, 10 waves ...,
+one to four rows per block); every other register-resident shape runs
 the plain loop.  Checks, on both sides of that rule: parity with the
 fp64 oracle on the first and the last rows (the last row group of every
-block goes through the loop's exit path) and dw over all rows; and dx of
+block goes through the loop's exit path) and dw over all rows; dx of
 the pipelined loop bit-identical to the plain loop's (forced through a
-512-thread block, same row geometry) for the VJP and the fused backward."""
+512-thread block, same row geometry) for the VJP and the fused backward;
+and for wave rows, the plan's geometry and dx bit-identical across rows
+per block and grids."""
 import sys
 
 import numpy as np
@@ -47,7 +51,18 @@ CASES = [
     (4093, 512, "bfloat16"),    # plain: last group of slots is ragged
     (2048, 1024, "float32"),    # pipelined: 128 lanes x 2 x 4 floats, 2 slots
     (2047, 1024, "float32"),    # plain: ragged
-    (3000, 3072, "float16"),    # plain: 384 vectors on 256 lanes x 2
+    (3000, 3072, "float16"),    # wave rows: 3 waves x 2 vectors, two rows per block
+    (1200, 1536, "bfloat16"),   # wave rows: 3 waves x 1 vector, four rows per block
+    (1202, 1536, "float16"),    # wave rows, rows % 4 == 2: two rows per block
+    (601, 2560, "float16"),     # wave rows: 5 waves x 1, odd rows: one row, two blocks per CU
+    (1001, 5120, "bfloat16"),   # wave rows: 5 waves x 2
+    (700, 6144, "float16"),     # wave rows: 6 waves x 2
+    (513, 3584, "bfloat16"),    # wave rows: 7 waves x 1, two blocks per CU
+    (257, 7168, "float16"),     # wave rows: 7 waves x 2
+    (300, 10240, "bfloat16"),   # wave rows: 10 waves x 2
+    (900, 3072, "float32"),     # wave rows: 6 waves x 2 x 4 floats
+    (333, 7168, "float32"),     # wave rows: 14 waves x 2 x 4 floats
+    (130, 12288, "float16"),    # 12 waves x 2 in 16-bit would spill: plain loop, 1024 lanes
     (1000, 1024, "bfloat16"),   # pipelined: 64 lanes, 4 slots
     (1024, 8192, "bfloat16"),   # pipelined: a 512-lane row per 512-thread block
     (1023, 8192, "float16"),    # pipelined, odd row count
@@ -87,6 +102,8 @@ def test_pipelined_dx_equals_plain_loop(R, rows, D, dtype):
     q = R.query_config(2, rows, D, x.dtype)
     if q["vecs_per_lane"] < 0 or q["lanes_per_row"] > 512:
         pytest.skip("streaming kernel or rows wider than 512 lanes")
+    if q["lanes_per_row"] & (q["lanes_per_row"] - 1):
+        pytest.skip("wave rows: no plain-loop instance at this width (test_wave_rows_geometry_and_bitwise)")
     if q["vecs_per_lane"] * q["vec_bytes"] // x.element_size() > 16 and q["lanes_per_row"] == 512:
         pytest.skip("no 1024-thread instance for this width")
     plain = dict(lanes_per_row=q["lanes_per_row"], vecs_per_lane=q["vecs_per_lane"],
@@ -101,3 +118,67 @@ def test_pipelined_dx_equals_plain_loop(R, rows, D, dtype):
     assert torch.equal(dx_a, dx_b)
     assert torch.equal(dh_a, dh_b)
     assert torch.equal(dx_g, dx_a)
+
+
+def _is_pow2(v):
+    return v > 0 and (v & (v - 1)) == 0
+
+
+# (rows, D, dtype, lanes, vectors per lane, rows per block, blocks per CU) of
+# the automatic plan for the VJP; None: not wave rows
+WAVE = [
+    (3000, 3072, "float16", 192, 2, 2, 1),
+    (1200, 1536, "bfloat16", 192, 1, 4, 1),
+    (1202, 1536, "float16", 192, 1, 2, 2),
+    (601, 2560, "float16", 320, 1, 1, 2),
+    (1001, 5120, "bfloat16", 320, 2, 1, 1),
+    (700, 6144, "float16", 384, 2, 1, 1),
+    (513, 3584, "bfloat16", 448, 1, 1, 2),
+    (257, 7168, "float16", 448, 2, 1, 1),
+    (300, 10240, "bfloat16", 640, 2, 1, 1),
+    (900, 3072, "float32", 384, 2, 1, 1),
+    (333, 7168, "float32", 896, 2, 1, 1),
+    (130, 12288, "float16", None, None, None, None),
+]
+
+
+@pytest.mark.parametrize("rows,D,dtype,lanes,k,slots,per_cu", WAVE)
+def test_wave_rows_geometry_and_bitwise(R, rows, D, dtype, lanes, k, slots, per_cu):
+    """The automatic plan tiles rows of a whole number of waves exactly (lanes
+    x K = D / vector elements) with the rows per block and grid of its
+    in-flight rule; dx and the fused backward's dh do not depend on the rows
+    per block or on the grid (each row is reduced inside its own slot)."""
+    c = I.generic(rows, D, dtype, seed=5 * rows + D)
+    x, w, dy, dr = (c[kk].to(DEV) for kk in ("x", "w", "dy", "residual"))
+    q = R.query_config(2, rows, D, x.dtype)
+    _say(f"wave rows rows={rows} D={D} {dtype} plan={q}")
+    nvec = D * x.element_size() // 16
+    if lanes is None:
+        assert _is_pow2(q["lanes_per_row"]), q
+        return
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert q["vec_bytes"] == 16 and q["lanes_per_row"] == lanes and q["vecs_per_lane"] == k, q
+    assert lanes * k == nvec and not _is_pow2(lanes)
+    assert q["block_threads"] == slots * lanes, q
+    groups = (rows + slots - 1) // slots
+    assert q["num_blocks"] == min(groups, per_cu * cus), q
+    qf = R.query_config(4, rows, D, x.dtype)
+    assert qf["lanes_per_row"] == lanes and qf["vecs_per_lane"] == k, qf
+    dx_a, dw_a = R.rmsnorm_vjp(x, w, dy, c["eps"], 0.25)
+    dh_a, _ = R.fused_add_rmsnorm_vjp(x, w, dy, dr, c["eps"], 1.0)
+    variants = [dict(lanes_per_row=lanes, vecs_per_lane=k, vec_bytes=16, block_threads=lanes, num_blocks=37)]
+    for s in (2, 4):
+        if rows % s == 0 and s * lanes <= 768:
+            variants.append(dict(lanes_per_row=lanes, vecs_per_lane=k, vec_bytes=16,
+                                 block_threads=s * lanes, num_blocks=0))
+    for v in variants:
+        dx_b, dw_b = R.rmsnorm_vjp(x, w, dy, c["eps"], 0.25, cfg=v)
+        dh_b, _ = R.fused_add_rmsnorm_vjp(x, w, dy, dr, c["eps"], 1.0, cfg=v)
+        torch.cuda.synchronize()
+        assert torch.equal(dx_a, dx_b), v
+        assert torch.equal(dh_a, dh_b), v
+    idx = _edge_rows(rows, 16)
+    dxref, dwref = O.rmsnorm_vjp(c["x"], c["w"], c["dy"], c["eps"], 0.25)
+    assert_close(dx_b[idx], dxref[idx], "dx (forced geometry)")
+    assert_dw_close(dw_b, dwref, "dw (forced geometry)")
+    assert_dw_close(dw_a, dwref, "dw")
