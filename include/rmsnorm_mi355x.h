@@ -112,7 +112,13 @@ typedef enum {
  * automatically.  An explicit choice that cannot serve the shape returns
  * RMSN_E_CONFIG. */
 typedef struct {
-    int32_t lanes_per_row;  /* threads cooperating on one row: power of two, 1..1024 */
+    int32_t lanes_per_row;  /* threads cooperating on one row: a power of two, 1..1024,
+                               or 64 W with W = 3, 5, 6, 7, 10, 12 or 14 ("wave rows":
+                               16-byte vectors, vecs_per_lane 1 or 2, rows of exactly
+                               lanes_per_row * vecs_per_lane vectors, 1, 2 or 4 rows
+                               per block; not for the grad call, and for the backward
+                               forms only where the instance exists: 16-bit rows of 12
+                               or 14 waves with 2 vectors per lane do not) */
     int32_t vecs_per_lane;  /* vectors each thread holds per row: 1, 2, 4 or 8;
                                -1 selects the streaming (looped) kernel */
     int32_t vec_bytes;      /* bytes per load/store: 16, 8, 4 or the element size */
@@ -242,9 +248,10 @@ int silu_gate_vjp_cfg(const void *x, const void *dy, void *dx, int64_t rows, int
  * alignments).  Returns RMSN_OK or an argument error.  For the backward forms
  * the library additionally picks, per call, between two row loops of the same
  * geometry and arithmetic: a software-pipelined one (blocks of at most 256
- * threads, rows of exactly lanes_per_row * vecs_per_lane vectors, a row count
- * that fills every row slot; not for the grad call) and the plain one; the
- * choice does not change any result. */
+ * threads or one 512-lane row, rows of exactly lanes_per_row * vecs_per_lane
+ * vectors, a row count that fills every row slot; not for the grad call) and
+ * the plain one; the choice does not change any result.  Wave rows (see
+ * lanes_per_row) always run pipelined. */
 int rmsn_query_config(int op, int64_t rows, int64_t D, int dt, int align_bytes,
                       rmsn_config_t *out);
 
