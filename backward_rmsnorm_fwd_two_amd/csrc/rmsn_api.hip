@@ -120,29 +120,36 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
         // with the lanes fixed at compile time -- pipelined and unmasked for
         // the backward forms -- instead of masking part of a power-of-two
         // lane group.  The grad call keeps the plain loop.
-        if (op != RMSN_OP_GRAD && vb == 16 && (lanes == 0 ? k == 0 : rmsn::wave_rows(lanes))) {
+        // Wide 16-bit VJP rows (D = 12288, 14336, 16384) take the same path
+        // with four vectors per lane on 384, 448 or 512 lanes, one row per
+        // block.
+        const bool wide_ok = op == RMSN_OP_VJP && s == 2;
+        if (op != RMSN_OP_GRAD && vb == 16 &&
+            (lanes == 0 ? k == 0 : (rmsn::wave_rows(lanes) || (wide_ok && k == 4 && lanes == 512)))) {
+            // the first of 2, 1, 4 vectors per lane that tiles the row and
+            // has an instance
             int wl = 0, wk = 0;
-            for (int kk = 2; kk >= 1 && wl == 0; --kk) {
-                if ((k != 0 && kk != k) || p->nvec % kk != 0) continue;
+            const void* fn = nullptr;
+            for (int kk : {2, 1, 4}) {
+                if (fn || (k != 0 && kk != k) || p->nvec % kk != 0 || (kk == 4 && !wide_ok)) continue;
                 const int l = p->nvec / kk;
-                if ((lanes == 0 || l == lanes) && rmsn::wave_rows(l) && rmsn::wave_rows_supported(l)) {
+                const bool tiles = (rmsn::wave_rows(l) && rmsn::wave_rows_supported(l)) || (kk == 4 && l == 512);
+                if ((lanes != 0 && l != lanes) || !tiles) continue;
+                // The automatic forward takes wave rows with two vectors per
+                // lane up to 768 lanes; with one vector, or at 896 lanes, the
+                // masked power-of-two layout measured as fast or faster (cold
+                // 64 MiB tensors: D = 5120 bf16 24.5 vs 25.8 us; D = 3584
+                // bf16 25.0 vs 24.2 us, 14336 bf16 28.2 vs 27.0 us).
+                if (lanes == 0 && !vjp && (kk != 2 || l > 768)) continue;
+                fn = vjp ? rmsn::vjp_kernel_fixed_lanes(dt, p->nv, kk, op == RMSN_OP_FUSED_VJP ? 2 : 0, l)
+                         : rmsn::fwd_kernel_fixed_lanes(dt, p->nv, kk, op == RMSN_OP_FUSED, l);
+                if (fn) {
                     wl = l;
                     wk = kk;
                 }
             }
-            // The automatic forward takes wave rows with two vectors per lane
-            // up to 768 lanes; with one vector, or at 896 lanes, the masked
-            // power-of-two layout measured as fast or faster (cold 64 MiB
-            // tensors: D = 5120 bf16 24.5 vs 25.8 us; D = 3584 bf16 25.0 vs
-            // 24.2 us, 14336 bf16 28.2 vs 27.0 us).
-            if (wl && lanes == 0 && !vjp && (wk != 2 || wl > 768)) wl = 0;
-            const void* fn = nullptr;
-            if (wl) {
-                fn = vjp ? rmsn::vjp_kernel_fixed_lanes(dt, p->nv, wk, op == RMSN_OP_FUSED_VJP ? 2 : 0, wl)
-                         : rmsn::fwd_kernel_fixed_lanes(dt, p->nv, wk, op == RMSN_OP_FUSED, wl);
-            }
             // one, two or four rows per block, as the registers allow
-            const int most = vjp ? rmsn::wave_rows_block_max(wl)
+            const int most = vjp ? rmsn::wave_rows_block_max(wl, wk * p->nv)
                                  : (4 * wl <= 1024 ? 4 * wl : 2 * wl <= 1024 ? 2 * wl : wl);
             const int maxb = fn ? std::min(rmsn::max_block_threads(budget_op, wk, p->nv, s), most) : 0;
             if (fn && wl <= maxb) {
@@ -201,7 +208,9 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
                 p->shmem = (vjp && nslots > 1) ? (size_t)block * p->nv * sizeof(float) : 0;
                 return RMSN_OK;
             }
-            if (lanes != 0) return RMSN_E_CONFIG;  // requested wave rows that do not apply
+            // requested wave rows that do not apply (a requested power of
+            // two continues below)
+            if (lanes != 0 && rmsn::wave_rows(lanes)) return RMSN_E_CONFIG;
         }
         if (lanes == 0 && k == 0) {
             // About 32 bytes of each row tensor per lane: 2 vectors of 16

@@ -338,9 +338,11 @@ __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int 
 // without branches on the row width; 0: taken from the arguments.
 template <typename T, int NV, int K, int MODE, bool PIPE = false, int LANES = 0>
 __global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
-                             : wave_rows(LANES) ? wave_rows_block_max(LANES)
+                             : wave_rows(LANES) ? wave_rows_block_max(LANES, K * NV)
                              : (LANES > kVjpPipeBlock ? LANES : kVjpPipeBlock)) void vjp_rows(RowArgs a) {
-    static_assert(!PIPE || K * NV <= kVjpPipeElems, "pipelined instances hold two row groups");
+    static_assert(!PIPE || K * NV <= kVjpPipeElems ||
+                      (K * NV <= kVjpPipeElemsWide && LANES > 0 && LANES <= kVjpPipeFixedMax),
+                  "pipelined instances hold two row groups");
     static_assert(LANES == 0 || (PIPE && (((LANES & (LANES - 1)) == 0 && LANES <= kVjpPipeFixedMax) ||
                                           wave_rows_supported(LANES))),
                   "fixed lane counts are pipelined: powers of two or supported whole numbers of waves");

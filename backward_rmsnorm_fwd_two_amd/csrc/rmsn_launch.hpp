@@ -55,17 +55,26 @@ constexpr bool wave_rows_supported(int lanes) {
     return lanes == 192 || lanes == 320 || lanes == 384 || lanes == 448 || lanes == 640 ||
            lanes == 768 || lanes == 896;
 }
-// Largest block of a pipelined VJP wave-row instance: up to four rows while
-// they fit 768 threads (the two register buffers need about 90-170 VGPRs;
-// 768 threads leave 170, larger blocks would cap below that).
-constexpr int wave_rows_block_max(int lanes) {
-    return 4 * lanes <= 768 ? 4 * lanes : 2 * lanes <= 768 ? 2 * lanes : lanes;
+// Wide 16-bit rows (D = 12288, 14336, 16384) also come pipelined with four
+// vectors per lane on 384, 448 or 512 lanes, one row per block: up to this
+// many elements per lane, where a block of at most 512 threads leaves the 256
+// VGPRs the two register buffers need.
+constexpr int kVjpPipeElemsWide = 32;
+// Largest block of a pipelined VJP wave-row instance (elems = K * NV): up to
+// four rows while they fit 768 threads (the two register buffers need about
+// 90-170 VGPRs; 768 threads leave 170, larger blocks would cap below that);
+// one row for the wide instances.
+constexpr int wave_rows_block_max(int lanes, int elems) {
+    return elems > kVjpPipeElems ? lanes : 4 * lanes <= 768 ? 4 * lanes : 2 * lanes <= 768 ? 2 * lanes : lanes;
 }
-// Pipelined VJP wave-row instances that hold their registers without
-// spilling at one row per block: 16-bit rows with two vectors per lane need
-// up to 168 VGPRs, more than rows of 12 or 14 waves leave (170 / 128).
-constexpr bool vjp_wave_rows_fit(int lanes, int k, int itemsize) {
-    return !(itemsize == 2 && k == 2 && lanes > 640);
+// Pipelined VJP instances of the wave-row family that hold their registers
+// without spilling: 16-bit rows with two vectors per lane need up to 168
+// VGPRs, more than rows of 12 or 14 waves leave (170 / 128); the wide
+// instances (243-255 VGPRs) exist for 384, 448 and 512 lanes and the VJP
+// only (mode 0: the fused backward's third row tensor would spill).
+constexpr bool vjp_wave_rows_fit(int lanes, int k, int itemsize, int mode) {
+    return k * (16 / itemsize) > kVjpPipeElems ? (mode == 0 && (lanes == 384 || lanes == 448 || lanes == 512))
+                                               : !(itemsize == 2 && k == 2 && lanes > 640);
 }
 
 inline int dtype_size(int dt) { return dt == kF32 ? 4 : 2; }

@@ -46,7 +46,7 @@ const void* pick_dt(int dt, int nv, int k, int lanes) {
 }  // namespace
 
 const void* vjp_kernel_fixed_lanes(int dt, int nv, int k, int mode, int lanes) {
-    if (wave_rows(lanes)) return vjp_kernel_wave_rows(dt, nv, k, mode, lanes);
+    if (wave_rows(lanes) || k == 4) return vjp_kernel_wave_rows(dt, nv, k, mode, lanes);
     switch (mode) {
         case kVjp: return pick_dt<kVjp>(dt, nv, k, lanes);
         case kResGrad: return pick_dt<kResGrad>(dt, nv, k, lanes);

@@ -2,7 +2,9 @@
 // of waves that is not a power of two: lanes = 64 W, W = 3, 5, 6, 7, 10, 12,
 // 14, one or two 16-byte vectors per lane, where the row is exactly lanes *
 // K vectors (D = 1536 .. 10240 in 16-bit storage, 768 .. 7168 in fp32; 16-bit
-// rows of 12 or 14 waves with two vectors per lane would spill registers).
+// rows of 12 or 14 waves with two vectors per lane would spill registers), and
+// wide 16-bit rows with four vectors per lane on 384, 448 or 512 lanes (D =
+// 12288, 14336, 16384), one row per block.
 // A power-of-two lane count would mask a quarter to a half of such a row and
 // fall back to the plain loop.  A separate translation unit, so that it
 // compiles in parallel with the other instances.
@@ -14,7 +16,7 @@ namespace {
 template <typename T, int K, int MODE, int LANES>
 const void* one() {
     constexpr int NV = 16 / static_cast<int>(sizeof(T));
-    if constexpr (vjp_wave_rows_fit(LANES, K, sizeof(T)))
+    if constexpr (vjp_wave_rows_fit(LANES, K, sizeof(T), MODE))
         return reinterpret_cast<const void*>(&vjp_rows<T, NV, K, MODE, true, LANES>);
     return nullptr;
 }
@@ -33,12 +35,27 @@ const void* pick_waves(int lanes) {
     }
 }
 
+// wide 16-bit rows: four vectors per lane, one row per block
+template <typename T, int MODE>
+const void* pick_wide(int lanes) {
+    if constexpr (sizeof(T) == 2) {
+        switch (lanes) {
+            case 384: return one<T, 4, MODE, 384>();
+            case 448: return one<T, 4, MODE, 448>();
+            case 512: return one<T, 4, MODE, 512>();
+            default: return nullptr;
+        }
+    }
+    return nullptr;
+}
+
 template <typename T, int MODE>
 const void* pick_k(int nv, int k, int lanes) {
     if (nv != 16 / static_cast<int>(sizeof(T))) return nullptr;
     switch (k) {
         case 1: return pick_waves<T, 1, MODE>(lanes);
         case 2: return pick_waves<T, 2, MODE>(lanes);
+        case 4: return pick_wide<T, MODE>(lanes);
         default: return nullptr;
     }
 }

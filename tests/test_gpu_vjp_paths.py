@@ -62,7 +62,10 @@ CASES = [
     (300, 10240, "bfloat16"),   # wave rows: 10 waves x 2
     (900, 3072, "float32"),     # wave rows: 6 waves x 2 x 4 floats
     (333, 7168, "float32"),     # wave rows: 14 waves x 2 x 4 floats
-    (130, 12288, "float16"),    # 12 waves x 2 in 16-bit would spill: plain loop, 1024 lanes
+    (130, 12288, "float16"),    # wide: 6 waves x 4 vectors, one row per block (VJP only)
+    (100, 14336, "bfloat16"),   # wide: 7 waves x 4 vectors
+    (99, 16384, "float16"),     # wide: 8 waves x 4 vectors (512 lanes)
+    (64, 12288, "float32"),     # plain loop: 1024 lanes x 3 of 4 vectors (no wave instance)
     (1000, 1024, "bfloat16"),   # pipelined: 64 lanes, 4 slots
     (1024, 8192, "bfloat16"),   # pipelined: a 512-lane row per 512-thread block
     (1023, 8192, "float16"),    # pipelined, odd row count
@@ -138,7 +141,10 @@ WAVE = [
     (300, 10240, "bfloat16", 640, 2, 1, 1),
     (900, 3072, "float32", 384, 2, 1, 1),
     (333, 7168, "float32", 896, 2, 1, 1),
-    (130, 12288, "float16", None, None, None, None),
+    (130, 12288, "float16", 384, 4, 1, 1),
+    (100, 14336, "bfloat16", 448, 4, 1, 1),
+    (99, 16384, "float16", 512, 4, 1, 1),
+    (64, 12288, "float32", None, None, None, None),
 ]
 
 
@@ -157,26 +163,35 @@ def test_wave_rows_geometry_and_bitwise(R, rows, D, dtype, lanes, k, slots, per_
         assert _is_pow2(q["lanes_per_row"]), q
         return
     cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wide = k == 4   # four vectors per lane: the VJP only, one row per block
     assert q["vec_bytes"] == 16 and q["lanes_per_row"] == lanes and q["vecs_per_lane"] == k, q
-    assert lanes * k == nvec and not _is_pow2(lanes)
+    assert lanes * k == nvec and (wide or not _is_pow2(lanes))
     assert q["block_threads"] == slots * lanes, q
     groups = (rows + slots - 1) // slots
     assert q["num_blocks"] == min(groups, per_cu * cus), q
     qf = R.query_config(4, rows, D, x.dtype)
-    assert qf["lanes_per_row"] == lanes and qf["vecs_per_lane"] == k, qf
+    if wide:
+        assert qf["vecs_per_lane"] != 4, qf
+    else:
+        assert qf["lanes_per_row"] == lanes and qf["vecs_per_lane"] == k, qf
     dx_a, dw_a = R.rmsnorm_vjp(x, w, dy, c["eps"], 0.25)
     dh_a, _ = R.fused_add_rmsnorm_vjp(x, w, dy, dr, c["eps"], 1.0)
     variants = [dict(lanes_per_row=lanes, vecs_per_lane=k, vec_bytes=16, block_threads=lanes, num_blocks=37)]
     for s in (2, 4):
-        if rows % s == 0 and s * lanes <= 768:
+        if not wide and rows % s == 0 and s * lanes <= 768:
             variants.append(dict(lanes_per_row=lanes, vecs_per_lane=k, vec_bytes=16,
                                  block_threads=s * lanes, num_blocks=0))
     for v in variants:
         dx_b, dw_b = R.rmsnorm_vjp(x, w, dy, c["eps"], 0.25, cfg=v)
-        dh_b, _ = R.fused_add_rmsnorm_vjp(x, w, dy, dr, c["eps"], 1.0, cfg=v)
+        if not wide:
+            dh_b, _ = R.fused_add_rmsnorm_vjp(x, w, dy, dr, c["eps"], 1.0, cfg=v)
         torch.cuda.synchronize()
         assert torch.equal(dx_a, dx_b), v
-        assert torch.equal(dh_a, dh_b), v
+        if not wide:
+            assert torch.equal(dh_a, dh_b), v
+    if wide:
+        dhref, _ = O.fused_add_rmsnorm_vjp(c["x"][:8], c["w"], c["dy"][:8], c["residual"][:8], c["eps"], 1.0)
+        assert_close(dh_a[:8], dhref, "dh (fused backward, its own layout)")
     idx = _edge_rows(rows, 16)
     dxref, dwref = O.rmsnorm_vjp(c["x"], c["w"], c["dy"], c["eps"], 0.25)
     assert_close(dx_b[idx], dxref[idx], "dx (forced geometry)")
