@@ -119,13 +119,13 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
         // 6144, 7168 ... in 16-bit storage) are tiled exactly by an instance
         // with the lanes fixed at compile time -- pipelined and unmasked for
         // the backward forms -- instead of masking part of a power-of-two
-        // lane group.  The grad call keeps the plain loop.
+        // lane group.
         // Wide 16-bit VJP rows (D = 12288, 14336, 16384) take the same path
         // with four vectors per lane on 384, 448 or 512 lanes, one row per
         // block.
         const bool wide_ok = op == RMSN_OP_VJP && s == 2;
-        if (op != RMSN_OP_GRAD && vb == 16 &&
-            (lanes == 0 ? k == 0 : (rmsn::wave_rows(lanes) || (wide_ok && k == 4 && lanes == 512)))) {
+        const int vmode = op == RMSN_OP_GRAD ? 1 : op == RMSN_OP_FUSED_VJP ? 2 : 0;
+        if (vb == 16 && (lanes == 0 ? k == 0 : (rmsn::wave_rows(lanes) || (wide_ok && k == 4 && lanes == 512)))) {
             // the first of 2, 1, 4 vectors per lane that tiles the row and
             // has an instance
             int wl = 0, wk = 0;
@@ -141,7 +141,7 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
                 // 64 MiB tensors: D = 5120 bf16 24.5 vs 25.8 us; D = 3584
                 // bf16 25.0 vs 24.2 us, 14336 bf16 28.2 vs 27.0 us).
                 if (lanes == 0 && !vjp && (kk != 2 || l > 768)) continue;
-                fn = vjp ? rmsn::vjp_kernel_fixed_lanes(dt, p->nv, kk, op == RMSN_OP_FUSED_VJP ? 2 : 0, l)
+                fn = vjp ? rmsn::vjp_kernel_fixed_lanes(dt, p->nv, kk, vmode, l)
                          : rmsn::fwd_kernel_fixed_lanes(dt, p->nv, kk, op == RMSN_OP_FUSED, l);
                 if (fn) {
                     wl = l;
@@ -270,21 +270,20 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
             // Backward forms: the software-pipelined kernel stores
             // unconditionally, so it serves rows that are exactly lanes * k
             // vectors and row counts that fill every row slot.  The grad
-            // call keeps the plain kernel: pipelined it measured slower (55.0
-            // vs 53 us at 8192 x 4096 fp16), and its dx then differed from
-            // the VJP's by one fp16 ulp in a few elements of the last row
-            // group.
+            // call runs pipelined only in an instance with the lanes fixed
+            // (8192 x 4096 fp16: 50.6 us against 53.5 in the plain loop; the
+            // generic pipelined kernel measured slower than the plain one).
             // Blocks wider than kVjpPipeBlock are pipelined only as a whole
             // 512-lane row in an instance with the lanes fixed (the generic
             // pipelined kernel needs more registers than two such blocks per
             // CU leave; with the width fixed, one block per CU runs faster).
             const bool whole_wide_row = lanes == rmsn::kVjpPipeFixedMax && block == lanes;
-            p->pipe = vjp && op != RMSN_OP_GRAD && k * p->nv <= rmsn::kVjpPipeElems &&
+            p->pipe = vjp && k * p->nv <= rmsn::kVjpPipeElems &&
                       (block <= rmsn::kVjpPipeBlock || whole_wide_row) && (int64_t)lanes * k == p->nvec &&
                       rows % nslots == 0;
-            p->fixed_lanes = p->pipe &&
-                             rmsn::vjp_kernel_fixed_lanes(dt, p->nv, k, op == RMSN_OP_FUSED_VJP ? 2 : 0, lanes) != nullptr;
-            if (p->pipe && !p->fixed_lanes && block > rmsn::kVjpPipeBlock) p->pipe = false;
+            p->fixed_lanes = p->pipe && rmsn::vjp_kernel_fixed_lanes(dt, p->nv, k, vmode, lanes) != nullptr;
+            // the grad call runs pipelined only with the lanes fixed
+            if (p->pipe && !p->fixed_lanes && (block > rmsn::kVjpPipeBlock || op == RMSN_OP_GRAD)) p->pipe = false;
             int64_t grid;
             if (cfg && cfg->num_blocks) {
                 grid = cfg->num_blocks;

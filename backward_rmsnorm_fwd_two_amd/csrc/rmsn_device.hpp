@@ -18,6 +18,18 @@ __device__ __forceinline__ float to_f32(__bf16 v) { return static_cast<float>(v)
 template <typename T>
 __device__ __forceinline__ T from_f32(float v) { return static_cast<T>(v); }
 
+// fp16: the value is first pinned as an fp32 register (an empty asm operand,
+// no instruction), so the compiler cannot fold the fma that produced it and
+// this conversion into one mixed-precision instruction that rounds to fp16
+// once (v_fma_mixlo_f16 / v_fma_mixhi_f16).  It did so in some instances and
+// not in others, and their outputs then differed by one ulp; pinned, every
+// kernel rounds the same fp32 value to nearest even.
+template <>
+__device__ __forceinline__ _Float16 from_f32<_Float16>(float v) {
+    __asm__("" : "+v"(v));
+    return static_cast<_Float16>(v);
+}
+
 // Raw row data as 32-bit words: NV elements moved by one load instruction
 // (NV * sizeof(T) bytes; 16 selects global_load_dwordx4).  Keeping the
 // words packed (rather than as 16-bit scalars) lets prefetched data stay in

@@ -1,5 +1,6 @@
-// rmsn_vjp_lanes.hip -- pipelined VJP row kernels with the lanes per row
-// fixed at compile time, for the common geometries: 16-byte loads, one or
+// rmsn_vjp_lanes.hip -- pipelined VJP, grad-call and fused-backward row
+// kernels with the lanes per row fixed at compile time, for the common
+// geometries: 16-byte loads, one or
 // two vectors per lane, 32 to 256 lanes per row (D = 256 .. 4096 in 16-bit
 // storage, 128 .. 2048 in fp32, with whole row groups).  With the row width
 // known, the per-row reductions compile without branches on it; everything
@@ -49,8 +50,9 @@ const void* vjp_kernel_fixed_lanes(int dt, int nv, int k, int mode, int lanes) {
     if (wave_rows(lanes) || k == 4) return vjp_kernel_wave_rows(dt, nv, k, mode, lanes);
     switch (mode) {
         case kVjp: return pick_dt<kVjp>(dt, nv, k, lanes);
+        case kGrad: return pick_dt<kGrad>(dt, nv, k, lanes);
         case kResGrad: return pick_dt<kResGrad>(dt, nv, k, lanes);
-        default: return nullptr;  // the grad call runs the plain loop
+        default: return nullptr;
     }
 }
 

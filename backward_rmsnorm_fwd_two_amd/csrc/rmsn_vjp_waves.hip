@@ -75,8 +75,9 @@ const void* pick_dt(int dt, int nv, int k, int lanes) {
 const void* vjp_kernel_wave_rows(int dt, int nv, int k, int mode, int lanes) {
     switch (mode) {
         case kVjp: return pick_dt<kVjp>(dt, nv, k, lanes);
+        case kGrad: return pick_dt<kGrad>(dt, nv, k, lanes);
         case kResGrad: return pick_dt<kResGrad>(dt, nv, k, lanes);
-        default: return nullptr;  // the grad call runs the plain loop
+        default: return nullptr;
     }
 }
 

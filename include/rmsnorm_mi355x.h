@@ -116,9 +116,9 @@ typedef struct {
                                or 64 W with W = 3, 5, 6, 7, 10, 12 or 14 ("wave rows":
                                16-byte vectors, vecs_per_lane 1 or 2, rows of exactly
                                lanes_per_row * vecs_per_lane vectors, 1, 2 or 4 rows
-                               per block; not for the grad call, and for the backward
-                               forms only where the instance exists: 16-bit rows of 12
-                               or 14 waves with 2 vectors per lane do not); the VJP
+                               per block; for the backward forms only where the
+                               instance exists: 16-bit rows of 12 or 14 waves with 2
+                               vectors per lane do not); the VJP
                                of 16-bit rows also takes 384, 448 or 512 lanes with 4
                                vectors per lane, one row per block */
     int32_t vecs_per_lane;  /* vectors each thread holds per row: 1, 2, 4 or 8;
@@ -251,9 +251,10 @@ int silu_gate_vjp_cfg(const void *x, const void *dy, void *dx, int64_t rows, int
  * the library additionally picks, per call, between two row loops of the same
  * geometry and arithmetic: a software-pipelined one (blocks of at most 256
  * threads or one 512-lane row, rows of exactly lanes_per_row * vecs_per_lane
- * vectors, a row count that fills every row slot; not for the grad call) and
- * the plain one; the choice does not change any result.  Wave rows (see
- * lanes_per_row) always run pipelined. */
+ * vectors, a row count that fills every row slot; for the grad call only
+ * where an instance with the lanes fixed exists) and the plain one; the
+ * choice does not change any result.  Wave rows (see lanes_per_row) always
+ * run pipelined. */
 int rmsn_query_config(int op, int64_t rows, int64_t D, int dt, int align_bytes,
                       rmsn_config_t *out);
 

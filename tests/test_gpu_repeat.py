@@ -75,10 +75,9 @@ def test_repeat_backward_ops(R, rows, D, dtype):
     _same(grad, "rmsnorm_fwd_vjp")
     _same(fused, "fused_add_rmsnorm_vjp")
     # the VJP and the grad call share dx bit for bit when they lay the row
-    # out alike (the grad call keeps power-of-two lanes, so wave rows sum a
-    # row in another order), and dw when both also use the same grid; the
-    # grad call's y (row sums in the VJP's lane order) is checked against
-    # the oracle
+    # out alike (a different layout sums a row in another order), and dw
+    # when both also use the same grid; the grad call's y (row sums in the
+    # VJP's lane order) is checked against the oracle
     q2, q3 = R.query_config(2, rows, D, x.dtype), R.query_config(3, rows, D, x.dtype)
     n = _lead(rows)
     geo = ("lanes_per_row", "vecs_per_lane", "vec_bytes")

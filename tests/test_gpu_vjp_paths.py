@@ -176,6 +176,17 @@ def test_wave_rows_geometry_and_bitwise(R, rows, D, dtype, lanes, k, slots, per_
         assert qf["lanes_per_row"] == lanes and qf["vecs_per_lane"] == k, qf
     dx_a, dw_a = R.rmsnorm_vjp(x, w, dy, c["eps"], 0.25)
     dh_a, _ = R.fused_add_rmsnorm_vjp(x, w, dy, dr, c["eps"], 1.0)
+    # the grad call lays these rows out alike (not the wide four-vector
+    # rows) and then gives the VJP's dx bit for bit, dw too on the same grid
+    # (fp16 included: every kernel rounds dx from the same fp32 value)
+    qg = R.query_config(3, rows, D, x.dtype)
+    _, dx_g, dw_g = R.rmsnorm_fwd_vjp(x, w, dy, c["eps"], 0.25)
+    torch.cuda.synchronize()
+    if not wide:
+        assert (qg["lanes_per_row"], qg["vecs_per_lane"]) == (lanes, k), qg
+        assert torch.equal(dx_g, dx_a)
+        if qg["num_blocks"] == q["num_blocks"]:
+            assert torch.equal(dw_g, dw_a)
     variants = [dict(lanes_per_row=lanes, vecs_per_lane=k, vec_bytes=16, block_threads=lanes, num_blocks=37)]
     for s in (2, 4):
         if not wide and rows % s == 0 and s * lanes <= 768:
