@@ -120,10 +120,10 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
         // with the lanes fixed at compile time -- pipelined and unmasked for
         // the backward forms -- instead of masking part of a power-of-two
         // lane group.
-        // Wide 16-bit VJP rows (D = 12288, 14336, 16384) take the same path
-        // with four vectors per lane on 384, 448 or 512 lanes, one row per
-        // block.
-        const bool wide_ok = op == RMSN_OP_VJP && s == 2;
+        // Four vectors per lane, one row per block, for the backward forms:
+        // wide 16-bit VJP rows (D = 12288, 14336, 16384 on 384, 448 or 512
+        // lanes) and fp32 rows of 512 lanes (D = 8192).
+        const bool wide_ok = vjp && (s == 4 || op == RMSN_OP_VJP);
         const int vmode = op == RMSN_OP_GRAD ? 1 : op == RMSN_OP_FUSED_VJP ? 2 : 0;
         if (vb == 16 && (lanes == 0 ? k == 0 : (rmsn::wave_rows(lanes) || (wide_ok && k == 4 && lanes == 512)))) {
             // the first of 2, 1, 4 vectors per lane that tiles the row and
@@ -152,38 +152,36 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
             const int most = vjp ? rmsn::wave_rows_block_max(wl, wk * p->nv)
                                  : (4 * wl <= 1024 ? 4 * wl : 2 * wl <= 1024 ? 2 * wl : wl);
             const int maxb = fn ? std::min(rmsn::max_block_threads(budget_op, wk, p->nv, s), most) : 0;
-            if (fn && wl <= maxb) {
-                // Rows per block and the persistent grid of the backward
-                // forms: each CU needs enough row data in flight, counted as
-                // waves per row x vectors per lane x row tensors loaded (2;
-                // 3 for the fused backward) x rows per block.  Rows per block
-                // double until that reaches kWaveRowsInFlight (as the
-                // registers allow); if it still falls short, two blocks per
-                // CU.  Cold 64 MiB tensors, VJP: D = 1536 bf16 (3 waves, one
-                // vector) 39.4 us at four rows per block vs 63.3 at one;
-                // 2560 fp16 39.4 vs 48.0 at two; 3072 fp16 40.0 vs 44.6 at
-                // two; 5120 fp16 40.7 at one vs 42.3 at two; 3584 bf16 41.1
-                // at two blocks per CU vs 42.2.  Fused backward: 1536 bf16
-                // 47.1 at two rows vs 63.1 at one, 3072 fp16 48.1 at one vs
-                // 51.6 at two.  The forward (not persistent) runs two
-                // three-wave rows per block (D = 3072 fp16 24.0 vs 24.6 us).
-                const int w_units = (wl / 64) * wk * (op == RMSN_OP_FUSED_VJP ? 3 : 2);
-                int block = req_b;
-                if (!block) {
-                    int slots = 1;
-                    if (vjp) {
-                        while (slots < 4 && w_units * slots < kWaveRowsInFlight && 2 * slots * wl <= maxb &&
-                               rows % (2 * slots) == 0)
-                            slots *= 2;
-                    } else if (wl == 192 && 2 * wl <= maxb) {
-                        slots = 2;
-                    }
-                    block = slots * wl;
+            // Rows per block and the persistent grid of the backward forms:
+            // each CU needs enough row data in flight, counted as waves per
+            // row x vectors per lane x row tensors loaded (2; 3 for the fused
+            // backward) x rows per block.  Rows per block double until that
+            // reaches kWaveRowsInFlight (as the registers allow); if it still
+            // falls short, two blocks per CU.  Cold 64 MiB tensors, VJP: D =
+            // 1536 bf16 (3 waves, one vector) 39.4 us at four rows per block
+            // vs 63.3 at one; 2560 fp16 39.4 vs 48.0 at two; 3072 fp16 40.0
+            // vs 44.6 at two; 5120 fp16 40.7 at one vs 42.3 at two; 3584
+            // bf16 41.1 at two blocks per CU vs 42.2.  Fused backward: 1536
+            // bf16 47.1 at two rows vs 63.1 at one, 3072 fp16 48.1 at one vs
+            // 51.6 at two.  The forward (not persistent) runs two three-wave
+            // rows per block (D = 3072 fp16 24.0 vs 24.6 us).
+            const int w_units = wl / 64 * wk * (op == RMSN_OP_FUSED_VJP ? 3 : 2);
+            int block = req_b;
+            if (fn && !block) {
+                int slots = 1;
+                if (vjp) {
+                    while (slots < 4 && w_units * slots < kWaveRowsInFlight && 2 * slots * wl <= maxb &&
+                           rows % (2 * slots) == 0)
+                        slots *= 2;
+                } else if (wl == 192 && 2 * wl <= maxb) {
+                    slots = 2;
                 }
-                if (block != wl && block != 2 * wl && block != 4 * wl) return RMSN_E_CONFIG;
-                if (block > maxb) return RMSN_E_CONFIG;
-                // the pipelined kernel fills every row slot
-                if (vjp && rows % (block / wl) != 0) return RMSN_E_CONFIG;
+                block = slots * wl;
+            }
+            // the pipelined kernel fills every row slot
+            const bool block_ok = fn && wl <= maxb && (block == wl || block == 2 * wl || block == 4 * wl) &&
+                                  block <= maxb && !(vjp && rows % (block / wl) != 0);
+            if (block_ok) {
                 const int nslots = block / wl;
                 const int64_t groups = (rows + nslots - 1) / nslots;
                 int64_t grid;
@@ -208,8 +206,9 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
                 p->shmem = (vjp && nslots > 1) ? (size_t)block * p->nv * sizeof(float) : 0;
                 return RMSN_OK;
             }
-            // requested wave rows that do not apply (a requested power of
-            // two continues below)
+            // requested wave rows that do not apply; a requested power of two
+            // (512 lanes x 4 in a block this path does not serve) continues
+            // to the power-of-two kernels below
             if (lanes != 0 && rmsn::wave_rows(lanes)) return RMSN_E_CONFIG;
         }
         if (lanes == 0 && k == 0) {

@@ -4,7 +4,8 @@
 // K vectors (D = 1536 .. 10240 in 16-bit storage, 768 .. 7168 in fp32; 16-bit
 // rows of 12 or 14 waves with two vectors per lane would spill registers), and
 // wide 16-bit rows with four vectors per lane on 384, 448 or 512 lanes (D =
-// 12288, 14336, 16384), one row per block.
+// 12288, 14336, 16384), one row per block; fp32 rows of 512 lanes x 4 vectors
+// (D = 8192).
 // A power-of-two lane count would mask a quarter to a half of such a row and
 // fall back to the plain loop.  A separate translation unit, so that it
 // compiles in parallel with the other instances.
@@ -35,7 +36,8 @@ const void* pick_waves(int lanes) {
     }
 }
 
-// wide 16-bit rows: four vectors per lane, one row per block
+// four vectors per lane, one row per block: wide 16-bit rows (the VJP only)
+// and fp32 rows of 512 lanes (D = 8192)
 template <typename T, int MODE>
 const void* pick_wide(int lanes) {
     if constexpr (sizeof(T) == 2) {
@@ -45,8 +47,12 @@ const void* pick_wide(int lanes) {
             case 512: return one<T, 4, MODE, 512>();
             default: return nullptr;
         }
+    } else {
+        // fp32 raw data takes twice the registers of 16-bit: only a whole
+        // 512-lane row per block (256 VGPRs) holds every form unspilled
+        if (lanes == 512) return one<T, 4, MODE, 512>();
+        return nullptr;
     }
-    return nullptr;
 }
 
 template <typename T, int MODE>

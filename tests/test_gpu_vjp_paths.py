@@ -66,6 +66,7 @@ CASES = [
     (100, 14336, "bfloat16"),   # wide: 7 waves x 4 vectors
     (99, 16384, "float16"),     # wide: 8 waves x 4 vectors (512 lanes)
     (64, 12288, "float32"),     # plain loop: 1024 lanes x 3 of 4 vectors (no wave instance)
+    (200, 8192, "float32"),     # fp32: 512 lanes x 4 vectors, one row per block
     (1000, 1024, "bfloat16"),   # pipelined: 64 lanes, 4 slots
     (1024, 8192, "bfloat16"),   # pipelined: a 512-lane row per 512-thread block
     (1023, 8192, "float16"),    # pipelined, odd row count
@@ -145,6 +146,7 @@ WAVE = [
     (100, 14336, "bfloat16", 448, 4, 1, 1),
     (99, 16384, "float16", 512, 4, 1, 1),
     (64, 12288, "float32", None, None, None, None),
+    (200, 8192, "float32", 512, 4, 1, 1),
 ]
 
 
@@ -163,9 +165,11 @@ def test_wave_rows_geometry_and_bitwise(R, rows, D, dtype, lanes, k, slots, per_
         assert _is_pow2(q["lanes_per_row"]), q
         return
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    wide = k == 4   # four vectors per lane: the VJP only, one row per block
+    # wide 16-bit rows (four vectors per lane): the VJP only, one row per
+    # block; fp32 rows of 512 lanes x 4 serve every backward form
+    wide = k == 4 and dtype != "float32"
     assert q["vec_bytes"] == 16 and q["lanes_per_row"] == lanes and q["vecs_per_lane"] == k, q
-    assert lanes * k == nvec and (wide or not _is_pow2(lanes))
+    assert lanes * k == nvec and (k == 4 or not _is_pow2(lanes))
     assert q["block_threads"] == slots * lanes, q
     groups = (rows + slots - 1) // slots
     assert q["num_blocks"] == min(groups, per_cu * cus), q

@@ -1,6 +1,7 @@
 """GPU: every compiled wave-row instance (rows of W = 3, 5, 6, 7, 10, 12 or
-14 waves, one or two 16-byte vectors per lane) and every wide VJP instance
-(four vectors per lane on 384, 448 or 512 lanes, 16-bit) runs, forced
+14 waves, one or two 16-byte vectors per lane), every wide VJP instance
+(four vectors per lane on 384, 448 or 512 lanes, 16-bit) and the fp32
+four-vector instances (512 lanes) run, forced
 through the *_cfg entry points, and matches the fp64 oracle on a few rows,
 one and two rows per block; combinations without an instance return
 RMSN_E_CONFIG.  The automatic plan selects only some of these instances,
@@ -38,15 +39,19 @@ def _say(msg):
 def _backward_instance(dtype, lanes, k, op):
     """Whether a pipelined instance exists for a backward form (mirror of the
     library's instance table): 16-bit rows with two vectors per lane stop at
-    640 lanes (wider would spill), and the wide four-vector instances serve
-    the VJP of 16-bit rows only."""
+    640 lanes (wider would spill), the wide four-vector instances serve the
+    VJP of 16-bit rows only, and fp32 rows take four vectors per lane on 512
+    lanes only."""
     if k == 4:
-        return op == "vjp" and dtype != "float32" and lanes in (384, 448, 512)
+        if dtype == "float32":
+            return lanes == 512
+        return op == "vjp" and lanes in (384, 448, 512)
     return not (dtype != "float32" and k == 2 and lanes > 640)
 
 
 CASES = [(dt, lanes, k) for dt in ("float32", "float16", "bfloat16") for lanes in WAVE_LANES for k in (1, 2)]
 CASES += [(dt, lanes, 4) for dt in ("float16", "bfloat16") for lanes in (384, 448, 512)]
+CASES += [("float32", 512, 4), ("float32", 448, 4)]
 
 
 def _id(c):
@@ -85,9 +90,11 @@ def test_wave_instance_parity(R, dtype, lanes, k):
         two_ok = elems <= 16 and 2 * lanes <= 768
         for op in ("vjp", "grad", "fused"):
             exists = _backward_instance(dtype, lanes, k, op) and (slots == 1 or two_ok)
-            if k == 4 and lanes == 512 and op != "vjp":
-                # 512 lanes is a power of two: these forms take the plain loop
-                exists = slots == 1
+            if k == 4 and lanes == 512:
+                # a power of two: a form or block the pipelined instances do
+                # not serve takes the plain loop, within its register budget
+                # (16 elements per lane, fp32: 1024 threads; 32, 16-bit: 512)
+                exists = slots == 1 or dtype == "float32"
             try:
                 if op == "vjp":
                     dx, dw = R.rmsnorm_vjp(x, w, dy, eps, wb, cfg=cfg)
