@@ -326,10 +326,27 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
         grid = cfg->num_blocks;
         if (grid > rows && rows > 0) return RMSN_E_CONFIG;  // every block must own a row
     } else if (vjp) {
-        // rows past the register dw (row-batched kernel): one block per CU,
-        // since every partial row there is D * 4 bytes written and re-read
-        // (measured best from 40000 to 262144 columns)
-        const int per_cu = p->jreg == 0 ? 1 : std::max(1, 2048 / block);
+        // Persistent: at most as many blocks per CU as the kernel's
+        // registers let reside at once.  Blocks past that run in a second
+        // round, which adds dw partial rows (D * 4 bytes each, written and
+        // re-read) but no parallelism: the instances that keep 4 vectors of
+        // dw per thread (D = 16392..32768 in 16-bit storage) hold 88-98
+        // VGPRs, one 1024-thread block per CU, and on 64 MiB tensors ran
+        // 63.5 us at 256 blocks against 80.0 at 512 (D = 32768 bf16; D =
+        // 16392 60.5 vs 69.9 us).  Rows past the register dw (row-batched
+        // kernel): one block per CU, since every partial row there is D * 4
+        // bytes written and re-read (measured best from 40000 to 262144
+        // columns).
+        int per_cu = 1;
+        if (p->jreg != 0) {
+            per_cu = std::max(1, 2048 / block);
+            const int mode = op == RMSN_OP_GRAD ? 1 : op == RMSN_OP_FUSED_VJP ? 2 : 0;
+            const void* fn = rmsn::vjp_kernel(dt, p->nv, -1, mode, p->jreg, false);
+            int resident = 0;
+            if (fn && hipOccupancyMaxActiveBlocksPerMultiprocessor(&resident, fn, block, 0) == hipSuccess &&
+                resident > 0)
+                per_cu = std::min(per_cu, resident);
+        }
         grid = std::min<int64_t>(rows, std::min<int64_t>(kMaxPartialRows, (int64_t)cus * per_cu));
     } else {
         grid = std::min<int64_t>(rows, (int64_t)1 << 20);

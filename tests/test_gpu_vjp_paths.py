@@ -212,3 +212,31 @@ def test_wave_rows_geometry_and_bitwise(R, rows, D, dtype, lanes, k, slots, per_
     assert_close(dx_b[idx], dxref[idx], "dx (forced geometry)")
     assert_dw_close(dw_b, dwref, "dw (forced geometry)")
     assert_dw_close(dw_a, dwref, "dw")
+
+
+@pytest.mark.parametrize("rows,D,dtype", [(300, 20480, "bfloat16"), (600, 32768, "float16"), (90, 20480, "float32")])
+def test_streaming_vjp_grid_follows_occupancy(R, rows, D, dtype):
+    """Rows past the register path stream (one 1024-thread block per row
+    iteration, dw in registers); the instances that keep 4 vectors of dw
+    per thread (16-bit) or 8 (fp32) hold more than 64 VGPRs, so only one
+    such block resides per CU and the persistent grid is one block per CU
+    (a second round of blocks would only add partial rows).  Parity with
+    the oracle at that grid."""
+    c = I.generic(rows, D, dtype, seed=rows + D)
+    x, w, dy, dr = (c[k].to(DEV) for k in ("x", "w", "dy", "residual"))
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for op in (2, 3, 4):
+        q = R.query_config(op, rows, D, x.dtype)
+        _say(f"streaming vjp op={op} rows={rows} D={D} {dtype} plan={q}")
+        assert q["vecs_per_lane"] == -1 and q["block_threads"] == 1024, q
+        assert q["num_blocks"] == min(rows, cus), q
+    dx, dw = R.rmsnorm_vjp(x, w, dy, c["eps"], 0.5)
+    dh, dwf = R.fused_add_rmsnorm_vjp(x, w, dy, dr, c["eps"], 0.5)
+    torch.cuda.synchronize()
+    idx = _edge_rows(rows, 8)
+    dxref, dwref = O.rmsnorm_vjp(c["x"], c["w"], c["dy"], c["eps"], 0.5)
+    assert_close(dx[idx], dxref[idx], "dx")
+    assert_dw_close(dw, dwref, "dw")
+    dhref, _ = O.fused_add_rmsnorm_vjp(c["x"][idx], c["w"], c["dy"][idx], c["residual"][idx], c["eps"], 0.5)
+    assert_close(dh[idx], dhref, "dh")
+    assert_dw_close(dwf, dwref, "fused dw")
