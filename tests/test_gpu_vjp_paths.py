@@ -62,7 +62,7 @@ CASES = [
     (300, 10240, "bfloat16"),   # wave rows: 10 waves x 2
     (900, 3072, "float32"),     # wave rows: 6 waves x 2 x 4 floats
     (333, 7168, "float32"),     # wave rows: 14 waves x 2 x 4 floats
-    (130, 12288, "float16"),    # wide: 6 waves x 4 vectors, one row per block (VJP only)
+    (130, 12288, "float16"),    # 12 waves x 2 (VJP, grad call); the fused backward keeps 1024 lanes
     (100, 14336, "bfloat16"),   # wide: 7 waves x 4 vectors
     (99, 16384, "float16"),     # wide: 8 waves x 4 vectors (512 lanes)
     (64, 12288, "float32"),     # plain loop: 1024 lanes x 3 of 4 vectors (no wave instance)
@@ -142,7 +142,7 @@ WAVE = [
     (300, 10240, "bfloat16", 640, 2, 1, 1),
     (900, 3072, "float32", 384, 2, 1, 1),
     (333, 7168, "float32", 896, 2, 1, 1),
-    (130, 12288, "float16", 384, 4, 1, 1),
+    (130, 12288, "float16", 768, 2, 1, 1),
     (100, 14336, "bfloat16", 448, 4, 1, 1),
     (99, 16384, "float16", 512, 4, 1, 1),
     (64, 12288, "float32", None, None, None, None),
@@ -166,16 +166,19 @@ def test_wave_rows_geometry_and_bitwise(R, rows, D, dtype, lanes, k, slots, per_
         return
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     # wide 16-bit rows (four vectors per lane): the VJP only, one row per
-    # block; fp32 rows of 512 lanes x 4 serve every backward form
+    # block; fp32 rows of 512 lanes x 4 serve every backward form; 16-bit
+    # rows of 12 waves x 2 serve the VJP and the grad call, not the fused
+    # backward (it would spill)
     wide = k == 4 and dtype != "float32"
+    fused_apart = wide or (dtype != "float32" and k == 2 and lanes > 640)
     assert q["vec_bytes"] == 16 and q["lanes_per_row"] == lanes and q["vecs_per_lane"] == k, q
     assert lanes * k == nvec and (k == 4 or not _is_pow2(lanes))
     assert q["block_threads"] == slots * lanes, q
     groups = (rows + slots - 1) // slots
     assert q["num_blocks"] == min(groups, per_cu * cus), q
     qf = R.query_config(4, rows, D, x.dtype)
-    if wide:
-        assert qf["vecs_per_lane"] != 4, qf
+    if fused_apart:
+        assert (qf["lanes_per_row"], qf["vecs_per_lane"]) != (lanes, k), qf
     else:
         assert qf["lanes_per_row"] == lanes and qf["vecs_per_lane"] == k, qf
     dx_a, dw_a = R.rmsnorm_vjp(x, w, dy, c["eps"], 0.25)
@@ -198,13 +201,13 @@ def test_wave_rows_geometry_and_bitwise(R, rows, D, dtype, lanes, k, slots, per_
                                  block_threads=s * lanes, num_blocks=0))
     for v in variants:
         dx_b, dw_b = R.rmsnorm_vjp(x, w, dy, c["eps"], 0.25, cfg=v)
-        if not wide:
+        if not fused_apart:
             dh_b, _ = R.fused_add_rmsnorm_vjp(x, w, dy, dr, c["eps"], 1.0, cfg=v)
         torch.cuda.synchronize()
         assert torch.equal(dx_a, dx_b), v
-        if not wide:
+        if not fused_apart:
             assert torch.equal(dh_a, dh_b), v
-    if wide:
+    if fused_apart:
         dhref, _ = O.fused_add_rmsnorm_vjp(c["x"][:8], c["w"], c["dy"][:8], c["residual"][:8], c["eps"], 1.0)
         assert_close(dh_a[:8], dhref, "dh (fused backward, its own layout)")
     idx = _edge_rows(rows, 16)

@@ -39,14 +39,19 @@ def _say(msg):
 def _backward_instance(dtype, lanes, k, op):
     """Whether a pipelined instance exists for a backward form (mirror of the
     library's instance table): 16-bit rows with two vectors per lane stop at
-    640 lanes (wider would spill), the wide four-vector instances serve the
+    640 lanes (768 for the VJP and the grad call; wider would spill), the
+    wide four-vector instances serve the
     VJP of 16-bit rows only, and fp32 rows take four vectors per lane on 512
     lanes only."""
     if k == 4:
         if dtype == "float32":
             return lanes == 512
         return op == "vjp" and lanes in (384, 448, 512)
-    return not (dtype != "float32" and k == 2 and lanes > 640)
+    if dtype != "float32" and k == 2 and lanes > 640:
+        # 12 waves fit the VJP and the grad call (151-162 VGPRs), not the
+        # fused backward; 14 waves fit none
+        return lanes == 768 and op != "fused"
+    return True
 
 
 CASES = [(dt, lanes, k) for dt in ("float32", "float16", "bfloat16") for lanes in WAVE_LANES for k in (1, 2)]
