@@ -249,14 +249,23 @@ struct VjpRow {
     Raw<T, NV> dr[K];   // d_new_residual (kResGrad only)
 };
 
-template <typename T, int NV, int K, int MODE>
+// WITH_DR: also the d_new_residual row (kResGrad) into d.dr; instances that
+// keep one d_new_residual buffer of their own load it with vjp_issue_dr.
+template <typename T, int NV, int K, int MODE, bool WITH_DR = true>
 __device__ __forceinline__ void vjp_issue(const RowArgs& a, int64_t row0, int slot, const Cols<K>& c,
                                           VjpRow<T, NV, K>& d) {
     const int64_t row = row0 + slot;
     const int64_t base = row < a.rows ? row * a.D : 0;
     issue_row<T, NV, K>(static_cast<const T*>(a.x), base, c, d.x);
     issue_row<T, NV, K>(static_cast<const T*>(a.dy), base, c, d.dy);
-    if constexpr (MODE == kResGrad) issue_row<T, NV, K>(static_cast<const T*>(a.res), base, c, d.dr);
+    if constexpr (MODE == kResGrad && WITH_DR) issue_row<T, NV, K>(static_cast<const T*>(a.res), base, c, d.dr);
+}
+
+template <typename T, int NV, int K>
+__device__ __forceinline__ void vjp_issue_dr(const RowArgs& a, int64_t row0, int slot, const Cols<K>& c,
+                                             Raw<T, NV> (&dr)[K]) {
+    const int64_t row = row0 + slot;
+    issue_row<T, NV, K>(static_cast<const T*>(a.res), row < a.rows ? row * a.D : 0, c, dr);
 }
 
 // FULL: every vector of the row is in range and every processed row exists
@@ -267,8 +276,8 @@ __device__ __forceinline__ void vjp_issue(const RowArgs& a, int64_t row0, int sl
 template <typename T, int NV, int K, int MODE, bool FULL = false>
 __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int slot, int lanes,
                                             const Cols<K>& c, const float (&g)[K][NV],
-                                            float (&acc)[K][NV], VjpRow<T, NV, K>& d, float* red,
-                                            int& parity) {
+                                            float (&acc)[K][NV], VjpRow<T, NV, K>& d,
+                                            const Raw<T, NV> (&dr)[K], float* red, int& parity) {
     const int64_t row = row0 + slot;
     const bool rok = FULL || row < a.rows;
     const int64_t base = row * a.D;
@@ -314,7 +323,7 @@ __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int 
                 // fixed evaluation order (explicit fma), so every instance
                 // that computes dx rounds it identically
                 o[e] = __builtin_fmaf(-xv, cc, (r * g[k][e]) * dv);
-                if constexpr (MODE == kResGrad) o[e] += elem(d.dr[k], e);
+                if constexpr (MODE == kResGrad) o[e] += elem(dr[k], e);
                 acc[k][e] = __builtin_fmaf(dv * xv, r, acc[k][e]);
             }
             if (FULL || c.ok[k]) store_f32<T, NV>(dx + base + c.off[k], o);
@@ -379,10 +388,18 @@ __global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
             // and vector is in range here (the plan selects this kernel only
             // then), so the processing masks nothing and stores
             // unconditionally.
+            // kDrOwn (the fused backward on rows of 12 waves x 2 16-bit
+            // vectors, one VGPR short otherwise): one d_new_residual buffer,
+            // loaded for the next group right after the current group has
+            // used it -- behind the next group's x / dy loads, so the
+            // in-order wait counts need not drain those to reach it.
+            constexpr bool kDrOwn = MODE == kResGrad && LANES > 640 && K * NV == kVjpPipeElems;
             Raw<T, NV> pw[K];
             issue_w<T, NV, K>(static_cast<const T*>(a.w), c, pw);
             VjpRow<T, NV, K> ra, rb;
-            vjp_issue<T, NV, K, MODE>(a, row0, slot, c, ra);
+            Raw<T, NV> drs[K];
+            vjp_issue<T, NV, K, MODE, !kDrOwn>(a, row0, slot, c, ra);
+            if constexpr (kDrOwn) vjp_issue_dr<T, NV, K>(a, row0, slot, c, drs);
             mask_cols<T, NV, K>(c, pw);
 #pragma unroll
             for (int k = 0; k < K; ++k)
@@ -391,20 +408,26 @@ __global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
             int64_t next = row0 + step;
             for (;;) {  // ra holds group row0
                 if (next >= a.rows) {
-                    vjp_process<T, NV, K, MODE, true>(a, row0, slot, lanes, c, g, acc, ra, red, parity);
+                    vjp_process<T, NV, K, MODE, true>(a, row0, slot, lanes, c, g, acc, ra, kDrOwn ? drs : ra.dr,
+                                                      red, parity);
                     break;
                 }
-                vjp_issue<T, NV, K, MODE>(a, next, slot, c, rb);
-                vjp_process<T, NV, K, MODE, true>(a, row0, slot, lanes, c, g, acc, ra, red, parity);
+                vjp_issue<T, NV, K, MODE, !kDrOwn>(a, next, slot, c, rb);
+                vjp_process<T, NV, K, MODE, true>(a, row0, slot, lanes, c, g, acc, ra, kDrOwn ? drs : ra.dr, red,
+                                                  parity);
+                if constexpr (kDrOwn) vjp_issue_dr<T, NV, K>(a, next, slot, c, drs);
                 row0 = next;
                 next += step;
                 // rb holds group row0
                 if (next >= a.rows) {
-                    vjp_process<T, NV, K, MODE, true>(a, row0, slot, lanes, c, g, acc, rb, red, parity);
+                    vjp_process<T, NV, K, MODE, true>(a, row0, slot, lanes, c, g, acc, rb, kDrOwn ? drs : rb.dr,
+                                                      red, parity);
                     break;
                 }
-                vjp_issue<T, NV, K, MODE>(a, next, slot, c, ra);
-                vjp_process<T, NV, K, MODE, true>(a, row0, slot, lanes, c, g, acc, rb, red, parity);
+                vjp_issue<T, NV, K, MODE, !kDrOwn>(a, next, slot, c, ra);
+                vjp_process<T, NV, K, MODE, true>(a, row0, slot, lanes, c, g, acc, rb, kDrOwn ? drs : rb.dr, red,
+                                                  parity);
+                if constexpr (kDrOwn) vjp_issue_dr<T, NV, K>(a, next, slot, c, drs);
                 row0 = next;
                 next += step;
             }
@@ -421,12 +444,12 @@ __global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
                 for (int k = 0; k < K; ++k)
 #pragma unroll
                     for (int e = 0; e < NV; ++e) g[k][e] = a.wb + elem(pw[k], e);
-                vjp_process<T, NV, K, MODE>(a, row0, slot, lanes, c, g, acc, d, red, parity);
+                vjp_process<T, NV, K, MODE>(a, row0, slot, lanes, c, g, acc, d, d.dr, red, parity);
             }
             for (row0 += step; row0 < a.rows; row0 += step) {
                 VjpRow<T, NV, K> d;
                 vjp_issue<T, NV, K, MODE>(a, row0, slot, c, d);
-                vjp_process<T, NV, K, MODE>(a, row0, slot, lanes, c, g, acc, d, red, parity);
+                vjp_process<T, NV, K, MODE>(a, row0, slot, lanes, c, g, acc, d, d.dr, red, parity);
             }
         }
     }

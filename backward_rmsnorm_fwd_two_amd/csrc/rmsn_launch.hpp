@@ -76,7 +76,7 @@ constexpr int wave_rows_block_max(int lanes, int elems) {
 constexpr bool vjp_wave_rows_fit(int lanes, int k, int itemsize, int mode) {
     return k * (16 / itemsize) > kVjpPipeElems ? (mode == 0 && (lanes == 384 || lanes == 448 || lanes == 512))
            : itemsize == 4 && k == 4                ? lanes == 512
-           : k * (16 / itemsize) == kVjpPipeElems && lanes > 640 ? (lanes == 768 && mode != 2)
+           : k * (16 / itemsize) == kVjpPipeElems && lanes > 640 ? lanes == 768
                                                     : true;
 }
 

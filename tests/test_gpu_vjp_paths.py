@@ -62,7 +62,7 @@ CASES = [
     (300, 10240, "bfloat16"),   # wave rows: 10 waves x 2
     (900, 3072, "float32"),     # wave rows: 6 waves x 2 x 4 floats
     (333, 7168, "float32"),     # wave rows: 14 waves x 2 x 4 floats
-    (130, 12288, "float16"),    # 12 waves x 2 (VJP, grad call); the fused backward keeps 1024 lanes
+    (130, 12288, "float16"),    # 12 waves x 2, one row per block
     (100, 14336, "bfloat16"),   # wide: 7 waves x 4 vectors
     (99, 16384, "float16"),     # wide: 8 waves x 4 vectors (512 lanes)
     (64, 12288, "float32"),     # plain loop: 1024 lanes x 3 of 4 vectors (no wave instance)
@@ -166,11 +166,10 @@ def test_wave_rows_geometry_and_bitwise(R, rows, D, dtype, lanes, k, slots, per_
         return
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     # wide 16-bit rows (four vectors per lane): the VJP only, one row per
-    # block; fp32 rows of 512 lanes x 4 serve every backward form; 16-bit
-    # rows of 12 waves x 2 serve the VJP and the grad call, not the fused
-    # backward (it would spill)
+    # block, the fused backward keeps its own layout; fp32 rows of 512 lanes
+    # x 4 serve every backward form
     wide = k == 4 and dtype != "float32"
-    fused_apart = wide or (dtype != "float32" and k == 2 and lanes > 640)
+    fused_apart = wide
     assert q["vec_bytes"] == 16 and q["lanes_per_row"] == lanes and q["vecs_per_lane"] == k, q
     assert lanes * k == nvec and (k == 4 or not _is_pow2(lanes))
     assert q["block_threads"] == slots * lanes, q

@@ -39,7 +39,7 @@ def _say(msg):
 def _backward_instance(dtype, lanes, k, op):
     """Whether a pipelined instance exists for a backward form (mirror of the
     library's instance table): 16-bit rows with two vectors per lane stop at
-    640 lanes (768 for the VJP and the grad call; wider would spill), the
+    768 lanes (wider would spill), the
     wide four-vector instances serve the
     VJP of 16-bit rows only, and fp32 rows take four vectors per lane on 512
     lanes only."""
@@ -48,9 +48,9 @@ def _backward_instance(dtype, lanes, k, op):
             return lanes == 512
         return op == "vjp" and lanes in (384, 448, 512)
     if dtype != "float32" and k == 2 and lanes > 640:
-        # 12 waves fit the VJP and the grad call (151-162 VGPRs), not the
-        # fused backward; 14 waves fit none
-        return lanes == 768 and op != "fused"
+        # 12 waves fit (151-166 VGPRs; the fused backward with one
+        # d_new_residual buffer); 14 waves fit none
+        return lanes == 768
     return True
 
 
