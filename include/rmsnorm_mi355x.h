@@ -118,8 +118,8 @@ typedef struct {
                                lanes_per_row * vecs_per_lane vectors, 1, 2 or 4 rows
                                per block; for the backward forms only where the
                                instance exists: 16-bit rows of 14 waves with 2
-                               vectors per lane do not, nor 12 waves for the fused
-                               backward); the VJP of 16-bit rows also takes 384, 448
+                               vectors per lane do not); the VJP of 16-bit rows also
+                               takes 384, 448
                                or 512 lanes with 4 vectors per lane, and every
                                backward form of fp32 rows 512 lanes with 4, one row
                                per block */
