@@ -121,9 +121,10 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
         // the backward forms -- instead of masking part of a power-of-two
         // lane group.
         // Four vectors per lane, one row per block, for the backward forms:
-        // wide 16-bit VJP rows (D = 12288, 14336, 16384 on 384, 448 or 512
-        // lanes) and fp32 rows of 512 lanes (D = 8192).
-        const bool wide_ok = vjp && (s == 4 || op == RMSN_OP_VJP);
+        // wide 16-bit rows (D = 12288, 14336, 16384 on 384, 448 or 512 lanes
+        // for the VJP, 512 for the grad call) and fp32 rows of 512 lanes (D
+        // = 8192).
+        const bool wide_ok = vjp && (s == 4 || op != RMSN_OP_FUSED_VJP);
         const int vmode = op == RMSN_OP_GRAD ? 1 : op == RMSN_OP_FUSED_VJP ? 2 : 0;
         if (vb == 16 && (lanes == 0 ? k == 0 : (rmsn::wave_rows(lanes) || (wide_ok && k == 4 && lanes == 512)))) {
             // the first of 2, 1, 4 vectors per lane that tiles the row and

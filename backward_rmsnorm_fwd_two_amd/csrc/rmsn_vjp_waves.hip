@@ -1,11 +1,13 @@
-// rmsn_vjp_waves.hip -- pipelined VJP row kernels for rows of a whole number
-// of waves that is not a power of two: lanes = 64 W, W = 3, 5, 6, 7, 10, 12,
-// 14, one or two 16-byte vectors per lane, where the row is exactly lanes *
-// K vectors (D = 1536 .. 10240 in 16-bit storage, 768 .. 7168 in fp32; 16-bit
-// rows of 12 or 14 waves with two vectors per lane would spill registers), and
-// wide 16-bit rows with four vectors per lane on 384, 448 or 512 lanes (D =
-// 12288, 14336, 16384), one row per block; fp32 rows of 512 lanes x 4 vectors
-// (D = 8192).
+// rmsn_vjp_waves.hip -- pipelined VJP, grad-call and fused-backward row
+// kernels for rows of a whole number of waves that is not a power of two:
+// lanes = 64 W, W = 3, 5, 6, 7, 10, 12, 14, one or two 16-byte vectors per
+// lane, where the row is exactly lanes * K vectors (D = 1536 .. 12288 in
+// 16-bit storage, 768 .. 7168 in fp32; 16-bit rows of 14 waves with two
+// vectors per lane would spill registers); wide 16-bit rows with four
+// vectors per lane, one row per block, on 384, 448 or 512 lanes for the VJP
+// and 512 for the grad call (D = 12288, 14336, 16384); fp32 rows of 512
+// lanes x 4 vectors (D = 8192).  The table of which exist is
+// vjp_wave_rows_fit.
 // A power-of-two lane count would mask a quarter to a half of such a row and
 // fall back to the plain loop.  A separate translation unit, so that it
 // compiles in parallel with the other instances.
