@@ -171,17 +171,15 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
             if (fn && !block) {
                 int slots = 1;
                 if (vjp) {
-                    while (slots < 4 && w_units * slots < kWaveRowsInFlight && 2 * slots * wl <= maxb &&
-                           rows % (2 * slots) == 0)
+                    while (slots < 4 && w_units * slots < kWaveRowsInFlight && 2 * slots * wl <= maxb)
                         slots *= 2;
                 } else if (wl == 192 && 2 * wl <= maxb) {
                     slots = 2;
                 }
                 block = slots * wl;
             }
-            // the pipelined kernel fills every row slot
             const bool block_ok = fn && wl <= maxb && (block == wl || block == 2 * wl || block == 4 * wl) &&
-                                  block <= maxb && !(vjp && rows % (block / wl) != 0);
+                                  block <= maxb;
             if (block_ok) {
                 const int nslots = block / wl;
                 const int64_t groups = (rows + nslots - 1) / nslots;
@@ -268,8 +266,8 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
             const int nslots = block / lanes;
             const int64_t groups = (rows + nslots - 1) / nslots;
             // Backward forms: the software-pipelined kernel stores
-            // unconditionally, so it serves rows that are exactly lanes * k
-            // vectors and row counts that fill every row slot.  The grad
+            // unconditionally (a block's ragged last row group aside), so it
+            // serves rows that are exactly lanes * k vectors.  The grad
             // call runs pipelined only in an instance with the lanes fixed
             // (8192 x 4096 fp16: 50.6 us against 53.5 in the plain loop; the
             // generic pipelined kernel measured slower than the plain one).
@@ -279,8 +277,7 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
             // CU leave; with the width fixed, one block per CU runs faster).
             const bool whole_wide_row = lanes == rmsn::kVjpPipeFixedMax && block == lanes;
             p->pipe = vjp && k * p->nv <= rmsn::kVjpPipeElems &&
-                      (block <= rmsn::kVjpPipeBlock || whole_wide_row) && (int64_t)lanes * k == p->nvec &&
-                      rows % nslots == 0;
+                      (block <= rmsn::kVjpPipeBlock || whole_wide_row) && (int64_t)lanes * k == p->nvec;
             p->fixed_lanes = p->pipe && rmsn::vjp_kernel_fixed_lanes(dt, p->nv, k, vmode, lanes) != nullptr;
             // the grad call runs pipelined only with the lanes fixed
             if (p->pipe && !p->fixed_lanes && (block > rmsn::kVjpPipeBlock || op == RMSN_OP_GRAD)) p->pipe = false;

@@ -384,10 +384,13 @@ __global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
             // register buffers alternate (the loop is unrolled twice): a copy
             // of loaded data would make the wave wait for the prefetch at the
             // end of every iteration.  The gain's loads go out first, so that
-            // none of them is still pending when the loop starts.  Every row
-            // and vector is in range here (the plan selects this kernel only
-            // then), so the processing masks nothing and stores
-            // unconditionally.
+            // none of them is still pending when the loop starts.  Every
+            // vector of a row is in range here (the plan selects this kernel
+            // only then), and every row group but a block's last is full, so the
+            // loop's processing masks nothing and stores unconditionally; a
+            // ragged last group (rows not a multiple of the row slots) is
+            // processed masked on the loop's exit path, after which the
+            // block only joins its dw.
             // kDrOwn (the fused backward on rows of 12 waves x 2 16-bit
             // vectors, one VGPR short otherwise): one d_new_residual buffer,
             // loaded for the next group right after the current group has
@@ -407,9 +410,13 @@ __global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
                 for (int e = 0; e < NV; ++e) g[k][e] = a.wb + elem(pw[k], e);
             int64_t next = row0 + step;
             for (;;) {  // ra holds group row0
-                if (next >= a.rows) {
-                    vjp_process<T, NV, K, MODE, true>(a, row0, slot, lanes, c, g, acc, ra, kDrOwn ? drs : ra.dr,
-                                                      red, parity);
+                if (next >= a.rows) {  // the block's last group, possibly ragged
+                    if (row0 + nslots <= a.rows)
+                        vjp_process<T, NV, K, MODE, true>(a, row0, slot, lanes, c, g, acc, ra,
+                                                          kDrOwn ? drs : ra.dr, red, parity);
+                    else
+                        vjp_process<T, NV, K, MODE, false>(a, row0, slot, lanes, c, g, acc, ra,
+                                                           kDrOwn ? drs : ra.dr, red, parity);
                     break;
                 }
                 vjp_issue<T, NV, K, MODE, !kDrOwn>(a, next, slot, c, rb);
@@ -419,9 +426,13 @@ __global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
                 row0 = next;
                 next += step;
                 // rb holds group row0
-                if (next >= a.rows) {
-                    vjp_process<T, NV, K, MODE, true>(a, row0, slot, lanes, c, g, acc, rb, kDrOwn ? drs : rb.dr,
-                                                      red, parity);
+                if (next >= a.rows) {  // the block's last group, possibly ragged
+                    if (row0 + nslots <= a.rows)
+                        vjp_process<T, NV, K, MODE, true>(a, row0, slot, lanes, c, g, acc, rb,
+                                                          kDrOwn ? drs : rb.dr, red, parity);
+                    else
+                        vjp_process<T, NV, K, MODE, false>(a, row0, slot, lanes, c, g, acc, rb,
+                                                           kDrOwn ? drs : rb.dr, red, parity);
                     break;
                 }
                 vjp_issue<T, NV, K, MODE, !kDrOwn>(a, next, slot, c, ra);

@@ -252,8 +252,8 @@ int silu_gate_vjp_cfg(const void *x, const void *dy, void *dx, int64_t rows, int
  * the library additionally picks, per call, between two row loops of the same
  * geometry and arithmetic: a software-pipelined one (blocks of at most 256
  * threads or one 512-lane row, rows of exactly lanes_per_row * vecs_per_lane
- * vectors, a row count that fills every row slot; for the grad call only
- * where an instance with the lanes fixed exists) and the plain one; the
+ * vectors; for the grad call only where an instance with the lanes fixed
+ * exists) and the plain one; the
  * choice does not change any result.  Wave rows (see lanes_per_row) always
  * run pipelined. */
 int rmsn_query_config(int op, int64_t rows, int64_t D, int dt, int align_bytes,

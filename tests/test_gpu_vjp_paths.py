@@ -1,7 +1,7 @@
 """GPU: the two VJP row loops.  Blocks of at most 256 threads (or a whole
 512-lane row in a 512-thread block) whose rows are exactly lanes x K
-vectors, with a row count that fills every row slot, run the
-software-pipelined unmasked loop, and so do rows of a whole number of
+vectors run the software-pipelined loop (unmasked; a ragged last row group
+is masked on the loop's exit path), and so do rows of a whole number of
 waves that is not a power of two (wave rows: 3, 5, 6, 7, 10 waves ...,
 one to four rows per block); every other register-resident shape runs
 the plain loop.  Checks, on both sides of that rule: parity with the
@@ -42,19 +42,19 @@ def _edge_rows(rows, n=48):
     return sorted(set(idx))
 
 
-# (rows, D, dtype): pipelined shapes (rows fill the slots, D tiles exactly)
-# next to plain ones (a ragged last group of slots, or D that does not tile)
+# (rows, D, dtype): pipelined shapes (D tiles exactly; full or ragged last
+# row groups) next to plain ones (D that does not tile)
 CASES = [
     (8192, 4096, "float16"),    # pipelined: 256 lanes x 2 vectors, one slot
     (8191, 4096, "float16"),    # still pipelined (one slot), odd row count
     (4096, 512, "bfloat16"),    # pipelined: 32 lanes, 8 row slots
-    (4093, 512, "bfloat16"),    # plain: last group of slots is ragged
+    (4093, 512, "bfloat16"),    # pipelined, 8 slots: the last group is ragged (masked exit path)
     (2048, 1024, "float32"),    # pipelined: 128 lanes x 2 x 4 floats, 2 slots
-    (2047, 1024, "float32"),    # plain: ragged
+    (2047, 1024, "float32"),    # pipelined, ragged last group
     (3000, 3072, "float16"),    # wave rows: 3 waves x 2 vectors, two rows per block
     (1200, 1536, "bfloat16"),   # wave rows: 3 waves x 1 vector, four rows per block
-    (1202, 1536, "float16"),    # wave rows, rows % 4 == 2: two rows per block
-    (601, 2560, "float16"),     # wave rows: 5 waves x 1, odd rows: one row, two blocks per CU
+    (1202, 1536, "float16"),    # wave rows, four rows per block, rows % 4 == 2: ragged last group
+    (601, 2560, "float16"),     # wave rows: 5 waves x 1, two rows per block, odd rows: ragged
     (1001, 5120, "bfloat16"),   # wave rows: 5 waves x 2
     (700, 6144, "float16"),     # wave rows: 6 waves x 2
     (513, 3584, "bfloat16"),    # wave rows: 7 waves x 1, two blocks per CU
@@ -133,8 +133,8 @@ def _is_pow2(v):
 WAVE = [
     (3000, 3072, "float16", 192, 2, 2, 1),
     (1200, 1536, "bfloat16", 192, 1, 4, 1),
-    (1202, 1536, "float16", 192, 1, 2, 2),
-    (601, 2560, "float16", 320, 1, 1, 2),
+    (1202, 1536, "float16", 192, 1, 4, 1),
+    (601, 2560, "float16", 320, 1, 2, 1),
     (1001, 5120, "bfloat16", 320, 2, 1, 1),
     (700, 6144, "float16", 384, 2, 1, 1),
     (513, 3584, "bfloat16", 448, 1, 1, 2),
@@ -195,7 +195,7 @@ def test_wave_rows_geometry_and_bitwise(R, rows, D, dtype, lanes, k, slots, per_
             assert torch.equal(dw_g, dw_a)
     variants = [dict(lanes_per_row=lanes, vecs_per_lane=k, vec_bytes=16, block_threads=lanes, num_blocks=37)]
     for s in (2, 4):
-        if not wide and rows % s == 0 and s * lanes <= 768:
+        if not wide and s * lanes <= 768:
             variants.append(dict(lanes_per_row=lanes, vecs_per_lane=k, vec_bytes=16,
                                  block_threads=s * lanes, num_blocks=0))
     for v in variants:

@@ -68,8 +68,8 @@ def test_wave_instance_parity(R, dtype, lanes, k):
     nv = 4 if dtype == "float32" else 8
     D = lanes * k * nv
     _say(f"wave instance {dtype} lanes={lanes} k={k} D={D}")
-    # ragged row counts: 13 rows in one-row blocks, 14 in two-row blocks
-    for rows, slots in ((13, 1), (14, 2)):
+    # 13 rows in one-row blocks, and in two-row blocks (a ragged last group)
+    for rows, slots in ((13, 1), (13, 2)):
         c = I.generic(rows, D, dtype, seed=lanes * 7 + k + rows)
         x, w, dy, res = (c[n].to(DEV) for n in ("x", "w", "dy", "residual"))
         eps, wb = c["eps"], 0.5
