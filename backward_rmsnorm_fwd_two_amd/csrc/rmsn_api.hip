@@ -137,11 +137,15 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
                 const bool tiles = (rmsn::wave_rows(l) && rmsn::wave_rows_supported(l)) || (kk == 4 && l == 512);
                 if ((lanes != 0 && l != lanes) || !tiles) continue;
                 // The automatic forward takes wave rows with two vectors per
-                // lane up to 768 lanes; with one vector, or at 896 lanes, the
-                // masked power-of-two layout measured as fast or faster (cold
-                // 64 MiB tensors: D = 5120 bf16 24.5 vs 25.8 us; D = 3584
-                // bf16 25.0 vs 24.2 us, 14336 bf16 28.2 vs 27.0 us).
-                if (lanes == 0 && !vjp && (kk != 2 || l > 768)) continue;
+                // lane on rows of at most 1024 vectors; with one vector per
+                // lane the masked power-of-two layout measured as fast or
+                // faster (cold 64 MiB tensors: D = 5120 bf16 24.5 vs 25.8 us;
+                // D = 3584 bf16 25.0 vs 24.2 us), and longer rows of the
+                // plain forward take 256 lanes x 8 (below); the fused
+                // forward keeps wave rows up to 768 lanes.
+                if (lanes == 0 && !vjp &&
+                    (kk != 2 || l > 768 || (op == RMSN_OP_FWD && p->nvec > 1024)))
+                    continue;
                 fn = vjp ? rmsn::vjp_kernel_fixed_lanes(dt, p->nv, kk, vmode, l)
                          : rmsn::fwd_kernel_fixed_lanes(dt, p->nv, kk, op == RMSN_OP_FUSED, l);
                 if (fn) {
@@ -215,7 +219,15 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
             // bytes, up to 8 of a narrower width (narrow loads on fewer
             // lanes keep more rows in flight per wave; measured 1.4-2.5x
             // faster than 2 narrow vectors per lane at D = 257..513 fp16)
-            const int kt = std::min(8, std::max(1, 32 / vb));
+            int kt = std::min(8, std::max(1, 32 / vb));
+            // The plain forward of rows of 1025..2048 16-byte vectors (D =
+            // 8200..16384 in 16-bit storage, 4100..8192 in fp32): 256 lanes
+            // x 8 vectors in 256-thread blocks, half-empty or full, ran
+            // faster than wave rows, 1024 lanes x 2 and the streaming kernel
+            // on cold data (bf16, 64 MiB tensors: D = 10240 25.6 vs 28.3-29.1
+            // us, 8200 27.9 vs 30.1-31.7, 16384 25.9 vs 26.7-28.7; 256 MiB:
+            // D = 10240 87.1 vs 96.9-102.6 us; fp32 D = 4100 26.6 vs 29.0).
+            if (op == RMSN_OP_FWD && vb == 16 && p->nvec > 1024 && p->nvec <= 2048) kt = 8;
             lanes = std::min(1024, next_pow2((p->nvec + kt - 1) / kt));
             k = next_pow2((p->nvec + lanes - 1) / lanes);
         } else if (lanes == 0) {
@@ -242,8 +254,9 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
         } else if (automatic && op == RMSN_OP_FWD && lanes == 1024 &&
                    (int64_t)p->nvec * 10 < (int64_t)lanes * k * 7 && !(k == 4 && p->nv == 4)) {
             // A forward row that needs 1024 lanes but fills under 70 % of
-            // their vectors streams faster, in 512-thread blocks (cold data,
-            // D = 8200..20480 bf16 and 4100..5120 fp32: 12-35 % faster; the
+            // their vectors streams faster, in 512-thread blocks (rows of
+            // more than 2048 vectors: D = 16392..22936 bf16, 8196..11468
+            // fp32; measured 12-35 % faster on cold 256 MiB tensors; the
             // 4-vector fp32 instance measured 4 % faster in registers)
             looped = true;
             loop_block = 512;

@@ -1,6 +1,8 @@
-"""GPU: forward rows that need 1024 lanes but fill under 70 % of their
-vector slots take the streaming kernel (512-thread blocks); full rows and
-the 4-vector fp32 instance stay in registers.  Checks the automatic plan on
+"""GPU: the plain forward of rows of 1025..2048 16-byte vectors takes 256
+lanes x 8 vectors in 256-thread blocks; longer rows that need 1024 lanes
+but fill under 70 % of their vector slots take the streaming kernel
+(512-thread blocks); full rows and the 4-vector fp32 instance stay in
+registers.  Checks the automatic plan on
 both sides of that rule and parity of the forward with the fp64 oracle on
 the first and last rows, plus the same rows forced through the register
 kernel.  Rows of a whole number of waves that is not a power of two (wave
@@ -28,22 +30,26 @@ def R():
     return pkg
 
 
-# (rows, D, dtype, streamed by the automatic plan)
-CASES = [(600, 8200, "bfloat16", True), (500, 10248, "float16", True), (300, 16392, "bfloat16", True),
-         (700, 4100, "float32", True), (400, 16384, "bfloat16", False), (300, 8200, "float32", False),
-         (500, 12288, "bfloat16", False)]
+# (rows, D, dtype, the automatic plan: "256x8" for rows of 1025..2048
+# 16-byte vectors, "stream" for sparser 1024-lane rows, "reg" otherwise)
+CASES = [(600, 8200, "bfloat16", "256x8"), (500, 10248, "float16", "256x8"), (300, 16392, "bfloat16", "stream"),
+         (700, 4100, "float32", "256x8"), (400, 16384, "bfloat16", "256x8"), (300, 8200, "float32", "reg"),
+         (500, 12288, "bfloat16", "256x8"), (250, 20480, "bfloat16", "stream"), (200, 22000, "float16", "stream")]
 
 
-@pytest.mark.parametrize("rows,D,dtype,streamed", CASES)
-def test_sparse_forward_rows_stream(R, rows, D, dtype, streamed):
+@pytest.mark.parametrize("rows,D,dtype,plan", CASES)
+def test_sparse_forward_rows_stream(R, rows, D, dtype, plan):
     print(f"forward paths rows={rows} D={D} {dtype}", flush=True)
     sys.stdout.flush()
     c = I.generic(rows, D, dtype, seed=rows + D)
     x, w = c["x"].to(DEV), c["w"].to(DEV)
     q = R.query_config(0, rows, D, x.dtype)
-    assert (q["vecs_per_lane"] == -1) == streamed, q
-    if streamed:
-        assert q["block_threads"] == 512, q
+    if plan == "stream":
+        assert q["vecs_per_lane"] == -1 and q["block_threads"] == 512, q
+    elif plan == "256x8":
+        assert (q["lanes_per_row"], q["vecs_per_lane"], q["block_threads"]) == (256, 8, 256), q
+    else:
+        assert q["vecs_per_lane"] > 0 and q["lanes_per_row"] == 1024, q
     y = R.rmsnorm_fwd(x, w, c["eps"], 1.0)
     reg = dict(lanes_per_row=1024, vecs_per_lane=0, vec_bytes=0, block_threads=1024, num_blocks=0)
     y_reg = R.rmsnorm_fwd(x, w, c["eps"], 1.0, cfg=reg)
@@ -76,12 +82,19 @@ def test_wave_rows_forward(R, rows, D, dtype, lanes, slots):
         q = R.query_config(op, rows, D, x.dtype)
         if lanes is None:
             assert _is_pow2(q["lanes_per_row"]) or q["vecs_per_lane"] == -1, q
+        elif op == 0 and nvec > 1024:
+            # the plain forward of longer rows takes 256 lanes x 8 instead
+            assert (q["lanes_per_row"], q["vecs_per_lane"]) == (256, 8), q
         else:
             assert q["lanes_per_row"] == lanes and q["vecs_per_lane"] == 2 and q["vec_bytes"] == 16, q
             assert q["block_threads"] == slots * lanes and q["num_blocks"] == (rows + slots - 1) // slots, q
-    # the automatic plan, and (power-of-two plans) the wave-row instance the
-    # row also tiles, forced: one vector per lane on 64 W lanes
+    # the automatic plan (the wave-row geometry forced where the plain
+    # forward's automatic plan is 256 x 8), and (power-of-two plans) the
+    # wave-row instance the row also tiles, forced: one vector per lane on
+    # 64 W lanes
     cfgs = [None]
+    if lanes is not None and nvec > 1024:
+        cfgs = [dict(lanes_per_row=lanes, vecs_per_lane=2, vec_bytes=16, block_threads=slots * lanes, num_blocks=0)]
     if lanes is None:
         for k in (1, 2):
             wl = nvec // k
