@@ -273,6 +273,25 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
             }
             if (block < 64 || block > maxb || block % 64 != 0 || block % lanes != 0 || !is_pow2(block))
                 return RMSN_E_CONFIG;
+            // A 16-bit backward row of 1536..2048 vectors (at least 3/4 of
+            // the 2048 slots) that no pipelined instance serves would run the
+            // plain loop on 1024 lanes x 2; on 256 lanes x 8 vectors, one
+            // 256-thread block per CU, it ran 5-12 % faster on cold data
+            // (bf16 64 MiB: D = 14336 grad call 67.7-70.9 vs 73.2-75.2 us,
+            // fused backward 68.1-68.5 vs 76.3-77.1 us; D = 16384 fused
+            // backward 65.9-66.0 vs 75.2-75.3 us; D = 13312 VJP 58.7 vs 62.1
+            // us).  Sparser rows measured slower that way (D = 8200 VJP 70.8
+            // vs 67.4 us), and where a pipelined instance exists (chosen
+            // above) it stays ahead (D = 10240 VJP 43.2 vs 61.7 us); no
+            // pipelined instance has 1024 lanes.
+            bool eight_wide = false;
+            if (vjp && automatic && !req_b && s == 2 && vb == 16 && lanes == 1024 && k == 2 && p->nvec >= 1536) {
+                lanes = 256;
+                k = 8;
+                block = 256;
+                eight_wide = true;
+                if (block > rmsn::max_block_threads(budget_op, k, p->nv, s)) return RMSN_E_CONFIG;
+            }
             p->lanes = lanes;
             p->k = k;
             p->block = block;
@@ -297,6 +316,8 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
             int64_t grid;
             if (cfg && cfg->num_blocks) {
                 grid = cfg->num_blocks;
+            } else if (eight_wide) {
+                grid = std::min<int64_t>(groups, std::min<int64_t>(kMaxPartialRows, cus));
             } else if (p->fixed_lanes) {
                 // one persistent block per CU: with the row width fixed at
                 // compile time the pipelined kernel keeps HBM busy with four

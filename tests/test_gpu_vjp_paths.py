@@ -242,3 +242,42 @@ def test_streaming_vjp_grid_follows_occupancy(R, rows, D, dtype):
     dhref, _ = O.fused_add_rmsnorm_vjp(c["x"][idx], c["w"], c["dy"][idx], c["residual"][idx], c["eps"], 0.5)
     assert_close(dh[idx], dhref, "dh")
     assert_dw_close(dwf, dwref, "fused dw")
+
+
+# (rows, D, dtype, op -> expected (lanes, vectors per lane) of the automatic
+# backward plan): dense 16-bit rows of 1536..2048 vectors without a pipelined
+# instance run the plain loop on 256 lanes x 8, one block per CU; sparser
+# rows keep 1024 lanes x 2
+EIGHT = [
+    (200, 13312, "bfloat16", {2: (256, 8), 3: (256, 8), 4: (256, 8)}),
+    (150, 14336, "float16", {2: (448, 4), 3: (256, 8), 4: (256, 8)}),
+    (130, 16384, "bfloat16", {2: (512, 4), 3: (512, 4), 4: (256, 8)}),
+    (300, 9216, "float16", {2: (1024, 2), 3: (1024, 2), 4: (1024, 2)}),
+]
+
+
+@pytest.mark.parametrize("rows,D,dtype,plans", EIGHT)
+def test_dense_wide_rows_eight_vectors(R, rows, D, dtype, plans):
+    c = I.generic(rows, D, dtype, seed=rows * 3 + D)
+    x, w, dy, dr = (c[k].to(DEV) for k in ("x", "w", "dy", "residual"))
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for op, (lanes, k) in plans.items():
+        q = R.query_config(op, rows, D, x.dtype)
+        _say(f"eight-wide op={op} rows={rows} D={D} {dtype} plan={q}")
+        assert (q["lanes_per_row"], q["vecs_per_lane"]) == (lanes, k), q
+        if (lanes, k) == (256, 8):
+            assert q["block_threads"] == 256 and q["num_blocks"] == min(rows, cus), q
+    dx, dw = R.rmsnorm_vjp(x, w, dy, c["eps"], 0.5)
+    y, dxg, dwg = R.rmsnorm_fwd_vjp(x, w, dy, c["eps"], 0.5)
+    dh, dwf = R.fused_add_rmsnorm_vjp(x, w, dy, dr, c["eps"], 0.5)
+    torch.cuda.synchronize()
+    idx = _edge_rows(rows, 8)
+    dxref, dwref = O.rmsnorm_vjp(c["x"], c["w"], c["dy"], c["eps"], 0.5)
+    yref, _ = O.rmsnorm_fwd(c["x"][idx], c["w"], c["eps"], 0.5)
+    dhref, _ = O.fused_add_rmsnorm_vjp(c["x"][idx], c["w"], c["dy"][idx], c["residual"][idx], c["eps"], 0.5)
+    assert_close(dx[idx], dxref[idx], "dx")
+    assert_close(dxg[idx], dxref[idx], "grad dx")
+    assert_close(y[idx], yref, "grad y")
+    assert_close(dh[idx], dhref, "dh")
+    for d, what in ((dw, "dw"), (dwg, "grad dw"), (dwf, "fused dw")):
+        assert_dw_close(d, dwref, what)
