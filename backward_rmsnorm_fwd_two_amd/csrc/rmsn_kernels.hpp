@@ -391,12 +391,18 @@ __global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
             // ragged last group (rows not a multiple of the row slots) is
             // processed masked on the loop's exit path, after which the
             // block only joins its dw.
-            // kDrOwn (the fused backward on rows of 12 waves x 2 16-bit
-            // vectors, one VGPR short otherwise): one d_new_residual buffer,
-            // loaded for the next group right after the current group has
-            // used it -- behind the next group's x / dy loads, so the
-            // in-order wait counts need not drain those to reach it.
-            constexpr bool kDrOwn = MODE == kResGrad && LANES > 640 && K * NV == kVjpPipeElems;
+            // kDrOwn (the fused backward on rows of 9 or 12 waves x 2 16-bit
+            // vectors, a VGPR or two short otherwise): one d_new_residual
+            // buffer, loaded for the next group right after the current
+            // group has used it -- behind the next group's x / dy loads, so
+            // the in-order wait counts need not drain those to reach it.
+            constexpr bool kDrOwn = MODE == kResGrad && (LANES == 576 || LANES == 768) && K * NV == kVjpPipeElems;
+            // Instances whose blocks hold exactly one row (the lane count
+            // fixes it) never see a ragged group and compile without the
+            // masked copy of the processing, which would cost the tightest
+            // of them registers.
+            constexpr bool kOneRow =
+                LANES > 0 && (wave_rows(LANES) ? wave_rows_block_max(LANES, K * NV) == LANES : LANES >= kVjpPipeBlock);
             Raw<T, NV> pw[K];
             issue_w<T, NV, K>(static_cast<const T*>(a.w), c, pw);
             VjpRow<T, NV, K> ra, rb;
@@ -411,10 +417,10 @@ __global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
             int64_t next = row0 + step;
             for (;;) {  // ra holds group row0
                 if (next >= a.rows) {  // the block's last group, possibly ragged
-                    if (row0 + nslots <= a.rows)
+                    if (kOneRow || row0 + nslots <= a.rows)
                         vjp_process<T, NV, K, MODE, true>(a, row0, slot, lanes, c, g, acc, ra,
                                                           kDrOwn ? drs : ra.dr, red, parity);
-                    else
+                    else if constexpr (!kOneRow)
                         vjp_process<T, NV, K, MODE, false>(a, row0, slot, lanes, c, g, acc, ra,
                                                            kDrOwn ? drs : ra.dr, red, parity);
                     break;
@@ -427,10 +433,10 @@ __global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
                 next += step;
                 // rb holds group row0
                 if (next >= a.rows) {  // the block's last group, possibly ragged
-                    if (row0 + nslots <= a.rows)
+                    if (kOneRow || row0 + nslots <= a.rows)
                         vjp_process<T, NV, K, MODE, true>(a, row0, slot, lanes, c, g, acc, rb,
                                                           kDrOwn ? drs : rb.dr, red, parity);
-                    else
+                    else if constexpr (!kOneRow)
                         vjp_process<T, NV, K, MODE, false>(a, row0, slot, lanes, c, g, acc, rb,
                                                            kDrOwn ? drs : rb.dr, red, parity);
                     break;

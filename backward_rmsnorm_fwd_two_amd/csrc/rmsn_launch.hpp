@@ -46,13 +46,13 @@ constexpr int kVjpPipeBlock = 256;
 constexpr int kVjpPipeFixedMax = 512;
 
 // Rows of a whole number of waves that is not a power of two (lanes = 64 W,
-// W = 3, 5, 6, 7, 10, 12, 14): D = 3072, 5120, 6144, 7168 ... in 16-bit
+// W = 3, 5, 6, 7, 9, 10, 12, 14): D = 3072, 4608, 5120, 6144, 7168 ... in 16-bit
 // storage tile such rows exactly, where a power-of-two lane count would leave
 // a quarter to a half of its vectors masked.  Instances exist with the lanes
 // fixed at compile time, in blocks of one or two rows.
 constexpr bool wave_rows(int lanes) { return lanes > 64 && (lanes & (lanes - 1)) != 0; }
 constexpr bool wave_rows_supported(int lanes) {
-    return lanes == 192 || lanes == 320 || lanes == 384 || lanes == 448 || lanes == 640 ||
+    return lanes == 192 || lanes == 320 || lanes == 384 || lanes == 448 || lanes == 576 || lanes == 640 ||
            lanes == 768 || lanes == 896;
 }
 // Wide 16-bit rows (D = 12288, 14336, 16384) also come pipelined with four

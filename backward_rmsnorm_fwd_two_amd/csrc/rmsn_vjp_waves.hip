@@ -1,6 +1,6 @@
 // rmsn_vjp_waves.hip -- pipelined VJP, grad-call and fused-backward row
 // kernels for rows of a whole number of waves that is not a power of two:
-// lanes = 64 W, W = 3, 5, 6, 7, 10, 12, 14, one or two 16-byte vectors per
+// lanes = 64 W, W = 3, 5, 6, 7, 9, 10, 12, 14, one or two 16-byte vectors per
 // lane, where the row is exactly lanes * K vectors (D = 1536 .. 12288 in
 // 16-bit storage, 768 .. 7168 in fp32; 16-bit rows of 14 waves with two
 // vectors per lane would spill registers); wide 16-bit rows with four
@@ -31,6 +31,7 @@ const void* pick_waves(int lanes) {
         case 320: return one<T, K, MODE, 320>();
         case 384: return one<T, K, MODE, 384>();
         case 448: return one<T, K, MODE, 448>();
+        case 576: return one<T, K, MODE, 576>();
         case 640: return one<T, K, MODE, 640>();
         case 768: return one<T, K, MODE, 768>();
         case 896: return one<T, K, MODE, 896>();

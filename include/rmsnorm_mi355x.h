@@ -113,7 +113,7 @@ typedef enum {
  * RMSN_E_CONFIG. */
 typedef struct {
     int32_t lanes_per_row;  /* threads cooperating on one row: a power of two, 1..1024,
-                               or 64 W with W = 3, 5, 6, 7, 10, 12 or 14 ("wave rows":
+                               or 64 W with W = 3, 5, 6, 7, 9, 10, 12 or 14 ("wave rows":
                                16-byte vectors, vecs_per_lane 1 or 2, rows of exactly
                                lanes_per_row * vecs_per_lane vectors, 1, 2 or 4 rows
                                per block; for the backward forms only where the

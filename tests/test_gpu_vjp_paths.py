@@ -60,6 +60,8 @@ CASES = [
     (513, 3584, "bfloat16"),    # wave rows: 7 waves x 1, two blocks per CU
     (257, 7168, "float16"),     # wave rows: 7 waves x 2
     (300, 10240, "bfloat16"),   # wave rows: 10 waves x 2
+    (300, 4608, "bfloat16"),    # wave rows: 9 waves x 1
+    (200, 9216, "float16"),     # wave rows: 9 waves x 2
     (900, 3072, "float32"),     # wave rows: 6 waves x 2 x 4 floats
     (333, 7168, "float32"),     # wave rows: 14 waves x 2 x 4 floats
     (130, 12288, "float16"),    # 12 waves x 2, one row per block
@@ -140,6 +142,8 @@ WAVE = [
     (513, 3584, "bfloat16", 448, 1, 1, 2),
     (257, 7168, "float16", 448, 2, 1, 1),
     (300, 10240, "bfloat16", 640, 2, 1, 1),
+    (300, 4608, "bfloat16", 576, 1, 1, 1),
+    (200, 9216, "float16", 576, 2, 1, 1),
     (900, 3072, "float32", 384, 2, 1, 1),
     (333, 7168, "float32", 896, 2, 1, 1),
     (130, 12288, "float16", 768, 2, 1, 1),
@@ -252,7 +256,7 @@ EIGHT = [
     (200, 13312, "bfloat16", {2: (256, 8), 3: (256, 8), 4: (256, 8)}),
     (150, 14336, "float16", {2: (448, 4), 3: (256, 8), 4: (256, 8)}),
     (130, 16384, "bfloat16", {2: (512, 4), 3: (512, 4), 4: (256, 8)}),
-    (300, 9216, "float16", {2: (1024, 2), 3: (1024, 2), 4: (1024, 2)}),
+    (300, 8200, "float16", {2: (1024, 2), 3: (1024, 2), 4: (1024, 2)}),
 ]
 
 

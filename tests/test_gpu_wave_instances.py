@@ -1,4 +1,4 @@
-"""GPU: every compiled wave-row instance (rows of W = 3, 5, 6, 7, 10, 12 or
+"""GPU: every compiled wave-row instance (rows of W = 3, 5, 6, 7, 9, 10, 12 or
 14 waves, one or two 16-byte vectors per lane), every wide VJP instance
 (four vectors per lane on 384, 448 or 512 lanes, 16-bit) and the fp32
 four-vector instances (512 lanes) run, forced
@@ -21,7 +21,7 @@ from oracle import oracle as O
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-WAVE_LANES = [192, 320, 384, 448, 640, 768, 896]
+WAVE_LANES = [192, 320, 384, 448, 576, 640, 768, 896]
 E_CONFIG = -8
 
 
