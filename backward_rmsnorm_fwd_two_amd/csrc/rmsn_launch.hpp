@@ -31,13 +31,11 @@ constexpr int max_block_threads(int op, int k, int nv, int itemsize) {
 
 // The VJP row kernel also comes software-pipelined (the next row group's
 // loads in flight while the current one is processed; two groups of raw data
-// live), for instances with at most this many elements per lane, run in
-// blocks of at most kVjpPipeBlock threads: there a block holds one row of up
-// to four waves, and two blocks per CU leave the registers the second buffer
-// needs.  Wider blocks (rows of eight or more waves) keep the plain loop,
-// whose lower register count lets two blocks share a CU.  The pipelined
-// kernel masks nothing: it serves rows that are exactly lanes * K vectors
-// and row counts that fill every row slot of the block.
+// live), for instances with at most this many elements per lane; the
+// generic (runtime-width) pipelined kernel runs in blocks of at most
+// kVjpPipeBlock threads, the fixed-width instances below also in wider
+// blocks of one row.  The pipelined kernel serves rows that are exactly
+// lanes * K vectors and masks nothing but a block's ragged last row group.
 constexpr int kVjpPipeElems = 16;
 constexpr int kVjpPipeBlock = 256;
 // Instances with the lanes per row fixed at compile time also exist for rows

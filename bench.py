@@ -500,7 +500,7 @@ def widths_bench(R, dev, args) -> int:
 
     dt = torch.bfloat16
     grid = []
-    for D in (1536, 2048, 2560, 3072, 3584, 4096, 5120, 6144, 7168, 8192, 10240, 12288, 14336, 16384):
+    for D in (1536, 2048, 2560, 3072, 3584, 4096, 4608, 5120, 6144, 7168, 8192, 9216, 10240, 12288, 14336, 16384):
         rows = (1 << 25) // D
         sets = []
         for _ in range(4):

@@ -250,12 +250,12 @@ int silu_gate_vjp_cfg(const void *x, const void *dy, void *dx, int64_t rows, int
  * largest power of two dividing every pointer, capped at 16, to model other
  * alignments).  Returns RMSN_OK or an argument error.  For the backward forms
  * the library additionally picks, per call, between two row loops of the same
- * geometry and arithmetic: a software-pipelined one (blocks of at most 256
- * threads or one 512-lane row, rows of exactly lanes_per_row * vecs_per_lane
- * vectors; for the grad call only where an instance with the lanes fixed
- * exists) and the plain one; the
- * choice does not change any result.  Wave rows (see lanes_per_row) always
- * run pipelined. */
+ * geometry and arithmetic: a software-pipelined one (rows of exactly
+ * lanes_per_row * vecs_per_lane vectors; power-of-two rows in blocks of at
+ * most 256 threads or as one 512-lane row per block; wave rows and
+ * four-vector rows always; the grad call only where an instance with the
+ * lanes fixed exists) and the plain one; the choice does not change any
+ * result. */
 int rmsn_query_config(int op, int64_t rows, int64_t D, int dt, int align_bytes,
                       rmsn_config_t *out);
 
