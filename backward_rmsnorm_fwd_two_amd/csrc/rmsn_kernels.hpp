@@ -269,10 +269,12 @@ __device__ __forceinline__ void vjp_issue_dr(const RowArgs& a, int64_t row0, int
 }
 
 // FULL: every vector of the row is in range and every processed row exists
-// (the plan guarantees it), so no element is masked and every store is
-// unconditional -- which also keeps the wave's count of outstanding memory
-// operations the same on every path (a store skipped on some paths would
-// make later waits for loads wait for everything).
+// (the plan selects the pipelined kernel only for rows of exactly lanes * K
+// vectors, and its loop passes FULL for every row group but a ragged last
+// one), so no element is masked and every store is unconditional -- which
+// also keeps the wave's count of outstanding memory operations the same on
+// every path (a store skipped on some paths would make later waits for loads
+// wait for everything).
 template <typename T, int NV, int K, int MODE, bool FULL = false>
 __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int slot, int lanes,
                                             const Cols<K>& c, const float (&g)[K][NV],
