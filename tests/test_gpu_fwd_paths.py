@@ -123,3 +123,26 @@ def test_wave_rows_forward(R, rows, D, dtype, lanes, slots):
                 first = (y, n, h)
             else:
                 assert torch.equal(y, first[0]) and torch.equal(n, first[1]) and torch.equal(h, first[2]), cfg
+
+
+# (rows, D, dtype, expected (lanes, vectors per lane) of the plain forward):
+# rows of 129..1024 16-byte vectors that a power-of-two layout with 2 vectors
+# per lane would leave under 90 % full take 4 vectors per lane on half the
+# lanes; full rows and wave rows keep 2
+SHORT = [(300, 4608, "bfloat16", (256, 4)), (301, 2560, "float16", (128, 4)), (300, 1536, "bfloat16", (64, 4)),
+         (257, 3584, "float16", (128, 4)), (300, 4096, "bfloat16", (256, 2)), (300, 3072, "float16", (192, 2))]
+
+
+@pytest.mark.parametrize("rows,D,dtype,plan", SHORT)
+def test_sparse_short_forward_rows(R, rows, D, dtype, plan):
+    print(f"short forward rows={rows} D={D} {dtype}", flush=True)
+    sys.stdout.flush()
+    c = I.generic(rows, D, dtype, seed=rows + 5 * D)
+    x, w = c["x"].to(DEV), c["w"].to(DEV)
+    q = R.query_config(0, rows, D, x.dtype)
+    assert (q["lanes_per_row"], q["vecs_per_lane"]) == plan, q
+    y = R.rmsnorm_fwd(x, w, c["eps"], 1.0)
+    torch.cuda.synchronize()
+    idx = list(range(16)) + list(range(rows - 16, rows))
+    yref, _ = O.rmsnorm_fwd(c["x"][idx], c["w"], c["eps"], 1.0)
+    assert_close(y[idx], yref, "y")
