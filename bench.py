@@ -475,12 +475,14 @@ def sweep_bench(R, I, dev, args) -> int:
 
 def widths_bench(R, dev, args) -> int:
     """Every RMSNorm op across common model widths (bf16, D = 1536 .. 16384,
-    rows = 2^25 / D: 64 MiB per row tensor), cold: 4 buffer sets rotate so
-    that no call finds its inputs in the 256 MB last-level cache.  Inputs
+    rows = 2^25 / D: 64 MiB per row tensor), cold: buffer sets rotate so that
+    no call finds its inputs in the 256 MB last-level cache.  Inputs
     are drawn on the device from a seeded generator (x, residual ~ N(0, 1),
     dy, d_new_residual ~ N(0, 0.01), w ~ N(0, 0.1); weight_bias 1, eps
     1e-6).  Per op: the plan (lanes x vectors per lane, block, grid) and the
-    algorithmic GB/s of back-to-back prepared calls between one event pair."""
+    algorithmic GB/s of back-to-back prepared calls between one event pair.
+    Ten buffer sets rotate (each op's cycle touches 1.25-2.5 GiB, five to ten
+    times the last-level cache)."""
     stream = torch.cuda.current_stream(dev)
     N = max(20, min(args.steps, 60))
     gen = torch.Generator(device=dev)
@@ -503,7 +505,7 @@ def widths_bench(R, dev, args) -> int:
     for D in (1536, 2048, 2560, 3072, 3584, 4096, 4608, 5120, 6144, 7168, 8192, 9216, 10240, 12288, 14336, 16384):
         rows = (1 << 25) // D
         sets = []
-        for _ in range(4):
+        for _ in range(10):
             x = torch.empty(rows, D, dtype=dt, device=dev).normal_(generator=gen)
             sets.append(dict(x=x, res=torch.empty_like(x).normal_(generator=gen),
                              dy=torch.empty_like(x).normal_(0.0, 0.01, generator=gen),
