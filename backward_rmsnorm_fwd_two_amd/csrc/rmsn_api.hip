@@ -192,8 +192,10 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
                     grid = cfg->num_blocks;
                 } else if (vjp) {
                     // persistent: one block per CU, two where the blocks hold
-                    // too little row data
-                    const int per_cu = w_units * nslots < kWaveRowsInFlight ? 2 : 1;
+                    // too little row data -- except the grad call, whose two
+                    // stored outputs keep the CU busy (D = 3584 bf16, 7 waves
+                    // x 1: 51.0 us at one block per CU vs 54.2 at two)
+                    const int per_cu = w_units * nslots < kWaveRowsInFlight && op != RMSN_OP_GRAD ? 2 : 1;
                     grid = std::min<int64_t>(groups, std::min<int64_t>(kMaxPartialRows, (int64_t)per_cu * cus));
                 } else {
                     grid = std::min<int64_t>(groups, (int64_t)1 << 20);
