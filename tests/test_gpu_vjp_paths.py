@@ -194,6 +194,11 @@ def test_wave_rows_geometry_and_bitwise(R, rows, D, dtype, lanes, k, slots, per_
     torch.cuda.synchronize()
     if not wide:
         assert (qg["lanes_per_row"], qg["vecs_per_lane"]) == (lanes, k), qg
+        # the grad call stores as many rows as it reads (y and dx for x and
+        # dy): one persistent block per CU at every width (the VJP may take
+        # two)
+        gslots = qg["block_threads"] // lanes
+        assert qg["num_blocks"] == min((rows + gslots - 1) // gslots, cus), qg
         assert torch.equal(dx_g, dx_a)
         if qg["num_blocks"] == q["num_blocks"]:
             assert torch.equal(dw_g, dw_a)
