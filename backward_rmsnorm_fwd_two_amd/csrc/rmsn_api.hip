@@ -122,7 +122,7 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
         // lane group.
         // Four vectors per lane, one row per block, for the backward forms:
         // wide 16-bit rows (D = 12288, 14336, 16384 on 384, 448 or 512 lanes
-        // for the VJP, 512 for the grad call) and fp32 rows of 512 lanes (D
+        // for the VJP, 448 or 512 for the grad call) and fp32 rows of 512 lanes (D
         // = 8192).
         const bool wide_ok = vjp && (s == 4 || op != RMSN_OP_FUSED_VJP);
         const int vmode = op == RMSN_OP_GRAD ? 1 : op == RMSN_OP_FUSED_VJP ? 2 : 0;

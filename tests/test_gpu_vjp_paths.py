@@ -259,7 +259,7 @@ def test_streaming_vjp_grid_follows_occupancy(R, rows, D, dtype):
 # rows keep 1024 lanes x 2
 EIGHT = [
     (200, 13312, "bfloat16", {2: (256, 8), 3: (256, 8), 4: (256, 8)}),
-    (150, 14336, "float16", {2: (448, 4), 3: (256, 8), 4: (256, 8)}),
+    (150, 14336, "float16", {2: (448, 4), 3: (448, 4), 4: (256, 8)}),
     (130, 16384, "bfloat16", {2: (512, 4), 3: (512, 4), 4: (256, 8)}),
     (300, 8200, "float16", {2: (1024, 2), 3: (1024, 2), 4: (1024, 2)}),
 ]

@@ -46,7 +46,7 @@ def _backward_instance(dtype, lanes, k, op):
     if k == 4:
         if dtype == "float32":
             return lanes == 512
-        return (op == "vjp" and lanes in (384, 448, 512)) or (op == "grad" and lanes == 512)
+        return (op == "vjp" and lanes in (384, 448, 512)) or (op == "grad" and lanes in (448, 512))
     if dtype != "float32" and k == 2 and lanes > 640:
         # 12 waves fit (151-166 VGPRs; the fused backward with one
         # d_new_residual buffer); 14 waves fit none
