@@ -122,9 +122,9 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
         // lane group.
         // Four vectors per lane, one row per block, for the backward forms:
         // wide 16-bit rows (D = 12288, 14336, 16384 on 384, 448 or 512 lanes
-        // for the VJP, 448 or 512 for the grad call) and fp32 rows of 512 lanes (D
-        // = 8192).
-        const bool wide_ok = vjp && (s == 4 || op != RMSN_OP_FUSED_VJP);
+        // for the VJP, 448 or 512 for the grad call and the fused backward)
+        // and fp32 rows of 512 lanes (D = 8192).
+        const bool wide_ok = vjp;
         const int vmode = op == RMSN_OP_GRAD ? 1 : op == RMSN_OP_FUSED_VJP ? 2 : 0;
         if (vb == 16 && (lanes == 0 ? k == 0 : (rmsn::wave_rows(lanes) || (wide_ok && k == 4 && lanes == 512)))) {
             // the first of 2, 1, 4 vectors per lane that tiles the row and

@@ -394,11 +394,14 @@ __global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
             // processed masked on the loop's exit path, after which the
             // block only joins its dw.
             // kDrOwn (the fused backward on rows of 9 or 12 waves x 2 16-bit
-            // vectors, a VGPR or two short otherwise): one d_new_residual
-            // buffer, loaded for the next group right after the current
-            // group has used it -- behind the next group's x / dy loads, so
-            // the in-order wait counts need not drain those to reach it.
-            constexpr bool kDrOwn = MODE == kResGrad && (LANES == 576 || LANES == 768) && K * NV == kVjpPipeElems;
+            // vectors, a VGPR or two short otherwise, and on the wide rows of
+            // four vectors per lane): one d_new_residual buffer, loaded for
+            // the next group right after the current group has used it --
+            // behind the next group's x / dy loads, so the in-order wait
+            // counts need not drain those to reach it.
+            constexpr bool kDrOwn =
+                MODE == kResGrad &&
+                (((LANES == 576 || LANES == 768) && K * NV == kVjpPipeElems) || K * NV > kVjpPipeElems);
             // Instances whose blocks hold exactly one row (the lane count
             // fixes it) never see a ragged group and compile without the
             // masked copy of the processing, which would cost the tightest

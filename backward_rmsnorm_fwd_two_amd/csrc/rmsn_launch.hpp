@@ -65,18 +65,18 @@ constexpr int kVjpPipeElemsWide = 32;
 constexpr int wave_rows_block_max(int lanes, int elems) {
     return elems > kVjpPipeElems ? lanes : 4 * lanes <= 768 ? 4 * lanes : 2 * lanes <= 768 ? 2 * lanes : lanes;
 }
-// Pipelined VJP instances of the wave-row family that hold their registers
-// without spilling: 16-bit rows with two vectors per lane need up to 168
-// VGPRs, more than rows of 14 waves leave (128); fp32 rows with four vectors
-// per lane fit only as one 512-lane row per block; the wide instances
-// (243-255 VGPRs) exist for 384, 448 and 512 lanes for the VJP (mode 0) and
-// 448 and 512 lanes for the grad call (mode 1: 254 VGPRs at 512 lanes; at
-// 448 three VGPRs go to scratch, and it still runs D = 14336 16-bit rows
-// 16-21 % faster than the plain loop on 256 lanes x 8), none for the fused
-// backward (its third row tensor would spill 20-30 VGPRs).
+// Pipelined VJP instances of the wave-row family: 16-bit rows with two
+// vectors per lane need up to 168 VGPRs, more than rows of 14 waves leave
+// (128); fp32 rows with four vectors per lane fit only as one 512-lane row
+// per block.  The wide instances exist for 384, 448 and 512 lanes for the
+// VJP (mode 0, 243-255 VGPRs, no spills) and for 448 and 512 lanes for the
+// grad call (mode 1: 254 VGPRs at 512 lanes, three spilled to scratch at
+// 448) and the fused backward (mode 2, one d_new_residual buffer: 9-15
+// VGPRs spilled to scratch).  Even spilling, these run D = 14336 and 16384
+// 16-bit rows 2-21 % faster than the plain loop on 256 lanes x 8.
 constexpr bool vjp_wave_rows_fit(int lanes, int k, int itemsize, int mode) {
     return k * (16 / itemsize) > kVjpPipeElems ? (mode == 0 ? (lanes == 384 || lanes == 448 || lanes == 512)
-                                                : mode == 1 && (lanes == 448 || lanes == 512))
+                                                            : (lanes == 448 || lanes == 512))
            : itemsize == 4 && k == 4                ? lanes == 512
            : k * (16 / itemsize) == kVjpPipeElems && lanes > 640 ? lanes == 768
                                                     : true;

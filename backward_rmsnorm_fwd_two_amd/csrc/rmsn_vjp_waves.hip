@@ -5,9 +5,9 @@
 // 16-bit storage, 768 .. 7168 in fp32; 16-bit rows of 14 waves with two
 // vectors per lane would spill registers); wide 16-bit rows with four
 // vectors per lane, one row per block, on 384, 448 or 512 lanes for the VJP
-// and 448 or 512 for the grad call (D = 12288, 14336, 16384); fp32 rows of 512
-// lanes x 4 vectors (D = 8192).  The table of which exist is
-// vjp_wave_rows_fit.
+// and 448 or 512 for the grad call and the fused backward (D = 12288, 14336,
+// 16384); fp32 rows of 512 lanes x 4 vectors (D = 8192).  The table of which
+// exist is vjp_wave_rows_fit.
 // A power-of-two lane count would mask a quarter to a half of such a row and
 // fall back to the plain loop.  A separate translation unit, so that it
 // compiles in parallel with the other instances.
@@ -39,8 +39,8 @@ const void* pick_waves(int lanes) {
     }
 }
 
-// four vectors per lane, one row per block: wide 16-bit rows (the VJP and the
-// grad call) and fp32 rows of 512 lanes (D = 8192)
+// four vectors per lane, one row per block: wide 16-bit rows and fp32 rows of
+// 512 lanes (D = 8192)
 template <typename T, int MODE>
 const void* pick_wide(int lanes) {
     if constexpr (sizeof(T) == 2) {

@@ -120,7 +120,7 @@ typedef struct {
                                instance exists: 16-bit rows of 14 waves with 2
                                vectors per lane do not); the VJP of 16-bit rows also
                                takes 384, 448 or 512 lanes with 4 vectors per lane,
-                               the grad call 448 or 512, and every backward form of fp32
+                               the grad call and fused backward 448 or 512, and every backward form of fp32
                                rows 512 lanes with 4, one row per block */
     int32_t vecs_per_lane;  /* vectors each thread holds per row: 1, 2, 4 or 8;
                                -1 selects the streaming (looped) kernel */

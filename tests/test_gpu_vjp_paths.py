@@ -169,39 +169,31 @@ def test_wave_rows_geometry_and_bitwise(R, rows, D, dtype, lanes, k, slots, per_
         assert _is_pow2(q["lanes_per_row"]), q
         return
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    # wide 16-bit rows (four vectors per lane): the VJP only, one row per
-    # block, the fused backward keeps its own layout; fp32 rows of 512 lanes
-    # x 4 serve every backward form
+    # wide 16-bit rows (four vectors per lane) hold one row per block
     wide = k == 4 and dtype != "float32"
-    fused_apart = wide
     assert q["vec_bytes"] == 16 and q["lanes_per_row"] == lanes and q["vecs_per_lane"] == k, q
     assert lanes * k == nvec and (k == 4 or not _is_pow2(lanes))
     assert q["block_threads"] == slots * lanes, q
     groups = (rows + slots - 1) // slots
     assert q["num_blocks"] == min(groups, per_cu * cus), q
+    # the fused backward and the grad call lay these rows out alike
     qf = R.query_config(4, rows, D, x.dtype)
-    if fused_apart:
-        assert (qf["lanes_per_row"], qf["vecs_per_lane"]) != (lanes, k), qf
-    else:
-        assert qf["lanes_per_row"] == lanes and qf["vecs_per_lane"] == k, qf
+    assert qf["lanes_per_row"] == lanes and qf["vecs_per_lane"] == k, qf
     dx_a, dw_a = R.rmsnorm_vjp(x, w, dy, c["eps"], 0.25)
     dh_a, _ = R.fused_add_rmsnorm_vjp(x, w, dy, dr, c["eps"], 1.0)
-    # the grad call lays these rows out alike (not the wide four-vector
-    # rows) and then gives the VJP's dx bit for bit, dw too on the same grid
+    # the grad call gives the VJP's dx bit for bit, dw too on the same grid
     # (fp16 included: every kernel rounds dx from the same fp32 value)
     qg = R.query_config(3, rows, D, x.dtype)
     _, dx_g, dw_g = R.rmsnorm_fwd_vjp(x, w, dy, c["eps"], 0.25)
     torch.cuda.synchronize()
-    if not wide:
-        assert (qg["lanes_per_row"], qg["vecs_per_lane"]) == (lanes, k), qg
-        # the grad call stores as many rows as it reads (y and dx for x and
-        # dy): one persistent block per CU at every width (the VJP may take
-        # two)
-        gslots = qg["block_threads"] // lanes
-        assert qg["num_blocks"] == min((rows + gslots - 1) // gslots, cus), qg
-        assert torch.equal(dx_g, dx_a)
-        if qg["num_blocks"] == q["num_blocks"]:
-            assert torch.equal(dw_g, dw_a)
+    assert (qg["lanes_per_row"], qg["vecs_per_lane"]) == (lanes, k), qg
+    # the grad call stores as many rows as it reads (y and dx for x and dy):
+    # one persistent block per CU at every width (the VJP may take two)
+    gslots = qg["block_threads"] // lanes
+    assert qg["num_blocks"] == min((rows + gslots - 1) // gslots, cus), qg
+    assert torch.equal(dx_g, dx_a)
+    if qg["num_blocks"] == q["num_blocks"]:
+        assert torch.equal(dw_g, dw_a)
     variants = [dict(lanes_per_row=lanes, vecs_per_lane=k, vec_bytes=16, block_threads=lanes, num_blocks=37)]
     for s in (2, 4):
         if not wide and s * lanes <= 768:
@@ -209,15 +201,12 @@ def test_wave_rows_geometry_and_bitwise(R, rows, D, dtype, lanes, k, slots, per_
                                  block_threads=s * lanes, num_blocks=0))
     for v in variants:
         dx_b, dw_b = R.rmsnorm_vjp(x, w, dy, c["eps"], 0.25, cfg=v)
-        if not fused_apart:
-            dh_b, _ = R.fused_add_rmsnorm_vjp(x, w, dy, dr, c["eps"], 1.0, cfg=v)
+        dh_b, _ = R.fused_add_rmsnorm_vjp(x, w, dy, dr, c["eps"], 1.0, cfg=v)
         torch.cuda.synchronize()
         assert torch.equal(dx_a, dx_b), v
-        if not fused_apart:
-            assert torch.equal(dh_a, dh_b), v
-    if fused_apart:
-        dhref, _ = O.fused_add_rmsnorm_vjp(c["x"][:8], c["w"], c["dy"][:8], c["residual"][:8], c["eps"], 1.0)
-        assert_close(dh_a[:8], dhref, "dh (fused backward, its own layout)")
+        assert torch.equal(dh_a, dh_b), v
+    dhref, _ = O.fused_add_rmsnorm_vjp(c["x"][:8], c["w"], c["dy"][:8], c["residual"][:8], c["eps"], 1.0)
+    assert_close(dh_a[:8], dhref, "dh")
     idx = _edge_rows(rows, 16)
     dxref, dwref = O.rmsnorm_vjp(c["x"], c["w"], c["dy"], c["eps"], 0.25)
     assert_close(dx_b[idx], dxref[idx], "dx (forced geometry)")
@@ -259,8 +248,8 @@ def test_streaming_vjp_grid_follows_occupancy(R, rows, D, dtype):
 # rows keep 1024 lanes x 2
 EIGHT = [
     (200, 13312, "bfloat16", {2: (256, 8), 3: (256, 8), 4: (256, 8)}),
-    (150, 14336, "float16", {2: (448, 4), 3: (448, 4), 4: (256, 8)}),
-    (130, 16384, "bfloat16", {2: (512, 4), 3: (512, 4), 4: (256, 8)}),
+    (150, 14336, "float16", {2: (448, 4), 3: (448, 4), 4: (448, 4)}),
+    (130, 16384, "bfloat16", {2: (512, 4), 3: (512, 4), 4: (512, 4)}),
     (300, 8200, "float16", {2: (1024, 2), 3: (1024, 2), 4: (1024, 2)}),
 ]
 

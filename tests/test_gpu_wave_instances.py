@@ -1,7 +1,8 @@
 """GPU: every compiled wave-row instance (rows of W = 3, 5, 6, 7, 9, 10, 12 or
-14 waves, one or two 16-byte vectors per lane), every wide VJP instance
-(four vectors per lane on 384, 448 or 512 lanes, 16-bit) and the fp32
-four-vector instances (512 lanes) run, forced
+14 waves, one or two 16-byte vectors per lane), every wide 16-bit instance
+(four vectors per lane: 384, 448 or 512 lanes for the VJP, 448 or 512 for
+the grad call and the fused backward) and the fp32 four-vector instances
+(512 lanes) run, forced
 through the *_cfg entry points, and matches the fp64 oracle on a few rows,
 one and two rows per block; combinations without an instance return
 RMSN_E_CONFIG.  The automatic plan selects only some of these instances,
@@ -39,14 +40,13 @@ def _say(msg):
 def _backward_instance(dtype, lanes, k, op):
     """Whether a pipelined instance exists for a backward form (mirror of the
     library's instance table): 16-bit rows with two vectors per lane stop at
-    768 lanes (wider would spill), the
-    wide four-vector instances serve the
-    VJP of 16-bit rows only, and fp32 rows take four vectors per lane on 512
-    lanes only."""
+    768 lanes (wider would spill), the wide four-vector 16-bit instances
+    serve the VJP on 384, 448 and 512 lanes and the other two forms on 448
+    and 512, and fp32 rows take four vectors per lane on 512 lanes only."""
     if k == 4:
         if dtype == "float32":
             return lanes == 512
-        return (op == "vjp" and lanes in (384, 448, 512)) or (op == "grad" and lanes in (448, 512))
+        return (op == "vjp" and lanes in (384, 448, 512)) or (op != "vjp" and lanes in (448, 512))
     if dtype != "float32" and k == 2 and lanes > 640:
         # 12 waves fit (151-166 VGPRs; the fused backward with one
         # d_new_residual buffer); 14 waves fit none
