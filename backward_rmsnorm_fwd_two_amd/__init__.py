@@ -16,7 +16,7 @@ _BINDING_NAMES = {
     "workspace_for", "query_config", "prepare", "prepared_fwd", "prepared_fused", "prepared_vjp",
     "Config", "RMSNormError", "LIB_PATH", "raw",
     "RMSN_F32", "RMSN_F16", "RMSN_BF16", "RMSN_OP_FWD", "RMSN_OP_FUSED", "RMSN_OP_VJP",
-    "RMSN_MAX_D", "STATUS",
+    "RMSN_MAX_D", "STATUS", "rmsnorm_vjp_noalloc", "RMSN_NOALLOC_SCRATCH_BYTES",
 }
 
 _AUTOGRAD_NAMES = {"rms_norm", "fused_add_rms_norm", "RMSNorm", "silu_gate_op"}

@@ -29,6 +29,7 @@ RMSN_F32, RMSN_F16, RMSN_BF16 = 0, 1, 2
 RMSN_OP_FWD, RMSN_OP_FUSED, RMSN_OP_VJP, RMSN_OP_GRAD, RMSN_OP_FUSED_VJP, RMSN_OP_GATE = 0, 1, 2, 3, 4, 5
 RMSN_MAX_D = 1 << 24
 RMSN_MAX_GATE_D = 1 << 28
+RMSN_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 STATUS = {
     0: "RMSN_OK", -1: "RMSN_E_NULLPTR", -2: "RMSN_E_SHAPE", -3: "RMSN_E_DTYPE",
@@ -66,6 +67,7 @@ _lib.rmsnorm_vjp_workspace_bytes.restype = _sz
 _lib.rmsnorm_vjp.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _int, _f32, _f32, _vp]
 _lib.rmsnorm_vjp_cfg.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _int, _f32, _f32,
                                  _cfgp, _vp]
+_lib.rmsnorm_vjp_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, _f32, _f32, _vp]
 _lib.rmsnorm_fwd_vjp.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _int, _f32, _f32,
                                  _vp]
 _lib.rmsnorm_fwd_vjp_cfg.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _int, _f32,
@@ -84,7 +86,7 @@ _lib.rmsn_query_config.argtypes = [_int, _i64, _i64, _int, _int, _cfgp]
 _lib.rmsn_status_str.argtypes = [_int]
 _lib.rmsn_status_str.restype = ctypes.c_char_p
 for _name in ("rmsnorm_fwd", "rmsnorm_fwd_cfg", "fused_add_rmsnorm_fwd", "fused_add_rmsnorm_fwd_cfg",
-              "rmsnorm_vjp", "rmsnorm_vjp_cfg", "rmsnorm_fwd_vjp", "rmsnorm_fwd_vjp_cfg",
+              "rmsnorm_vjp", "rmsnorm_vjp_cfg", "rmsnorm_vjp_noalloc", "rmsnorm_fwd_vjp", "rmsnorm_fwd_vjp_cfg",
               "fused_add_rmsnorm_vjp", "fused_add_rmsnorm_vjp_cfg", "silu_gate", "silu_gate_cfg",
               "silu_gate_vjp", "silu_gate_vjp_cfg", "rmsnorm_backward", "rmsn_query_config"):
     getattr(_lib, _name).restype = _int
@@ -237,6 +239,24 @@ def rmsnorm_vjp(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, eps: float =
     else:
         st = _lib.rmsnorm_vjp_cfg(*args, _cfg(cfg), _stream(x))
     _check(st, "rmsnorm_vjp")
+    return dx, dw
+
+
+def rmsnorm_vjp_noalloc(x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, dx: torch.Tensor,
+                        dw: torch.Tensor, eps: float = 1e-5, weight_bias: float = 0.0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """rmsnorm_vjp into caller-provided dx and dw (fp32) with the library's own
+    device scratch: the call allocates nothing.  Calls that overlap on one
+    GPU share that scratch and race."""
+    dt = _dt(x)
+    rows, D = _rows_d(x)
+    _req(x, "x", x.dtype, x.device)
+    _req(w, "w", x.dtype, x.device, D)
+    _req(dy, "dy", x.dtype, x.device, x.numel())
+    _req(dx, "dx", x.dtype, x.device, x.numel())
+    _req(dw, "dw", torch.float32, x.device, D)
+    st = _lib.rmsnorm_vjp_noalloc(x.data_ptr(), w.data_ptr(), dy.data_ptr(), dx.data_ptr(), dw.data_ptr(),
+                                  rows, D, dt, float(eps), float(weight_bias), _stream(x))
+    _check(st, "rmsnorm_vjp_noalloc")
     return dx, dw
 
 

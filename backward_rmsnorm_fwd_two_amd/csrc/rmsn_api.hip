@@ -8,6 +8,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "rmsn_device.hpp"
 #include "rmsn_launch.hpp"
@@ -23,6 +24,33 @@ constexpr int kMaxPartialRows = 2048;   // bound on dw partial rows (workspace)
 // wave's 16-byte vector of one row tensor (see make_plan).
 constexpr int kWaveRowsInFlight = 15;
 std::atomic<int> g_cu_count[kMaxDevices];
+
+// Scratch of rmsnorm_vjp_noalloc: its dw partial rows live in this
+// file-scope device array (one copy per GPU, held until the process ends)
+// instead of a caller workspace.  Host code never passes the array's name to
+// a kernel (on the host it is a stand-in, not a device address): the first
+// call on a device resolves the device address once, with that device
+// current, and every launch takes that pointer.
+static __device__ __align__(256) unsigned char scratch[RMSN_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device (resolved once per device).
+int scratch_ptr(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RMSN_E_HIP;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return RMSN_E_HIP;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return RMSN_OK;
+}
 
 // Compute units of the current device (cached per device; the cache is the
 // library's only global state).
@@ -755,6 +783,22 @@ int rmsnorm_vjp(const void* x, const void* w, const void* dy, void* dx, float* d
                 size_t workspace_bytes, int64_t rows, int64_t D, int dt, float eps, float weight_bias,
                 void* hip_stream) {
     return vjp_impl(x, w, dy, nullptr, nullptr, dx, dw, RMSN_F32, workspace, workspace_bytes, rows, D, dt, eps,
+                    weight_bias, nullptr, hip_stream);
+}
+
+int rmsnorm_vjp_noalloc(const void* x, const void* w, const void* dy, void* dx, float* dw, int64_t rows,
+                        int64_t D, int dt, float eps, float weight_bias, void* hip_stream) {
+    // argument errors first, so that they do not depend on the device
+    int st = check_common(rows, D, dt);
+    if (st != RMSN_OK) return st;
+    void* ws = nullptr;
+    if (rows > 0) {
+        st = scratch_ptr(&ws);
+        if (st != RMSN_OK) return st;
+    }
+    // vjp_impl plans the launch and returns RMSN_E_WORKSPACE when the plan's
+    // partial rows need more than the scratch holds
+    return vjp_impl(x, w, dy, nullptr, nullptr, dx, dw, RMSN_F32, ws, RMSN_NOALLOC_SCRATCH_BYTES, rows, D, dt, eps,
                     weight_bias, nullptr, hip_stream);
 }
 

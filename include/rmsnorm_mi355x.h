@@ -56,7 +56,8 @@
  *     Arithmetic is fp32 throughout, rounded once (to nearest, ties to even)
  *     on store.
  *   - Pointers: device pointers owned by the caller; the library allocates
- *     no device memory and keeps no pointer after the call returns.  Each
+ *     no device memory and keeps no pointer after the call returns (the one
+ *     fixed array it holds is the scratch of rmsnorm_vjp_noalloc).  Each
  *     pointer must be aligned to its element size; wider alignment (16 B) and
  *     D * itemsize divisible by 16 select the widest loads.
  *   - In place: a [rows, D] output may be the very buffer of a [rows, D]
@@ -155,6 +156,28 @@ int rmsnorm_vjp(const void *x, const void *w, const void *dy,
                 void *dx, float *dw, void *workspace, size_t workspace_bytes,
                 int64_t rows, int64_t D, int dt,
                 float eps, float weight_bias, void *hip_stream);
+
+/* Bytes of the library's own device scratch used by rmsnorm_vjp_noalloc
+ * (one array per GPU, held until the process ends). */
+#define RMSN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* rmsnorm_vjp without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same operation,
+ * kernels and results as rmsnorm_vjp (dx and dw bit-identical for the same
+ * arguments); the dw partial rows live in a file-scope device array of
+ * RMSN_NOALLOC_SCRATCH_BYTES bytes inside the library.  The first call on a
+ * device looks up that array's device address once (hipGetSymbolAddress);
+ * no call allocates or frees memory.  Shapes whose partial rows need more
+ * than RMSN_NOALLOC_SCRATCH_BYTES (num_blocks * D * 4 bytes, e.g. D above
+ * 2^14 with 256 partial rows) return RMSN_E_WORKSPACE before any launch.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap in
+ * time on one GPU (two streams, two threads) race and must be serialised by
+ * the caller.  Nothing in the scratch needs to start at any value. */
+int rmsnorm_vjp_noalloc(const void *x, const void *w, const void *dy,
+                        void *dx, float *dw,
+                        int64_t rows, int64_t D, int dt,
+                        float eps, float weight_bias, void *hip_stream);
 
 /* Grad call: y (as rmsnorm_fwd), dx and dw (as rmsnorm_vjp) from one pass
  * over x and dy.  Same workspace rule as rmsnorm_vjp; y may be x or dy in

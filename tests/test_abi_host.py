@@ -55,6 +55,10 @@ def test_status_strings_without_gpu():
     assert lib.rmsnorm_fwd(None, None, None, 4, 8, 9, 1e-5, 0.0, None) == -3
     assert lib.rmsnorm_fwd(None, None, None, -1, 8, 1, 1e-5, 0.0, None) == -2
     assert lib.rmsnorm_fwd(None, None, None, 0, 8, 1, 1e-5, 0.0, None) == 0
+    lib.rmsnorm_vjp_noalloc.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                                                 ctypes.c_float, ctypes.c_float, ctypes.c_void_p]
+    assert lib.rmsnorm_vjp_noalloc(None, None, None, None, None, 4, 8, 9, 1e-5, 0.0, None) == -3
+    assert lib.rmsnorm_vjp_noalloc(None, None, None, None, None, 4, 0, 1, 1e-5, 0.0, None) == -2
 
 
 def _py_sources(d):
