@@ -18,10 +18,6 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "librmsnorm_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-# Measurement tool (HBM ceilings of trivial streaming kernels), not linked
-# into the library.
-CEILING_SRC = "stream_ceiling.hip"
-CEILING_BIN = os.path.join(HERE, "stream_ceiling")
 SOURCES = ["rmsn_fwd.hip", "rmsn_fwd_waves.hip", "rmsn_vjp.hip", "rmsn_vjp_lanes.hip", "rmsn_vjp_waves.hip",
            "rmsn_gate.hip", "rmsn_api.hip"]
 ARCH = "gfx950"
@@ -62,14 +58,8 @@ def build(verbose: bool = True) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB_PATH)
-    tmpb = CEILING_BIN + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + [os.path.join(CSRC, CEILING_SRC), "-o", tmpb]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {CEILING_SRC}:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmpb, CEILING_BIN)
     if verbose:
-        print(f"built {LIB_PATH} and {CEILING_BIN}")
+        print(f"built {LIB_PATH}")
     return LIB_PATH
 
 

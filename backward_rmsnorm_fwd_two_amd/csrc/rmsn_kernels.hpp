@@ -344,10 +344,29 @@ __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int 
     }
 }
 
+// What a VJP block does with its finished dw partial.  The library's policy
+// stores it as the block's row of the [gridDim.x, D] partial buffer (or as
+// dw itself for a one-block grid) for the separate combine pass; begin and
+// end do nothing.  The hook lets a measurement program run the very same
+// row kernel with other ways of finishing the reduction.
+struct PartialRowOut {
+    __device__ __forceinline__ static void begin(const RowArgs&) {}
+    template <int NV>
+    __device__ __forceinline__ static void store(float* out, const float (&v)[NV], bool vec_ok) {
+        if (vec_ok) {
+            store_floats<NV>(out, v);
+        } else {
+#pragma unroll
+            for (int e = 0; e < NV; ++e) out[e] = v[e];
+        }
+    }
+    __device__ __forceinline__ static void end(const RowArgs&) {}
+};
+
 // LANES > 0: the lanes per row are a compile-time constant (pipelined
 // instances for the common geometries), so the row reductions compile
 // without branches on the row width; 0: taken from the arguments.
-template <typename T, int NV, int K, int MODE, bool PIPE = false, int LANES = 0>
+template <typename T, int NV, int K, int MODE, bool PIPE = false, int LANES = 0, class DwOut = PartialRowOut>
 __global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
                              : wave_rows(LANES) ? wave_rows_block_max(LANES, K * NV)
                              : (LANES > kVjpPipeBlock ? LANES : kVjpPipeBlock)) void vjp_rows(RowArgs a) {
@@ -359,6 +378,7 @@ __global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
                   "fixed lane counts are pipelined: powers of two or supported whole numbers of waves");
     extern __shared__ float dyn[];
     __shared__ float red[2 * 16 * 2];
+    DwOut::begin(a);
     const int lanes = LANES > 0 ? LANES : a.lanes;
     const RowSlot rs = row_slot<LANES>(a.lshift);
     const int lane = rs.lane;
@@ -501,16 +521,9 @@ __global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
             }
             lds_barrier();
         }
-        if (slot == 0 && c.ok[k]) {
-            float* out = dst + c.off[k];
-            if (vec_ok) {
-                store_floats<NV>(out, acc[k]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < NV; ++e) out[e] = acc[k][e];
-            }
-        }
+        if (slot == 0 && c.ok[k]) DwOut::template store<NV>(dst + c.off[k], acc[k], vec_ok);
     }
+    DwOut::end(a);
 }
 
 // ---------------------------------------------------- streaming kernel

@@ -159,15 +159,43 @@ def cpu_oracle_threads(c, sample_rows, per_row_bytes, fused):
                       f"one thread each, {dt:.1f} s"}
 
 
+BENCHSRC = os.path.join(ROOT, "benchsrc")
+
+
+def bench_tool(name: str, link_library: bool = False) -> str:
+    """The measurement program benchsrc/<name>.hip (not part of the library),
+    compiled for gfx950 into benchsrc/bin/ when it is missing or older than
+    its sources.  link_library: it also includes the library's kernel headers
+    and links librmsnorm_mi355x.so (which must be built)."""
+    import subprocess
+    from backward_rmsnorm_fwd_two_amd import build as B
+    src = os.path.join(BENCHSRC, name + ".hip")
+    exe = os.path.join(BENCHSRC, "bin", name)
+    deps = [src]
+    if link_library:
+        if not os.path.exists(B.LIB_PATH):
+            raise RuntimeError(f"{B.LIB_PATH} is not built; run __graft_entry__.build() first")
+        deps += [B.LIB_PATH] + [os.path.join(B.CSRC, f) for f in os.listdir(B.CSRC) if f.endswith(".hpp")]
+    if os.path.exists(exe) and os.path.getmtime(exe) >= max(os.path.getmtime(d) for d in deps):
+        return exe
+    os.makedirs(os.path.dirname(exe), exist_ok=True)
+    cmd = [B.hipcc()] + B.HIPCC_FLAGS + [src, "-o", exe + ".tmp"]
+    if link_library:
+        cmd += [f"-L{B.HERE}", "-lrmsnorm_mi355x", "-Wl,-rpath,$ORIGIN/../../backward_rmsnorm_fwd_two_amd"]
+    log(f"building {exe}")
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")
+    os.replace(exe + ".tmp", exe)
+    return exe
+
+
 def ceiling_bench() -> int:
     """HBM throughput of trivial streaming kernels for each traffic mix the
-    RMSNorm kernels have (the `stream_ceiling` tool built with the library):
-    the practical ceiling each kernel is measured against."""
+    RMSNorm kernels have (benchsrc/stream_ceiling.hip): the practical ceiling
+    each kernel is measured against."""
     import subprocess
-    exe = os.path.join(ROOT, "backward_rmsnorm_fwd_two_amd", "stream_ceiling")
-    if not os.path.exists(exe):
-        print(f"{exe} is not built; run __graft_entry__.build()", file=sys.stderr)
-        return 2
+    exe = bench_tool("stream_ceiling")
     out = subprocess.run([exe], capture_output=True, text=True, timeout=240)
     if out.returncode != 0:
         print(out.stdout + out.stderr, file=sys.stderr)
@@ -184,6 +212,28 @@ def ceiling_bench() -> int:
     print(json.dumps({"metric": "HBM ceiling of trivial streaming kernels (1R1W, 512 MiB streams)",
                       "value": cold, "unit": "GB/s", "n_gpus": 1, "higher_is_better": True,
                       "data": "synthetic", "config": {"workload": "stream ceiling", "grid": grid}}))
+    return 0
+
+
+def dwreduce_bench() -> int:
+    """Ways of finishing the VJP's dw reduction at [8192, 4096] fp16
+    (benchsrc/dw_reduction.hip): the library's separate combine launch
+    against a deterministic last-arrival reduction inside the row kernel's
+    launch, with per-block timestamps of each stage."""
+    import subprocess
+    exe = bench_tool("dw_reduction", link_library=True)
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=240)
+    if out.returncode != 0:
+        print(out.stdout + out.stderr, file=sys.stderr)
+        return out.returncode
+    res = json.loads(out.stdout.strip().splitlines()[-1])
+    lib = res["library"]
+    print(json.dumps({
+        "metric": "RMSNorm fwd+VJP step, 8192x4096 fp16, by way of finishing the dw reduction",
+        "value": round(335577088 / (lib["step_us"] * 1e-6) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "higher_is_better": True, "data": "synthetic",
+        "config": {"workload": "dw reduction variants, [8192, 4096] fp16, U(0,1), eps 1e-5"},
+        "probe": res}), flush=True)
     return 0
 
 
@@ -548,7 +598,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", choices=["poc", "prefill", "decode", "grad", "gate", "sweep", "widths", "ceiling"],
+    ap.add_argument("--workload", choices=["poc", "prefill", "decode", "grad", "gate", "sweep", "widths", "ceiling",
+                                           "dwreduce"],
                     default="poc")
     ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -561,6 +612,8 @@ def main() -> int:
         return 2
     if args.workload == "ceiling":
         return ceiling_bench()
+    if args.workload == "dwreduce":
+        return dwreduce_bench()
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
