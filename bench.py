@@ -13,8 +13,9 @@ different buffer sets (rotating through enough copies that a set is touched
 again only after >= 1 GiB of other traffic), so no step is served from the
 256 MB last-level cache left warm by the step before it.
 
-Prints one JSON line (rank 0).  `--workload prefill` measures the fused
-add+RMSNorm forward + VJP at [32768, 8192] bf16 instead (not the headline);
+Prints one JSON line (rank 0); its `prefill` key holds the fused add+RMSNorm
+forward + VJP at [32768, 8192] bf16 (the prefill-scale workload), measured the
+same way.  `--workload prefill` prints that one alone;
 `--workload gate` the gated activation silu(x[:, :d]) * x[:, d:2d] at the
 Llama-3 8B MLP width (d = 14336) in bf16, prefill chunk and decode batches.
 """
@@ -92,71 +93,67 @@ def copy_ceiling(nbytes: int = 256 << 20, reps: int = 20) -> float:
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_oracle_baseline(c, rows, D, fwd_bytes, vjp_bytes, fused=False):
-    """The fp64 CPU oracle as it stands (single thread), on a bounded sample
-    of the same workload: the first `sample_rows` rows, repeated until about
-    10 s of CPU work; reported in GB/s on the same algorithmic byte model."""
-    from oracle import oracle as O
-    sample_rows = min(rows, 2048 if fused else 8192)
-    x = c["x"][:sample_rows]
-    dy = c["dy"][:sample_rows]
-    res = c["residual"][:sample_rows] if fused else None
-    per_row_bytes = (fwd_bytes + vjp_bytes) / rows
-    t0 = time.perf_counter()
-    passes = 0
-    while True:
-        if fused:
-            _, h = O.fused_add_rmsnorm_fwd(x, res, c["w"], c["eps"], c["weight_bias"])
-            O.rmsnorm_vjp(h, c["w"], dy, c["eps"], c["weight_bias"])
-        else:
-            O.rmsnorm_fwd(x, c["w"], c["eps"], c["weight_bias"])
-            O.rmsnorm_vjp(x, c["w"], dy, c["eps"], c["weight_bias"])
-        passes += 1
-        dt = time.perf_counter() - t0
-        if dt >= 10.0 or passes >= 20:
-            break
-    gbps = passes * sample_rows * per_row_bytes / dt / 1e9
-    out = {
-        "value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": f"{passes} pass(es) of fwd+VJP over the first {sample_rows} of {rows} rows "
-                  f"(D={D}), fp64 C oracle incl. widening, {dt:.1f} s",
-    }
-    out["all_cores"] = cpu_oracle_threads(c, sample_rows, per_row_bytes, fused)
-    return out
+def cpu_threads():
+    """(threads, affinity): the host cores this process may run on
+    (sched_getaffinity), capped by OMP_NUM_THREADS when the environment sets
+    it (the CPU share a shared host declares for this job)."""
+    affinity = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    threads = min(affinity, int(cap)) if cap.isdigit() and int(cap) > 0 else affinity
+    return max(1, threads), affinity
 
 
-def cpu_oracle_threads(c, sample_rows, per_row_bytes, fused):
-    """The same oracle calls on a static row split over one thread per
-    available host core (at most 16); the C oracle runs without the GIL.
-    The per-shard dw are not summed: timing only."""
+def cpu_oracle_baseline(c, rows, D, fwd_bytes, vjp_bytes, fused=False, seconds=8.0):
+    """The fp64 CPU oracle as it stands, on a bounded sample of the same
+    workload (its first `sample_rows` rows, repeated for about `seconds`),
+    in GB/s on the same algorithmic byte model.  The inputs are widened to
+    fp64 before the clock starts.  Headline figure: the same oracle calls on
+    a static row split over one thread per host core (the C oracle runs
+    without the GIL); also the single-thread figure."""
     import concurrent.futures as cf
     from oracle import oracle as O
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
-    bounds = [(i * sample_rows // cores, (i + 1) * sample_rows // cores) for i in range(cores)]
-    shards = [(c["x"][a:b], c["dy"][a:b], c["residual"][a:b] if fused else None) for a, b in bounds]
+    sample_rows = min(rows, 2048 if fused else 8192)
+    w = O.widen(c["w"])
+    x = O.widen(c["x"][:sample_rows])
+    dy = O.widen(c["dy"][:sample_rows])
+    res = O.widen(c["residual"][:sample_rows]) if fused else None
+    eps, wb = c["eps"], c["weight_bias"]
+    per_row_bytes = (fwd_bytes + vjp_bytes) / rows
 
-    def work(sh):
-        x, dy, res = sh
+    def work(lo, hi):
         if fused:
-            _, h = O.fused_add_rmsnorm_fwd(x, res, c["w"], c["eps"], c["weight_bias"])
-            O.rmsnorm_vjp(h, c["w"], dy, c["eps"], c["weight_bias"])
+            _, h = O.fused_add_rmsnorm_fwd(x[lo:hi], res[lo:hi], w, eps, wb)
+            O.rmsnorm_vjp(h, w, dy[lo:hi], eps, wb)
         else:
-            O.rmsnorm_fwd(x, c["w"], c["eps"], c["weight_bias"])
-            O.rmsnorm_vjp(x, c["w"], dy, c["eps"], c["weight_bias"])
+            O.rmsnorm_fwd(x[lo:hi], w, eps, wb)
+            O.rmsnorm_vjp(x[lo:hi], w, dy[lo:hi], eps, wb)
 
-    with cf.ThreadPoolExecutor(cores) as ex:
+    def timed(fn):
         t0 = time.perf_counter()
         passes = 0
         while True:
-            list(ex.map(work, shards))
+            fn()
             passes += 1
             dt = time.perf_counter() - t0
-            if dt >= 10.0 or passes >= 40:
-                break
-    return {"value": round(passes * sample_rows * per_row_bytes / dt / 1e9, 4), "unit": "GB/s",
-            "cores": cores, "kind": "oracle",
-            "sample": f"{passes} pass(es) over the same {sample_rows} rows split into {cores} row shards, "
-                      f"one thread each, {dt:.1f} s"}
+            if dt >= seconds or passes >= 400:
+                return passes, dt
+
+    threads, affinity = cpu_threads()
+    bounds = [(i * sample_rows // threads, (i + 1) * sample_rows // threads) for i in range(threads)]
+    with cf.ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda b: work(*b), bounds))  # first touch of the output buffers' pages
+        passes, dt = timed(lambda: list(ex.map(lambda b: work(*b), bounds)))
+    p1, dt1 = timed(lambda: work(0, sample_rows))
+    return {
+        "value": round(passes * sample_rows * per_row_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+        "kind": "oracle",
+        "sample": f"{passes} pass(es) of fwd+VJP over the first {sample_rows} of {rows} rows (D={D}) split into "
+                  f"{threads} row shards, one thread each; fp64 C oracle on inputs widened before timing; "
+                  f"{dt:.1f} s",
+        "affinity_cores": affinity,
+        "single_thread": {"value": round(p1 * sample_rows * per_row_bytes / dt1 / 1e9, 4), "unit": "GB/s",
+                          "cores": 1, "sample": f"{p1} pass(es) over the same rows, {dt1:.1f} s"},
+    }
 
 
 BENCHSRC = os.path.join(ROOT, "benchsrc")
@@ -633,7 +630,36 @@ def main() -> int:
     if args.workload == "widths":
         return widths_bench(R, dev, args)
     fused = args.workload == "prefill"
-    log(f"generating inputs ({args.workload})")
+    out = step_bench(R, I, dev, args, fused)
+    if not fused:
+        # the second headline (fused add+RMSNorm fwd + VJP at prefill scale)
+        # as an extra key of the same line
+        out["prefill"] = step_bench(R, I, dev, args, True, nested=True)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def timed_b2b(calls, n, stream):
+    """Average duration (us) of `n` back-to-back calls rotating through
+    `calls`, from one HIP event pair on the stream the kernels run on."""
+    for i in range(3):
+        calls[i % len(calls)]()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        calls[i % len(calls)]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def step_bench(R, I, dev, args, fused, nested=False):
+    """One step = forward (fused add+RMSNorm for the prefill workload) +
+    VJP over one batch; value = algorithmic bytes per step / wall time per
+    step over exactly args.steps steps between device syncs.  The timed
+    region holds nothing but the steps; per-op figures come from separate
+    passes after it."""
+    log(f"generating inputs ({'prefill' if fused else 'poc'})")
     if fused:
         c = I.prefill()
         workload = "fused add+RMSNorm fwd + VJP, [32768, 8192] bf16, weight_bias 1, eps 1e-6"
@@ -651,8 +677,7 @@ def main() -> int:
     step_bytes = fwd_bytes + vjp_bytes
 
     set_bytes = (4 * rows * D * s) + (2 * rows * D * s if fused else 0)
-    nsets = args.sets or max(1, -(-(1 << 30) // set_bytes) + 1) if set_bytes < (1 << 30) else 1
-    nsets = args.sets or nsets
+    nsets = args.sets or (max(1, -(-(1 << 30) // set_bytes) + 1) if set_bytes < (1 << 30) else 1)
     log(f"uploading {nsets} buffer set(s) of {set_bytes / 2**20:.0f} MiB")
     w = c["w"].to(dev)
     sets = []
@@ -681,41 +706,46 @@ def main() -> int:
         xin = st["newres"] if fused else st["x"]
         v_calls.append(R.prepared_vjp(xin, w, st["dy"], st["dx"], dw, ws, eps, wb))
 
-    def step(i, ev=None):
+    def step(i):
         k = i % nsets
-        if ev is not None:
-            ev[0].record(stream)
         f_calls[k]()
-        if ev is not None:
-            ev[1].record(stream)
         v_calls[k]()
-        if ev is not None:
-            ev[2].record(stream)
 
     log(f"warmup {args.warmup}")
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # Timed region: exactly `steps` steps, bracketed by device syncs.  Every
-    # SAMPLE-th step also carries HIP events (on the stream the kernels run
-    # on) around its forward and its VJP: an event record costs the GPU a
-    # few microseconds, so recording every step would distort the region.
-    SAMPLE = 10
-    nsamp = (args.steps + SAMPLE - 1) // SAMPLE
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nsamp)]
+    # Timed region: exactly `steps` steps bracketed by device syncs, nothing else.
     log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i // SAMPLE] if i % SAMPLE == 0 else None)
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fwd_ms = np.array([elapsed_ms(e[0], e[1]) for e in evs])
-    vjp_ms = np.array([elapsed_ms(e[1], e[2]) for e in evs])
-    step_ms = np.array([elapsed_ms(e[0], e[2]) for e in evs])
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # After the timed region: per-op event figures.  (1) Sampled steps with
+    # event pairs around each op: an event record costs the GPU a few
+    # microseconds, so these run high.  (2) Each op back to back on the
+    # rotating sets with one event pair around 100 calls: the launch
+    # durations the roofline uses (they agree with the kernel trace).
+    nsamp = 20
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nsamp)]
+    for i in range(nsamp):
+        k = i % nsets
+        evs[i][0].record(stream)
+        f_calls[k]()
+        evs[i][1].record(stream)
+        v_calls[k]()
+        evs[i][2].record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = np.array([elapsed_ms(e[0], e[1]) for e in evs])
+    vjp_ms = np.array([elapsed_ms(e[1], e[2]) for e in evs])
+    NB = 100
+    vjp_b2b_us = timed_b2b(v_calls, NB, stream)
+    fwd_b2b_us = timed_b2b(f_calls, NB, stream)
 
     extra = {}
     if fused:
@@ -723,97 +753,66 @@ def main() -> int:
         # (fused_add_rmsnorm_vjp): reads h, dy and d_new_residual, writes dh.
         dr = torch.empty_like(sets[0]["x"]).normal_(0.0, 0.01)
         rg = R.prepared_fused_vjp(sets[0]["newres"], w, sets[0]["dy"], dr, sets[0]["dx"], dw, ws, eps, wb)
-        for _ in range(3):
-            rg()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(10):
-            rg()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        t_rg = e0.elapsed_time(e1) / 10 * 1e-3
+        t_rg = timed_b2b([rg], 10, stream) * 1e-6
         rg_bytes = 4 * rows * D * s + D * s + 4 * D
         extra = {"fused_vjp_with_residual_grad_us": round(t_rg * 1e6, 2),
                  "fused_vjp_with_residual_grad_GBps": round(rg_bytes / t_rg / 1e9, 1)}
         del dr
-
-    # The VJP's launch duration for the roofline: one event pair (on the
-    # stream the kernels run on) around 100 back-to-back VJP calls that
-    # rotate through the buffer sets like the timed steps.  Per-call event
-    # records cost the GPU a few microseconds each, so the sampled in-step
-    # figures above run high; this one agrees with the kernel trace's
-    # vjp_rows + dw_combine averages.
-    NB = 100
-    for i in range(3):
-        v_calls[i % nsets]()
-    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    b0.record(stream)
-    for i in range(NB):
-        v_calls[i % nsets]()
-    b1.record(stream)
-    torch.cuda.synchronize()
-    vjp_b2b_us = b0.elapsed_time(b1) * 1e3 / NB
-
-    # Warm ("effective") figure, reported beside the cold headline: the same
-    # buffer set every step, so the 256 MB last-level cache serves part of
-    # the traffic -- not an HBM number.
-    warm = None
-    if not fused:
-        for i in range(5):
-            step(0)
-        w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        w0.record(stream)
-        for i in range(100):
-            step(0)
-        w1.record(stream)
-        torch.cuda.synchronize()
-        warm_us = w0.elapsed_time(w1) * 1e3 / 100
-        warm = {"step_us": round(warm_us, 3), "GBps": round(step_bytes / (warm_us * 1e-6) / 1e9, 1),
-                "note": "one buffer set reused every step: partly served by the last-level cache"}
-
-    # Context: the same outputs (y, dx, dw) from the one-launch grad call,
-    # which reads x and dy once (4*R*D*s + w + dw bytes instead of 5*R*D*s).
-    grad_ctx = None
-    if not fused:
+    else:
+        # Warm ("effective") figure: the same buffer set every step, so the
+        # 256 MB last-level cache serves part of the traffic -- not an HBM number.
+        warm_us = timed_b2b([lambda: step(0)], 100, stream)
+        extra["warm_effective"] = {
+            "step_us": round(warm_us, 3), "GBps": round(step_bytes / (warm_us * 1e-6) / 1e9, 1),
+            "note": "one buffer set reused every step: partly served by the last-level cache"}
+        # The same outputs (y, dx, dw) from the one-launch grad call, which
+        # reads x and dy once (4*R*D*s + w + dw bytes instead of 5*R*D*s).
         g_calls = [R.prepared_grad(st["x"], w, st["dy"], st["y"], st["dx"], dw, ws, eps, wb) for st in sets]
-        for i in range(3):
-            g_calls[i % nsets]()
-        q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        q0.record(stream)
-        for i in range(100):
-            g_calls[i % nsets]()
-        q1.record(stream)
-        torch.cuda.synchronize()
-        g_us = q0.elapsed_time(q1) * 1e3 / 100
+        g_us = timed_b2b(g_calls, NB, stream)
         g_bytes = 4 * rows * D * s + D * s + 4 * D
-        grad_ctx = {"us_per_call": round(g_us, 3), "GBps_on_its_bytes": round(g_bytes / (g_us * 1e-6) / 1e9, 1),
-                    "note": "rmsnorm_fwd_vjp: the same y, dx, dw in one launch; not the headline"}
+        extra["grad_call_same_outputs"] = {
+            "us_per_call": round(g_us, 3), "GBps_on_its_bytes": round(g_bytes / (g_us * 1e-6) / 1e9, 1),
+            "note": "rmsnorm_fwd_vjp: the same y, dx, dw in one launch; not the headline"}
 
-    # The forward the same way (100 back-to-back calls over the rotating
-    # sets): with the VJP leg this gives the sum-of-cold-ops figure, fwd and
-    # VJP each timed on data the previous launch did not touch.
-    fwd_b2b_us = None
-    if not fused:
-        for i in range(3):
-            f_calls[i % nsets]()
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record(stream)
-        for i in range(NB):
-            f_calls[i % nsets]()
-        c1.record(stream)
-        torch.cuda.synchronize()
-        fwd_b2b_us = c0.elapsed_time(c1) * 1e3 / NB
-
-    vjp_avg_s = vjp_b2b_us * 1e-6
-    vjp_gbps = vjp_bytes / vjp_avg_s / 1e9
     src_hash = kernel_source_hash()
-    prof_name = ("vjp_prefill_32768x8192_bf16" if fused else "vjp_poc_8192x4096_fp16")
-    traffic = stored_traffic(prof_name, src_hash)
+    vjp_gbps = vjp_bytes / (vjp_b2b_us * 1e-6) / 1e9
+    vjp_roofline = {
+        "kernel": "rmsnorm_vjp (vjp_rows + dw_combine launches)", "bound": "hbm",
+        "achieved": round(vjp_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "frac": round(vjp_gbps / HBM_PEAK_GBPS, 4),
+        "traffic": stored_traffic("vjp_prefill_32768x8192_bf16" if fused else "vjp_poc_8192x4096_fp16", src_hash),
+        "algorithmic_bytes": vjp_bytes, "avg_us": round(vjp_b2b_us, 3),
+        "method": "events around 100 back-to-back VJP calls on the launch stream, after the timed region"}
+    fwd_gbps = fwd_bytes / (fwd_b2b_us * 1e-6) / 1e9
+    fwd_roofline = {
+        "kernel": "fused_add_rmsnorm_fwd (fwd_rows<FUSED>)" if fused else "rmsnorm_fwd (fwd_rows)",
+        "bound": "hbm", "achieved": round(fwd_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "frac": round(fwd_gbps / HBM_PEAK_GBPS, 4),
+        "traffic": stored_traffic("fused_fwd_prefill_32768x8192_bf16", src_hash) if fused else None,
+        "algorithmic_bytes": fwd_bytes, "avg_us": round(fwd_b2b_us, 3),
+        "method": "events around 100 back-to-back forward calls on the launch stream, after the timed region"}
+    # the roofline object is the dominant kernel's: the one that takes the
+    # larger share of the step
+    roofline, other = (vjp_roofline, fwd_roofline) if vjp_b2b_us >= fwd_b2b_us else (fwd_roofline, vjp_roofline)
+    ops = {
+        "fwd_sampled_mean": round(float(fwd_ms.mean()) * 1e3, 3),
+        "vjp_sampled_mean": round(float(vjp_ms.mean()) * 1e3, 3),
+        "sampled_steps": nsamp,
+        "fwd_back_to_back": round(fwd_b2b_us, 3), "vjp_back_to_back": round(vjp_b2b_us, 3),
+        "summed_back_to_back_GBps": round(step_bytes / ((fwd_b2b_us + vjp_b2b_us) * 1e-6) / 1e9, 1),
+        "note": "after the timed region; sampled_* carry per-call event overhead, back_to_back_* do not"}
+    if nested:
+        res = {"workload": workload, "rows": rows, "D": D, "storage_dtype": str(c["x"].dtype).replace("torch.", ""),
+               "bytes_per_step": step_bytes, "buffer_sets": nsets, "steps": args.steps, "warmup": args.warmup,
+               "ms_per_step": round(ms_per_step, 5), "value": round(value, 2), "unit": "GB/s",
+               "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2), "roofline": roofline,
+               "other_kernel": other, "ops_event_us": ops, **extra}
+        del sets, f_calls, v_calls
+        torch.cuda.empty_cache()
+        return res
 
     log("copy ceiling")
     ceiling = copy_ceiling()
-
     out = {
         "metric": METRIC if not fused else "achieved HBM GB/s for fused add+RMSNorm fwd + VJP, 32768x8192 bf16",
         "value": round(value, 2),
@@ -833,50 +832,25 @@ def main() -> int:
             "bytes_per_step": step_bytes, "buffer_sets": nsets,
             "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         },
-        "roofline": {
-            "kernel": "rmsnorm_vjp (vjp_rows + dw_combine launches)",
-            "bound": "hbm",
-            "achieved": round(vjp_gbps, 2),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(vjp_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes": vjp_bytes,
-            "avg_us": round(vjp_avg_s * 1e6, 3),
-            "method": "events around 100 back-to-back VJP calls on the bench stream, after the timed region",
-        },
-        "ops_event_us": {
-            "fwd_mean": round(float(fwd_ms.mean()) * 1e3, 3),
-            "fwd_min": round(float(fwd_ms.min()) * 1e3, 3),
-            "vjp_mean": round(float(vjp_ms.mean()) * 1e3, 3),
-            "vjp_min": round(float(vjp_ms.min()) * 1e3, 3),
-            "step_mean": round(float(step_ms.mean()) * 1e3, 3),
-            "sampled_steps": int(len(evs)),
-            "fwd_GBps": round(fwd_bytes / (float(fwd_ms.mean()) * 1e-3) / 1e9, 1),
-            "vjp_back_to_back": round(vjp_b2b_us, 3),
-            "note": "fwd_*/vjp_*/step_* carry per-call event overhead; the roofline uses vjp_back_to_back",
-        },
+        "roofline": roofline,
+        "other_kernel": other,
+        "ops_event_us": ops,
         "copy_ceiling_GBps": round(ceiling, 1),
         "pct_of_copy_ceiling": round(100.0 * value / ceiling, 2),
-        "warm_effective": warm,
-        "grad_call_same_outputs": grad_ctx,
-        "cold_ops_summed": None if fwd_b2b_us is None else {
-            "fwd_us": round(fwd_b2b_us, 3), "vjp_us": round(vjp_b2b_us, 3),
-            "GBps": round(step_bytes / ((fwd_b2b_us + vjp_b2b_us) * 1e-6) / 1e9, 1),
-            "note": "fwd and VJP each timed back to back on rotating buffer sets, then summed"},
         **extra,
         "kernel_source_hash": src_hash,
         "context": "MLX PR POC, Metal, model not stated: ~1.65 ms per grad call at this shape "
                    "(= %.0f GB/s on this byte model); not comparable hardware" % (step_bytes / 1.65e-3 / 1e9)
                    if not fused else None,
     }
+    del sets, f_calls, v_calls
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
         out["cpu_baseline"] = cpu_oracle_baseline(c, rows, D, fwd_bytes, vjp_bytes, fused)
     else:
         out["cpu_baseline"] = None
-    print(json.dumps(out), flush=True)
-    return 0
+    return out
 
 
 if __name__ == "__main__":
