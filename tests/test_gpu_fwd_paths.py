@@ -4,18 +4,18 @@ but fill under 70 % of their vector slots take the streaming kernel
 (512-thread blocks); full rows and the 4-vector fp32 instance stay in
 registers.  Checks the automatic plan on
 both sides of that rule and parity of the forward with the fp64 oracle on
-the first and last rows, plus the same rows forced through the register
-kernel.  Rows of a whole number of waves that is not a power of two (wave
+every row, plus the same rows forced through the register kernel.  Rows of a whole number of waves that is not a power of two (wave
 rows) with two 16-byte vectors per lane take an exact-tiling instance of
 up to 768 lanes (two three-wave rows per block); its plan, parity of the
 forward and the fused forward, forced one-vector and 896-lane instances,
 and outputs bit-identical across rows per block."""
 import sys
 
+import numpy as np
 import pytest
 import torch
 
-from _parity import assert_close
+from _parity import assert_close, to64
 from backward_rmsnorm_fwd_two_amd import inputs as I
 from oracle import oracle as O
 
@@ -54,10 +54,9 @@ def test_sparse_forward_rows_stream(R, rows, D, dtype, plan):
     reg = dict(lanes_per_row=1024, vecs_per_lane=0, vec_bytes=0, block_threads=1024, num_blocks=0)
     y_reg = R.rmsnorm_fwd(x, w, c["eps"], 1.0, cfg=reg)
     torch.cuda.synchronize()
-    idx = list(range(32)) + list(range(rows - 32, rows))
-    yref, _ = O.rmsnorm_fwd(c["x"][idx], c["w"], c["eps"], 1.0)
-    assert_close(y[idx], yref, "y")
-    assert_close(y_reg[idx], yref, "y (register kernel)")
+    yref, _ = O.rmsnorm_fwd(c["x"], c["w"], c["eps"], 1.0)
+    assert_close(y, yref, "y")
+    assert_close(y_reg, yref, "y (register kernel)")
 
 
 def _is_pow2(v):
@@ -106,17 +105,16 @@ def test_wave_rows_forward(R, rows, D, dtype, lanes, slots):
                 cfgs.append(dict(lanes_per_row=lanes, vecs_per_lane=2, vec_bytes=16, block_threads=s_ * lanes,
                                  num_blocks=0))
     assert lanes is not None or len(cfgs) > 1
-    idx = list(range(16)) + list(range(rows - 16, rows))
-    yref, _ = O.rmsnorm_fwd(c["x"][idx], c["w"], c["eps"], 1.0)
-    nref, href = O.fused_add_rmsnorm_fwd(c["x"][idx], c["residual"][idx], c["w"], c["eps"], 1.0)
+    yref, _ = O.rmsnorm_fwd(c["x"], c["w"], c["eps"], 1.0)
+    nref, href = O.fused_add_rmsnorm_fwd(c["x"], c["residual"], c["w"], c["eps"], 1.0)
     first = None
     for cfg in cfgs:
         y = R.rmsnorm_fwd(x, w, c["eps"], 1.0, cfg=cfg)
         n, h = R.fused_add_rmsnorm_fwd(x, res, w, c["eps"], 1.0, cfg=cfg)
         torch.cuda.synchronize()
-        assert_close(y[idx], yref, f"y cfg={cfg}")
-        assert_close(n[idx], nref, f"normed cfg={cfg}")
-        assert_close(h[idx], href, f"new_residual cfg={cfg}")
+        assert_close(y, yref, f"y cfg={cfg}")
+        assert_close(n, nref, f"normed cfg={cfg}")
+        np.testing.assert_array_equal(to64(h), O.round_to(href, dtype), f"new_residual cfg={cfg}")
         if lanes is not None:
             # same lanes and vectors: rows per block change nothing
             if first is None:
@@ -143,6 +141,5 @@ def test_sparse_short_forward_rows(R, rows, D, dtype, plan):
     assert (q["lanes_per_row"], q["vecs_per_lane"]) == plan, q
     y = R.rmsnorm_fwd(x, w, c["eps"], 1.0)
     torch.cuda.synchronize()
-    idx = list(range(16)) + list(range(rows - 16, rows))
-    yref, _ = O.rmsnorm_fwd(c["x"][idx], c["w"], c["eps"], 1.0)
-    assert_close(y[idx], yref, "y")
+    yref, _ = O.rmsnorm_fwd(c["x"], c["w"], c["eps"], 1.0)
+    assert_close(y, yref, "y")
