@@ -92,6 +92,17 @@ int log2i(int v) {
 
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
+// Persistent grid of a backward launch: at most `cap` blocks, and whenever
+// there are at least two row groups every block owns at least two, so the dw
+// partial rows number at most half the row groups -- never one partial row
+// per row, the [rows, D] temporary the MLX pull request "RMSNormVJP backward
+// writes a full {n_rows, D} gw_temp intermediate" removes (Proposed changes).
+int64_t vjp_grid(int64_t groups, int64_t cap) {
+    int64_t g = std::min(groups, cap);
+    if (groups > 1) g = std::min(g, (groups + 1) / 2);
+    return std::max<int64_t>(g, 1);
+}
+
 struct Plan {
     int nv = 1;       // elements per load
     int nvec = 1;     // D / nv
@@ -224,7 +235,7 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
                     // stored outputs keep the CU busy (D = 3584 bf16, 7 waves
                     // x 1: 51.0 us at one block per CU vs 54.2 at two)
                     const int per_cu = w_units * nslots < kWaveRowsInFlight && op != RMSN_OP_GRAD ? 2 : 1;
-                    grid = std::min<int64_t>(groups, std::min<int64_t>(kMaxPartialRows, (int64_t)per_cu * cus));
+                    grid = vjp_grid(groups, std::min<int64_t>(kMaxPartialRows, (int64_t)per_cu * cus));
                 } else {
                     grid = std::min<int64_t>(groups, (int64_t)1 << 20);
                 }
@@ -359,7 +370,7 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
             if (cfg && cfg->num_blocks) {
                 grid = cfg->num_blocks;
             } else if (eight_wide) {
-                grid = std::min<int64_t>(groups, std::min<int64_t>(kMaxPartialRows, cus));
+                grid = vjp_grid(groups, std::min<int64_t>(kMaxPartialRows, cus));
             } else if (p->fixed_lanes) {
                 // one persistent block per CU: with the row width fixed at
                 // compile time the pipelined kernel keeps HBM busy with four
@@ -367,11 +378,11 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
                 // combine cheaper (8192 x 4096 fp16: VJP 39.2 us vs 40.9 at
                 // two blocks per CU; 32768 x 8192 bf16: 260 us vs 266 for the
                 // plain loop)
-                grid = std::min<int64_t>(groups, std::min<int64_t>(kMaxPartialRows, cus));
+                grid = vjp_grid(groups, std::min<int64_t>(kMaxPartialRows, cus));
             } else if (vjp) {
                 // Two persistent blocks per CU: every extra partial row costs
                 // D * 4 bytes written and re-read by the combine.
-                grid = std::min<int64_t>(groups, std::min<int64_t>(kMaxPartialRows, 2 * cus));
+                grid = vjp_grid(groups, std::min<int64_t>(kMaxPartialRows, 2 * cus));
             } else {
                 grid = std::min<int64_t>(groups, (int64_t)1 << 20);
             }
@@ -421,7 +432,7 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
                 resident > 0)
                 per_cu = std::min(per_cu, resident);
         }
-        grid = std::min<int64_t>(rows, std::min<int64_t>(kMaxPartialRows, (int64_t)cus * per_cu));
+        grid = vjp_grid(rows, std::min<int64_t>(kMaxPartialRows, (int64_t)cus * per_cu));
     } else {
         grid = std::min<int64_t>(rows, (int64_t)1 << 20);
     }

@@ -131,6 +131,16 @@ def _is_pow2(v):
     return v > 0 and (v & (v - 1)) == 0
 
 
+def _grid(groups, cap):
+    """The backward forms' persistent grid: at most `cap` blocks, and at
+    least two row groups per block whenever there are two (so the dw partial
+    rows are never one per row)."""
+    g = min(groups, cap)
+    if groups > 1:
+        g = min(g, (groups + 1) // 2)
+    return max(g, 1)
+
+
 # (rows, D, dtype, lanes, vectors per lane, rows per block, blocks per CU) of
 # the automatic plan for the VJP; None: not wave rows
 WAVE = [
@@ -176,7 +186,7 @@ def test_wave_rows_geometry_and_bitwise(R, rows, D, dtype, lanes, k, slots, per_
     assert lanes * k == nvec and (k == 4 or not _is_pow2(lanes))
     assert q["block_threads"] == slots * lanes, q
     groups = (rows + slots - 1) // slots
-    assert q["num_blocks"] == min(groups, per_cu * cus), q
+    assert q["num_blocks"] == _grid(groups, per_cu * cus), q
     # the fused backward and the grad call lay these rows out alike
     qf = R.query_config(4, rows, D, x.dtype)
     assert qf["lanes_per_row"] == lanes and qf["vecs_per_lane"] == k, qf
@@ -191,7 +201,7 @@ def test_wave_rows_geometry_and_bitwise(R, rows, D, dtype, lanes, k, slots, per_
     # the grad call stores as many rows as it reads (y and dx for x and dy):
     # one persistent block per CU at every width (the VJP may take two)
     gslots = qg["block_threads"] // lanes
-    assert qg["num_blocks"] == min((rows + gslots - 1) // gslots, cus), qg
+    assert qg["num_blocks"] == _grid((rows + gslots - 1) // gslots, cus), qg
     assert torch.equal(dx_g, dx_a)
     if qg["num_blocks"] == q["num_blocks"]:
         assert torch.equal(dw_g, dw_a)
@@ -221,8 +231,8 @@ def test_streaming_vjp_grid_follows_occupancy(R, rows, D, dtype):
     iteration, dw in registers); the instances that keep 4 vectors of dw
     per thread (16-bit) or 8 (fp32) hold more than 64 VGPRs, so only one
     such block resides per CU and the persistent grid is one block per CU
-    (a second round of blocks would only add partial rows).  Parity with
-    the oracle at that grid."""
+    (a second round of blocks would only add partial rows), at most half
+    the rows.  Parity with the oracle at that grid."""
     c = I.generic(rows, D, dtype, seed=rows + D)
     x, w, dy, dr = (c[k].to(DEV) for k in ("x", "w", "dy", "residual"))
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -230,7 +240,7 @@ def test_streaming_vjp_grid_follows_occupancy(R, rows, D, dtype):
         q = R.query_config(op, rows, D, x.dtype)
         _say(f"streaming vjp op={op} rows={rows} D={D} {dtype} plan={q}")
         assert q["vecs_per_lane"] == -1 and q["block_threads"] == 1024, q
-        assert q["num_blocks"] == min(rows, cus), q
+        assert q["num_blocks"] == _grid(rows, cus), q
     dx, dw = R.rmsnorm_vjp(x, w, dy, c["eps"], 0.5)
     dh, dwf = R.fused_add_rmsnorm_vjp(x, w, dy, dr, c["eps"], 0.5)
     torch.cuda.synchronize()
@@ -264,7 +274,7 @@ def test_dense_wide_rows_eight_vectors(R, rows, D, dtype, plans):
         _say(f"eight-wide op={op} rows={rows} D={D} {dtype} plan={q}")
         assert (q["lanes_per_row"], q["vecs_per_lane"]) == (lanes, k), q
         if (lanes, k) == (256, 8):
-            assert q["block_threads"] == 256 and q["num_blocks"] == min(rows, cus), q
+            assert q["block_threads"] == 256 and q["num_blocks"] == _grid(rows, cus), q
     dx, dw = R.rmsnorm_vjp(x, w, dy, c["eps"], 0.5)
     y, dxg, dwg = R.rmsnorm_fwd_vjp(x, w, dy, c["eps"], 0.5)
     dh, dwf = R.fused_add_rmsnorm_vjp(x, w, dy, dr, c["eps"], 0.5)
@@ -307,3 +317,19 @@ def test_wide_rows_steady_state_many_rows_per_block(R, D, dtype, lanes):
     assert torch.equal(dxg, dx)
     for d, what in ((dw, "dw"), (dwg, "grad dw"), (dwf, "fused dw")):
         assert_dw_close(d, dwref, what)
+
+
+@pytest.mark.parametrize("dtype", ["float32", "float16", "bfloat16"])
+def test_partial_rows_never_one_per_row(R, dtype):
+    """Every backward form's plan, over a sweep of row counts and widths:
+    whenever there are two rows or more, the dw partial rows (the persistent
+    grid) number fewer than the rows, and the workspace is smaller than a
+    [rows, D] fp32 buffer -- the gw_temp layout the MLX pull request removes."""
+    dt = getattr(torch, dtype)
+    for rows in (2, 3, 7, 64, 255, 256, 257, 511, 1000, 5000, 100000):
+        for D in (1, 64, 257, 512, 1000, 4096, 8192, 14336, 16384, 20480, 70000, 1 << 20):
+            for op in (2, 3, 4):
+                q = R.query_config(op, rows, D, dt)
+                assert q["num_blocks"] < rows, (op, rows, D, q)
+            ws = R.rmsnorm_vjp_workspace_bytes(rows, D, dt)
+            assert ws <= max(256, ((rows + 1) // 2) * D * 4), (rows, D, ws)
