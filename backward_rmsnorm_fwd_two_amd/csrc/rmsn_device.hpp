@@ -224,8 +224,9 @@ __device__ __forceinline__ void lds_barrier() {
 // (waves = lanes_per_row / 64 > 1).  Each value must already be a wave
 // total.  `red` is LDS of 2 * 16 * NV floats used in alternation (parity),
 // so one barrier per call suffices: a wave cannot rewrite a buffer before
-// every wave has passed the barrier that follows the reads of it.
-template <int NV>
+// every wave has passed the barrier that follows the reads of it.  FIRST0:
+// the block holds one row, whose first wave is wave 0.
+template <int NV, bool FIRST0 = false>
 __device__ __forceinline__ void cross_wave_sum(float (&v)[NV], int waves, float* red, int parity) {
     const int wave = threadIdx.x >> 6;
     float* buf = red + parity * (16 * NV);
@@ -234,7 +235,7 @@ __device__ __forceinline__ void cross_wave_sum(float (&v)[NV], int waves, float*
         for (int n = 0; n < NV; ++n) buf[wave * NV + n] = v[n];
     }
     lds_barrier();
-    const int first = (wave / waves) * waves;
+    const int first = FIRST0 ? 0 : (wave / waves) * waves;
 #pragma unroll
     for (int n = 0; n < NV; ++n) {
         float s = buf[first * NV + n];

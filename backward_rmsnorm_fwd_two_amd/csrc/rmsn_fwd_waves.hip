@@ -1,6 +1,7 @@
 // rmsn_fwd_waves.hip -- forward and fused add + RMSNorm forward row kernels
 // for rows of a whole number of waves that is not a power of two: lanes =
-// 64 W, W = 3, 5, 6, 7, 9, 10, 12, 14, one or two 16-byte vectors per lane.
+// 64 W, W = 3, 5, 6, 7, 9, 10, 11, 12, 13, 14, 15, one or two 16-byte vectors
+// per lane.
 // Such rows (D = 3072, 5120, 6144, 7168 ... in 16-bit storage) then tile
 // exactly instead of leaving part of a power-of-two lane group masked.  A
 // separate translation unit, so that it compiles in parallel with the other
@@ -20,8 +21,11 @@ const void* pick_waves(int lanes) {
         case 448: return reinterpret_cast<const void*>(&fwd_rows<T, NV, K, FUSED, 448>);
         case 576: return reinterpret_cast<const void*>(&fwd_rows<T, NV, K, FUSED, 576>);
         case 640: return reinterpret_cast<const void*>(&fwd_rows<T, NV, K, FUSED, 640>);
+        case 704: return reinterpret_cast<const void*>(&fwd_rows<T, NV, K, FUSED, 704>);
         case 768: return reinterpret_cast<const void*>(&fwd_rows<T, NV, K, FUSED, 768>);
+        case 832: return reinterpret_cast<const void*>(&fwd_rows<T, NV, K, FUSED, 832>);
         case 896: return reinterpret_cast<const void*>(&fwd_rows<T, NV, K, FUSED, 896>);
+        case 960: return reinterpret_cast<const void*>(&fwd_rows<T, NV, K, FUSED, 960>);
         default: return nullptr;
     }
 }

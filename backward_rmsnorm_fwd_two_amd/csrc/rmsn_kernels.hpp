@@ -275,7 +275,7 @@ __device__ __forceinline__ void vjp_issue_dr(const RowArgs& a, int64_t row0, int
 // also keeps the wave's count of outstanding memory operations the same on
 // every path (a store skipped on some paths would make later waits for loads
 // wait for everything).
-template <typename T, int NV, int K, int MODE, bool FULL = false>
+template <typename T, int NV, int K, int MODE, bool FULL = false, bool ONE_ROW = false>
 __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int slot, int lanes,
                                             const Cols<K>& c, const float (&g)[K][NV],
                                             float (&acc)[K][NV], VjpRow<T, NV, K>& d,
@@ -299,11 +299,22 @@ __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int 
             s2[1] = __builtin_fmaf(dv * g[k][e], xv, s2[1]);
         }
     }
+    if constexpr (K * NV > kVjpPipeElems) {
+        // Wide rows (32 elements per lane): the row's raw 16-bit words are
+        // pinned (an empty asm operand, no instruction) so that the fp32
+        // values widened for the sums above are not kept alive across the
+        // row reduction for the output loop below, which widens the words
+        // again: that frees the registers the two-buffer pipeline needs.
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+#pragma unroll
+            for (int i = 0; i < Raw<T, NV>::kWords; ++i) __asm__("" : "+v"(d.x[k].w[i]), "+v"(d.dy[k].w[i]));
+    }
     const int gl = lanes < 64 ? lanes : 64;
     s2[0] = group_sum(s2[0], gl);
     s2[1] = group_sum(s2[1], gl);
     if (lanes > 64) {
-        cross_wave_sum<2>(s2, lanes >> 6, red, parity);
+        cross_wave_sum<2, ONE_ROW>(s2, lanes >> 6, red, parity);
         parity ^= 1;
     }
     const float inv_d = 1.0f / static_cast<float>(a.D);
@@ -413,7 +424,7 @@ __global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
             // ragged last group (rows not a multiple of the row slots) is
             // processed masked on the loop's exit path, after which the
             // block only joins its dw.
-            // kDrOwn (the fused backward on rows of 9 or 12 waves x 2 16-bit
+            // kDrOwn (the fused backward on rows of 9, 11 or 12 waves x 2 16-bit
             // vectors, a VGPR or two short otherwise, and on the wide rows of
             // four vectors per lane): one d_new_residual buffer, loaded for
             // the next group right after the current group has used it --
@@ -421,7 +432,8 @@ __global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
             // counts need not drain those to reach it.
             constexpr bool kDrOwn =
                 MODE == kResGrad &&
-                (((LANES == 576 || LANES == 768) && K * NV == kVjpPipeElems) || K * NV > kVjpPipeElems);
+                (((LANES == 576 || LANES == 704 || LANES == 768) && K * NV == kVjpPipeElems) ||
+                 K * NV > kVjpPipeElems);
             // Instances whose blocks hold exactly one row (the lane count
             // fixes it) never see a ragged group and compile without the
             // masked copy of the processing, which would cost the tightest
@@ -443,7 +455,7 @@ __global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
             for (;;) {  // ra holds group row0
                 if (next >= a.rows) {  // the block's last group, possibly ragged
                     if (kOneRow || row0 + nslots <= a.rows)
-                        vjp_process<T, NV, K, MODE, true>(a, row0, slot, lanes, c, g, acc, ra,
+                        vjp_process<T, NV, K, MODE, true, kOneRow>(a, row0, slot, lanes, c, g, acc, ra,
                                                           kDrOwn ? drs : ra.dr, red, parity);
                     else if constexpr (!kOneRow)
                         vjp_process<T, NV, K, MODE, false>(a, row0, slot, lanes, c, g, acc, ra,
@@ -451,7 +463,7 @@ __global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
                     break;
                 }
                 vjp_issue<T, NV, K, MODE, !kDrOwn>(a, next, slot, c, rb);
-                vjp_process<T, NV, K, MODE, true>(a, row0, slot, lanes, c, g, acc, ra, kDrOwn ? drs : ra.dr, red,
+                vjp_process<T, NV, K, MODE, true, kOneRow>(a, row0, slot, lanes, c, g, acc, ra, kDrOwn ? drs : ra.dr, red,
                                                   parity);
                 if constexpr (kDrOwn) vjp_issue_dr<T, NV, K>(a, next, slot, c, drs);
                 row0 = next;
@@ -459,7 +471,7 @@ __global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
                 // rb holds group row0
                 if (next >= a.rows) {  // the block's last group, possibly ragged
                     if (kOneRow || row0 + nslots <= a.rows)
-                        vjp_process<T, NV, K, MODE, true>(a, row0, slot, lanes, c, g, acc, rb,
+                        vjp_process<T, NV, K, MODE, true, kOneRow>(a, row0, slot, lanes, c, g, acc, rb,
                                                           kDrOwn ? drs : rb.dr, red, parity);
                     else if constexpr (!kOneRow)
                         vjp_process<T, NV, K, MODE, false>(a, row0, slot, lanes, c, g, acc, rb,
@@ -467,7 +479,7 @@ __global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
                     break;
                 }
                 vjp_issue<T, NV, K, MODE, !kDrOwn>(a, next, slot, c, ra);
-                vjp_process<T, NV, K, MODE, true>(a, row0, slot, lanes, c, g, acc, rb, kDrOwn ? drs : rb.dr, red,
+                vjp_process<T, NV, K, MODE, true, kOneRow>(a, row0, slot, lanes, c, g, acc, rb, kDrOwn ? drs : rb.dr, red,
                                                   parity);
                 if constexpr (kDrOwn) vjp_issue_dr<T, NV, K>(a, next, slot, c, drs);
                 row0 = next;

@@ -44,14 +44,15 @@ constexpr int kVjpPipeBlock = 256;
 constexpr int kVjpPipeFixedMax = 512;
 
 // Rows of a whole number of waves that is not a power of two (lanes = 64 W,
-// W = 3, 5, 6, 7, 9, 10, 12, 14): D = 3072, 4608, 5120, 6144, 7168 ... in 16-bit
-// storage tile such rows exactly, where a power-of-two lane count would leave
-// a quarter to a half of its vectors masked.  Instances exist with the lanes
-// fixed at compile time, in blocks of one or two rows.
+// W = 3, 5, 6, 7, 9, 10, 11, 12, 13, 14, 15): D = 3072, 4608, 5120, 6144,
+// 6656, 7168 ... in 16-bit storage tile such rows exactly, where a
+// power-of-two lane count would leave a quarter to a half of its vectors
+// masked.  Instances exist with the lanes fixed at compile time, in blocks of
+// one or two rows.
 constexpr bool wave_rows(int lanes) { return lanes > 64 && (lanes & (lanes - 1)) != 0; }
 constexpr bool wave_rows_supported(int lanes) {
     return lanes == 192 || lanes == 320 || lanes == 384 || lanes == 448 || lanes == 576 || lanes == 640 ||
-           lanes == 768 || lanes == 896;
+           lanes == 704 || lanes == 768 || lanes == 832 || lanes == 896 || lanes == 960;
 }
 // Wide 16-bit rows (D = 12288, 14336, 16384) also come pipelined with four
 // vectors per lane on 384, 448 or 512 lanes, one row per block: up to this
@@ -66,8 +67,9 @@ constexpr int wave_rows_block_max(int lanes, int elems) {
     return elems > kVjpPipeElems ? lanes : 4 * lanes <= 768 ? 4 * lanes : 2 * lanes <= 768 ? 2 * lanes : lanes;
 }
 // Pipelined VJP instances of the wave-row family: 16-bit rows with two
-// vectors per lane need up to 168 VGPRs, more than rows of 14 waves leave
-// (128); fp32 rows with four vectors per lane fit only as one 512-lane row
+// vectors per lane need up to 168 VGPRs, which rows of up to 12 waves leave
+// (170) and rows of 13 to 15 waves do not (128); fp32 rows with four vectors
+// per lane fit only as one 512-lane row
 // per block.  The wide instances exist for 384, 448 and 512 lanes for the
 // VJP (mode 0, 243-255 VGPRs, no spills) and for 448 and 512 lanes for the
 // grad call (mode 1: 254 VGPRs at 512 lanes, three spilled to scratch at
@@ -78,7 +80,7 @@ constexpr bool vjp_wave_rows_fit(int lanes, int k, int itemsize, int mode) {
     return k * (16 / itemsize) > kVjpPipeElems ? (mode == 0 ? (lanes == 384 || lanes == 448 || lanes == 512)
                                                             : (lanes == 448 || lanes == 512))
            : itemsize == 4 && k == 4                ? lanes == 512
-           : k * (16 / itemsize) == kVjpPipeElems && lanes > 640 ? lanes == 768
+           : k * (16 / itemsize) == kVjpPipeElems && lanes > 640 ? (lanes == 704 || lanes == 768)
                                                     : true;
 }
 

@@ -1,9 +1,9 @@
 // rmsn_vjp_waves.hip -- pipelined VJP, grad-call and fused-backward row
 // kernels for rows of a whole number of waves that is not a power of two:
-// lanes = 64 W, W = 3, 5, 6, 7, 9, 10, 12, 14, one or two 16-byte vectors per
-// lane, where the row is exactly lanes * K vectors (D = 1536 .. 12288 in
-// 16-bit storage, 768 .. 7168 in fp32; 16-bit rows of 14 waves with two
-// vectors per lane would spill registers); wide 16-bit rows with four
+// lanes = 64 W, W = 3, 5, 6, 7, 9, 10, 11, 12, 13, 14, 15, one or two 16-byte
+// vectors per lane, where the row is exactly lanes * K vectors (D = 1536 ..
+// 12288 in 16-bit storage, 768 .. 7680 in fp32; 16-bit rows of 13 to 15 waves
+// with two vectors per lane would spill registers); wide 16-bit rows with four
 // vectors per lane, one row per block, on 384, 448 or 512 lanes for the VJP
 // and 448 or 512 for the grad call and the fused backward (D = 12288, 14336,
 // 16384); fp32 rows of 512 lanes x 4 vectors (D = 8192).  The table of which
@@ -33,8 +33,11 @@ const void* pick_waves(int lanes) {
         case 448: return one<T, K, MODE, 448>();
         case 576: return one<T, K, MODE, 576>();
         case 640: return one<T, K, MODE, 640>();
+        case 704: return one<T, K, MODE, 704>();
         case 768: return one<T, K, MODE, 768>();
+        case 832: return one<T, K, MODE, 832>();
         case 896: return one<T, K, MODE, 896>();
+        case 960: return one<T, K, MODE, 960>();
         default: return nullptr;
     }
 }

@@ -208,6 +208,66 @@ struct TicketWriteThrough {
     }
 };
 
+// Partial rows stored non-temporally (the row tensors' cache policy).
+struct NtPartial {
+    __device__ static void begin(const RowArgs&) {}
+    template <int NV>
+    __device__ static void store(float* out, const float (&v)[NV], bool) {
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int e = 0; e < NV; e += 4) {
+            const f32x4 q = {v[e], v[e + 1], v[e + 2], v[e + 3]};
+            __builtin_nontemporal_store(q, reinterpret_cast<f32x4*>(out + e));
+        }
+    }
+    __device__ static void end(const RowArgs&) {}
+};
+
+// Combine layouts: a block adds COLS columns over all nb partial rows.  COLS
+// / 4 threads cover one row's columns with float4 loads (COLS = 32: one
+// 128-byte line per row), RG = THREADS * 4 / COLS row groups; thread (rg, q)
+// adds rows rg, rg + RG, ... in order, then the RG sums of each column are
+// added in row-group order from LDS.  D % COLS == 0, nb % RG == 0.
+template <int COLS, int THREADS>
+__global__ __launch_bounds__(THREADS) void combine_cols(const float* __restrict__ partial, float* __restrict__ dw,
+                                                        int nb, int D) {
+    constexpr int TPR = COLS / 4;
+    constexpr int RG = THREADS / TPR;
+    __shared__ float4 buf[RG][TPR];
+    const int q = threadIdx.x % TPR, rg = threadIdx.x / TPR;
+    const int col = blockIdx.x * COLS + 4 * q;
+    const int per = nb / RG;  // rows per thread
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int r0 = 0; r0 < per; r0 += 8) {
+        float4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int r = r0 + u < per ? r0 + u : r0;
+            v[u] = *reinterpret_cast<const float4*>(partial + (int64_t)(rg + r * RG) * D + col);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (r0 + u < per) {
+                s.x += v[u].x;
+                s.y += v[u].y;
+                s.z += v[u].z;
+                s.w += v[u].w;
+            }
+        }
+    }
+    buf[rg][q] = s;
+    __syncthreads();
+    if (threadIdx.x < COLS) {
+        const int qq = threadIdx.x / 4, e = threadIdx.x % 4;
+        float t = 0.f;
+        for (int g = 0; g < RG; ++g) {
+            const float4 b = buf[g][qq];
+            t += e == 0 ? b.x : e == 1 ? b.y : e == 2 ? b.z : b.w;
+        }
+        dw[blockIdx.x * COLS + threadIdx.x] = t;
+    }
+}
+
 __global__ void empty_kernel() {}
 
 __global__ void init_u01(_Float16* p, size_t n, unsigned seed) {
@@ -413,6 +473,53 @@ int main() {
                    t.n ? t.lo : 0.0, t.n ? t.hi : 0.0);
         }
         printf("}}");
+        fflush(stdout);
+    }
+    printf("], \"combine_layouts\": [");
+    // rows (library policy or non-temporal partial stores) + a combine layout
+    struct Comb {
+        const char* name;
+        const void* rows;
+        const void* comb;
+        int cols, threads;
+    };
+    const void* lib_rows = row_kernel<rmsn::PartialRowOut>();
+    const void* nt_rows = row_kernel<probe::NtPartial>();
+    const Comb combs[] = {
+        {"cols16_t256", lib_rows, reinterpret_cast<const void*>(&probe::combine_cols<16, 256>), 16, 256},
+        {"cols32_t256", lib_rows, reinterpret_cast<const void*>(&probe::combine_cols<32, 256>), 32, 256},
+        {"cols64_t256", lib_rows, reinterpret_cast<const void*>(&probe::combine_cols<64, 256>), 64, 256},
+        {"cols128_t256", lib_rows, reinterpret_cast<const void*>(&probe::combine_cols<128, 256>), 128, 256},
+        {"cols32_t512", lib_rows, reinterpret_cast<const void*>(&probe::combine_cols<32, 512>), 32, 512},
+        {"cols32_t1024", lib_rows, reinterpret_cast<const void*>(&probe::combine_cols<32, 1024>), 32, 1024},
+        {"cols64_t1024", lib_rows, reinterpret_cast<const void*>(&probe::combine_cols<64, 1024>), 64, 1024},
+        {"nt_rows_cols32_t256", nt_rows, reinterpret_cast<const void*>(&probe::combine_cols<32, 256>), 32, 256},
+        {"nt_rows_cols64_t1024", nt_rows, reinterpret_cast<const void*>(&probe::combine_cols<64, 1024>), 64, 1024},
+    };
+    first = true;
+    for (const Comb& cb : combs) {
+        auto vjp2 = [&](int s) {
+            launch(cb.rows, s);
+            const float* pp = partial;
+            float* dd = dw;
+            int nbv = nb, dv = static_cast<int>(D);
+            void* args[] = {&pp, &dd, &nbv, &dv};
+            CK(hipLaunchKernel(cb.comb, dim3(static_cast<unsigned>(D / cb.cols)), dim3(cb.threads), args, 0, st));
+        };
+        const double t_vjp = timed(vjp2);
+        const double t_step = timed([&](int s) {
+            fwd(s);
+            vjp2(s);
+        });
+        vjp2(0);
+        CK(hipStreamSynchronize(st));
+        CK(hipMemcpy(dw_a.data(), dw, D * 4, hipMemcpyDeviceToHost));
+        double md = 0;
+        for (int j = 0; j < D; ++j) md = std::max(md, (double)std::fabs(dw_a[j] - dw_lib[j]));
+        printf("%s{\"name\": \"%s\", \"vjp_us\": %.3f, \"step_us\": %.3f, \"step_GBps\": %.1f, "
+               "\"dw_rel_diff_vs_library\": %.3g}",
+               first ? "" : ", ", cb.name, t_vjp, t_step, 335577088.0 / (t_step * 1e-6) / 1e9, md / dwmax);
+        first = false;
         fflush(stdout);
     }
     printf("]}\n");

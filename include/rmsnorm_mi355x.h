@@ -114,11 +114,11 @@ typedef enum {
  * RMSN_E_CONFIG. */
 typedef struct {
     int32_t lanes_per_row;  /* threads cooperating on one row: a power of two, 1..1024,
-                               or 64 W with W = 3, 5, 6, 7, 9, 10, 12 or 14 ("wave rows":
-                               16-byte vectors, vecs_per_lane 1 or 2, rows of exactly
-                               lanes_per_row * vecs_per_lane vectors, 1, 2 or 4 rows
-                               per block; for the backward forms only where the
-                               instance exists: 16-bit rows of 14 waves with 2
+                               or 64 W with W = 3, 5, 6, 7, 9, 10, 11, 12, 13, 14 or 15
+                               ("wave rows": 16-byte vectors, vecs_per_lane 1 or 2, rows
+                               of exactly lanes_per_row * vecs_per_lane vectors, 1, 2 or
+                               4 rows per block; for the backward forms only where the
+                               instance exists: 16-bit rows of 13 to 15 waves with 2
                                vectors per lane do not); the VJP of 16-bit rows also
                                takes 384, 448 or 512 lanes with 4 vectors per lane,
                                the grad call and fused backward 448 or 512, and every backward form of fp32

@@ -67,7 +67,8 @@ def _is_pow2(v):
 # lanes None: the power-of-two layout
 WAVE = [(4000, 3072, "float16", 192, 2), (4001, 3072, "bfloat16", 192, 2), (1001, 5120, "bfloat16", 320, 1),
         (700, 6144, "float16", 384, 1), (333, 12288, "bfloat16", 768, 1), (500, 10240, "float16", 640, 1),
-        (700, 3072, "float32", 384, 1), (500, 3584, "bfloat16", None, None), (200, 14336, "bfloat16", None, None)]
+        (700, 3072, "float32", 384, 1), (500, 3584, "bfloat16", None, None), (200, 14336, "bfloat16", None, None),
+        (300, 11264, "bfloat16", 704, 1)]
 
 
 @pytest.mark.parametrize("rows,D,dtype,lanes,slots", WAVE)

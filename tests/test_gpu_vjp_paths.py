@@ -68,6 +68,11 @@ CASES = [
     (1024, 8192, "bfloat16"),   # pipelined: a 512-lane row per 512-thread block
     (1023, 8192, "float16"),    # pipelined, odd row count
     (512, 4096, "float32"),     # pipelined: 512 lanes x 2 x 4 floats
+    (300, 11264, "bfloat16"),   # wave rows: 11 waves x 2
+    (401, 6656, "float16"),     # wave rows: 13 waves x 1
+    (350, 7680, "bfloat16"),    # wave rows: 15 waves x 1
+    (300, 5632, "float32"),     # wave rows: 11 waves x 2 x 4 floats
+    (257, 3328, "float32"),     # wave rows: 13 waves x 1 x 4 floats
 ]
 
 
@@ -162,6 +167,11 @@ WAVE = [
     (99, 16384, "float16", 512, 4, 1, 1),
     (64, 12288, "float32", None, None, None, None),
     (200, 8192, "float32", 512, 4, 1, 1),
+    (300, 11264, "bfloat16", 704, 2, 1, 1),
+    (401, 6656, "float16", 832, 1, 1, 1),
+    (350, 7680, "bfloat16", 960, 1, 1, 1),
+    (300, 5632, "float32", 704, 2, 1, 1),
+    (257, 3328, "float32", 832, 1, 1, 1),
 ]
 
 
