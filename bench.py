@@ -521,7 +521,7 @@ def sweep_bench(R, I, dev, args) -> int:
 
 
 def widths_bench(R, dev, args) -> int:
-    """Every RMSNorm op across common model widths (bf16, D = 1536 .. 16384,
+    """Every RMSNorm op across model widths (bf16, D = 1536 .. 16384,
     rows = 2^25 / D: 64 MiB per row tensor), cold: buffer sets rotate so that
     no call finds its inputs in the 256 MB last-level cache.  Inputs
     are drawn on the device from a seeded generator (x, residual ~ N(0, 1),
@@ -549,7 +549,8 @@ def widths_bench(R, dev, args) -> int:
 
     dt = torch.bfloat16
     grid = []
-    for D in (1536, 2048, 2560, 3072, 3584, 4096, 4608, 5120, 6144, 7168, 8192, 9216, 10240, 12288, 14336, 16384):
+    for D in (1536, 2048, 2560, 3072, 3584, 4096, 4608, 5120, 5632, 6144, 6656, 7168, 7680, 8192, 9216, 10240, 11264,
+              12288, 14336, 16384):
         rows = (1 << 25) // D
         sets = []
         for _ in range(10):
