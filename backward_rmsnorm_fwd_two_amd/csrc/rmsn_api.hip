@@ -70,14 +70,6 @@ int cu_count(int* out) {
 
 int itemsize(int dt) { return dt == RMSN_F32 ? 4 : 2; }
 
-// Largest power of two dividing the address, capped at 16.
-int ptr_align(const void* p) {
-    const uintptr_t u = reinterpret_cast<uintptr_t>(p);
-    if (u == 0) return 16;
-    const uintptr_t low = u & (~u + 1);
-    return low >= 16 ? 16 : static_cast<int>(low);
-}
-
 int next_pow2(int64_t v) {
     int p = 1;
     while (p < v) p <<= 1;
@@ -116,12 +108,12 @@ struct Plan {
     bool fixed_lanes = false; // ... in an instance with the lanes fixed at compile time
 };
 
-// The kernel plan for one call.  `align` is the largest power of two (<= 16)
-// dividing every pointer the kernels read or write row-wise.
+// The kernel plan for one call.  The load width depends on the row pitch
+// only: row vectors are read and written at element alignment, so a base
+// pointer that is not 16-byte aligned still gets the widest loads.
 // op: RMSN_OP_FWD, RMSN_OP_FUSED, or one of the backward forms RMSN_OP_VJP,
 // RMSN_OP_GRAD, RMSN_OP_FUSED_VJP (all planned alike).
-int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_config_t* cfg,
-              Plan* p) {
+int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg, Plan* p) {
     const bool vjp = op == RMSN_OP_VJP || op == RMSN_OP_GRAD || op == RMSN_OP_FUSED_VJP;
     const int budget_op = vjp ? 2 : op;
     const int s = itemsize(dt);
@@ -133,11 +125,10 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, int align, const rmsn_con
     int vb = 0;
     if (cfg && cfg->vec_bytes) {
         vb = cfg->vec_bytes;
-        if (vb < s || vb > 16 || !is_pow2(vb) || (D * s) % vb != 0 || align % vb != 0)
-            return RMSN_E_CONFIG;
+        if (vb < s || vb > 16 || !is_pow2(vb) || (D * s) % vb != 0) return RMSN_E_CONFIG;
     } else {
         for (int c = 16; c >= s; c >>= 1) {
-            if ((D * s) % c == 0 && align % c == 0) { vb = c; break; }
+            if ((D * s) % c == 0) { vb = c; break; }
         }
         if (vb == 0) vb = s;
     }
@@ -507,11 +498,9 @@ int fwd_impl(bool fused, const void* x, const void* res, const void* w, void* y,
     } else {
         if (bad_alias(ry, rx) || overlaps(ry, rw)) return RMSN_E_OVERLAP;
     }
-    int align = std::min(std::min(ptr_align(x), ptr_align(w)), ptr_align(y));
-    if (fused) align = std::min(align, std::min(ptr_align(res), ptr_align(newres)));
 
     Plan p;
-    st = make_plan(fused ? RMSN_OP_FUSED : RMSN_OP_FWD, rows, D, dt, align, cfg, &p);
+    st = make_plan(fused ? RMSN_OP_FUSED : RMSN_OP_FWD, rows, D, dt, cfg, &p);
     if (st != RMSN_OK) return st;
     const void* fn = p.k > 0 ? rmsn::fwd_kernel_fixed_lanes(dt, p.nv, p.k, fused, p.lanes) : nullptr;
     if (!fn && !(p.k > 0 && rmsn::wave_rows(p.lanes))) fn = rmsn::fwd_kernel(dt, p.nv, p.k, fused);
@@ -581,12 +570,8 @@ int vjp_impl(const void* x, const void* w, const void* dy, void* y, const void* 
         if (overlaps(rdx, rw) || overlaps(ry, rw) || overlaps(rdw, rw)) return RMSN_E_OVERLAP;
         if (overlaps(rdx, rdw) || overlaps(ry, rdx) || overlaps(ry, rdw)) return RMSN_E_OVERLAP;
     }
-    int align =
-        std::min(std::min(ptr_align(x), ptr_align(w)), std::min(ptr_align(dy), ptr_align(dx)));
-    if (grad) align = std::min(align, ptr_align(y));
-    if (resgrad) align = std::min(align, ptr_align(dres));
     Plan p;
-    st = make_plan(resgrad ? RMSN_OP_FUSED_VJP : (grad ? RMSN_OP_GRAD : RMSN_OP_VJP), rows, D, dt, align, cfg, &p);
+    st = make_plan(resgrad ? RMSN_OP_FUSED_VJP : (grad ? RMSN_OP_GRAD : RMSN_OP_VJP), rows, D, dt, cfg, &p);
     if (st != RMSN_OK) return st;
     const size_t need = ws_bytes(p, D, typed_dw);
     if (need > 0) {
@@ -649,18 +634,18 @@ int check_gate(int64_t rows, int64_t d, int dt) {
     return RMSN_OK;
 }
 
-int make_gate_plan(int64_t rows, int64_t d, int dt, int align, const rmsn_config_t* cfg,
+int make_gate_plan(int64_t rows, int64_t d, int dt, const rmsn_config_t* cfg,
                    GatePlan* p) {
     const int s = itemsize(dt);
     if (cfg && (cfg->lanes_per_row != 0 || cfg->vecs_per_lane < 0)) return RMSN_E_CONFIG;
     int vb = 0;
     if (cfg && cfg->vec_bytes) {
         vb = cfg->vec_bytes;
-        if (vb < s || vb > 16 || !is_pow2(vb) || (d * s) % vb != 0 || align % vb != 0)
+        if (vb < s || vb > 16 || !is_pow2(vb) || (d * s) % vb != 0)
             return RMSN_E_CONFIG;
     } else {
         for (int c = 16; c >= s; c >>= 1) {
-            if ((d * s) % c == 0 && align % c == 0) { vb = c; break; }
+            if ((d * s) % c == 0) { vb = c; break; }
         }
         if (vb == 0) vb = s;
     }
@@ -698,16 +683,14 @@ int gate_impl(bool vjp, const void* x, const void* dy, void* out, int64_t rows, 
     const int s = itemsize(dt);
     if (!elem_aligned(x, s) || !elem_aligned(out, s) || (vjp && !elem_aligned(dy, s))) return RMSN_E_ALIGN;
     const Range rx = range_of(x, rows * 2 * d * s);
-    int align = std::min(ptr_align(x), ptr_align(out));
     if (vjp) {
         const Range rdx = range_of(out, rows * 2 * d * s), rdy = range_of(dy, rows * d * s);
         if (bad_alias(rdx, rx) || overlaps(rdx, rdy)) return RMSN_E_OVERLAP;
-        align = std::min(align, ptr_align(dy));
     } else if (overlaps(range_of(out, rows * d * s), rx)) {
         return RMSN_E_OVERLAP;
     }
     GatePlan p;
-    st = make_gate_plan(rows, d, dt, align, cfg, &p);
+    st = make_gate_plan(rows, d, dt, cfg, &p);
     if (st != RMSN_OK) return st;
     const void* fn = vjp ? rmsn::gate_vjp_kernel(dt, p.nv, p.u) : rmsn::gate_kernel(dt, p.nv, p.u);
     if (!fn) return RMSN_E_CONFIG;
@@ -778,13 +761,10 @@ size_t rmsnorm_vjp_workspace_bytes(int64_t rows, int64_t D, int dt) {
     if (check_common(rows, D, dt) != RMSN_OK) return 0;
     size_t best = 0;
     if (rows > 0) {
-        // The plan depends on pointer alignment; size for the largest.
         for (int op : {RMSN_OP_VJP, RMSN_OP_GRAD, RMSN_OP_FUSED_VJP}) {
-            for (int align = 16; align >= itemsize(dt); align >>= 1) {
-                Plan p;
-                if (make_plan(op, rows, D, dt, align, nullptr, &p) != RMSN_OK) return 0;
-                best = std::max(best, ws_bytes(p, D, /*typed_dw=*/true));
-            }
+            Plan p;
+            if (make_plan(op, rows, D, dt, nullptr, &p) != RMSN_OK) return 0;
+            best = std::max(best, ws_bytes(p, D, /*typed_dw=*/true));
         }
     }
     return std::max<size_t>(best, 256);
@@ -869,7 +849,7 @@ int rmsn_query_config(int op, int64_t rows, int64_t D, int dt, int align_bytes, 
         if (st != RMSN_OK) return st;
         if (align_bytes <= 0 || !is_pow2(align_bytes)) return RMSN_E_ALIGN;
         GatePlan g;
-        st = make_gate_plan(std::max<int64_t>(rows, 1), D, dt, std::min(align_bytes, 16), nullptr, &g);
+        st = make_gate_plan(std::max<int64_t>(rows, 1), D, dt, nullptr, &g);
         if (st != RMSN_OK) return st;
         out->lanes_per_row = 0;
         out->vecs_per_lane = g.u;
@@ -883,7 +863,7 @@ int rmsn_query_config(int op, int64_t rows, int64_t D, int dt, int align_bytes, 
     if (st != RMSN_OK) return st;
     if (align_bytes <= 0 || !is_pow2(align_bytes)) return RMSN_E_ALIGN;
     Plan p;
-    st = make_plan(op, std::max<int64_t>(rows, 1), D, dt, std::min(align_bytes, 16), nullptr, &p);
+    st = make_plan(op, std::max<int64_t>(rows, 1), D, dt, nullptr, &p);
     if (st != RMSN_OK) return st;
     out->lanes_per_row = p.k < 0 ? 0 : p.lanes;
     out->vecs_per_lane = p.k;

@@ -56,38 +56,48 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #endif
 
 // STREAM: a row tensor read once; otherwise data that every block re-reads.
-template <typename V, bool STREAM>
-__device__ __forceinline__ V ld_stream(const V* p) {
+// A: the alignment the address is known to have, the element size of the
+// tensor.  A row vector may start at any element (a base pointer that is not
+// 16-byte aligned, or a row pitch that is not a multiple of 16 bytes); gfx950
+// reads and writes 8 and 16 bytes of global memory at any such address with
+// the same instructions as at an aligned one.
+template <typename V, bool STREAM, int A>
+__device__ __forceinline__ V ld_stream(const void* p) {
+    typedef V VA __attribute__((aligned(A)));
+    const VA* q = static_cast<const VA*>(p);
 #if RMSN_NT_ROWS
-    if constexpr (STREAM) return __builtin_nontemporal_load(p);
+    if constexpr (STREAM) return __builtin_nontemporal_load(q);
 #endif
-    return *p;
+    return *q;
 }
 
-template <typename V>
-__device__ __forceinline__ void st_stream(V* p, V v) {
+template <typename V, int A>
+__device__ __forceinline__ void st_stream(void* p, V v) {
+    typedef V VA __attribute__((aligned(A)));
+    VA* q = static_cast<VA*>(p);
 #if RMSN_NT_ROWS
-    __builtin_nontemporal_store(v, p);
+    __builtin_nontemporal_store(v, q);
 #else
-    *p = v;
+    *q = v;
 #endif
 }
 
 template <typename T, int NV, bool STREAM = true>
 __device__ __forceinline__ Raw<T, NV> load_raw(const T* p) {
+    constexpr int A = static_cast<int>(sizeof(T));
     Raw<T, NV> r;
     constexpr int B = Raw<T, NV>::kBytes;
     if constexpr (B == 16) {
-        const u32x4 v = ld_stream<u32x4, STREAM>(reinterpret_cast<const u32x4*>(p));
+        const u32x4 v = ld_stream<u32x4, STREAM, A>(p);
         r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
     } else if constexpr (B == 8) {
-        const u32x2 v = ld_stream<u32x2, STREAM>(reinterpret_cast<const u32x2*>(p));
+        const u32x2 v = ld_stream<u32x2, STREAM, A>(p);
         r.w[0] = v.x; r.w[1] = v.y;
     } else if constexpr (B == 4) {
-        r.w[0] = ld_stream<uint32_t, STREAM>(reinterpret_cast<const uint32_t*>(p));
+        r.w[0] = ld_stream<uint32_t, STREAM, A>(p);
     } else {
         static_assert(B == 2, "unsupported vector width");
-        r.w[0] = ld_stream<uint16_t, STREAM>(reinterpret_cast<const uint16_t*>(p));
+        r.w[0] = ld_stream<uint16_t, STREAM, 2>(p);
     }
     return r;
 }
@@ -130,19 +140,20 @@ struct alignas(sizeof(T) * N) Pack {
 
 template <typename T, int N>
 __device__ __forceinline__ void store_f32(T* p, const float (&v)[N]) {
+    constexpr int A = static_cast<int>(sizeof(T));
     Pack<T, N> pk;
 #pragma unroll
     for (int i = 0; i < N; ++i) pk.v[i] = from_f32<T>(v[i]);
     constexpr int B = N * static_cast<int>(sizeof(T));
     if constexpr (B == 16) {
-        st_stream(reinterpret_cast<u32x4*>(p), __builtin_bit_cast(u32x4, pk));
+        st_stream<u32x4, A>(p, __builtin_bit_cast(u32x4, pk));
     } else if constexpr (B == 8) {
-        st_stream(reinterpret_cast<u32x2*>(p), __builtin_bit_cast(u32x2, pk));
+        st_stream<u32x2, A>(p, __builtin_bit_cast(u32x2, pk));
     } else if constexpr (B == 4) {
-        st_stream(reinterpret_cast<uint32_t*>(p), __builtin_bit_cast(uint32_t, pk));
+        st_stream<uint32_t, A>(p, __builtin_bit_cast(uint32_t, pk));
     } else {
         static_assert(B == 2, "unsupported vector width");
-        st_stream(reinterpret_cast<uint16_t*>(p), __builtin_bit_cast(uint16_t, pk));
+        st_stream<uint16_t, 2>(p, __builtin_bit_cast(uint16_t, pk));
     }
 }
 

@@ -58,8 +58,10 @@
  *   - Pointers: device pointers owned by the caller; the library allocates
  *     no device memory and keeps no pointer after the call returns (the one
  *     fixed array it holds is the scratch of rmsnorm_vjp_noalloc).  Each
- *     pointer must be aligned to its element size; wider alignment (16 B) and
- *     D * itemsize divisible by 16 select the widest loads.
+ *     pointer must be aligned to its element size.  Row vectors are read and
+ *     written at element alignment, so the load width (16 bytes where D *
+ *     itemsize is a multiple of 16) does not depend on the pointers'
+ *     alignment.
  *   - In place: a [rows, D] output may be the very buffer of a [rows, D]
  *     input of the same call (same address, same extent) -- y over x;
  *     normed or new_residual over x or residual; dx (dh) or y over x (h), dy
@@ -269,9 +271,9 @@ int silu_gate_vjp_cfg(const void *x, const void *dy, void *dx, int64_t rows, int
 #define RMSN_OP_GATE 5      /* D is the half width d */
 
 /* Fill *out with the configuration the automatic choice makes for `op` on
- * this shape, assuming every pointer is 16-byte aligned (`align_bytes` = the
- * largest power of two dividing every pointer, capped at 16, to model other
- * alignments).  Returns RMSN_OK or an argument error.  For the backward forms
+ * this shape.  `align_bytes` (a power of two: the alignment of the
+ * pointers) is validated but does not change the choice, which depends on
+ * the shape only.  Returns RMSN_OK or an argument error.  For the backward forms
  * the library additionally picks, per call, between two row loops of the same
  * geometry and arithmetic: a software-pipelined one (rows of exactly
  * lanes_per_row * vecs_per_lane vectors; power-of-two rows in blocks of at

@@ -113,9 +113,12 @@ def test_gate_argument_errors_and_plan_without_gpu():
     # 14336 * 2 / 16 = 1792 vectors per row, 64 per chunk (one-wave blocks)
     assert plan(8192, 14336, 2) == (0, 1, 16, 64, 8192 * 1792 // 64)
     assert plan(1, 14336, 2) == (0, 1, 16, 64, 28)
-    # odd d in bf16: element loads; fp32 with 8-byte alignment
+    # odd d in bf16: element loads
     assert plan(3, 1001, 2)[2] == 2 and plan(3, 1001, 2)[1] == 8
-    assert plan(3, 1000, 0, align=8)[2] == 8
+    # the load width follows the row pitch, not the pointers' alignment
+    for align in (16, 8, 4):
+        assert plan(3, 1000, 0, align=align)[2] == 16
+    assert plan(3, 1002, 0)[2] == 8
 
 
 def test_in_place_alias_rules_without_gpu():

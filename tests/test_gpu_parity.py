@@ -182,6 +182,71 @@ def test_misaligned_base_pointers(R, dtype, offset):
     assert_dw_close(dw, dwref)
 
 
+@pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
+@pytest.mark.parametrize("D", [4096, 3072, 14336])
+@pytest.mark.parametrize("offset", [1, 3])
+def test_misaligned_pointers_every_form_bitwise(R, dtype, D, offset):
+    """Row vectors are read and written at element alignment, so the plan
+    (16-byte vectors; the pipelined fixed-width backward instances at these
+    widths) does not depend on the pointers: each form run on buffers shifted
+    by a few elements gives bitwise the results of the aligned run, and both
+    match the oracle on every element."""
+    rows = 600
+    c = I.generic(rows, D, dtype, seed=D + offset)
+    rng = np.random.default_rng(offset)
+    dr = I.normal(rng, (rows, D), 0.0, 0.5, dtype)
+    td = I.torch_dtype(dtype)
+
+    def placed(t, off):
+        buf = torch.zeros(t.numel() + 16, dtype=td, device=DEV)
+        v = buf[off:off + t.numel()]
+        v.copy_(_gpu(t).reshape(-1))
+        return v.view(t.shape)
+
+    def empty(shape, off):
+        n = int(np.prod(shape))
+        return torch.empty(n + 16, dtype=td, device=DEV)[off:off + n].view(shape)
+
+    def run(o):
+        x, w, dy, drg = (placed(c["x"], o), placed(c["w"], (o + 5) % 8), placed(c["dy"], (o + 3) % 8),
+                         placed(dr, (o + 6) % 8))
+        out = {}
+        out["y"] = R.rmsnorm_fwd(x, w, c["eps"], 0.5, out=empty((rows, D), (o + 1) % 8))
+        out["dx"], out["dw"] = R.rmsnorm_vjp(x, w, dy, c["eps"], 0.5, dx=empty((rows, D), (o + 2) % 8))
+        out["gy"], out["gdx"], out["gdw"] = R.rmsnorm_fwd_vjp(
+            x, w, dy, c["eps"], 0.5, y=empty((rows, D), (o + 4) % 8), dx=empty((rows, D), (o + 7) % 8))
+        out["dh"], out["hdw"] = R.fused_add_rmsnorm_vjp(x, w, dy, drg, c["eps"], 0.5,
+                                                        dh=empty((rows, D), (o + 1) % 8))
+        out["normed"] = empty((rows, D), (o + 2) % 8)
+        out["newres"] = empty((rows, D), (o + 3) % 8)
+        R.fused_add_rmsnorm_fwd(x, drg, w, c["eps"], 0.5, normed=out["normed"], new_residual=out["newres"])
+        return out
+
+    _say(f"misaligned every form {dtype} D={D} offset={offset}")
+    for op in (2, 3, 4):
+        assert R.query_config(op, rows, D, td, align_bytes=2)["vec_bytes"] == 16
+    base, moved = run(0), run(offset)
+    torch.cuda.synchronize()
+    for k in base:
+        a, b = base[k], moved[k]
+        iv = torch.int32 if a.dtype == torch.float32 else torch.int16
+        assert torch.equal(a.contiguous().view(iv), b.contiguous().view(iv)), k
+    yref, _ = O.rmsnorm_fwd(c["x"], c["w"], c["eps"], 0.5)
+    dxref, dwref = O.rmsnorm_vjp(c["x"], c["w"], c["dy"], c["eps"], 0.5)
+    dhref, hdwref = O.fused_add_rmsnorm_vjp(c["x"], c["w"], c["dy"], dr, c["eps"], 0.5)
+    nref, href = O.fused_add_rmsnorm_fwd(c["x"], dr, c["w"], c["eps"], 0.5)
+    assert_close(moved["y"], yref, "y")
+    assert_close(moved["gy"], yref, "grad y")
+    assert_close(moved["dx"], dxref, "dx")
+    assert_close(moved["gdx"], dxref, "grad dx")
+    assert_dw_close(moved["dw"], dwref)
+    assert_dw_close(moved["gdw"], dwref, "grad dw")
+    assert_close(moved["dh"], dhref, "dh")
+    assert_dw_close(moved["hdw"], hdwref, "fused dw")
+    assert_close(moved["normed"], nref, "normed")
+    np.testing.assert_array_equal(to64(moved["newres"]), O.round_to(href, dtype))
+
+
 def _max_block(op, k, nv, itemsize):
     """Mirrors the library's register budget (0 forward, 1 fused forward, 2
     and 3 the VJP forms)."""
