@@ -106,14 +106,18 @@ struct Plan {
     size_t shmem = 0;
     bool pipe = false;        // backward forms: the software-pipelined row kernel
     bool fixed_lanes = false; // ... in an instance with the lanes fixed at compile time
+    bool ovl = false;         // rows of ceil(D / nv) vectors, the last one overlapped
 };
 
-// The kernel plan for one call.  The load width depends on the row pitch
+// The kernel plan for one call.  The load width depends on the row length
 // only: row vectors are read and written at element alignment, so a base
 // pointer that is not 16-byte aligned still gets the widest loads.
 // op: RMSN_OP_FWD, RMSN_OP_FUSED, or one of the backward forms RMSN_OP_VJP,
-// RMSN_OP_GRAD, RMSN_OP_FUSED_VJP (all planned alike).
-int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg, Plan* p) {
+// RMSN_OP_GRAD, RMSN_OP_FUSED_VJP (all planned alike).  ovl_ok: rows that are
+// not a whole number of 16-byte vectors may take 16-byte vectors with the
+// last one overlapped (register kernels); otherwise narrower loads.
+int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg, Plan* p,
+              bool ovl_ok = true) {
     const bool vjp = op == RMSN_OP_VJP || op == RMSN_OP_GRAD || op == RMSN_OP_FUSED_VJP;
     const int budget_op = vjp ? 2 : op;
     const int s = itemsize(dt);
@@ -123,17 +127,33 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
 
     // load width
     int vb = 0;
+    bool ovl = false;
     if (cfg && cfg->vec_bytes) {
         vb = cfg->vec_bytes;
-        if (vb < s || vb > 16 || !is_pow2(vb) || (D * s) % vb != 0) return RMSN_E_CONFIG;
+        if (vb < s || vb > 16 || !is_pow2(vb)) return RMSN_E_CONFIG;
+        if ((D * s) % vb != 0) {
+            // 16-byte vectors on a row that is not a whole number of them:
+            // the last vector overlapped
+            if (vb != 16 || D * s < 16 || !ovl_ok) return RMSN_E_CONFIG;
+            ovl = true;
+        }
     } else {
         for (int c = 16; c >= s; c >>= 1) {
             if ((D * s) % c == 0) { vb = c; break; }
         }
         if (vb == 0) vb = s;
+        // A row that is not a whole number of 16-byte vectors (D = 257, 500,
+        // 511, 513 in 16-bit storage) takes 16-byte vectors with the last
+        // one shifted back to end at the row's end, rather than loads of the
+        // largest width dividing the row (2 bytes for an odd D).
+        if (vb < 16 && ovl_ok && D * s > 16) {
+            vb = 16;
+            ovl = true;
+        }
     }
     p->nv = vb / s;
-    p->nvec = static_cast<int>(D / p->nv);
+    p->nvec = static_cast<int>(ovl ? (D + p->nv - 1) / p->nv : D / p->nv);
+    p->ovl = ovl;
 
     const int req_k = cfg ? cfg->vecs_per_lane : 0;
     const int req_l = cfg ? cfg->lanes_per_row : 0;
@@ -156,7 +176,8 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
         // and fp32 rows of 512 lanes (D = 8192).
         const bool wide_ok = vjp;
         const int vmode = op == RMSN_OP_GRAD ? 1 : op == RMSN_OP_FUSED_VJP ? 2 : 0;
-        if (vb == 16 && (lanes == 0 ? k == 0 : (rmsn::wave_rows(lanes) || (wide_ok && k == 4 && lanes == 512)))) {
+        if (vb == 16 && !ovl &&
+            (lanes == 0 ? k == 0 : (rmsn::wave_rows(lanes) || (wide_ok && k == 4 && lanes == 512)))) {
             // the first of 2, 1, 4 vectors per lane that tiles the row and
             // has an instance
             int wl = 0, wk = 0;
@@ -260,6 +281,19 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
             // us, 8200 27.9 vs 30.1-31.7, 16384 25.9 vs 26.7-28.7; 256 MiB:
             // D = 10240 87.1 vs 96.9-102.6 us; fp32 D = 4100 26.6 vs 29.0).
             if (op == RMSN_OP_FWD && vb == 16 && p->nvec > 1024 && p->nvec <= 2048) kt = 8;
+            // Forward forms on overlapped rows (their vector counts rarely
+            // fill a power of two): 8 vectors per lane on rows of 513..1024
+            // vectors, 4 from 129 (the forward) or 257 (the fused forward)
+            // -- fp16, 64 MiB tensors: forward D = 6001 33.0 -> 29.9 us,
+            // 8191 31.3 -> 28.5, 4097 39.8 -> 34.8; fused forward D = 2049
+            // 71.6 -> 58.9, 3001 60.9 -> 51.6, 6001 63.7 -> 54.9, 8191
+            // 57.5 -> 50.8 (D = 4500 ran 8 % slower that way).
+            if (ovl && !vjp && p->nvec <= 1024) {
+                if (p->nvec > 512)
+                    kt = 8;
+                else if (p->nvec > (op == RMSN_OP_FWD ? 128 : 256))
+                    kt = 4;
+            }
             lanes = std::min(1024, next_pow2((p->nvec + kt - 1) / kt));
             k = next_pow2((p->nvec + lanes - 1) / lanes);
             // The plain forward of a row of 129..1024 vectors that this
@@ -283,13 +317,17 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
         if (!is_pow2(lanes) || lanes > 1024) return RMSN_E_CONFIG;
         if (k != 1 && k != 2 && k != 4 && k != 8) return RMSN_E_CONFIG;
         if ((int64_t)lanes * k < p->nvec) return RMSN_E_CONFIG;
-        int maxb = rmsn::max_block_threads(budget_op, k, p->nv, s);
+        auto block_max = [&](int kk) {
+            return ovl ? rmsn::max_block_threads_ovl(budget_op, kk, p->nv, s)
+                       : rmsn::max_block_threads(budget_op, kk, p->nv, s);
+        };
+        int maxb = block_max(k);
         // automatic choice: more vectors per lane on fewer lanes while the
         // row does not fit the budget's block
         while (!req_l && !req_k && lanes > maxb && k < 8 && lanes > 64) {
             k <<= 1;
             lanes >>= 1;
-            maxb = rmsn::max_block_threads(budget_op, k, p->nv, s);
+            maxb = block_max(k);
         }
         const bool automatic = !req_l && !req_k;
         if (lanes > maxb) {
@@ -311,8 +349,16 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
                 // waves in lock step (measured fastest for both kernels) --
                 // except the persistent VJP on narrow loads, whose 512-block
                 // grid then needs 512-thread blocks to keep enough waves
-                // resident (measured 10-25 % faster at D = 257..513).
-                const int cap = (vjp && vb <= 4) ? 512 : 256;
+                // resident (measured 10-25 % faster at D = 257..513), and on
+                // overlapped rows that fill under 90 % of their vector slots,
+                // on row tensors of 24 MiB or more (fp16, 64 MiB tensors: D =
+                // 513 64.9 -> 58.9 us, 1025 75.7 -> 64.0, 2049 79.0 -> 62.7,
+                // 257 64.6 -> 60.2; but at 16384 rows, 8-16 MiB, and on
+                // nearly full rows such as D = 500 and 511, 256 threads ran
+                // 4-20 % faster).
+                const bool ovl_sparse_big = ovl && (int64_t)p->nvec * 10 < (int64_t)lanes * k * 9 &&
+                                            rows * D * s >= ((int64_t)24 << 20);
+                const int cap = (vjp && (vb <= 4 || ovl_sparse_big)) ? 512 : 256;
                 block = std::max(std::max(lanes, 64), std::min(cap, maxb));
             }
             if (block < 64 || block > maxb || block % 64 != 0 || block % lanes != 0 || !is_pow2(block))
@@ -334,7 +380,7 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
                 k = 8;
                 block = 256;
                 eight_wide = true;
-                if (block > rmsn::max_block_threads(budget_op, k, p->nv, s)) return RMSN_E_CONFIG;
+                if (block > block_max(k)) return RMSN_E_CONFIG;
             }
             p->lanes = lanes;
             p->k = k;
@@ -352,7 +398,7 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
             // pipelined kernel needs more registers than two such blocks per
             // CU leave; with the width fixed, one block per CU runs faster).
             const bool whole_wide_row = lanes == rmsn::kVjpPipeFixedMax && block == lanes;
-            p->pipe = vjp && k * p->nv <= rmsn::kVjpPipeElems &&
+            p->pipe = vjp && !ovl && k * p->nv <= rmsn::kVjpPipeElems &&
                       (block <= rmsn::kVjpPipeBlock || whole_wide_row) && (int64_t)lanes * k == p->nvec;
             p->fixed_lanes = p->pipe && rmsn::vjp_kernel_fixed_lanes(dt, p->nv, k, vmode, lanes) != nullptr;
             // the grad call runs pipelined only with the lanes fixed
@@ -385,7 +431,12 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
         }
     }
 
-    // streaming kernel: one block per row
+    // streaming kernel: one block per row, whole vectors only
+    if (ovl) {
+        if (cfg && cfg->vec_bytes) return RMSN_E_CONFIG;
+        *p = Plan();
+        return make_plan(op, rows, D, dt, cfg, p, false);
+    }
     int block = req_b ? req_b : loop_block;
     if (block < 64 || block > 1024 || block % 64 != 0) return RMSN_E_CONFIG;
     p->k = -1;
@@ -502,8 +553,13 @@ int fwd_impl(bool fused, const void* x, const void* res, const void* w, void* y,
     Plan p;
     st = make_plan(fused ? RMSN_OP_FUSED : RMSN_OP_FWD, rows, D, dt, cfg, &p);
     if (st != RMSN_OK) return st;
-    const void* fn = p.k > 0 ? rmsn::fwd_kernel_fixed_lanes(dt, p.nv, p.k, fused, p.lanes) : nullptr;
-    if (!fn && !(p.k > 0 && rmsn::wave_rows(p.lanes))) fn = rmsn::fwd_kernel(dt, p.nv, p.k, fused);
+    const void* fn = nullptr;
+    if (p.ovl) {
+        fn = rmsn::fwd_kernel_ovl(dt, p.k, fused);
+    } else {
+        fn = p.k > 0 ? rmsn::fwd_kernel_fixed_lanes(dt, p.nv, p.k, fused, p.lanes) : nullptr;
+        if (!fn && !(p.k > 0 && rmsn::wave_rows(p.lanes))) fn = rmsn::fwd_kernel(dt, p.nv, p.k, fused);
+    }
     if (!fn) return RMSN_E_CONFIG;
 
     RowArgs a;
@@ -583,8 +639,14 @@ int vjp_impl(const void* x, const void* w, const void* dy, void* y, const void* 
             if (overlaps(rws, o)) return RMSN_E_OVERLAP;
     }
     const int mode = grad ? 1 : resgrad ? 2 : 0;
-    const void* fn = p.fixed_lanes ? rmsn::vjp_kernel_fixed_lanes(dt, p.nv, p.k, mode, p.lanes) : nullptr;
-    if (!fn && !(p.k > 0 && rmsn::wave_rows(p.lanes))) fn = rmsn::vjp_kernel(dt, p.nv, p.k, mode, p.jreg, p.pipe);
+    const void* fn = nullptr;
+    if (p.ovl) {
+        fn = rmsn::vjp_kernel_ovl(dt, p.k, mode);
+    } else {
+        fn = p.fixed_lanes ? rmsn::vjp_kernel_fixed_lanes(dt, p.nv, p.k, mode, p.lanes) : nullptr;
+        if (!fn && !(p.k > 0 && rmsn::wave_rows(p.lanes)))
+            fn = rmsn::vjp_kernel(dt, p.nv, p.k, mode, p.jreg, p.pipe);
+    }
     if (!fn) return RMSN_E_CONFIG;
 
     RowArgs a;

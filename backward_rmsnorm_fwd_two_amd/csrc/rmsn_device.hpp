@@ -268,7 +268,7 @@ struct RowArgs {
     float* dw;      // [D] fp32
     int64_t rows;
     int32_t D;
-    int32_t nvec;   // D / NV
+    int32_t nvec;   // vectors per row: D / NV (ceil(D / NV), the last overlapped)
     int32_t lanes;  // lanes per row (power of two)
     int32_t lshift; // log2(lanes)
     float eps;

@@ -35,19 +35,62 @@ namespace rmsn {
 // lane; vectors at or past nvec are masked.  Loads are issued
 // unconditionally from a clamped (always valid) offset so that every load
 // of a row is in flight at once; masked data is zeroed after arrival.
+//
+// Overlapped last vector (second constructor): a row of D elements that is
+// not a whole number of NV-element vectors is covered by nvec = ceil(D / NV)
+// vectors, the last one shifted back to end at the row's end (columns
+// [D - NV, D)).  Its first skip elements are also the previous vector's
+// last ones: they take no part in the row sums or in dw, and the outputs
+// stored for them are the very values the previous vector stores (same
+// inputs, same arithmetic).  skip is 0 everywhere else, and a compile-time 0
+// with the first constructor.
 template <int K>
 struct Cols {
     int64_t off[K];
     bool ok[K];
+    int skip[K];
     __device__ __forceinline__ Cols(int lanes, int lane, int nvec, int nv) {
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int v = k * lanes + lane;
             ok[k] = v < nvec;
             off[k] = ok[k] ? (int64_t)v * nv : 0;
+            skip[k] = 0;
+        }
+    }
+    __device__ __forceinline__ Cols(int lanes, int lane, int nvec, int nv, int64_t D) {
+        const int64_t last = D - nv;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int v = k * lanes + lane;
+            const int64_t o = (int64_t)v * nv;
+            ok[k] = v < nvec;
+            off[k] = ok[k] ? (o < last ? o : last) : 0;
+            skip[k] = ok[k] && o > last ? static_cast<int>(o - last) : 0;
         }
     }
 };
+
+// The column bookkeeping of a kernel: OVL selects the overlapped last vector.
+template <int K, bool OVL>
+__device__ __forceinline__ Cols<K> make_cols(int lanes, int lane, int nvec, int nv, int64_t D) {
+    if constexpr (OVL) return Cols<K>(lanes, lane, nvec, nv, D);
+    return Cols<K>(lanes, lane, nvec, nv);
+}
+
+// A finished dw vector into the block's partial row: an overlapped last
+// vector stores only its own columns (the previous vector's lane stores the
+// others).
+template <class DwOut, int NV>
+__device__ __forceinline__ void store_dw(float* out, const float (&v)[NV], bool vec_ok, int skip) {
+    if (skip > 0) {
+#pragma unroll
+        for (int e = 0; e < NV; ++e)
+            if (e >= skip) out[e] = v[e];
+    } else {
+        DwOut::template store<NV>(out, v, vec_ok);
+    }
+}
 
 template <typename T, int NV, int K>
 __device__ __forceinline__ void issue_row(const T* p, int64_t base, const Cols<K>& c,
@@ -119,7 +162,7 @@ __device__ __forceinline__ void fwd_issue(const RowArgs& a, int64_t row0, int sl
     if constexpr (FUSED) issue_row<T, NV, K>(static_cast<const T*>(a.res), base, c, d.r);
 }
 
-template <typename T, int NV, int K, bool FUSED>
+template <typename T, int NV, int K, bool FUSED, bool OVL = false>
 __device__ __forceinline__ void fwd_process(const RowArgs& a, int64_t row0, int slot, int lanes,
                                             const Cols<K>& c, const float (&g)[K][NV],
                                             FwdRow<T, NV, K, FUSED>& d, float* red, int& parity) {
@@ -138,11 +181,17 @@ __device__ __forceinline__ void fwd_process(const RowArgs& a, int64_t row0, int 
             float hv = elem(d.x[k], e);
             if constexpr (FUSED) hv += elem(d.r[k], e);
             h[k][e] = hv;
-            ss = __builtin_fmaf(hv, hv, ss);
+            const float hs = !OVL || e >= c.skip[k] ? hv : 0.0f;
+            ss = __builtin_fmaf(hs, hs, ss);
         }
     }
-    if constexpr (FUSED) {
-        T* newres = static_cast<T*>(a.newres);
+    // new_residual goes out before the row reduction -- except with an
+    // overlapped last vector: there two lanes, possibly in different waves,
+    // read the overlapped elements, and new_residual may be stored over x or
+    // residual, so it waits until the reduction has seen every wave's loads
+    // complete
+    T* newres = static_cast<T*>(a.newres);
+    if constexpr (FUSED && !OVL) {
 #pragma unroll
         for (int k = 0; k < K; ++k)
             if (rok && c.ok[k]) store_f32<T, NV>(newres + base + c.off[k], h[k]);
@@ -156,6 +205,11 @@ __device__ __forceinline__ void fwd_process(const RowArgs& a, int64_t row0, int 
         parity ^= 1;
     }
     const float r = rsqrtf(ss / static_cast<float>(a.D) + a.eps);
+    if constexpr (FUSED && OVL) {
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            if (rok && c.ok[k]) store_f32<T, NV>(newres + base + c.off[k], h[k]);
+    }
 
     T* y = static_cast<T*>(a.y);
 #pragma unroll
@@ -172,17 +226,20 @@ __device__ __forceinline__ void fwd_process(const RowArgs& a, int64_t row0, int 
 // LANES > 0: the lanes per row fixed at compile time (instances for the
 // common geometries), so the row reduction compiles without branches on the
 // row width; 0: taken from the arguments.
-template <typename T, int NV, int K, bool FUSED, int LANES = 0>
+// OVL: rows that are not a whole number of vectors, the last vector
+// overlapped (generic instances only).
+template <typename T, int NV, int K, bool FUSED, int LANES = 0, bool OVL = false>
 __global__ __launch_bounds__(max_block_threads(FUSED ? 1 : 0, K, NV, sizeof(T))) void fwd_rows(RowArgs a) {
     static_assert(LANES == 0 || ((LANES & (LANES - 1)) == 0 && LANES <= 1024) || wave_rows_supported(LANES),
                   "lanes: a power of two or a supported whole number of waves");
+    static_assert(!OVL || LANES == 0, "overlapped rows run in the generic instances");
     __shared__ float red[2 * 16];
     const int lanes = LANES > 0 ? LANES : a.lanes;
     const RowSlot rs = row_slot<LANES>(a.lshift);
     const int lane = rs.lane;
     const int slot = rs.slot;
     const int nslots = rs.nslots;
-    const Cols<K> c(lanes, lane, a.nvec, NV);
+    const Cols<K> c = make_cols<K, OVL>(lanes, lane, a.nvec, NV, a.D);
     const int64_t step = (int64_t)gridDim.x * nslots;
     int64_t row0 = (int64_t)blockIdx.x * nslots;
     if (row0 >= a.rows) return;  // whole block
@@ -210,7 +267,7 @@ __global__ __launch_bounds__(max_block_threads(FUSED ? 1 : 0, K, NV, sizeof(T)))
 #pragma unroll
         for (int u = 0; u < U; ++u)
             if (row0 + u * step < a.rows)
-                fwd_process<T, NV, K, FUSED>(a, row0 + u * step, slot, lanes, c, g, d[u], red, parity);
+                fwd_process<T, NV, K, FUSED, OVL>(a, row0 + u * step, slot, lanes, c, g, d[u], red, parity);
     }
     for (row0 += U * step; row0 < a.rows; row0 += U * step) {
         FwdRow<T, NV, K, FUSED> d[U];
@@ -222,7 +279,7 @@ __global__ __launch_bounds__(max_block_threads(FUSED ? 1 : 0, K, NV, sizeof(T)))
 #pragma unroll
         for (int u = 0; u < U; ++u)
             if (row0 + u * step < a.rows)
-                fwd_process<T, NV, K, FUSED>(a, row0 + u * step, slot, lanes, c, g, d[u], red, parity);
+                fwd_process<T, NV, K, FUSED, OVL>(a, row0 + u * step, slot, lanes, c, g, d[u], red, parity);
     }
 }
 
@@ -275,7 +332,8 @@ __device__ __forceinline__ void vjp_issue_dr(const RowArgs& a, int64_t row0, int
 // also keeps the wave's count of outstanding memory operations the same on
 // every path (a store skipped on some paths would make later waits for loads
 // wait for everything).
-template <typename T, int NV, int K, int MODE, bool FULL = false, bool ONE_ROW = false>
+// OVL: the row's last vector may be overlapped (Cols).
+template <typename T, int NV, int K, int MODE, bool FULL = false, bool ONE_ROW = false, bool OVL = false>
 __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int slot, int lanes,
                                             const Cols<K>& c, const float (&g)[K][NV],
                                             float (&acc)[K][NV], VjpRow<T, NV, K>& d,
@@ -293,10 +351,18 @@ __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int 
     for (int k = 0; k < K; ++k) {
 #pragma unroll
         for (int e = 0; e < NV; ++e) {
-            const float xv = elem(d.x[k], e);
-            const float dv = elem(d.dy[k], e);
-            s2[0] = __builtin_fmaf(xv, xv, s2[0]);
-            s2[1] = __builtin_fmaf(dv * g[k][e], xv, s2[1]);
+            if constexpr (OVL) {
+                const bool live = e >= c.skip[k];  // not an overlapped element
+                const float xv = live ? elem(d.x[k], e) : 0.0f;
+                const float dg = live ? elem(d.dy[k], e) * g[k][e] : 0.0f;
+                s2[0] = __builtin_fmaf(xv, xv, s2[0]);
+                s2[1] = __builtin_fmaf(dg, xv, s2[1]);
+            } else {
+                const float xv = elem(d.x[k], e);
+                const float dv = elem(d.dy[k], e);
+                s2[0] = __builtin_fmaf(xv, xv, s2[0]);
+                s2[1] = __builtin_fmaf(dv * g[k][e], xv, s2[1]);
+            }
         }
     }
     if constexpr (K * NV > kVjpPipeElems) {
@@ -337,7 +403,7 @@ __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int 
                 // that computes dx rounds it identically
                 o[e] = __builtin_fmaf(-xv, cc, (r * g[k][e]) * dv);
                 if constexpr (MODE == kResGrad) o[e] += elem(dr[k], e);
-                acc[k][e] = __builtin_fmaf(dv * xv, r, acc[k][e]);
+                if (!OVL || e >= c.skip[k]) acc[k][e] = __builtin_fmaf(dv * xv, r, acc[k][e]);
             }
             if (FULL || c.ok[k]) store_f32<T, NV>(dx + base + c.off[k], o);
         }
@@ -376,9 +442,12 @@ struct PartialRowOut {
 
 // LANES > 0: the lanes per row are a compile-time constant (pipelined
 // instances for the common geometries), so the row reductions compile
-// without branches on the row width; 0: taken from the arguments.
-template <typename T, int NV, int K, int MODE, bool PIPE = false, int LANES = 0, class DwOut = PartialRowOut>
-__global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
+// without branches on the row width; 0: taken from the arguments.  OVL:
+// rows that are not a whole number of vectors, the last vector overlapped
+// (the plain row loop only).
+template <typename T, int NV, int K, int MODE, bool PIPE = false, int LANES = 0, class DwOut = PartialRowOut,
+          bool OVL = false>
+__global__ __launch_bounds__(!PIPE ? (OVL ? max_block_threads_ovl(2, K, NV, sizeof(T)) : max_block_threads(2, K, NV, sizeof(T)))
                              : wave_rows(LANES) ? wave_rows_block_max(LANES, K * NV)
                              : (LANES > kVjpPipeBlock ? LANES : kVjpPipeBlock)) void vjp_rows(RowArgs a) {
     static_assert(!PIPE || K * NV <= kVjpPipeElems ||
@@ -387,6 +456,7 @@ __global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
     static_assert(LANES == 0 || (PIPE && (((LANES & (LANES - 1)) == 0 && LANES <= kVjpPipeFixedMax) ||
                                           wave_rows_supported(LANES))),
                   "fixed lane counts are pipelined: powers of two or supported whole numbers of waves");
+    static_assert(!OVL || (!PIPE && LANES == 0), "overlapped rows run in the plain row loop");
     extern __shared__ float dyn[];
     __shared__ float red[2 * 16 * 2];
     DwOut::begin(a);
@@ -395,7 +465,7 @@ __global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
     const int lane = rs.lane;
     const int slot = rs.slot;
     const int nslots = rs.nslots;
-    const Cols<K> c(lanes, lane, a.nvec, NV);
+    const Cols<K> c = make_cols<K, OVL>(lanes, lane, a.nvec, NV, a.D);
     const int64_t step = (int64_t)gridDim.x * nslots;
     int64_t row0 = (int64_t)blockIdx.x * nslots;
 
@@ -498,12 +568,12 @@ __global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
                 for (int k = 0; k < K; ++k)
 #pragma unroll
                     for (int e = 0; e < NV; ++e) g[k][e] = a.wb + elem(pw[k], e);
-                vjp_process<T, NV, K, MODE>(a, row0, slot, lanes, c, g, acc, d, d.dr, red, parity);
+                vjp_process<T, NV, K, MODE, false, false, OVL>(a, row0, slot, lanes, c, g, acc, d, d.dr, red, parity);
             }
             for (row0 += step; row0 < a.rows; row0 += step) {
                 VjpRow<T, NV, K> d;
                 vjp_issue<T, NV, K, MODE>(a, row0, slot, c, d);
-                vjp_process<T, NV, K, MODE>(a, row0, slot, lanes, c, g, acc, d, d.dr, red, parity);
+                vjp_process<T, NV, K, MODE, false, false, OVL>(a, row0, slot, lanes, c, g, acc, d, d.dr, red, parity);
             }
         }
     }
@@ -533,7 +603,7 @@ __global__ __launch_bounds__(!PIPE ? max_block_threads(2, K, NV, sizeof(T))
             }
             lds_barrier();
         }
-        if (slot == 0 && c.ok[k]) DwOut::template store<NV>(dst + c.off[k], acc[k], vec_ok);
+        if (slot == 0 && c.ok[k]) store_dw<DwOut, NV>(dst + c.off[k], acc[k], vec_ok, c.skip[k]);
     }
     DwOut::end(a);
 }

@@ -29,6 +29,14 @@ constexpr int max_block_threads(int op, int k, int nv, int itemsize) {
     return elems <= lim1024 ? 1024 : (elems <= 2 * lim1024 ? 512 : 256);
 }
 
+// The instances for rows with an overlapped last vector also hold a skip
+// count per vector and the masks built from it: their backward forms are
+// compiled for at most 512 threads (256 VGPRs; at 1024 threads the fp32
+// fused backward with 16 elements per lane would spill).
+constexpr int max_block_threads_ovl(int op, int k, int nv, int itemsize) {
+    return op == 2 && max_block_threads(op, k, nv, itemsize) > 512 ? 512 : max_block_threads(op, k, nv, itemsize);
+}
+
 // The VJP row kernel also comes software-pipelined (the next row group's
 // loads in flight while the current one is processed; two groups of raw data
 // live), for instances with at most this many elements per lane; the
@@ -105,6 +113,10 @@ const void* vjp_kernel_fixed_lanes(int dt, int nv, int k, int mode, int lanes);
 // The wave-row instances (lanes = 64 W, W not a power of two), or nullptr.
 const void* fwd_kernel_wave_rows(int dt, int nv, int k, bool fused, int lanes);
 const void* vjp_kernel_wave_rows(int dt, int nv, int k, int mode, int lanes);
+// Rows that are not a whole number of 16-byte vectors, the last vector
+// overlapped (forward, and the backward forms' plain row loop), or nullptr.
+const void* fwd_kernel_ovl(int dt, int k, bool fused);
+const void* vjp_kernel_ovl(int dt, int k, int mode);
 // dw_dt: dtype of dw (fp32, or the weight dtype).
 const void* dw_combine_kernel(int dw_dt);
 // Gated activation silu(x[:, :d]) * x[:, d:2d]: NV elements per load, U

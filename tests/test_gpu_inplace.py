@@ -25,6 +25,12 @@ CASES = [
     (5, 1000, "float32", None),
     (6, 5000, "bfloat16", dict(vecs_per_lane=-1, block_threads=256)),
     (2, 70000, "bfloat16", None),
+    # rows that are not a whole number of 16-byte vectors (last vector
+    # overlapped): its neighbour vector in another wave of the row; in one
+    # wave; fp32
+    (33, 1025, "float16", None),
+    (19, 513, "bfloat16", dict(lanes_per_row=128, vecs_per_lane=1, vec_bytes=16, block_threads=256)),
+    (23, 1023, "float32", None),
 ]
 VJP_GRIDS = [None, 1, 3]
 

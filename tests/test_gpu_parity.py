@@ -257,15 +257,20 @@ def _max_block(op, k, nv, itemsize):
 
 def _legal_configs(op, D, itemsize):
     """Every (lanes, K, vec_bytes, block) combination the register kernels
-    accept for D, plus the streaming kernel at two block sizes."""
+    accept for D, plus the streaming kernel at two block sizes.  16-byte
+    vectors on a row that is not a whole number of them overlap the last
+    vector (backward forms then in blocks of at most 512 threads)."""
     out = []
     for vb in (16, 8, 4, 2):
-        if vb < itemsize or (D * itemsize) % vb:
+        ovl = (D * itemsize) % vb != 0
+        if vb < itemsize or (ovl and (vb != 16 or D * itemsize < 16)):
             continue
         nv = vb // itemsize
-        nvec = D // nv
+        nvec = -(-D // nv)
         for k in (1, 2, 4, 8):
             maxb = _max_block(op, k, nv, itemsize)
+            if ovl and op >= 2:
+                maxb = min(maxb, 512)
             for lanes in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024):
                 if lanes * k < nvec or lanes > maxb:
                     continue
