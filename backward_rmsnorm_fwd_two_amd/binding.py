@@ -207,8 +207,14 @@ def workspace_for(rows: int, D: int, dtype: torch.dtype, device, cfg=None) -> to
     n = rmsnorm_vjp_workspace_bytes(rows, D, dtype)
     if cfg is not None:
         c = cfg if isinstance(cfg, dict) else cfg.as_dict()
-        nb = c.get("num_blocks", 0) or 2048
-        n = max(n, nb * D * 4)
+        if c.get("vecs_per_lane", 0) == -2:
+            # column split: row statistics [rows, slices, 2] fp32 (a slice is
+            # 1024 vectors of at least one element), then the chunks' dw rows
+            slices = -(-D // 1024)
+            n = max(n, -(-(rows * slices * 8) // 256) * 256 + (c.get("num_blocks", 0) or 1024) * D * 4)
+        else:
+            nb = c.get("num_blocks", 0) or 2048
+            n = max(n, nb * D * 4)
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 

@@ -20,6 +20,7 @@ using rmsn::RowArgs;
 
 constexpr int kMaxDevices = 64;
 constexpr int kMaxPartialRows = 2048;   // bound on dw partial rows (workspace)
+
 // Row data a CU should hold in flight in the wave-row VJP, in units of one
 // wave's 16-byte vector of one row tensor (see make_plan).
 constexpr int kWaveRowsInFlight = 15;
@@ -107,7 +108,49 @@ struct Plan {
     bool pipe = false;        // backward forms: the software-pipelined row kernel
     bool fixed_lanes = false; // ... in an instance with the lanes fixed at compile time
     bool ovl = false;         // rows of ceil(D / nv) vectors, the last one overlapped
+    // column-split backward (k == -2): statistics slices per row, column
+    // tiles, rows per chunk (grid = chunks), workspace bytes of the row
+    // statistics (ahead of the dw partial rows)
+    int cs_slices = 0;
+    int cs_tiles = 0;
+    int cs_chunk = 0;
+    size_t cs_stats_bytes = 0;
 };
+
+// The column-split backward forms for `rows` rows of p->nvec vectors (p->nv
+// set): statistics slices of 256 threads x 4 vectors, apply tiles of 256
+// vectors, and row chunks -- enough (tiles x chunks) blocks for two per CU,
+// unless `chunks` asks for a number.
+int plan_colsplit(int64_t rows, int cus, int64_t chunks, Plan* p) {
+    if (rows > 65535) return RMSN_E_CONFIG;
+    const int64_t per_slice = (int64_t)rmsn::kCsThreads * rmsn::kCsStatVecs;
+    const int64_t slices = (p->nvec + per_slice - 1) / per_slice;
+    const int64_t tiles = (p->nvec + rmsn::kCsThreads - 1) / rmsn::kCsThreads;
+    int64_t rc = chunks;
+    if (rc == 0) rc = std::max<int64_t>(1, (2 * (int64_t)cus + tiles - 1) / tiles);
+    // at least two rows per chunk whenever there are two: the chunks' dw
+    // rows never number one per row (as vjp_grid for the persistent grids)
+    rc = std::min(rc, rows > 1 ? (rows + 1) / 2 : rows);
+    int64_t chunk = (rows + rc - 1) / rc;
+    if (chunk > rmsn::kCsMaxChunk) {
+        if (chunks != 0) return RMSN_E_CONFIG;
+        chunk = rmsn::kCsMaxChunk;
+    }
+    rc = (rows + chunk - 1) / chunk;  // every chunk holds at least one row
+    if (rc < 1 || rc > 1024) return RMSN_E_CONFIG;
+    p->k = -2;
+    p->lanes = 0;
+    p->block = rmsn::kCsThreads;
+    p->grid = rc;
+    p->shmem = 0;
+    p->pipe = p->fixed_lanes = p->ovl = false;
+    p->cs_slices = static_cast<int>(slices);
+    p->cs_tiles = static_cast<int>(tiles);
+    p->cs_chunk = static_cast<int>(chunk);
+    p->cs_stats_bytes = ((static_cast<size_t>(rows) * static_cast<size_t>(slices) * 2 * sizeof(float)) + 255) &
+                        ~static_cast<size_t>(255);
+    return RMSN_OK;
+}
 
 // The kernel plan for one call.  The load width depends on the row length
 // only: row vectors are read and written at element alignment, so a base
@@ -128,6 +171,11 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
     // load width
     int vb = 0;
     bool ovl = false;
+    if (cfg && cfg->vecs_per_lane == -2) {
+        if (!vjp || cfg->lanes_per_row != 0 || (cfg->block_threads != 0 && cfg->block_threads != rmsn::kCsThreads))
+            return RMSN_E_CONFIG;
+        ovl_ok = false;  // whole vectors only
+    }
     if (cfg && cfg->vec_bytes) {
         vb = cfg->vec_bytes;
         if (vb < s || vb > 16 || !is_pow2(vb)) return RMSN_E_CONFIG;
@@ -158,6 +206,7 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
     const int req_k = cfg ? cfg->vecs_per_lane : 0;
     const int req_l = cfg ? cfg->lanes_per_row : 0;
     const int req_b = cfg ? cfg->block_threads : 0;
+    if (req_k == -2) return plan_colsplit(rows, cus, cfg->num_blocks, p);
     bool looped = req_k == -1 || (req_k == 0 && req_l == 0 && p->nvec > 1024 * 8);
     int loop_block = 1024;  // streaming kernel's default block
 
@@ -437,6 +486,19 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
         *p = Plan();
         return make_plan(op, rows, D, dt, cfg, p, false);
     }
+    // Backward forms: the column split where the streaming kernel would
+    // leave CUs idle (fewer rows than two per CU: at most one persistent
+    // block per two rows) or its second pass would miss the caches (long
+    // rows; from enough rows on, its single pass over dy and dx wins back).
+    // bf16, three rotating sets, VJP: 128 x 2^20 1145 -> 244 us; 511 x
+    // 262144 464 -> 250; 1024 x 65536 168 -> 126; 4096 x 65536 522 -> 496;
+    // 1024 x 32768 69.1 -> 61.7 (2048 rows: 112.8 against 124.8 split); 256
+    // x 16392 21.0 -> 18.6 (1024 rows: 37.2 against 39.8 split).
+    if (vjp && !cfg) {
+        const int64_t per_cu = (rows + cus - 1) / cus;
+        if (rows < 2 * (int64_t)cus || (p->nvec >= 8192 && per_cu <= 16) || (p->nvec >= 4096 && per_cu <= 4))
+            return plan_colsplit(rows, cus, 0, p);
+    }
     int block = req_b ? req_b : loop_block;
     if (block < 64 || block > 1024 || block % 64 != 0) return RMSN_E_CONFIG;
     p->k = -1;
@@ -581,7 +643,58 @@ int fwd_impl(bool fused, const void* x, const void* res, const void* w, void* y,
 // sum is staged there and rounded by the combine).
 size_t ws_bytes(const Plan& p, int64_t D, bool typed_dw = false) {
     const int64_t nrows = p.grid > 1 ? p.grid : (typed_dw ? 1 : 0);
-    return static_cast<size_t>(nrows) * static_cast<size_t>(D) * sizeof(float);
+    return p.cs_stats_bytes + static_cast<size_t>(nrows) * static_cast<size_t>(D) * sizeof(float);
+}
+
+// The column-split backward forms: statistics, apply, and (for more than one
+// row chunk, or dw in the weight dtype) the combine of the chunks' dw rows.
+// Workspace: the row statistics [rows, slices, 2] fp32, then the partial
+// rows [chunks, D] fp32.
+int colsplit_launch(const Plan& p, const void* x, const void* w, const void* dy, void* y, const void* dres,
+                    void* dx, void* dw, int dw_dt, void* ws, int64_t rows, int64_t D, int dt, float eps, float wb,
+                    hipStream_t hs) {
+    const int mode = y ? 1 : dres ? 2 : 0;
+    const void* sfn = nullptr;
+    const void* afn = nullptr;
+    if (!rmsn::vjp_cs_kernels(dt, p.nv, mode, &sfn, &afn)) return RMSN_E_CONFIG;
+    const bool typed_dw = dw_dt != RMSN_F32;
+    float* stats = static_cast<float*>(ws);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.cs_stats_bytes);
+    RowArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.x = x;
+    a.w = w;
+    a.dy = dy;
+    a.y = y;
+    a.res = dres;
+    a.dx = dx;
+    a.partial = part;
+    a.dw = (p.grid == 1 && !typed_dw) ? static_cast<float*>(dw) : part;
+    a.rows = rows;
+    a.D = static_cast<int32_t>(D);
+    a.nvec = p.nvec;
+    a.eps = eps;
+    a.wb = wb;
+    int slices = p.cs_slices;
+    void* sargs[] = {&a, &stats, &slices};
+    if (hipLaunchKernel(sfn, dim3(static_cast<unsigned>(slices), static_cast<unsigned>(rows)), dim3(p.block),
+                        sargs, 0, hs) != hipSuccess)
+        return RMSN_E_HIP;
+    const float* cstats = stats;
+    int chunk = p.cs_chunk;
+    void* aargs[] = {&a, &cstats, &slices, &chunk};
+    if (hipLaunchKernel(afn, dim3(static_cast<unsigned>(p.cs_tiles), static_cast<unsigned>(p.grid)),
+                        dim3(p.block), aargs, 0, hs) != hipSuccess)
+        return RMSN_E_HIP;
+    if (p.grid == 1 && !typed_dw) return RMSN_OK;
+    const float* cpart = part;
+    int nb = static_cast<int>(p.grid);
+    int d32 = static_cast<int>(D);
+    void* cargs[] = {&cpart, &dw, &nb, &d32};
+    const unsigned cg = static_cast<unsigned>((D + 15) / 16);
+    if (hipLaunchKernel(rmsn::dw_combine_kernel(dw_dt), dim3(cg), dim3(256), cargs, 0, hs) != hipSuccess)
+        return RMSN_E_HIP;
+    return RMSN_OK;
 }
 
 // y != nullptr: the grad call (forward output too); dres != nullptr: the
@@ -639,6 +752,7 @@ int vjp_impl(const void* x, const void* w, const void* dy, void* y, const void* 
             if (overlaps(rws, o)) return RMSN_E_OVERLAP;
     }
     const int mode = grad ? 1 : resgrad ? 2 : 0;
+    if (p.k == -2) return colsplit_launch(p, x, w, dy, y, dres, dx, dw, dw_dt, ws, rows, D, dt, eps, wb, hs);
     const void* fn = nullptr;
     if (p.ovl) {
         fn = rmsn::vjp_kernel_ovl(dt, p.k, mode);

@@ -622,6 +622,47 @@ __global__ __launch_bounds__(!PIPE ? (OVL ? max_block_threads_ovl(2, K, NV, size
 // at D = 16392..65536: the re-read went back to HBM).
 constexpr bool kPass1Stream = false;
 
+// The streaming forward keeps this many vectors per thread in flight: each
+// iteration issues the loads of kStreamUnroll vectors (v, v + blockDim.x,
+// ...; a lane skips those past the row's end), then consumes them.  With one
+// load per iteration a 1024-thread block holds 16 KiB in flight, and a few
+// rows of a very wide D (one block per row) ran at 2.8 TB/s.
+constexpr int kStreamUnroll = 4;
+
+// Pass 1 of the streaming forward: this thread's share of a row's sum of
+// h^2 (h = x, or x + residual for OP 1) in s2[0].
+template <typename T, int NV, int OP>
+__device__ __forceinline__ void stream_row_sums(const RowArgs& a, int64_t base, float (&s2)[2]) {
+    static_assert(OP == 0 || OP == 1, "forward forms");
+    const T* x = static_cast<const T*>(a.x);
+    const T* res = static_cast<const T*>(a.res);
+    constexpr int U = kStreamUnroll;
+    const int bd = static_cast<int>(blockDim.x);
+    for (int v0 = threadIdx.x; v0 < a.nvec; v0 += U * bd) {
+        Raw<T, NV> px[U], pr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = v0 + u * bd;
+            if (v < a.nvec) {
+                const int64_t off = base + (int64_t)v * NV;
+                px[u] = load_raw<T, NV, kPass1Stream>(x + off);
+                if constexpr (OP == 1) pr[u] = load_raw<T, NV, kPass1Stream>(res + off);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (v0 + u * bd < a.nvec) {
+#pragma unroll
+                for (int e = 0; e < NV; ++e) {
+                    float hv = elem(px[u], e);
+                    if constexpr (OP == 1) hv += elem(pr[u], e);
+                    s2[0] = __builtin_fmaf(hv, hv, s2[0]);
+                }
+            }
+        }
+    }
+}
+
 template <int NV>
 __device__ __forceinline__ void block_sum(float (&v)[NV], float* red, int& parity) {
 #pragma unroll
@@ -655,10 +696,10 @@ __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
         const int64_t base = row * a.D;
         float s2[2] = {0.0f, 0.0f};
-        for (int v = threadIdx.x; v < a.nvec; v += blockDim.x) {
-            const int64_t off = base + (int64_t)v * NV;
-            const Raw<T, NV> px = load_raw<T, NV, kPass1Stream>(x + off);
-            if constexpr (OP >= 2) {
+        if constexpr (OP >= 2) {
+            for (int v = threadIdx.x; v < a.nvec; v += blockDim.x) {
+                const int64_t off = base + (int64_t)v * NV;
+                const Raw<T, NV> px = load_raw<T, NV, kPass1Stream>(x + off);
                 const Raw<T, NV> pd = load_raw<T, NV, kPass1Stream>(dy + off);
                 const Raw<T, NV> pw = load_w<T, NV>(w + (int64_t)v * NV);
 #pragma unroll
@@ -667,18 +708,9 @@ __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
                     s2[0] = __builtin_fmaf(xv, xv, s2[0]);
                     s2[1] = __builtin_fmaf(elem(pd, e) * (a.wb + elem(pw, e)), xv, s2[1]);
                 }
-            } else {
-                float h[NV];
-#pragma unroll
-                for (int e = 0; e < NV; ++e) h[e] = elem(px, e);
-                if constexpr (OP == 1) {
-                    const Raw<T, NV> pr = load_raw<T, NV, kPass1Stream>(res + off);
-#pragma unroll
-                    for (int e = 0; e < NV; ++e) h[e] += elem(pr, e);
-                }
-#pragma unroll
-                for (int e = 0; e < NV; ++e) s2[0] = __builtin_fmaf(h[e], h[e], s2[0]);
             }
+        } else {
+            stream_row_sums<T, NV, OP>(a, base, s2);
         }
         if constexpr (OP >= 2) {
             block_sum<2>(s2, red, parity);
@@ -721,23 +753,38 @@ __global__ __launch_bounds__(1024) void rows_looped(RowArgs a) {
                 }
             }
         } else {
-            for (int v = threadIdx.x; v < a.nvec; v += blockDim.x) {
-                const int64_t off = base + (int64_t)v * NV;
-                const Raw<T, NV> px = load_raw<T, NV>(x + off);
-                const Raw<T, NV> pw = load_w<T, NV>(w + (int64_t)v * NV);
-                float h[NV], o[NV];
+            constexpr int U = kStreamUnroll;
+            const int bd = static_cast<int>(blockDim.x);
+            for (int v0 = threadIdx.x; v0 < a.nvec; v0 += U * bd) {
+                Raw<T, NV> px[U], pr[U], pw[U];
 #pragma unroll
-                for (int e = 0; e < NV; ++e) h[e] = elem(px, e);
-                if constexpr (OP == 1) {
-                    const Raw<T, NV> pr = load_raw<T, NV>(res + off);
-#pragma unroll
-                    for (int e = 0; e < NV; ++e) h[e] += elem(pr, e);
+                for (int u = 0; u < U; ++u) {
+                    const int v = v0 + u * bd;
+                    if (v < a.nvec) {
+                        const int64_t off = base + (int64_t)v * NV;
+                        px[u] = load_raw<T, NV>(x + off);
+                        pw[u] = load_w<T, NV>(w + (int64_t)v * NV);
+                        if constexpr (OP == 1) pr[u] = load_raw<T, NV>(res + off);
+                    }
                 }
+                // every output after every load of the iteration: x or
+                // residual may be overwritten
 #pragma unroll
-                for (int e = 0; e < NV; ++e) o[e] = h[e] * r * (a.wb + elem(pw, e));
-                // both outputs after both loads: x or residual may be overwritten
-                if constexpr (OP == 1) store_f32<T, NV>(newres + off, h);
-                store_f32<T, NV>(y + off, o);
+                for (int u = 0; u < U; ++u) {
+                    const int v = v0 + u * bd;
+                    if (v < a.nvec) {
+                        const int64_t off = base + (int64_t)v * NV;
+                        float h[NV], o[NV];
+#pragma unroll
+                        for (int e = 0; e < NV; ++e) {
+                            h[e] = elem(px[u], e);
+                            if constexpr (OP == 1) h[e] += elem(pr[u], e);
+                            o[e] = h[e] * r * (a.wb + elem(pw[u], e));
+                        }
+                        if constexpr (OP == 1) store_f32<T, NV>(newres + off, h);
+                        store_f32<T, NV>(y + off, o);
+                    }
+                }
             }
         }
     }
@@ -847,6 +894,158 @@ __global__ __launch_bounds__(1024) void rows_batched_vjp(RowArgs a) {
         }
         first = false;
     }
+}
+
+}  // namespace rmsn
+
+namespace rmsn {
+
+// ------------------------------------------- column-split backward forms
+// For few rows of a wide D, where one block per row (or per pair of rows)
+// leaves CUs idle.  Two kernels:
+//   vjp_cs_stats  one block per (column slice, row): the slice's partial
+//                 sums (sum x^2, sum dy g x) into stats[row, slice, 2];
+//   vjp_cs_apply  one block per (column tile, row chunk): every row's r and
+//                 c from its slices' partials (added in a fixed order, so
+//                 every block derives the same values), then the tile's
+//                 columns walked over the chunk's rows -- dx (y, the
+//                 residual-stream gradient) stored, dw summed in registers in
+//                 row order and written once per chunk (to dw itself when the
+//                 rows form one chunk).
+// x and dy are read twice (a slice of a row is 16 KiB, gone from the caches
+// by the time the apply pass comes back to it): 5 row passes for the VJP
+// against 3, traded for every CU at work.
+// (kCsThreads, kCsStatVecs and kCsMaxChunk: rmsn_launch.hpp)
+constexpr int kCsRowUnroll = 4;   // rows whose loads the apply pass issues together
+
+template <typename T, int NV>
+__global__ __launch_bounds__(kCsThreads) void vjp_cs_stats(RowArgs a, float* stats, int slices) {
+    __shared__ float red[2 * 16 * 2];
+    const T* x = static_cast<const T*>(a.x);
+    const T* dy = static_cast<const T*>(a.dy);
+    const T* w = static_cast<const T*>(a.w);
+    const int64_t row = blockIdx.y;
+    const int v0 = static_cast<int>(blockIdx.x) * (kCsThreads * kCsStatVecs) + static_cast<int>(threadIdx.x);
+    const int64_t base = row * a.D;
+    Raw<T, NV> px[kCsStatVecs], pd[kCsStatVecs], pw[kCsStatVecs];
+#pragma unroll
+    for (int u = 0; u < kCsStatVecs; ++u) {
+        const int v = v0 + u * kCsThreads;
+        if (v < a.nvec) {
+            px[u] = load_raw<T, NV, kPass1Stream>(x + base + (int64_t)v * NV);
+            pd[u] = load_raw<T, NV, kPass1Stream>(dy + base + (int64_t)v * NV);
+            pw[u] = load_w<T, NV>(w + (int64_t)v * NV);
+        }
+    }
+    float s2[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < kCsStatVecs; ++u) {
+        if (v0 + u * kCsThreads < a.nvec) {
+#pragma unroll
+            for (int e = 0; e < NV; ++e) {
+                const float xv = elem(px[u], e);
+                s2[0] = __builtin_fmaf(xv, xv, s2[0]);
+                s2[1] = __builtin_fmaf(elem(pd[u], e) * (a.wb + elem(pw[u], e)), xv, s2[1]);
+            }
+        }
+    }
+    int parity = 0;
+    block_sum<2>(s2, red, parity);
+    if (threadIdx.x == 0) {
+        float* dst = stats + (row * slices + blockIdx.x) * 2;
+        dst[0] = s2[0];
+        dst[1] = s2[1];
+    }
+}
+
+template <typename T, int NV, int MODE>
+__global__ __launch_bounds__(kCsThreads) void vjp_cs_apply(RowArgs a, const float* stats, int slices,
+                                                           int chunk_rows) {
+    __shared__ float rc[2 * kCsMaxChunk];
+    const T* x = static_cast<const T*>(a.x);
+    const T* dy = static_cast<const T*>(a.dy);
+    const T* dr = static_cast<const T*>(a.res);
+    const T* w = static_cast<const T*>(a.w);
+    T* dx = static_cast<T*>(a.dx);
+    T* y = static_cast<T*>(a.y);
+    const int64_t r0 = (int64_t)blockIdx.y * chunk_rows;
+    const int nrows = static_cast<int>(a.rows - r0 < chunk_rows ? a.rows - r0 : chunk_rows);
+    const float inv_d = 1.0f / static_cast<float>(a.D);
+
+    // r and c of the chunk's rows: wave i takes rows i, i + 4, ...; lane l
+    // adds slices l, l + 64, ... in order, then the wave's fixed tree
+    const int wave = static_cast<int>(threadIdx.x) >> 6;
+    const int lane = static_cast<int>(threadIdx.x) & 63;
+    for (int i = wave; i < nrows; i += kCsThreads / 64) {
+        const float* st = stats + (r0 + i) * slices * 2;
+        float s0 = 0.0f, s1 = 0.0f;
+        for (int sl = lane; sl < slices; sl += 64) {
+            s0 += st[2 * sl];
+            s1 += st[2 * sl + 1];
+        }
+        s0 = wave_sum(s0);
+        s1 = wave_sum(s1);
+        if (lane == 0) {
+            // explicit fma: the same rounding as the other backward kernels
+            const float r = rsqrtf(__builtin_fmaf(s0, inv_d, a.eps));
+            rc[2 * i] = r;
+            rc[2 * i + 1] = r * r * r * s1 * inv_d;
+        }
+    }
+    lds_barrier();
+
+    const int v = static_cast<int>(blockIdx.x) * kCsThreads + static_cast<int>(threadIdx.x);
+    if (v >= a.nvec) return;  // no barrier follows
+    const int64_t col = (int64_t)v * NV;
+    const Raw<T, NV> pw = load_w<T, NV>(w + col);
+    float g[NV], acc[NV];
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+        g[e] = a.wb + elem(pw, e);
+        acc[e] = 0.0f;
+    }
+    for (int i0 = 0; i0 < nrows; i0 += kCsRowUnroll) {
+        // the loads of kCsRowUnroll rows before their first store (an
+        // output may be the very buffer of an input); rows past the chunk
+        // are skipped (uniform across the block)
+        Raw<T, NV> px[kCsRowUnroll], pd[kCsRowUnroll], pr[kCsRowUnroll];
+#pragma unroll
+        for (int u = 0; u < kCsRowUnroll; ++u) {
+            if (i0 + u < nrows) {
+                const int64_t off = (r0 + i0 + u) * a.D + col;
+                px[u] = load_raw<T, NV>(x + off);
+                pd[u] = load_raw<T, NV>(dy + off);
+                if constexpr (MODE == kResGrad) pr[u] = load_raw<T, NV>(dr + off);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kCsRowUnroll; ++u) {
+            const int i = i0 + u;
+            if (i < nrows) {
+                const float r = rc[2 * i];
+                const float cc = rc[2 * i + 1];
+                const int64_t off = (r0 + i) * a.D + col;
+                float o[NV];
+#pragma unroll
+                for (int e = 0; e < NV; ++e) {
+                    const float xv = elem(px[u], e);
+                    const float dv = elem(pd[u], e);
+                    o[e] = __builtin_fmaf(-xv, cc, (r * g[e]) * dv);
+                    if constexpr (MODE == kResGrad) o[e] += elem(pr[u], e);
+                    acc[e] = __builtin_fmaf(dv * xv, r, acc[e]);
+                }
+                store_f32<T, NV>(dx + off, o);
+                if constexpr (MODE == kGrad) {
+#pragma unroll
+                    for (int e = 0; e < NV; ++e) o[e] = elem(px[u], e) * r * g[e];
+                    store_f32<T, NV>(y + off, o);
+                }
+            }
+        }
+    }
+    float* dst = (gridDim.y == 1 ? a.dw : a.partial + (int64_t)blockIdx.y * a.D) + col;
+#pragma unroll
+    for (int e = 0; e < NV; ++e) dst[e] = acc[e];
 }
 
 }  // namespace rmsn

@@ -117,6 +117,16 @@ const void* vjp_kernel_wave_rows(int dt, int nv, int k, int mode, int lanes);
 // overlapped (forward, and the backward forms' plain row loop), or nullptr.
 const void* fwd_kernel_ovl(int dt, int k, bool fused);
 const void* vjp_kernel_ovl(int dt, int k, int mode);
+// Column-split backward forms: threads per block (both kernels), vectors per
+// thread in a statistics slice, rows per chunk of the apply kernel (their r
+// and c live in LDS).
+constexpr int kCsThreads = 256;
+constexpr int kCsStatVecs = 4;
+constexpr int kCsMaxChunk = 512;
+
+// The column-split backward forms (few rows of a wide D): the statistics
+// and apply kernels for (dt, nv, mode); false where not compiled.
+bool vjp_cs_kernels(int dt, int nv, int mode, const void** stats_fn, const void** apply_fn);
 // dw_dt: dtype of dw (fp32, or the weight dtype).
 const void* dw_combine_kernel(int dw_dt);
 // Gated activation silu(x[:, :d]) * x[:, d:2d]: NV elements per load, U

@@ -126,7 +126,11 @@ typedef struct {
                                the grad call and fused backward 448 or 512, and every backward form of fp32
                                rows 512 lanes with 4, one row per block */
     int32_t vecs_per_lane;  /* vectors each thread holds per row: 1, 2, 4 or 8;
-                               -1 selects the streaming (looped) kernel */
+                               -1 selects the streaming (looped) kernel; -2 the
+                               column-split backward forms (backward entry points
+                               only; lanes_per_row 0, block_threads 0 or 256,
+                               num_blocks the row chunks, at most 1024, each of at
+                               most 512 rows; rows at most 65535) */
     int32_t vec_bytes;      /* bytes per load/store: 16, 8, 4 or the element size */
     int32_t block_threads;  /* threads per block: 64..1024, multiple of lanes_per_row */
     int32_t num_blocks;     /* grid size (for rmsnorm_vjp also the number of dw partial rows) */

@@ -163,9 +163,12 @@ def test_forced_streaming_with_16_byte_vectors_rejected(R):
     assert_close(y, O.rmsnorm_fwd(c["x"], c["w"], c["eps"], 0.0)[0], "streaming y")
 
 
-def test_wide_odd_row_falls_back_to_streaming(R):
-    # 8192 * 8 + 1 fp16 elements: more vectors than the register kernels hold
+def test_wide_odd_row_falls_back_to_narrow_loads(R):
+    # 8192 * 8 + 1 fp16 elements: more vectors than the register kernels hold;
+    # the forward streams them, the backward forms on 3 rows split columns
     D = 65537
-    q = R.query_config(2, 3, D, torch.float16)
+    q = R.query_config(0, 3, D, torch.float16)
     assert q["vecs_per_lane"] == -1 and q["vec_bytes"] == 2, q
+    q = R.query_config(2, 3, D, torch.float16)
+    assert q["vecs_per_lane"] == -2 and q["vec_bytes"] == 2, q
     _check_every_form(R, 3, D, "float16", seed=3)

@@ -60,16 +60,17 @@ def test_noalloc_matches_vjp_two_calls():
 
 def test_noalloc_refuses_shapes_beyond_the_scratch():
     import backward_rmsnorm_fwd_two_amd as R
-    # 16 rows of 2^20 bf16: 16 partial rows of 4 MiB, beyond the 16 MiB scratch.
-    # Real buffers (never filled), so that a wrong acceptance could not touch
+    # 2048 rows of 32768 bf16 (the streaming kernel, one persistent block per
+    # CU): 256 partial rows of 128 KiB, beyond the 16 MiB scratch.  Real
+    # buffers (never filled), so that a wrong acceptance could not touch
     # memory outside them.
-    rows, D = 16, 1 << 20
+    rows, D = 2048, 32768
     assert R.rmsnorm_vjp_workspace_bytes(rows, D, torch.bfloat16) > R.RMSN_NOALLOC_SCRATCH_BYTES
     x = torch.empty(rows, D, dtype=torch.bfloat16, device=DEV)
     dy, dx = torch.empty_like(x), torch.empty_like(x)
     w = torch.empty(D, dtype=torch.bfloat16, device=DEV)
     dw = torch.empty(D, dtype=torch.float32, device=DEV)
-    _say("noalloc refusal: 16 x 2^20 bf16")
+    _say("noalloc refusal: 2048 x 32768 bf16")
     assert _raw_noalloc(R, x, w, dy, dx, dw, 1e-6, 0.0) == -4  # RMSN_E_WORKSPACE
 
 
