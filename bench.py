@@ -789,7 +789,7 @@ def step_bench(R, I, dev, args, fused, nested=False):
         "kernel": "fused_add_rmsnorm_fwd (fwd_rows<FUSED>)" if fused else "rmsnorm_fwd (fwd_rows)",
         "bound": "hbm", "achieved": round(fwd_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
         "frac": round(fwd_gbps / HBM_PEAK_GBPS, 4),
-        "traffic": stored_traffic("fused_fwd_prefill_32768x8192_bf16", src_hash) if fused else None,
+        "traffic": stored_traffic("fused_fwd_prefill_32768x8192_bf16" if fused else "fwd_poc_8192x4096_fp16", src_hash),
         "algorithmic_bytes": fwd_bytes, "avg_us": round(fwd_b2b_us, 3),
         "method": "events around 100 back-to-back forward calls on the launch stream, after the timed region"}
     # the roofline object is the dominant kernel's: the one that takes the
