@@ -150,8 +150,11 @@ int fused_add_rmsnorm_fwd(const void *x, const void *residual, const void *w,
 /* Bytes of workspace rmsnorm_vjp (and every backward entry point, including
  * rmsnorm_backward with dw in the weight dtype) needs for this shape on the
  * current device: fp32 dw partials, [num_blocks, D] with num_blocks bounded
- * independently of rows (at least one row).  0 for invalid arguments.  Never
- * more than 2048 * D * 4 + 256. */
+ * independently of rows and below the rows whenever there are two or more
+ * (at least one row); for few rows of a wide D (the column-split plan),
+ * also the rows' statistics, two floats per row and slice of 1024 vectors,
+ * ahead of the partial rows.  0 for invalid arguments.  Never more than
+ * 2048 * D * 4 + 256. */
 size_t rmsnorm_vjp_workspace_bytes(int64_t rows, int64_t D, int dt);
 
 /* dx[rows, D] (dtype dt) and dw[D] (fp32, overwritten).  `workspace` is
@@ -174,9 +177,10 @@ int rmsnorm_vjp(const void *x, const void *w, const void *dy,
  * arguments); the dw partial rows live in a file-scope device array of
  * RMSN_NOALLOC_SCRATCH_BYTES bytes inside the library.  The first call on a
  * device looks up that array's device address once (hipGetSymbolAddress);
- * no call allocates or frees memory.  Shapes whose partial rows need more
- * than RMSN_NOALLOC_SCRATCH_BYTES (num_blocks * D * 4 bytes, e.g. D above
- * 2^14 with 256 partial rows) return RMSN_E_WORKSPACE before any launch.
+ * no call allocates or frees memory.  Shapes whose workspace
+ * (rmsnorm_vjp_workspace_bytes) exceeds RMSN_NOALLOC_SCRATCH_BYTES (e.g.
+ * num_blocks * D * 4 bytes of partial rows for D above 2^14 with 256
+ * partial rows) return RMSN_E_WORKSPACE before any launch.
  * Every call on one GPU shares that GPU's scratch: calls that overlap in
  * time on one GPU (two streams, two threads) race and must be serialised by
  * the caller.  Nothing in the scratch needs to start at any value. */
