@@ -425,7 +425,9 @@ __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int 
 // stores it as the block's row of the [gridDim.x, D] partial buffer (or as
 // dw itself for a one-block grid) for the separate combine pass; begin and
 // end do nothing.  The hook lets a measurement program run the very same
-// row kernel with other ways of finishing the reduction.
+// row kernel with other ways of finishing the reduction (its store serves
+// blocks of one row slot; blocks of several slots store their joined row
+// directly).
 struct PartialRowOut {
     __device__ __forceinline__ static void begin(const RowArgs&) {}
     template <int NV>
@@ -459,6 +461,12 @@ __global__ __launch_bounds__(!PIPE ? (OVL ? max_block_threads_ovl(2, K, NV, size
     static_assert(!OVL || (!PIPE && LANES == 0), "overlapped rows run in the plain row loop");
     extern __shared__ float dyn[];
     __shared__ float red[2 * 16 * 2];
+    // Instances whose blocks hold exactly one row (the lane count fixes it)
+    // never see a ragged group and compile without the masked copy of the
+    // processing, which would cost the tightest of them registers, nor with
+    // the join of several row slots' dw.
+    constexpr bool kOneRow =
+        LANES > 0 && (wave_rows(LANES) ? wave_rows_block_max(LANES, K * NV) == LANES : LANES >= kVjpPipeBlock);
     DwOut::begin(a);
     const int lanes = LANES > 0 ? LANES : a.lanes;
     const RowSlot rs = row_slot<LANES>(a.lshift);
@@ -504,12 +512,6 @@ __global__ __launch_bounds__(!PIPE ? (OVL ? max_block_threads_ovl(2, K, NV, size
                 MODE == kResGrad &&
                 (((LANES == 576 || LANES == 704 || LANES == 768) && K * NV == kVjpPipeElems) ||
                  K * NV > kVjpPipeElems);
-            // Instances whose blocks hold exactly one row (the lane count
-            // fixes it) never see a ragged group and compile without the
-            // masked copy of the processing, which would cost the tightest
-            // of them registers.
-            constexpr bool kOneRow =
-                LANES > 0 && (wave_rows(LANES) ? wave_rows_block_max(LANES, K * NV) == LANES : LANES >= kVjpPipeBlock);
             Raw<T, NV> pw[K];
             issue_w<T, NV, K>(static_cast<const T*>(a.w), c, pw);
             VjpRow<T, NV, K> ra, rb;
@@ -578,32 +580,47 @@ __global__ __launch_bounds__(!PIPE ? (OVL ? max_block_threads_ovl(2, K, NV, size
         }
     }
 
-    // Join the row slots' accumulators (fixed tree order) and write this
-    // block's dw row.  A block without rows writes zeros.
+    // Join the row slots' accumulators and write this block's dw row (a
+    // block without rows writes zeros).  One slot: the lanes store their
+    // vectors (through DwOut).  Several: every slot's accumulators go to LDS,
+    // then thread t adds columns t, t + blockDim.x, ... of the vector group
+    // over the slots in slot order and stores them -- two barriers per
+    // vector group whatever the slot count (a pairwise tree took log2(slots)
+    // + 2: five rounds at 32 one-vector-group rows per block).
     float* dst = (gridDim.x == 1) ? a.dw : a.partial + (int64_t)blockIdx.x * a.D;
     const bool vec_ok = (reinterpret_cast<uintptr_t>(dst) % (NV * sizeof(float))) == 0;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        if (nslots > 1) {
-            float* mine = dyn + (int64_t)threadIdx.x * NV;
+        if (!kOneRow && nslots > 1) {
+            float* mine = dyn + (int64_t)threadIdx.x * NV;  // slot * lanes + lane
 #pragma unroll
             for (int e = 0; e < NV; ++e) mine[e] = acc[k][e];
             lds_barrier();
-            for (int s = nslots >> 1; s >= 1; s >>= 1) {
-                if (slot < s) {
-                    const float* other = mine + (int64_t)s * lanes * NV;
-#pragma unroll
-                    for (int e = 0; e < NV; ++e) mine[e] += other[e];
+            const int cols = lanes * NV;
+            for (int j = threadIdx.x; j < cols; j += blockDim.x) {
+                float sum = dyn[j];
+                for (int sl = 1; sl < nslots; ++sl) sum += dyn[(int64_t)sl * cols + j];
+                const int l = j / NV;
+                const int e = j - l * NV;
+                const int v = k * lanes + l;
+                if (v < a.nvec) {
+                    const int64_t o = (int64_t)v * NV;
+                    if constexpr (OVL) {
+                        // the overlapped last vector stores only its own columns
+                        const int64_t last = static_cast<int64_t>(a.D) - NV;
+                        if (o <= last)
+                            dst[o + e] = sum;
+                        else if (e >= o - last)
+                            dst[last + e] = sum;
+                    } else {
+                        dst[o + e] = sum;
+                    }
                 }
-                lds_barrier();
             }
-            if (slot == 0) {
-#pragma unroll
-                for (int e = 0; e < NV; ++e) acc[k][e] = mine[e];
-            }
-            lds_barrier();
+            lds_barrier();  // before the next vector group reuses the LDS
+        } else if (c.ok[k]) {
+            store_dw<DwOut, NV>(dst + c.off[k], acc[k], vec_ok, c.skip[k]);
         }
-        if (slot == 0 && c.ok[k]) store_dw<DwOut, NV>(dst + c.off[k], acc[k], vec_ok, c.skip[k]);
     }
     DwOut::end(a);
 }
