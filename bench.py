@@ -520,6 +520,77 @@ def sweep_bench(R, I, dev, args) -> int:
     return 0
 
 
+def measure_ops(R, dev, rows, D, nsets, timed, gen, dt=torch.bfloat16) -> dict:
+    """Every RMSNorm op on [rows, D] (nsets rotating buffer sets of seeded
+    device-drawn inputs: x, residual ~ N(0, 1), dy ~ N(0, 0.01), w ~ N(0,
+    0.1); weight_bias 1, eps 1e-6): per op the plan (lanes x vectors per
+    lane, block, grid; vectors per lane -1 is the streaming kernel, -2 the
+    column split) and the algorithmic GB/s of back-to-back prepared calls."""
+    sets = []
+    for _ in range(nsets):
+        x = torch.empty(rows, D, dtype=dt, device=dev).normal_(generator=gen)
+        sets.append(dict(x=x, res=torch.empty_like(x).normal_(generator=gen),
+                         dy=torch.empty_like(x).normal_(0.0, 0.01, generator=gen),
+                         o1=torch.empty_like(x), o2=torch.empty_like(x)))
+    w = torch.empty(D, dtype=dt, device=dev).normal_(0.0, 0.1, generator=gen)
+    dw = torch.empty(D, dtype=torch.float32, device=dev)
+    ws = R.workspace_for(rows, D, dt, dev)
+    el = rows * D * sets[0]["x"].element_size()
+    ops = {
+        "fwd": (0, 2, [R.prepared_fwd(t["x"], w, t["o1"], 1e-6, 1.0) for t in sets]),
+        "fused_fwd": (1, 4, [R.prepared_fused(t["x"], t["res"], w, t["o1"], t["o2"], 1e-6, 1.0) for t in sets]),
+        "vjp": (2, 3, [R.prepared_vjp(t["x"], w, t["dy"], t["o1"], dw, ws, 1e-6, 1.0) for t in sets]),
+        "grad": (3, 4, [R.prepared_grad(t["x"], w, t["dy"], t["o2"], t["o1"], dw, ws, 1e-6, 1.0) for t in sets]),
+        "fused_bwd": (4, 4, [R.prepared_fused_vjp(t["x"], w, t["dy"], t["res"], t["o1"], dw, ws, 1e-6, 1.0)
+                             for t in sets]),
+    }
+    row = {"D": D, "rows": rows}
+    for name, (op, tensors, calls) in ops.items():
+        us = timed(calls)
+        q = R.query_config(op, rows, D, dt)
+        row[name] = {"us": round(us, 2), "GBps": round((tensors * el + 2 * D) / (us * 1e-6) / 1e9, 1),
+                     "plan": f"{q['lanes_per_row']}x{q['vecs_per_lane']} b{q['block_threads']} g{q['num_blocks']}"}
+    log(f"{rows}x{D}: " + " | ".join(f"{n} {row[n]['us']} us {row[n]['GBps']} GB/s ({row[n]['plan']})" for n in ops))
+    del sets, ops
+    torch.cuda.empty_cache()
+    return row
+
+
+def wide_bench(R, dev, args) -> int:
+    """Few rows of a very wide D (bf16, four rotating buffer sets; the
+    backward forms take the column split there): every op per shape as in
+    the widths mode."""
+    stream = torch.cuda.current_stream(dev)
+    N = max(10, min(args.steps, 30))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+
+    def timed(calls):
+        for i in range(2):
+            calls[i % len(calls)]()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(N):
+            calls[i % len(calls)]()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / N
+
+    grid = [measure_ops(R, dev, rows, D, 4, timed, gen)
+            for rows, D in ((16, 1 << 20), (128, 1 << 20), (256, 1 << 20), (511, 262144), (1024, 65536),
+                            (4096, 65536))]
+    worst = min(r["vjp"]["GBps"] for r in grid)
+    print(json.dumps({
+        "metric": "achieved HBM GB/s of the RMSNorm VJP on few rows of a wide D, bf16 (value = worst shape)",
+        "value": worst, "unit": "GB/s", "n_gpus": 1, "steps": N, "warmup": 2, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "fwd, fused fwd, VJP, grad call, fused backward at bf16 [rows, D], 16..4096 rows, "
+                               "D = 65536 .. 2^20", "grid": grid},
+    }), flush=True)
+    return 0
+
+
 def widths_bench(R, dev, args) -> int:
     """Every RMSNorm op across model widths (bf16, D = 1536 .. 16384,
     rows = 2^25 / D: 64 MiB per row tensor), cold: buffer sets rotate so that
@@ -547,39 +618,10 @@ def widths_bench(R, dev, args) -> int:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / N
 
-    dt = torch.bfloat16
     grid = []
     for D in (1536, 2048, 2560, 3072, 3584, 4096, 4608, 5120, 5632, 6144, 6656, 7168, 7680, 8192, 9216, 10240, 11264,
               12288, 14336, 16384):
-        rows = (1 << 25) // D
-        sets = []
-        for _ in range(10):
-            x = torch.empty(rows, D, dtype=dt, device=dev).normal_(generator=gen)
-            sets.append(dict(x=x, res=torch.empty_like(x).normal_(generator=gen),
-                             dy=torch.empty_like(x).normal_(0.0, 0.01, generator=gen),
-                             o1=torch.empty_like(x), o2=torch.empty_like(x)))
-        w = torch.empty(D, dtype=dt, device=dev).normal_(0.0, 0.1, generator=gen)
-        dw = torch.empty(D, dtype=torch.float32, device=dev)
-        ws = R.workspace_for(rows, D, dt, dev)
-        el = rows * D * 2
-        ops = {
-            "fwd": (0, 2, [R.prepared_fwd(t["x"], w, t["o1"], 1e-6, 1.0) for t in sets]),
-            "fused_fwd": (1, 4, [R.prepared_fused(t["x"], t["res"], w, t["o1"], t["o2"], 1e-6, 1.0) for t in sets]),
-            "vjp": (2, 3, [R.prepared_vjp(t["x"], w, t["dy"], t["o1"], dw, ws, 1e-6, 1.0) for t in sets]),
-            "grad": (3, 4, [R.prepared_grad(t["x"], w, t["dy"], t["o2"], t["o1"], dw, ws, 1e-6, 1.0) for t in sets]),
-            "fused_bwd": (4, 4, [R.prepared_fused_vjp(t["x"], w, t["dy"], t["res"], t["o1"], dw, ws, 1e-6, 1.0)
-                                 for t in sets]),
-        }
-        row = {"D": D, "rows": rows}
-        for name, (op, tensors, calls) in ops.items():
-            us = timed(calls)
-            q = R.query_config(op, rows, D, dt)
-            row[name] = {"us": round(us, 2), "GBps": round((tensors * el + 2 * D) / (us * 1e-6) / 1e9, 1),
-                         "plan": f"{q['lanes_per_row']}x{q['vecs_per_lane']} b{q['block_threads']} g{q['num_blocks']}"}
-        grid.append(row)
-        log(f"D={D}: " + " | ".join(f"{n} {row[n]['us']} us {row[n]['GBps']} GB/s ({row[n]['plan']})" for n in ops))
-        del sets, ops
-        torch.cuda.empty_cache()
+        grid.append(measure_ops(R, dev, (1 << 25) // D, D, 10, timed, gen))
     worst = min(r["vjp"]["GBps"] for r in grid)
     print(json.dumps({
         "metric": "achieved HBM GB/s of the RMSNorm VJP across model widths, bf16, 64 MiB tensors (value = worst D)",
@@ -596,8 +638,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", choices=["poc", "prefill", "decode", "grad", "gate", "sweep", "widths", "ceiling",
-                                           "dwreduce"],
+    ap.add_argument("--workload", choices=["poc", "prefill", "decode", "grad", "gate", "sweep", "widths", "wide",
+                                           "ceiling", "dwreduce"],
                     default="poc")
     ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -630,6 +672,8 @@ def main() -> int:
         return sweep_bench(R, I, dev, args)
     if args.workload == "widths":
         return widths_bench(R, dev, args)
+    if args.workload == "wide":
+        return wide_bench(R, dev, args)
     fused = args.workload == "prefill"
     out = step_bench(R, I, dev, args, fused)
     if not fused:
