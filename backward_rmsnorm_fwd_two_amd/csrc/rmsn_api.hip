@@ -20,7 +20,6 @@ using rmsn::RowArgs;
 
 constexpr int kMaxDevices = 64;
 constexpr int kMaxPartialRows = 2048;   // bound on dw partial rows (workspace)
-
 // Row data a CU should hold in flight in the wave-row VJP, in units of one
 // wave's 16-byte vector of one row tensor (see make_plan).
 constexpr int kWaveRowsInFlight = 15;
@@ -207,6 +206,18 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
     const int req_l = cfg ? cfg->lanes_per_row : 0;
     const int req_b = cfg ? cfg->block_threads : 0;
     if (req_k == -2) return plan_colsplit(rows, cus, cfg->num_blocks, p);
+    // Few rows (no more than the CUs) of 64..384 whole 16-byte vectors, a
+    // multiple of 64 (D = 512..3072 in 16-bit storage; decode batches): the
+    // forward forms take one vector per lane on as many lanes as the row has
+    // vectors, one row per block.  There latency, not bandwidth, decides:
+    // 32 calls chained through a residual stream and replayed from one
+    // graph, bf16, 1..256 rows, per call: forward D = 2560 2.47 -> 1.96 us,
+    // 1536 2.26 -> 1.88, 2048 2.10 -> 1.87; fused forward D = 2048 at 8 rows
+    // 2.71 -> 2.21, 3072 at 256 rows 3.46 -> 3.01.  At 512..4096 rows the
+    // layouts ran alike, and at 512 vectors two per lane stayed ahead for
+    // the fused forward.
+    const bool few_rows_k1 = !vjp && req_k == 0 && req_l == 0 && vb == 16 && !ovl && rows <= cus &&
+                             p->nvec >= 64 && p->nvec <= 384 && p->nvec % 64 == 0;
     bool looped = req_k == -1 || (req_k == 0 && req_l == 0 && p->nvec > 1024 * 8);
     int loop_block = 1024;  // streaming kernel's default block
 
@@ -233,6 +244,7 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
             const void* fn = nullptr;
             for (int kk : {2, 1, 4}) {
                 if (fn || (k != 0 && kk != k) || p->nvec % kk != 0 || (kk == 4 && !wide_ok)) continue;
+                if (few_rows_k1 && kk != 1) continue;
                 const int l = p->nvec / kk;
                 const bool tiles = (rmsn::wave_rows(l) && rmsn::wave_rows_supported(l)) || (kk == 4 && l == 512);
                 if ((lanes != 0 && l != lanes) || !tiles) continue;
@@ -243,7 +255,7 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
                 // D = 3584 bf16 25.0 vs 24.2 us), and longer rows of the
                 // plain forward take 256 lanes x 8 (below); the fused
                 // forward keeps wave rows up to 768 lanes.
-                if (lanes == 0 && !vjp &&
+                if (lanes == 0 && !vjp && !few_rows_k1 &&
                     (kk != 2 || l > 768 || (op == RMSN_OP_FWD && p->nvec > 1024)))
                     continue;
                 fn = vjp ? rmsn::vjp_kernel_fixed_lanes(dt, p->nv, kk, vmode, l)
@@ -277,7 +289,7 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
                 if (vjp) {
                     while (slots < 4 && w_units * slots < kWaveRowsInFlight && 2 * slots * wl <= maxb)
                         slots *= 2;
-                } else if (wl == 192 && 2 * wl <= maxb) {
+                } else if (wl == 192 && 2 * wl <= maxb && !few_rows_k1) {
                     slots = 2;
                 }
                 block = slots * wl;
@@ -343,6 +355,7 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
                 else if (p->nvec > (op == RMSN_OP_FWD ? 128 : 256))
                     kt = 4;
             }
+            if (few_rows_k1) kt = 1;
             lanes = std::min(1024, next_pow2((p->nvec + kt - 1) / kt));
             k = next_pow2((p->nvec + lanes - 1) / lanes);
             // The plain forward of a row of 129..1024 vectors that this
@@ -408,7 +421,7 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
                 const bool ovl_sparse_big = ovl && (int64_t)p->nvec * 10 < (int64_t)lanes * k * 9 &&
                                             rows * D * s >= ((int64_t)24 << 20);
                 const int cap = (vjp && (vb <= 4 || ovl_sparse_big)) ? 512 : 256;
-                block = std::max(std::max(lanes, 64), std::min(cap, maxb));
+                block = few_rows_k1 ? std::max(lanes, 64) : std::max(std::max(lanes, 64), std::min(cap, maxb));
             }
             if (block < 64 || block > maxb || block % 64 != 0 || block % lanes != 0 || !is_pow2(block))
                 return RMSN_E_CONFIG;

@@ -269,8 +269,8 @@ struct RowArgs {
     int64_t rows;
     int32_t D;
     int32_t nvec;   // vectors per row: D / NV (ceil(D / NV), the last overlapped)
-    int32_t lanes;  // lanes per row (power of two)
-    int32_t lshift; // log2(lanes)
+    int32_t lanes;  // lanes per row: a power of two, or 64 W for wave rows (lanes fixed at compile time)
+    int32_t lshift; // log2(lanes) when lanes is a power of two
     float eps;
     float wb;
 };

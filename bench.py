@@ -283,12 +283,67 @@ def grad_bench(R, I, dev, args) -> int:
     return 0
 
 
+def decode_layers_graph(R, dev, x, res0, w, eps, wb, fused: bool, layers: int = 32, reps: int = 50):
+    """A decoder's residual stream through `layers` norms, captured in one HIP
+    graph: layer i adds its sublayer output x to the running residual and
+    normalises the sum (fused: one call; unfused: torch add, then
+    rmsnorm_fwd), and its new_residual is layer i+1's residual.  Returns the
+    per-call time of graph replays (us) -- the GPU-side latency with the host
+    launch path taken out, as a decode loop captured once and replayed per
+    token runs -- after checking a replay against the same chain run eagerly,
+    bit for bit."""
+    newres = [torch.empty_like(x) for _ in range(layers)]
+    normed = [torch.empty_like(x) for _ in range(layers)]
+
+    def chain():
+        r = res0
+        for i in range(layers):
+            if fused:
+                R.fused_add_rmsnorm_fwd(x, r, w, eps, wb, normed=normed[i], new_residual=newres[i])
+            else:
+                torch.add(x, r, out=newres[i])
+                R.rmsnorm_fwd(newres[i], w, eps, wb, out=normed[i])
+            r = newres[i]
+
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        chain()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        chain()
+    torch.cuda.synchronize()
+    for t in normed + newres:
+        t.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    got = (normed[-1].clone(), newres[-1].clone())
+    chain()
+    torch.cuda.synchronize()
+    if not (torch.equal(got[0], normed[-1]) and torch.equal(got[1], newres[-1])):
+        raise RuntimeError("graph replay differs from the eager chain")
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * layers)
+
+
 def decode_bench(R, I, dev, args) -> int:
     """Decode-shaped fused add+RMSNorm: latency per call, fused (one launch)
     against the unfused composition (torch add, then rmsnorm_fwd) over the
     (batch, hidden) grid of the fused-kernel microbenchmark; bf16, eps 1e-6,
     weight_bias 0 and 1.  Per-call time = events around N back-to-back calls
-    / N (launch-bound: the host path is part of the latency)."""
+    / N (launch-bound: the host path is part of the latency); and the same
+    calls chained through a 32-layer residual stream and replayed from one
+    HIP graph (`decode_layers_graph`)."""
     N = max(args.steps, 100)
     rows = []
     for wb in (0.0, 1.0):
@@ -317,15 +372,23 @@ def decode_bench(R, I, dev, args) -> int:
                     e1.record()
                     torch.cuda.synchronize()
                     out[name] = e0.elapsed_time(e1) * 1e3 / N
+                gf = decode_layers_graph(R, dev, x, res, w, c["eps"], wb, fused=True)
+                gu = decode_layers_graph(R, dev, x, res, w, c["eps"], wb, fused=False)
                 rows.append({"B": B, "H": H, "weight_bias": wb, "fused_us": round(out["fused"], 3),
                              "unfused_us": round(out["unfused"], 3),
-                             "speedup": round(out["unfused"] / out["fused"], 3)})
-                log(f"decode B={B} H={H} wb={wb}: fused {out['fused']:.2f} us, unfused {out['unfused']:.2f} us")
+                             "speedup": round(out["unfused"] / out["fused"], 3),
+                             "graph_fused_us": round(gf, 3), "graph_unfused_us": round(gu, 3),
+                             "graph_speedup": round(gu / gf, 3)})
+                log(f"decode B={B} H={H} wb={wb}: fused {out['fused']:.2f} us, unfused {out['unfused']:.2f} us; "
+                    f"32-layer graph: fused {gf:.2f} us, unfused {gu:.2f} us per layer")
     mean_fused = float(np.mean([r["fused_us"] for r in rows]))
+    mean_graph = float(np.mean([r["graph_fused_us"] for r in rows]))
+    mean_graph_unfused = float(np.mean([r["graph_unfused_us"] for r in rows]))
     print(json.dumps({
         "metric": "fused add+RMSNorm decode latency per call (bf16)", "value": round(mean_fused, 3),
         "unit": "us", "n_gpus": 1, "steps": N, "warmup": 20, "higher_is_better": False,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "graph_fused_us": round(mean_graph, 3), "graph_unfused_us": round(mean_graph_unfused, 3),
         "config": {"workload": "decode fused add+RMSNorm, B in {1,4,8} x H in {2048,4096,8192}, "
                                "weight_bias in {0,1}", "grid": rows},
     }), flush=True)

@@ -8,7 +8,9 @@ every row, plus the same rows forced through the register kernel.  Rows of a who
 rows) with two 16-byte vectors per lane take an exact-tiling instance of
 up to 768 lanes (two three-wave rows per block); its plan, parity of the
 forward and the fused forward, forced one-vector and 896-lane instances,
-and outputs bit-identical across rows per block."""
+and outputs bit-identical across rows per block.  Few rows (at most one per
+CU) of 64..384 16-byte vectors in a multiple of 64 take one vector per lane,
+one row per block, in both forward forms."""
 import sys
 
 import numpy as np
@@ -144,3 +146,56 @@ def test_sparse_short_forward_rows(R, rows, D, dtype, plan):
     torch.cuda.synchronize()
     yref, _ = O.rmsnorm_fwd(c["x"], c["w"], c["eps"], 1.0)
     assert_close(y, yref, "y")
+
+
+# Few rows (at most one per CU) of 64..384 whole 16-byte vectors, a multiple
+# of 64: both forward forms take one vector per lane on as many lanes as the
+# row has vectors, one row per block (decode batches are latency-bound).
+FEW = [(1, 2048, "bfloat16"), (8, 512, "float16"), (4, 1536, "bfloat16"), (64, 2560, "float16"),
+       (8, 3072, "bfloat16"), (3, 1024, "float32"), (17, 768, "float32"), (5, 1536, "float32")]
+
+
+def _cus():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+@pytest.mark.parametrize("rows,D,dtype", FEW)
+def test_few_rows_one_vector_per_lane(R, rows, D, dtype):
+    print(f"few-row forward rows={rows} D={D} {dtype}", flush=True)
+    sys.stdout.flush()
+    td = I.torch_dtype(dtype)
+    nvec = D * td.itemsize // 16
+    for op in (0, 1):
+        q = R.query_config(op, rows, D, td)
+        assert (q["lanes_per_row"], q["vecs_per_lane"], q["vec_bytes"]) == (nvec, 1, 16), (op, q)
+        assert q["block_threads"] == max(nvec, 64) and q["num_blocks"] == rows, (op, q)
+        # more rows than CUs: the bandwidth layouts (two or four vectors per lane)
+        qb = R.query_config(op, _cus() + 1, D, td)
+        assert qb["vecs_per_lane"] in (2, 4), (op, qb)
+    c = I.generic(rows, D, dtype, seed=rows + 7 * D)
+    x, res, w = c["x"].to(DEV), c["residual"].to(DEV), c["w"].to(DEV)
+    for wb in (0.0, 1.0):
+        y = R.rmsnorm_fwd(x, w, c["eps"], wb)
+        n, h = R.fused_add_rmsnorm_fwd(x, res, w, c["eps"], wb)
+        torch.cuda.synchronize()
+        assert_close(y, O.rmsnorm_fwd(c["x"], c["w"], c["eps"], wb)[0], f"y wb={wb}")
+        nref, href = O.fused_add_rmsnorm_fwd(c["x"], c["residual"], c["w"], c["eps"], wb)
+        assert_close(n, nref, f"normed wb={wb}")
+        np.testing.assert_array_equal(to64(h), O.round_to(href, dtype), f"new_residual wb={wb}")
+
+
+def test_few_rows_rule_limits(R):
+    """Outside the rule the plans are the bandwidth ones: at the CU count
+    plus one, at 512 vectors, at 32 vectors, for a count that is not a
+    multiple of 64, and for the backward forms."""
+    cus = _cus()
+    bf = torch.bfloat16
+    assert R.query_config(1, cus, 2048, bf)["vecs_per_lane"] == 1
+    assert R.query_config(1, cus + 1, 2048, bf)["vecs_per_lane"] == 2
+    assert R.query_config(0, 8, 4096, bf)["vecs_per_lane"] == 2          # 512 vectors
+    q = R.query_config(0, 8, 256, bf)                                     # 32 vectors
+    assert (q["lanes_per_row"], q["vecs_per_lane"], q["block_threads"]) == (16, 2, 256), q
+    q = R.query_config(1, 8, 1280, bf)                                    # 160 vectors
+    assert (q["lanes_per_row"], q["vecs_per_lane"]) == (128, 2), q
+    for op in (2, 3, 4):
+        assert R.query_config(op, 8, 2048, bf)["vecs_per_lane"] == 2
