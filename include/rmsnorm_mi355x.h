@@ -281,7 +281,9 @@ int silu_gate_vjp_cfg(const void *x, const void *dy, void *dx, int64_t rows, int
 /* Fill *out with the configuration the automatic choice makes for `op` on
  * this shape.  `align_bytes` (a power of two: the alignment of the
  * pointers) is validated but does not change the choice, which depends on
- * the shape only.  Returns RMSN_OK or an argument error.  For the backward forms
+ * the shape, the dtype and the current device's compute-unit count only
+ * (persistent grids; forward calls on no more rows than compute units take
+ * one row per block).  Returns RMSN_OK or an argument error.  For the backward forms
  * the library additionally picks, per call, between two row loops of the same
  * geometry and arithmetic: a software-pipelined one (rows of exactly
  * lanes_per_row * vecs_per_lane vectors; power-of-two rows in blocks of at
