@@ -215,8 +215,9 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
     // 1536 2.26 -> 1.88, 2048 2.10 -> 1.87; fused forward D = 2048 at 8 rows
     // 2.71 -> 2.21, 3072 at 256 rows 3.46 -> 3.01.  At 512..4096 rows the
     // layouts ran alike, and at 512 vectors two per lane stayed ahead for
-    // the fused forward.
-    const bool few_rows_k1 = !vjp && req_k == 0 && req_l == 0 && vb == 16 && !ovl && rows <= cus &&
+    // the fused forward.  Only when the whole geometry is automatic: a
+    // requested block size keeps the bandwidth layouts it fits.
+    const bool few_rows_k1 = !vjp && req_k == 0 && req_l == 0 && req_b == 0 && vb == 16 && !ovl && rows <= cus &&
                              p->nvec >= 64 && p->nvec <= 384 && p->nvec % 64 == 0;
     bool looped = req_k == -1 || (req_k == 0 && req_l == 0 && p->nvec > 1024 * 8);
     int loop_block = 1024;  // streaming kernel's default block

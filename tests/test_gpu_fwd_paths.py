@@ -199,3 +199,22 @@ def test_few_rows_rule_limits(R):
     assert (q["lanes_per_row"], q["vecs_per_lane"]) == (128, 2), q
     for op in (2, 3, 4):
         assert R.query_config(op, 8, 2048, bf)["vecs_per_lane"] == 2
+
+
+@pytest.mark.parametrize("D,block", [(3072, 256), (2048, 128)])
+def test_few_rows_with_a_requested_block(R, D, block):
+    """A configuration that fixes only the block size keeps the layout that
+    block fits (the few-rows rule applies to a fully automatic geometry)."""
+    rows = 4
+    c = I.generic(rows, D, "bfloat16", seed=D + block)
+    x, res, w = c["x"].to(DEV), c["residual"].to(DEV), c["w"].to(DEV)
+    cfg = dict(block_threads=block)
+    y = R.rmsnorm_fwd(x, w, c["eps"], 1.0, cfg=cfg)
+    n, h = R.fused_add_rmsnorm_fwd(x, res, w, c["eps"], 1.0, cfg=cfg)
+    torch.cuda.synchronize()
+    assert_close(y, O.rmsnorm_fwd(c["x"], c["w"], c["eps"], 1.0)[0], "y")
+    nref, href = O.fused_add_rmsnorm_fwd(c["x"], c["residual"], c["w"], c["eps"], 1.0)
+    assert_close(n, nref, "normed")
+    np.testing.assert_array_equal(to64(h), O.round_to(href, "bfloat16"), "new_residual")
+    # the automatic plan of the same shape is the few-rows one
+    assert R.query_config(0, rows, D, torch.bfloat16)["vecs_per_lane"] == 1
