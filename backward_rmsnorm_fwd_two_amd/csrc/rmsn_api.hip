@@ -107,6 +107,7 @@ struct Plan {
     bool pipe = false;        // backward forms: the software-pipelined row kernel
     bool fixed_lanes = false; // ... in an instance with the lanes fixed at compile time
     bool ovl = false;         // rows of ceil(D / nv) vectors, the last one overlapped
+    bool fwd_generic = false; // forward forms: the runtime-width kernel although a fixed-width one exists
     // column-split backward (k == -2): statistics slices per row, column
     // tiles, rows per chunk (grid = chunks), workspace bytes of the row
     // statistics (ahead of the dw partial rows)
@@ -448,6 +449,13 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
             p->lanes = lanes;
             p->k = k;
             p->block = block;
+            // The fused forward on rows of 512 or 1024 lanes takes the instance
+            // with the lanes fixed at compile time on no more rows than CUs
+            // (bf16, per call: D = 8192 at 1..8 rows 2.92-3.08 -> 2.52-2.69 us;
+            // D = 16384 at 8..256 rows 2-8 % faster) and the runtime-width
+            // kernel beyond (D = 16384 at 1024 / 4096 rows 0.9 / 2.9 us slower
+            // fixed; 32768 x 8192 355 vs 351 us).
+            p->fwd_generic = op == RMSN_OP_FUSED && lanes >= 512 && rows > cus;
             const int nslots = block / lanes;
             const int64_t groups = (rows + nslots - 1) / nslots;
             // Backward forms: the software-pipelined kernel stores
@@ -633,7 +641,7 @@ int fwd_impl(bool fused, const void* x, const void* res, const void* w, void* y,
     if (p.ovl) {
         fn = rmsn::fwd_kernel_ovl(dt, p.k, fused);
     } else {
-        fn = p.k > 0 ? rmsn::fwd_kernel_fixed_lanes(dt, p.nv, p.k, fused, p.lanes) : nullptr;
+        fn = p.k > 0 && !p.fwd_generic ? rmsn::fwd_kernel_fixed_lanes(dt, p.nv, p.k, fused, p.lanes) : nullptr;
         if (!fn && !(p.k > 0 && rmsn::wave_rows(p.lanes))) fn = rmsn::fwd_kernel(dt, p.nv, p.k, fused);
     }
     if (!fn) return RMSN_E_CONFIG;

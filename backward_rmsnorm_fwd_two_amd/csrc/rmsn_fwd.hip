@@ -40,10 +40,11 @@ const void* pick_fwd_dt(int dt, int nv, int k) {
 }
 
 // 16-byte loads, one or two vectors per lane: the instance with the lanes
-// fixed at compile time -- 32 to 1024 lanes per row for the forward, 32 to
-// 256 for the fused forward (measured on cold data: forward 0.8-3 % faster
-// at every width, e.g. 8192 x 4096 fp16 24.4 vs 25.3 us; fused forward 4 %
-// faster up to 256 lanes, 1-2 % slower at 512 and 1024)
+// fixed at compile time, 32 to 1024 lanes per row (measured on cold data:
+// forward 0.8-3 % faster at every width, e.g. 8192 x 4096 fp16 24.4 vs 25.3
+// us; fused forward 4 % faster up to 256 lanes; at 512 and 1024 lanes the
+// fused forward takes it only on few rows, where it is faster, and the
+// runtime-width kernel on many -- the plan decides)
 template <typename T, int K, bool FUSED>
 const void* pick_fixed(int lanes) {
     constexpr int NV = 16 / static_cast<int>(sizeof(T));
@@ -53,6 +54,8 @@ const void* pick_fixed(int lanes) {
             case 64: return reinterpret_cast<const void*>(&fwd_rows<T, NV, K, FUSED, 64>);
             case 128: return reinterpret_cast<const void*>(&fwd_rows<T, NV, K, FUSED, 128>);
             case 256: return reinterpret_cast<const void*>(&fwd_rows<T, NV, K, FUSED, 256>);
+            case 512: return reinterpret_cast<const void*>(&fwd_rows<T, NV, K, FUSED, 512>);
+            case 1024: return reinterpret_cast<const void*>(&fwd_rows<T, NV, K, FUSED, 1024>);
             default: return nullptr;
         }
     }

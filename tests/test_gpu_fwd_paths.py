@@ -218,3 +218,27 @@ def test_few_rows_with_a_requested_block(R, D, block):
     np.testing.assert_array_equal(to64(h), O.round_to(href, "bfloat16"), "new_residual")
     # the automatic plan of the same shape is the few-rows one
     assert R.query_config(0, rows, D, torch.bfloat16)["vecs_per_lane"] == 1
+
+
+@pytest.mark.parametrize("D,dtype", [(8192, "bfloat16"), (8192, "float16"), (16384, "bfloat16"), (4096, "float32"),
+                                     (8192, "float32")])
+def test_few_rows_wide_fused_fixed_width_matches_runtime_width(R, D, dtype):
+    """The fused forward of 512- and 1024-lane rows runs the instance with the
+    lanes fixed at compile time on no more rows than CUs, the runtime-width
+    kernel on more: the same lanes, vectors and reduction order, so a row
+    comes out bit for bit the same either way."""
+    few, many = 5, _cus() + 45
+    c = I.generic(many, D, dtype, seed=D + few)
+    td = I.torch_dtype(dtype)
+    nvec = D * td.itemsize // 16
+    for rows in (few, many):
+        q = R.query_config(1, rows, D, td)
+        assert q["lanes_per_row"] * q["vecs_per_lane"] == nvec and q["lanes_per_row"] >= 512, q
+    x, res, w = c["x"].to(DEV), c["residual"].to(DEV), c["w"].to(DEV)
+    n_few, h_few = R.fused_add_rmsnorm_fwd(x[:few].contiguous(), res[:few].contiguous(), w, c["eps"], 1.0)
+    n_many, h_many = R.fused_add_rmsnorm_fwd(x, res, w, c["eps"], 1.0)
+    torch.cuda.synchronize()
+    nref, href = O.fused_add_rmsnorm_fwd(c["x"][:few], c["residual"][:few], c["w"], c["eps"], 1.0)
+    assert_close(n_few, nref, "normed (few rows)")
+    np.testing.assert_array_equal(to64(h_few), O.round_to(href, dtype), "new_residual (few rows)")
+    assert torch.equal(n_few, n_many[:few]) and torch.equal(h_few, h_many[:few])
