@@ -207,19 +207,20 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
     const int req_l = cfg ? cfg->lanes_per_row : 0;
     const int req_b = cfg ? cfg->block_threads : 0;
     if (req_k == -2) return plan_colsplit(rows, cus, cfg->num_blocks, p);
-    // Few rows (no more than the CUs) of 64..384 whole 16-byte vectors, a
-    // multiple of 64 (D = 512..3072 in 16-bit storage; decode batches): the
+    // Few rows (no more than the CUs) of 64..768 whole 16-byte vectors, a
+    // multiple of 64 (D = 512..6144 in 16-bit storage; decode batches): the
     // forward forms take one vector per lane on as many lanes as the row has
-    // vectors, one row per block.  There latency, not bandwidth, decides:
-    // 32 calls chained through a residual stream and replayed from one
-    // graph, bf16, 1..256 rows, per call: forward D = 2560 2.47 -> 1.96 us,
-    // 1536 2.26 -> 1.88, 2048 2.10 -> 1.87; fused forward D = 2048 at 8 rows
-    // 2.71 -> 2.21, 3072 at 256 rows 3.46 -> 3.01.  At 512..4096 rows the
-    // layouts ran alike, and at 512 vectors two per lane stayed ahead for
-    // the fused forward.  Only when the whole geometry is automatic: a
-    // requested block size keeps the bandwidth layouts it fits.
+    // vectors (a fixed-width power-of-two or wave-row instance), one row per
+    // block.  There latency, not bandwidth, decides: 32 calls chained
+    // through a residual stream and replayed from one graph, bf16, 1..256
+    // rows, per call: forward D = 2560 2.47 -> 1.96 us, 3584 2.57 -> 1.99,
+    // 4608 2.51 -> 2.08, 6144 2.22 -> 2.14; fused forward D = 2048 at 8 rows
+    // 2.71 -> 2.21, 4096 2.31 -> 2.12, 4608 2.38 -> 2.24, 6144 2.43 -> 2.31.
+    // At 1024 vectors the two layouts ran alike, and at 512..4096 rows too
+    // (warm).  Only when the whole geometry is automatic: a requested block
+    // size keeps the bandwidth layouts it fits.
     const bool few_rows_k1 = !vjp && req_k == 0 && req_l == 0 && req_b == 0 && vb == 16 && !ovl && rows <= cus &&
-                             p->nvec >= 64 && p->nvec <= 384 && p->nvec % 64 == 0;
+                             p->nvec >= 64 && p->nvec <= 768 && p->nvec % 64 == 0;
     bool looped = req_k == -1 || (req_k == 0 && req_l == 0 && p->nvec > 1024 * 8);
     int loop_block = 1024;  // streaming kernel's default block
 

@@ -9,7 +9,7 @@ rows) with two 16-byte vectors per lane take an exact-tiling instance of
 up to 768 lanes (two three-wave rows per block); its plan, parity of the
 forward and the fused forward, forced one-vector and 896-lane instances,
 and outputs bit-identical across rows per block.  Few rows (at most one per
-CU) of 64..384 16-byte vectors in a multiple of 64 take one vector per lane,
+CU) of 64..768 16-byte vectors in a multiple of 64 take one vector per lane,
 one row per block, in both forward forms."""
 import sys
 
@@ -148,11 +148,13 @@ def test_sparse_short_forward_rows(R, rows, D, dtype, plan):
     assert_close(y, yref, "y")
 
 
-# Few rows (at most one per CU) of 64..384 whole 16-byte vectors, a multiple
+# Few rows (at most one per CU) of 64..768 whole 16-byte vectors, a multiple
 # of 64: both forward forms take one vector per lane on as many lanes as the
 # row has vectors, one row per block (decode batches are latency-bound).
 FEW = [(1, 2048, "bfloat16"), (8, 512, "float16"), (4, 1536, "bfloat16"), (64, 2560, "float16"),
-       (8, 3072, "bfloat16"), (3, 1024, "float32"), (17, 768, "float32"), (5, 1536, "float32")]
+       (8, 3072, "bfloat16"), (3, 1024, "float32"), (17, 768, "float32"), (5, 1536, "float32"),
+       (2, 3584, "float16"), (1, 4096, "bfloat16"), (7, 4608, "bfloat16"), (3, 5120, "float16"),
+       (4, 5632, "bfloat16"), (8, 6144, "bfloat16"), (2, 2048, "float32"), (6, 3072, "float32")]
 
 
 def _cus():
@@ -186,13 +188,14 @@ def test_few_rows_one_vector_per_lane(R, rows, D, dtype):
 
 def test_few_rows_rule_limits(R):
     """Outside the rule the plans are the bandwidth ones: at the CU count
-    plus one, at 512 vectors, at 32 vectors, for a count that is not a
+    plus one, at 1024 vectors, at 32 vectors, for a count that is not a
     multiple of 64, and for the backward forms."""
     cus = _cus()
     bf = torch.bfloat16
     assert R.query_config(1, cus, 2048, bf)["vecs_per_lane"] == 1
     assert R.query_config(1, cus + 1, 2048, bf)["vecs_per_lane"] == 2
-    assert R.query_config(0, 8, 4096, bf)["vecs_per_lane"] == 2          # 512 vectors
+    assert R.query_config(0, 8, 8192, bf)["vecs_per_lane"] == 2          # 1024 vectors
+    assert R.query_config(1, 8, 8192, bf)["vecs_per_lane"] == 2
     q = R.query_config(0, 8, 256, bf)                                     # 32 vectors
     assert (q["lanes_per_row"], q["vecs_per_lane"], q["block_threads"]) == (16, 2, 256), q
     q = R.query_config(1, 8, 1280, bf)                                    # 160 vectors

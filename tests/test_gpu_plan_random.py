@@ -6,7 +6,7 @@ the lanes and vectors, blocks are whole waves holding whole row slots, the
 persistent backward grids never hold one dw partial row per row and stay
 within the partial-row bound, the VJP workspace is smaller than a [rows, D]
 fp32 temporary (beyond its 256-byte floor), and forward calls on no more
-rows than compute units take one row per block on 64..384 whole 16-byte
+rows than compute units take one row per block on 64..768 whole 16-byte
 vectors.  Then 40
 random shapes (up to ~1.5 M elements) run through every form and are
 compared with the fp64 oracle on every element."""
@@ -85,7 +85,7 @@ def test_plan_invariants_random_shapes(R):
                     assert nb <= (rows + 1) // 2, (what, q)
                     ws = R.rmsnorm_vjp_workspace_bytes(rows, D, td)
                     assert ws == 256 or ws < rows * D * 4, (what, q, ws)    # 256: the size floor
-            elif rows <= cus and D * s % 16 == 0 and 64 <= D * s // 16 <= 384 and (D * s // 16) % 64 == 0:
+            elif rows <= cus and D * s % 16 == 0 and 64 <= D * s // 16 <= 768 and (D * s // 16) % 64 == 0:
                 assert (lanes, k, vb, block, nb) == (D * s // 16, 1, 16, max(D * s // 16, 64), rows), (what, q)
             checked += 1
     _say(f"plan invariants: {checked} plans")
