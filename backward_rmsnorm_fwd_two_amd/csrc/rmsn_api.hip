@@ -221,6 +221,23 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
     // size keeps the bandwidth layouts it fits.
     const bool few_rows_k1 = !vjp && req_k == 0 && req_l == 0 && req_b == 0 && vb == 16 && !ovl && rows <= cus &&
                              p->nvec >= 64 && p->nvec <= 768 && p->nvec % 64 == 0;
+    // The backward forms on rows that all fit one block with one 16-byte
+    // vector per lane on at most 512 lanes (next_pow2(vectors) x
+    // next_pow2(rows) <= 1024: a single row up to 4096 elements in 16-bit
+    // storage, 64 rows of D = 128):
+    // one vector per lane, the block sized to the rows, one block and so no
+    // combine launch.  The default block holds up to 32 row slots whatever
+    // the row count, and the empty slots still take part in the dw join:
+    // fp16, 32 calls replayed from one graph, per call, one row: D = 128
+    // 3.90 -> 2.52 us, 512 3.21 -> 1.91, 1024 3.32 -> 2.01, 2048 3.62 ->
+    // 2.26, 4096 3.93 -> 2.50; D = 128 at 64 rows 4.74 -> 3.72, 512 at 8
+    // rows 3.27 -> 2.86, 1024 at 2 rows 3.40 -> 2.72 (at 4..8 rows of 1024
+    // and 2..4 of 2048 the layouts ran alike; where the rows do not fit one
+    // block, more blocks and a combine ran faster).  Rows with an overlapped
+    // last vector too, within the 512 threads their instances are built for.
+    const bool few_rows_vjp = vjp && req_k == 0 && req_l == 0 && req_b == 0 && vb == 16 && rows >= 1 &&
+                              rows <= 1024 && p->nvec <= 512 &&
+                              (int64_t)next_pow2(p->nvec) * next_pow2(rows) <= (ovl ? 512 : 1024);
     bool looped = req_k == -1 || (req_k == 0 && req_l == 0 && p->nvec > 1024 * 8);
     int loop_block = 1024;  // streaming kernel's default block
 
@@ -247,7 +264,7 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
             const void* fn = nullptr;
             for (int kk : {2, 1, 4}) {
                 if (fn || (k != 0 && kk != k) || p->nvec % kk != 0 || (kk == 4 && !wide_ok)) continue;
-                if (few_rows_k1 && kk != 1) continue;
+                if ((few_rows_k1 || few_rows_vjp) && kk != 1) continue;
                 const int l = p->nvec / kk;
                 const bool tiles = (rmsn::wave_rows(l) && rmsn::wave_rows_supported(l)) || (kk == 4 && l == 512);
                 if ((lanes != 0 && l != lanes) || !tiles) continue;
@@ -289,7 +306,9 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
             int block = req_b;
             if (fn && !block) {
                 int slots = 1;
-                if (vjp) {
+                if (few_rows_vjp) {
+                    slots = next_pow2(rows);  // <= 4 here: wl >= 192
+                } else if (vjp) {
                     while (slots < 4 && w_units * slots < kWaveRowsInFlight && 2 * slots * wl <= maxb)
                         slots *= 2;
                 } else if (wl == 192 && 2 * wl <= maxb && !few_rows_k1) {
@@ -358,7 +377,7 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
                 else if (p->nvec > (op == RMSN_OP_FWD ? 128 : 256))
                     kt = 4;
             }
-            if (few_rows_k1) kt = 1;
+            if (few_rows_k1 || few_rows_vjp) kt = 1;
             lanes = std::min(1024, next_pow2((p->nvec + kt - 1) / kt));
             k = next_pow2((p->nvec + lanes - 1) / lanes);
             // The plain forward of a row of 129..1024 vectors that this
@@ -424,7 +443,9 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
                 const bool ovl_sparse_big = ovl && (int64_t)p->nvec * 10 < (int64_t)lanes * k * 9 &&
                                             rows * D * s >= ((int64_t)24 << 20);
                 const int cap = (vjp && (vb <= 4 || ovl_sparse_big)) ? 512 : 256;
-                block = few_rows_k1 ? std::max(lanes, 64) : std::max(std::max(lanes, 64), std::min(cap, maxb));
+                block = few_rows_k1    ? std::max(lanes, 64)
+                        : few_rows_vjp ? std::max(64, lanes * next_pow2(rows))
+                                       : std::max(std::max(lanes, 64), std::min(cap, maxb));
             }
             if (block < 64 || block > maxb || block % 64 != 0 || block % lanes != 0 || !is_pow2(block))
                 return RMSN_E_CONFIG;

@@ -50,6 +50,13 @@ def _shape(rng):
     return max(1, rows), max(1, D)
 
 
+def _np2(n):
+    p = 1
+    while p < n:
+        p *= 2
+    return p
+
+
 def test_plan_invariants_random_shapes(R):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     rng = np.random.default_rng(20261202)
@@ -80,6 +87,12 @@ def test_plan_invariants_random_shapes(R):
                 assert k == -2 and op >= 2 and block == 256 and rows <= 65535, (what, q)
             if op >= 2:
                 assert nb <= 2048, (what, q)
+                nvec16 = D * s // 16
+                if (D * s % 16 == 0 and rows <= 1024 and 1 <= nvec16 <= 512 and
+                        _np2(nvec16) * _np2(rows) <= 1024):
+                    # all rows in one block, one vector per lane
+                    assert k == 1 and vb == 16 and nb == 1 and lanes in (nvec16, _np2(nvec16)), (what, q)
+                    assert block == max(64, lanes * _np2(rows)), (what, q)
                 if rows >= 2:
                     # never one dw partial row per row (the [rows, D] temporary)
                     assert nb <= (rows + 1) // 2, (what, q)

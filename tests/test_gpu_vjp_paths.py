@@ -10,7 +10,10 @@ the loop's exit path) and dw over all rows; dx of
 the pipelined loop bit-identical to the plain loop's (forced through a
 512-thread block, same row geometry) for the VJP and the fused backward;
 and for wave rows, the plan's geometry and dx bit-identical across rows
-per block and grids."""
+per block and grids.  Rows that all fit one block with one vector per lane
+(next_pow2(vectors) x next_pow2(rows) <= 1024, at most 512 lanes) take that
+layout in one block: plan, every form against the oracle, and the grad
+call's dx and dw equal to the VJP's."""
 import sys
 
 import numpy as np
@@ -348,3 +351,61 @@ def test_partial_rows_never_one_per_row(R, dtype):
             ws = R.rmsnorm_vjp_workspace_bytes(rows, D, dt)
             stats = -(-(rows * -(-D // 1024) * 8) // 256) * 256
             assert ws <= max(256, ((rows + 1) // 2) * D * 4 + stats), (rows, D, ws)
+
+
+def _np2(n):
+    p = 1
+    while p < n:
+        p *= 2
+    return p
+
+
+# Rows that all fit one block with one 16-byte vector per lane on at most 512
+# lanes (next_pow2(vectors) x next_pow2(rows) <= 1024): one vector per lane,
+# the block sized to the rows, one block (no combine launch).
+FEW = [(1, 128, "float16"), (2, 256, "bfloat16"), (1, 4096, "float16"), (16, 512, "float16"), (64, 128, "bfloat16"),
+       (3, 1024, "bfloat16"), (4, 2048, "float16"), (1, 1536, "bfloat16"), (2, 2560, "float16"), (5, 64, "float32"),
+       (1, 2048, "float32"), (7, 256, "float32"), (4, 1536, "float16"),
+       # overlapped last vector (within 512 threads)
+       (1, 257, "float16"), (2, 513, "float16"), (4, 500, "bfloat16"), (1, 2049, "bfloat16"), (3, 97, "float32")]
+
+
+@pytest.mark.parametrize("rows,D,dtype", FEW)
+def test_few_rows_one_block_every_form(R, rows, D, dtype):
+    td = I.torch_dtype(dtype)
+    nvec = -(-D * td.itemsize // 16)   # the last vector overlapped when D * itemsize is not a multiple of 16
+    for op in (2, 3, 4):
+        q = R.query_config(op, rows, D, td)
+        _say(f"few-row backward op={op} {dtype} {rows}x{D} plan={q}")
+        assert q["vecs_per_lane"] == 1 and q["vec_bytes"] == 16, q
+        assert q["lanes_per_row"] in (nvec, _np2(nvec)), q
+        assert q["num_blocks"] == 1 and q["block_threads"] == max(64, q["lanes_per_row"] * _np2(rows)), q
+    c = I.generic(rows, D, dtype, seed=rows * 7 + D)
+    x, w, dy, dr = (c[k].to(DEV) for k in ("x", "w", "dy", "residual"))
+    dx, dw = R.rmsnorm_vjp(x, w, dy, c["eps"], 1.0)
+    y, dxg, dwg = R.rmsnorm_fwd_vjp(x, w, dy, c["eps"], 1.0)
+    dh, dwf = R.fused_add_rmsnorm_vjp(x, w, dy, dr, c["eps"], 1.0)
+    torch.cuda.synchronize()
+    dxref, dwref = O.rmsnorm_vjp(c["x"], c["w"], c["dy"], c["eps"], 1.0)
+    yref, _ = O.rmsnorm_fwd(c["x"], c["w"], c["eps"], 1.0)
+    dhref, _ = O.fused_add_rmsnorm_vjp(c["x"], c["w"], c["dy"], c["residual"], c["eps"], 1.0)
+    assert_close(dx, dxref, "dx")
+    assert_dw_close(dw, dwref, "dw")
+    assert_close(y, yref, "grad y")
+    assert_close(dh, dhref, "dh")
+    assert_dw_close(dwf, dwref, "fused dw")
+    # the three forms share the plan: the grad call's dx and dw are the VJP's, bit for bit
+    assert torch.equal(dxg, dx) and torch.equal(dwg, dw)
+
+
+def test_few_rows_rule_stops_where_rows_do_not_fit_one_block(R):
+    bf = torch.bfloat16
+    assert R.query_config(2, 1, 8192, bf)["vecs_per_lane"] == 2       # 1024 vectors
+    assert R.query_config(2, 3, 4096, bf)["vecs_per_lane"] == 2       # 512 x 4 rows
+    assert R.query_config(2, 128, 128, bf)["vecs_per_lane"] == 2      # 16 x 128 rows
+    q = R.query_config(2, 8, 1001, torch.float16)                      # overlapped: 128 lanes x 8 rows > 512
+    assert (q["lanes_per_row"], q["vecs_per_lane"]) == (64, 2), q
+    q = R.query_config(2, 1, 1000, torch.float16)                      # 125 whole vectors: inside
+    assert (q["lanes_per_row"], q["vecs_per_lane"], q["block_threads"], q["num_blocks"]) == (128, 1, 128, 1), q
+    # one row of 256 vectors: inside the rule
+    assert R.query_config(2, 1, 2048, bf)["vecs_per_lane"] == 1
