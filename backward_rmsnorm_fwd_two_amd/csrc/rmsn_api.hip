@@ -221,23 +221,34 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
     // size keeps the bandwidth layouts it fits.
     const bool few_rows_k1 = !vjp && req_k == 0 && req_l == 0 && req_b == 0 && vb == 16 && !ovl && rows <= cus &&
                              p->nvec >= 64 && p->nvec <= 768 && p->nvec % 64 == 0;
-    // The backward forms on rows that all fit one block with one 16-byte
-    // vector per lane on at most 512 lanes (next_pow2(vectors) x
-    // next_pow2(rows) <= 1024: a single row up to 4096 elements in 16-bit
-    // storage, 64 rows of D = 128):
-    // one vector per lane, the block sized to the rows, one block and so no
-    // combine launch.  The default block holds up to 32 row slots whatever
-    // the row count, and the empty slots still take part in the dw join:
-    // fp16, 32 calls replayed from one graph, per call, one row: D = 128
-    // 3.90 -> 2.52 us, 512 3.21 -> 1.91, 1024 3.32 -> 2.01, 2048 3.62 ->
-    // 2.26, 4096 3.93 -> 2.50; D = 128 at 64 rows 4.74 -> 3.72, 512 at 8
-    // rows 3.27 -> 2.86, 1024 at 2 rows 3.40 -> 2.72 (at 4..8 rows of 1024
-    // and 2..4 of 2048 the layouts ran alike; where the rows do not fit one
-    // block, more blocks and a combine ran faster).  Rows with an overlapped
-    // last vector too, within the 512 threads their instances are built for.
+    // The backward forms on few rows (rows x D x itemsize <= 32 KiB, at most
+    // 1024 16-byte vectors per row in 16-bit storage and 512 in fp32 or
+    // with the last one overlapped, whose instances are built for 512
+    // threads): one
+    // block, which loops over the rows, so no combine launch follows; one
+    // vector per lane; a block of lanes x min(next_pow2(rows), cap / lanes)
+    // threads, at least 64 -- cap 512 for rows of 16 lanes or fewer (D = 128
+    // in 16-bit storage), 256 above.  The default plan put such rows in
+    // 256-thread blocks of up to 32 row slots, the empty slots still part of
+    // the dw join, and on more than one block it adds the combine launch.
+    // fp16, 32 calls replayed from one graph, per call (VJP; the grad call
+    // and the fused backward alike): one row: D = 128 3.83 -> 2.45 us, 512
+    // 3.16 -> 1.84, 1024 3.32 -> 2.10, 2048 3.59 -> 2.24, 4096 3.94 -> 2.49;
+    // D = 128 x 128 rows 7.02 -> 5.05, 256 x 64 6.95 -> 4.72, 512 x 32 6.25
+    // -> 5.23, 1024 x 16 6.48 -> 5.94, 2048 x 8 6.67 -> 5.65, 4096 x 4 7.14
+    // -> 4.39 (at 64 KiB the combine was ahead again: 2048 x 16 6.78
+    // against 7.82 us in one block).  Rows of 513..1024 16-bit vectors take
+    // their exact wave-row instance (D = 5120 / 6144 / 7168: 4.56 / 4.90 /
+    // 5.48 -> 2.74 / 2.74 / 3.01 us at one row) or 1024 lanes (D = 8192:
+    // 6.04 -> 3.98); fp32 rows of 1024 vectors keep 512 x 2 (3.14 against
+    // 3.34 us on 1024 lanes).
     const bool few_rows_vjp = vjp && req_k == 0 && req_l == 0 && req_b == 0 && vb == 16 && rows >= 1 &&
-                              rows <= 1024 && p->nvec <= 512 &&
-                              (int64_t)next_pow2(p->nvec) * next_pow2(rows) <= (ovl ? 512 : 1024);
+                              rows <= 32768 && p->nvec <= (s == 2 && !ovl ? 1024 : 512) && rows * D * s <= 32768;
+    // slots of the few-rows backward block for a row of `l` lanes
+    auto few_rows_slots = [&](int l) {
+        const int cap = l <= 16 ? 512 : 256;
+        return std::min<int64_t>(next_pow2(std::min<int64_t>(rows, 1024)), std::max(1, cap / l));
+    };
     bool looped = req_k == -1 || (req_k == 0 && req_l == 0 && p->nvec > 1024 * 8);
     int loop_block = 1024;  // streaming kernel's default block
 
@@ -307,7 +318,7 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
             if (fn && !block) {
                 int slots = 1;
                 if (few_rows_vjp) {
-                    slots = next_pow2(rows);  // <= 4 here: wl >= 192
+                    slots = static_cast<int>(few_rows_slots(wl));  // 1 here: wl >= 192
                 } else if (vjp) {
                     while (slots < 4 && w_units * slots < kWaveRowsInFlight && 2 * slots * wl <= maxb)
                         slots *= 2;
@@ -324,6 +335,8 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
                 int64_t grid;
                 if (cfg && cfg->num_blocks) {
                     grid = cfg->num_blocks;
+                } else if (few_rows_vjp) {
+                    grid = 1;
                 } else if (vjp) {
                     // persistent: one block per CU, two where the blocks hold
                     // too little row data -- except the grad call, whose two
@@ -444,7 +457,7 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
                                             rows * D * s >= ((int64_t)24 << 20);
                 const int cap = (vjp && (vb <= 4 || ovl_sparse_big)) ? 512 : 256;
                 block = few_rows_k1    ? std::max(lanes, 64)
-                        : few_rows_vjp ? std::max(64, lanes * next_pow2(rows))
+                        : few_rows_vjp ? std::max<int>(64, lanes * static_cast<int>(few_rows_slots(lanes)))
                                        : std::max(std::max(lanes, 64), std::min(cap, maxb));
             }
             if (block < 64 || block > maxb || block % 64 != 0 || block % lanes != 0 || !is_pow2(block))
@@ -499,6 +512,8 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
             int64_t grid;
             if (cfg && cfg->num_blocks) {
                 grid = cfg->num_blocks;
+            } else if (few_rows_vjp) {
+                grid = 1;  // the block loops over the rows; dw written directly
             } else if (eight_wide) {
                 grid = vjp_grid(groups, std::min<int64_t>(kMaxPartialRows, cus));
             } else if (p->fixed_lanes) {

@@ -7,7 +7,8 @@ persistent backward grids never hold one dw partial row per row and stay
 within the partial-row bound, the VJP workspace is smaller than a [rows, D]
 fp32 temporary (beyond its 256-byte floor), and forward calls on no more
 rows than compute units take one row per block on 64..768 whole 16-byte
-vectors.  Then 40
+vectors, and the backward forms on few rows (<= 32 KiB per tensor) one
+block with one vector per lane.  Then 40
 random shapes (up to ~1.5 M elements) run through every form and are
 compared with the fp64 oracle on every element."""
 import sys
@@ -87,12 +88,14 @@ def test_plan_invariants_random_shapes(R):
                 assert k == -2 and op >= 2 and block == 256 and rows <= 65535, (what, q)
             if op >= 2:
                 assert nb <= 2048, (what, q)
-                nvec16 = D * s // 16
-                if (D * s % 16 == 0 and rows <= 1024 and 1 <= nvec16 <= 512 and
-                        _np2(nvec16) * _np2(rows) <= 1024):
-                    # all rows in one block, one vector per lane
+                ovl = D * s % 16 != 0 and D * s > 16
+                nvec16 = -(-D * s // 16)
+                if ((D * s % 16 == 0 or ovl) and rows * D * s <= 32768 and
+                        nvec16 <= (1024 if s == 2 and not ovl else 512)):
+                    # few rows: one block looping over them, one vector per lane
                     assert k == 1 and vb == 16 and nb == 1 and lanes in (nvec16, _np2(nvec16)), (what, q)
-                    assert block == max(64, lanes * _np2(rows)), (what, q)
+                    cap = 512 if lanes <= 16 else 256
+                    assert block == max(64, lanes * min(_np2(rows), max(1, cap // lanes))), (what, q)
                 if rows >= 2:
                     # never one dw partial row per row (the [rows, D] temporary)
                     assert nb <= (rows + 1) // 2, (what, q)

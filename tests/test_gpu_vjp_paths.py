@@ -10,10 +10,9 @@ the loop's exit path) and dw over all rows; dx of
 the pipelined loop bit-identical to the plain loop's (forced through a
 512-thread block, same row geometry) for the VJP and the fused backward;
 and for wave rows, the plan's geometry and dx bit-identical across rows
-per block and grids.  Rows that all fit one block with one vector per lane
-(next_pow2(vectors) x next_pow2(rows) <= 1024, at most 512 lanes) take that
-layout in one block: plan, every form against the oracle, and the grad
-call's dx and dw equal to the VJP's."""
+per block and grids.  Few rows (rows x D x itemsize <= 32 KiB) take one
+vector per lane in one block that loops over them: plan, every form against
+the oracle, and the grad call's dx and dw equal to the VJP's."""
 import sys
 
 import numpy as np
@@ -360,14 +359,24 @@ def _np2(n):
     return p
 
 
-# Rows that all fit one block with one 16-byte vector per lane on at most 512
-# lanes (next_pow2(vectors) x next_pow2(rows) <= 1024): one vector per lane,
-# the block sized to the rows, one block (no combine launch).
+def _few_rows_block(lanes, rows):
+    cap = 512 if lanes <= 16 else 256
+    return max(64, lanes * min(_np2(rows), max(1, cap // lanes)))
+
+
+# Few rows for the backward forms: rows x D x itemsize <= 32 KiB and at most
+# 1024 16-byte vectors per row in 16-bit storage (512 in fp32 or with the
+# last vector overlapped): one block looping over the rows (no combine
+# launch), one vector per lane, lanes x min(next_pow2(rows), cap / lanes)
+# threads (cap 512 for rows of 16 lanes or fewer, else 256).
 FEW = [(1, 128, "float16"), (2, 256, "bfloat16"), (1, 4096, "float16"), (16, 512, "float16"), (64, 128, "bfloat16"),
        (3, 1024, "bfloat16"), (4, 2048, "float16"), (1, 1536, "bfloat16"), (2, 2560, "float16"), (5, 64, "float32"),
        (1, 2048, "float32"), (7, 256, "float32"), (4, 1536, "float16"),
-       # overlapped last vector (within 512 threads)
-       (1, 257, "float16"), (2, 513, "float16"), (4, 500, "bfloat16"), (1, 2049, "bfloat16"), (3, 97, "float32")]
+       (32, 512, "float16"), (128, 128, "float16"), (8, 2048, "bfloat16"), (4, 4096, "bfloat16"),
+       (1, 8192, "float16"), (2, 6144, "bfloat16"), (1, 5120, "float16"), (2, 7168, "float16"),
+       # overlapped last vector
+       (1, 257, "float16"), (2, 513, "float16"), (4, 500, "bfloat16"), (1, 2049, "bfloat16"), (3, 97, "float32"),
+       (8, 1001, "float16")]
 
 
 @pytest.mark.parametrize("rows,D,dtype", FEW)
@@ -379,7 +388,7 @@ def test_few_rows_one_block_every_form(R, rows, D, dtype):
         _say(f"few-row backward op={op} {dtype} {rows}x{D} plan={q}")
         assert q["vecs_per_lane"] == 1 and q["vec_bytes"] == 16, q
         assert q["lanes_per_row"] in (nvec, _np2(nvec)), q
-        assert q["num_blocks"] == 1 and q["block_threads"] == max(64, q["lanes_per_row"] * _np2(rows)), q
+        assert q["num_blocks"] == 1 and q["block_threads"] == _few_rows_block(q["lanes_per_row"], rows), q
     c = I.generic(rows, D, dtype, seed=rows * 7 + D)
     x, w, dy, dr = (c[k].to(DEV) for k in ("x", "w", "dy", "residual"))
     dx, dw = R.rmsnorm_vjp(x, w, dy, c["eps"], 1.0)
@@ -400,10 +409,11 @@ def test_few_rows_one_block_every_form(R, rows, D, dtype):
 
 def test_few_rows_rule_stops_where_rows_do_not_fit_one_block(R):
     bf = torch.bfloat16
-    assert R.query_config(2, 1, 8192, bf)["vecs_per_lane"] == 2       # 1024 vectors
-    assert R.query_config(2, 3, 4096, bf)["vecs_per_lane"] == 2       # 512 x 4 rows
-    assert R.query_config(2, 128, 128, bf)["vecs_per_lane"] == 2      # 16 x 128 rows
-    q = R.query_config(2, 8, 1001, torch.float16)                      # overlapped: 128 lanes x 8 rows > 512
+    assert R.query_config(2, 3, 8192, bf)["vecs_per_lane"] == 2       # 48 KiB per tensor
+    assert R.query_config(2, 5, 4096, bf)["vecs_per_lane"] == 2       # 40 KiB
+    assert R.query_config(2, 129, 128, bf)["vecs_per_lane"] == 2      # 33 KiB
+    assert R.query_config(2, 1, 4096, torch.float32)["vecs_per_lane"] == 2   # fp32 rows of 1024 vectors
+    q = R.query_config(2, 17, 1001, torch.float16)                     # overlapped, 34 KiB
     assert (q["lanes_per_row"], q["vecs_per_lane"]) == (64, 2), q
     q = R.query_config(2, 1, 1000, torch.float16)                      # 125 whole vectors: inside
     assert (q["lanes_per_row"], q["vecs_per_lane"], q["block_threads"], q["num_blocks"]) == (128, 1, 128, 1), q
