@@ -1,6 +1,7 @@
 """Host-side checks (no GPU): the C-ABI library loads and exports every
-function include/rmsnorm_mi355x.h declares; the product path and the oracle
-share no code and never import each other."""
+function include/rmsnorm_mi355x.h declares; the header compiles as strict
+C99 and a C program links against the library; the product path and the
+oracle share no code and never import each other."""
 import ctypes
 import os
 import re
@@ -157,3 +158,47 @@ def test_in_place_alias_rules_without_gpu():
     for dh in (X, DY, RES, OUT):
         assert lib.fused_add_rmsnorm_vjp(X, W, DY, RES, dh, DW, WS, ws_bytes, R, D, 1, 1e-5, 0.0, None) == HIP
     assert lib.fused_add_rmsnorm_vjp(X, W, DY, RES, RES + 64, DW, WS, ws_bytes, R, D, 1, 1e-5, 0.0, None) == OVL
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include <string.h>
+#include "rmsnorm_mi355x.h"
+
+int main(void) {
+    /* every status has a message */
+    for (int st = -8; st <= 0; ++st) {
+        const char *s = rmsn_status_str(st);
+        if (s == NULL || strlen(s) == 0) return 10;
+    }
+    /* host-side argument checks, before any device call */
+    if (rmsnorm_fwd(NULL, NULL, NULL, 4, 8, RMSN_F16, 1e-5f, 0.0f, NULL) != RMSN_E_NULLPTR) return 11;
+    if (rmsnorm_fwd(NULL, NULL, NULL, -1, 8, RMSN_F16, 1e-5f, 0.0f, NULL) != RMSN_E_SHAPE) return 12;
+    if (rmsnorm_fwd(NULL, NULL, NULL, 0, 8, RMSN_F16, 1e-5f, 0.0f, NULL) != RMSN_OK) return 13;
+    if (fused_add_rmsnorm_fwd(NULL, NULL, NULL, NULL, NULL, 4, 8, 7, 1e-6f, 1.0f, NULL) != RMSN_E_DTYPE) return 14;
+    if (rmsnorm_vjp(NULL, NULL, NULL, NULL, NULL, NULL, 0, 4, 0, RMSN_BF16, 1e-6f, 0.0f, NULL) != RMSN_E_SHAPE)
+        return 15;
+    if (rmsnorm_vjp_workspace_bytes(-1, 4096, RMSN_F16) != 0) return 16;
+    printf("c abi ok\n");
+    return 0;
+}
+"""
+
+
+def test_header_is_plain_c_and_links_from_c(tmp_path):
+    """The header compiles as strict C99 (no C++ in the declarations) and a C
+    program links against the library and calls it: status strings and the
+    argument checks that run before any device call."""
+    if not os.path.exists(LIB):
+        from backward_rmsnorm_fwd_two_amd import build
+        build.build(verbose=False)
+    src = tmp_path / "abi.c"
+    exe = tmp_path / "abi"
+    src.write_text(C_PROGRAM)
+    cc = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                         "-I", os.path.join(ROOT, "include"), str(src), "-L", PKG, "-lrmsnorm_mi355x",
+                         f"-Wl,-rpath,{PKG}", "-o", str(exe)], capture_output=True, text=True)
+    assert cc.returncode == 0, cc.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0, (run.returncode, run.stdout, run.stderr)
+    assert run.stdout.strip() == "c abi ok"
