@@ -107,6 +107,12 @@ def _check(status: int, where: str) -> None:
 
 
 def _stream(t: torch.Tensor):
+    """The current stream of t's device, which must be the current device:
+    the library plans and launches on the current device."""
+    cur = torch.cuda.current_device()
+    if t.device.index != cur:
+        raise ValueError(f"tensors are on {t.device} but the current device is cuda:{cur}; "
+                         "call inside torch.cuda.device(...) of the tensors' device")
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 

@@ -71,6 +71,10 @@
  *   - Execution: asynchronous on `hip_stream` (a hipStream_t; NULL is the
  *     null stream).  No call synchronises.  The functions are thread-safe;
  *     one workspace must not serve two calls in flight at once.
+ *   - Device: the calling thread's current device (hipSetDevice) must hold
+ *     every pointer and `hip_stream`; the launch configuration (from its
+ *     compute-unit count) and rmsnorm_vjp_noalloc's scratch are that
+ *     device's.
  *   - Errors: a status is returned, nothing is thrown.  Arguments are checked
  *     before any launch; launch failures return RMSN_E_HIP.
  *   - rows == 0 is valid: nothing is written, except that the backward
