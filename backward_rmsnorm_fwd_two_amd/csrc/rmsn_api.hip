@@ -108,6 +108,7 @@ struct Plan {
     bool fixed_lanes = false; // ... in an instance with the lanes fixed at compile time
     bool ovl = false;         // rows of ceil(D / nv) vectors, the last one overlapped
     bool fwd_generic = false; // forward forms: the runtime-width kernel although a fixed-width one exists
+    bool dup = false;         // backward forms: the duplicate-slot instance (lanes * k > nvec)
     // column-split backward (k == -2): statistics slices per row, column
     // tiles, rows per chunk (grid = chunks), workspace bytes of the row
     // statistics (ahead of the dw partial rows)
@@ -296,8 +297,40 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
                     wk = kk;
                 }
             }
+            // Backward rows of whole 16-byte vectors that no instance tiles
+            // (D = 1152, 2304, 3840, 5376 ... in 16-bit storage) take the
+            // smallest whole number of waves holding the row with one or two
+            // vectors per lane, where the row fills at least three quarters
+            // of the slots (equal fill: two vectors), in the duplicate-slot
+            // instances: the slots past the row's end redo columns inside
+            // it, so the pipelined loop masks nothing.  The masked plain loop
+            // ran these rows 25-45 % slower (bf16, 64 MiB tensors, VJP /
+            // grad call / fused backward: D = 1152 57.2 / 63.1 / 70.6 ->
+            // 41.4 / 54.0 / 50.0 us; 2304 60.8 / 66.1 / 73.7 -> 40.3 / 52.4 /
+            // 49.6; 5376 51.2 / 59.2 / 60.7 -> 40.7 / 52.7 / 50.6).  A
+            // requested wave-row lane count with more slots than the row's
+            // vectors (at most twice as many) takes them too.
+            bool dup = false;
+            if (!fn && vjp && !few_rows_vjp) {
+                double best = lanes == 0 ? 0.75 : 0.5;
+                for (int kk : {2, 1}) {
+                    if (k != 0 && kk != k) continue;
+                    const int l = lanes != 0 ? lanes : 64 * static_cast<int>((p->nvec + 64 * kk - 1) / (64 * kk));
+                    const int64_t nslot = (int64_t)l * kk;
+                    if (nslot <= p->nvec || nslot > 2 * (int64_t)p->nvec) continue;
+                    const double fill = static_cast<double>(p->nvec) / static_cast<double>(nslot);
+                    if (fill < best || (dup && fill == best)) continue;
+                    const void* f = rmsn::vjp_kernel_dup(dt, p->nv, kk, vmode, l);
+                    if (!f) continue;
+                    fn = f;
+                    wl = l;
+                    wk = kk;
+                    best = fill;
+                    dup = true;
+                }
+            }
             // one, two or four rows per block, as the registers allow
-            const int most = vjp ? rmsn::wave_rows_block_max(wl, wk * p->nv)
+            const int most = vjp ? rmsn::vjp_pipe_block_max(wl, wk * p->nv)
                                  : (4 * wl <= 1024 ? 4 * wl : 2 * wl <= 1024 ? 2 * wl : wl);
             const int maxb = fn ? std::min(rmsn::max_block_threads(budget_op, wk, p->nv, s), most) : 0;
             // Rows per block and the persistent grid of the backward forms:
@@ -341,8 +374,14 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
                     // persistent: one block per CU, two where the blocks hold
                     // too little row data -- except the grad call, whose two
                     // stored outputs keep the CU busy (D = 3584 bf16, 7 waves
-                    // x 1: 51.0 us at one block per CU vs 54.2 at two)
-                    const int per_cu = w_units * nslots < kWaveRowsInFlight && op != RMSN_OP_GRAD ? 2 : 1;
+                    // x 1: 51.0 us at one block per CU vs 54.2 at two) -- and
+                    // two for the VJP on duplicate-slot rows of one or two
+                    // waves (bf16, 64 MiB: D = 768 / 896 / 1600 4.45 / 4.76 /
+                    // 4.30 -> 4.90 / 5.03 / 4.76 TB/s; the grad call and the
+                    // fused backward ran 4-10 % slower that way)
+                    const bool two = (w_units * nslots < kWaveRowsInFlight && op != RMSN_OP_GRAD) ||
+                                     (dup && op == RMSN_OP_VJP && wl <= 128);
+                    const int per_cu = two ? 2 : 1;
                     grid = vjp_grid(groups, std::min<int64_t>(kMaxPartialRows, (int64_t)per_cu * cus));
                 } else {
                     grid = std::min<int64_t>(groups, (int64_t)1 << 20);
@@ -354,6 +393,7 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
                 p->block = block;
                 p->pipe = vjp;
                 p->fixed_lanes = true;
+                p->dup = dup;
                 p->grid = grid;
                 p->shmem = (vjp && nslots > 1) ? (size_t)block * p->nv * sizeof(float) : 0;
                 return RMSN_OK;
@@ -816,8 +856,10 @@ int vjp_impl(const void* x, const void* w, const void* dy, void* y, const void* 
     if (p.ovl) {
         fn = rmsn::vjp_kernel_ovl(dt, p.k, mode);
     } else {
-        fn = p.fixed_lanes ? rmsn::vjp_kernel_fixed_lanes(dt, p.nv, p.k, mode, p.lanes) : nullptr;
-        if (!fn && !(p.k > 0 && rmsn::wave_rows(p.lanes)))
+        fn = p.dup           ? rmsn::vjp_kernel_dup(dt, p.nv, p.k, mode, p.lanes)
+             : p.fixed_lanes ? rmsn::vjp_kernel_fixed_lanes(dt, p.nv, p.k, mode, p.lanes)
+                             : nullptr;
+        if (!fn && !p.dup && !(p.k > 0 && rmsn::wave_rows(p.lanes)))
             fn = rmsn::vjp_kernel(dt, p.nv, p.k, mode, p.jreg, p.pipe);
     }
     if (!fn) return RMSN_E_CONFIG;

@@ -78,6 +78,21 @@ __device__ __forceinline__ Cols<K> make_cols(int lanes, int lane, int nvec, int 
     return Cols<K>(lanes, lane, nvec, nv);
 }
 
+// Duplicate slots: a vector slot past the row's end (v >= nvec, with lanes *
+// K <= 2 nvec) takes the columns of vector v - nvec, which another slot owns.
+// It loads the same data and the same gain, and stores the very values the
+// owner stores; only the row sums and dw leave it out (ok[k] false).
+template <int K>
+__device__ __forceinline__ Cols<K> make_dup_cols(int lanes, int lane, int nvec, int nv) {
+    Cols<K> c(lanes, lane, nvec, nv);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int v = k * lanes + lane;
+        if (!c.ok[k]) c.off[k] = (int64_t)(v - nvec) * nv;
+    }
+    return c;
+}
+
 // A finished dw vector into the block's partial row: an overlapped last
 // vector stores only its own columns (the previous vector's lane stores the
 // others).
@@ -333,7 +348,8 @@ __device__ __forceinline__ void vjp_issue_dr(const RowArgs& a, int64_t row0, int
 // every path (a store skipped on some paths would make later waits for loads
 // wait for everything).
 // OVL: the row's last vector may be overlapped (Cols).
-template <typename T, int NV, int K, int MODE, bool FULL = false, bool ONE_ROW = false, bool OVL = false>
+template <typename T, int NV, int K, int MODE, bool FULL = false, bool ONE_ROW = false, bool OVL = false,
+          bool DUP = false>
 __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int slot, int lanes,
                                             const Cols<K>& c, const float (&g)[K][NV],
                                             float (&acc)[K][NV], VjpRow<T, NV, K>& d,
@@ -351,7 +367,12 @@ __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int 
     for (int k = 0; k < K; ++k) {
 #pragma unroll
         for (int e = 0; e < NV; ++e) {
-            if constexpr (OVL) {
+            if constexpr (DUP) {
+                const float xv = c.ok[k] ? elem(d.x[k], e) : 0.0f;  // a duplicate slot adds nothing
+                const float dv = elem(d.dy[k], e);
+                s2[0] = __builtin_fmaf(xv, xv, s2[0]);
+                s2[1] = __builtin_fmaf(dv * g[k][e], xv, s2[1]);
+            } else if constexpr (OVL) {
                 const bool live = e >= c.skip[k];  // not an overlapped element
                 const float xv = live ? elem(d.x[k], e) : 0.0f;
                 const float dg = live ? elem(d.dy[k], e) * g[k][e] : 0.0f;
@@ -446,9 +467,12 @@ struct PartialRowOut {
 // instances for the common geometries), so the row reductions compile
 // without branches on the row width; 0: taken from the arguments.  OVL:
 // rows that are not a whole number of vectors, the last vector overlapped
-// (the plain row loop only).
+// (the plain row loop only).  DUP: rows of fewer vectors than lanes x K
+// (at least half of them), pipelined and unmasked through duplicate slots
+// (make_dup_cols): the slots past the row's end load, compute and store
+// the columns another slot owns, and only the row sums leave them out.
 template <typename T, int NV, int K, int MODE, bool PIPE = false, int LANES = 0, class DwOut = PartialRowOut,
-          bool OVL = false>
+          bool OVL = false, bool DUP = false>
 __global__ __launch_bounds__(!PIPE ? (OVL ? max_block_threads_ovl(2, K, NV, sizeof(T)) : max_block_threads(2, K, NV, sizeof(T)))
                              : wave_rows(LANES) ? wave_rows_block_max(LANES, K * NV)
                              : (LANES > kVjpPipeBlock ? LANES : kVjpPipeBlock)) void vjp_rows(RowArgs a) {
@@ -459,6 +483,7 @@ __global__ __launch_bounds__(!PIPE ? (OVL ? max_block_threads_ovl(2, K, NV, size
                                           wave_rows_supported(LANES))),
                   "fixed lane counts are pipelined: powers of two or supported whole numbers of waves");
     static_assert(!OVL || (!PIPE && LANES == 0), "overlapped rows run in the plain row loop");
+    static_assert(!DUP || (PIPE && LANES > 0), "duplicate slots run in the pipelined fixed-width instances");
     extern __shared__ float dyn[];
     __shared__ float red[2 * 16 * 2];
     // Instances whose blocks hold exactly one row (the lane count fixes it)
@@ -473,7 +498,8 @@ __global__ __launch_bounds__(!PIPE ? (OVL ? max_block_threads_ovl(2, K, NV, size
     const int lane = rs.lane;
     const int slot = rs.slot;
     const int nslots = rs.nslots;
-    const Cols<K> c = make_cols<K, OVL>(lanes, lane, a.nvec, NV, a.D);
+    const Cols<K> c =
+        DUP ? make_dup_cols<K>(lanes, lane, a.nvec, NV) : make_cols<K, OVL>(lanes, lane, a.nvec, NV, a.D);
     const int64_t step = (int64_t)gridDim.x * nslots;
     int64_t row0 = (int64_t)blockIdx.x * nslots;
 
@@ -496,8 +522,9 @@ __global__ __launch_bounds__(!PIPE ? (OVL ? max_block_threads_ovl(2, K, NV, size
             // of loaded data would make the wave wait for the prefetch at the
             // end of every iteration.  The gain's loads go out first, so that
             // none of them is still pending when the loop starts.  Every
-            // vector of a row is in range here (the plan selects this kernel
-            // only then), and every row group but a block's last is full, so the
+            // vector slot of a row is in range here (the plan selects this
+            // kernel only then) or, in DUP instances, a duplicate of one that
+            // is, and every row group but a block's last is full, so the
             // loop's processing masks nothing and stores unconditionally; a
             // ragged last group (rows not a multiple of the row slots) is
             // processed masked on the loop's exit path, after which the
@@ -518,7 +545,7 @@ __global__ __launch_bounds__(!PIPE ? (OVL ? max_block_threads_ovl(2, K, NV, size
             Raw<T, NV> drs[K];
             vjp_issue<T, NV, K, MODE, !kDrOwn>(a, row0, slot, c, ra);
             if constexpr (kDrOwn) vjp_issue_dr<T, NV, K>(a, row0, slot, c, drs);
-            mask_cols<T, NV, K>(c, pw);
+            if constexpr (!DUP) mask_cols<T, NV, K>(c, pw);
 #pragma unroll
             for (int k = 0; k < K; ++k)
 #pragma unroll
@@ -527,32 +554,32 @@ __global__ __launch_bounds__(!PIPE ? (OVL ? max_block_threads_ovl(2, K, NV, size
             for (;;) {  // ra holds group row0
                 if (next >= a.rows) {  // the block's last group, possibly ragged
                     if (kOneRow || row0 + nslots <= a.rows)
-                        vjp_process<T, NV, K, MODE, true, kOneRow>(a, row0, slot, lanes, c, g, acc, ra,
-                                                          kDrOwn ? drs : ra.dr, red, parity);
+                        vjp_process<T, NV, K, MODE, true, kOneRow, false, DUP>(a, row0, slot, lanes, c, g, acc,
+                                                                               ra, kDrOwn ? drs : ra.dr, red, parity);
                     else if constexpr (!kOneRow)
                         vjp_process<T, NV, K, MODE, false>(a, row0, slot, lanes, c, g, acc, ra,
                                                            kDrOwn ? drs : ra.dr, red, parity);
                     break;
                 }
                 vjp_issue<T, NV, K, MODE, !kDrOwn>(a, next, slot, c, rb);
-                vjp_process<T, NV, K, MODE, true, kOneRow>(a, row0, slot, lanes, c, g, acc, ra, kDrOwn ? drs : ra.dr, red,
-                                                  parity);
+                vjp_process<T, NV, K, MODE, true, kOneRow, false, DUP>(a, row0, slot, lanes, c, g, acc, ra,
+                                                                       kDrOwn ? drs : ra.dr, red, parity);
                 if constexpr (kDrOwn) vjp_issue_dr<T, NV, K>(a, next, slot, c, drs);
                 row0 = next;
                 next += step;
                 // rb holds group row0
                 if (next >= a.rows) {  // the block's last group, possibly ragged
                     if (kOneRow || row0 + nslots <= a.rows)
-                        vjp_process<T, NV, K, MODE, true, kOneRow>(a, row0, slot, lanes, c, g, acc, rb,
-                                                          kDrOwn ? drs : rb.dr, red, parity);
+                        vjp_process<T, NV, K, MODE, true, kOneRow, false, DUP>(a, row0, slot, lanes, c, g, acc,
+                                                                               rb, kDrOwn ? drs : rb.dr, red, parity);
                     else if constexpr (!kOneRow)
                         vjp_process<T, NV, K, MODE, false>(a, row0, slot, lanes, c, g, acc, rb,
                                                            kDrOwn ? drs : rb.dr, red, parity);
                     break;
                 }
                 vjp_issue<T, NV, K, MODE, !kDrOwn>(a, next, slot, c, ra);
-                vjp_process<T, NV, K, MODE, true, kOneRow>(a, row0, slot, lanes, c, g, acc, rb, kDrOwn ? drs : rb.dr, red,
-                                                  parity);
+                vjp_process<T, NV, K, MODE, true, kOneRow, false, DUP>(a, row0, slot, lanes, c, g, acc, rb,
+                                                                       kDrOwn ? drs : rb.dr, red, parity);
                 if constexpr (kDrOwn) vjp_issue_dr<T, NV, K>(a, next, slot, c, drs);
                 row0 = next;
                 next += step;

@@ -92,6 +92,20 @@ constexpr bool vjp_wave_rows_fit(int lanes, int k, int itemsize, int mode) {
                                                     : true;
 }
 
+// Duplicate-slot instances (rows that lanes x K does not tile exactly): one
+// or two 16-byte vectors per lane on 64 W lanes, W = 1..15, wherever the
+// exact instance of that geometry fits its registers.
+constexpr bool vjp_dup_fit(int lanes, int k, int itemsize, int mode) {
+    return (k == 1 || k == 2) && lanes % 64 == 0 && lanes >= 64 && lanes <= 960 &&
+           vjp_wave_rows_fit(lanes, k, itemsize, mode);
+}
+// Largest block of a pipelined instance with the lanes fixed at compile
+// time (its launch bound): wave rows as above; power-of-two lanes one row of
+// 256 lanes or more, or up to 256 threads of shorter rows.
+constexpr int vjp_pipe_block_max(int lanes, int elems) {
+    return wave_rows(lanes) ? wave_rows_block_max(lanes, elems) : (lanes > kVjpPipeBlock ? lanes : kVjpPipeBlock);
+}
+
 inline int dtype_size(int dt) { return dt == kF32 ? 4 : 2; }
 
 // Kernel entry for (op, dtype, NV, K); K == -1 is the streaming kernel.
@@ -113,6 +127,8 @@ const void* vjp_kernel_fixed_lanes(int dt, int nv, int k, int mode, int lanes);
 // The wave-row instances (lanes = 64 W, W not a power of two), or nullptr.
 const void* fwd_kernel_wave_rows(int dt, int nv, int k, bool fused, int lanes);
 const void* vjp_kernel_wave_rows(int dt, int nv, int k, int mode, int lanes);
+// The duplicate-slot instances (vjp_dup_fit), or nullptr.
+const void* vjp_kernel_dup(int dt, int nv, int k, int mode, int lanes);
 // Rows that are not a whole number of 16-byte vectors, the last vector
 // overlapped (forward, and the backward forms' plain row loop), or nullptr.
 const void* fwd_kernel_ovl(int dt, int k, bool fused);

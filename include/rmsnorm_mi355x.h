@@ -128,7 +128,10 @@ typedef struct {
                                vectors per lane do not); the VJP of 16-bit rows also
                                takes 384, 448 or 512 lanes with 4 vectors per lane,
                                the grad call and fused backward 448 or 512, and every backward form of fp32
-                               rows 512 lanes with 4, one row per block */
+                               rows 512 lanes with 4, one row per block; the backward forms
+                               also take wave rows with more vector slots than the row has
+                               vectors (at most twice as many; the slots past the row's end
+                               redo slots inside it) */
     int32_t vecs_per_lane;  /* vectors each thread holds per row: 1, 2, 4 or 8;
                                -1 selects the streaming (looped) kernel; -2 the
                                column-split backward forms (backward entry points

@@ -1,0 +1,161 @@
+"""GPU: backward rows that no lane count tiles exactly (whole 16-byte vectors,
+but not lanes x K of them for any instance: D = 1152, 2304, 3840, 5376,
+8200 ... in 16-bit storage) run the pipelined duplicate-slot instances: the
+smallest whole number of waves holding the row with one or two vectors per
+lane, when the row fills at least three quarters of the slots; the slots
+past the row's end load, compute and store columns another slot owns and
+are left out of the row sums and dw.  Checks:
+- the automatic plan's lanes and vectors per lane for every backward form;
+- every element of dx, dh and the grad call's y, and dw, against the fp64
+  oracle, with ragged last row groups;
+- the grad call's dx equal to the VJP's bit for bit (dw too on a shared
+  grid), and the fused backward with a zero residual gradient equal to the
+  VJP;
+- in place (dx over x, over dy; dh over d_new_residual) bit-identical to
+  out of place -- the duplicate slots read columns that their owners
+  overwrite in place;
+- forced geometries (wave-row lane counts with more slots than vectors, one
+  to four rows per block, small grids) against the oracle, and a request
+  with more than twice the row's vectors refused (RMSN_E_CONFIG)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from _parity import assert_close, assert_dw_close
+from backward_rmsnorm_fwd_two_amd import inputs as I
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+E_CONFIG = -8
+BACKWARD_OPS = (2, 3, 4)   # VJP, grad call, fused backward
+
+# (rows, D, dtype, expected (lanes, vectors per lane) of every backward form)
+CASES = [
+    (301, 1152, "bfloat16", (192, 1)),    # 144 vectors in 3 waves x 1 (75 %)
+    (301, 2304, "float16", (320, 1)),     # 288 in 5 waves x 1 (90 %)
+    (150, 5376, "bfloat16", (704, 1)),    # 672 in 11 waves x 1 (95 %)
+    (257, 3840, "bfloat16", (256, 2)),    # 480 in 4 waves x 2 (94 %; 8 x 1 the same fill)
+    (1001, 896, "float16", (64, 2)),      # 112 in 1 wave x 2 (88 %)
+    (333, 1600, "bfloat16", (128, 2)),    # 200 in 2 waves x 2 (78 %)
+    (200, 4544, "float16", (576, 1)),     # 568 in 9 waves x 1 (99 %)
+    (120, 6400, "bfloat16", (832, 1)),    # 800 in 13 waves x 1 (96 %)
+    (130, 8200, "float16", (576, 2)),     # 1025 in 9 waves x 2 (89 %)
+    (501, 1152, "float32", (320, 1)),     # fp32: 288 vectors in 5 waves x 1
+    (90, 2900, "float32", (384, 2)),      # fp32: 725 in 6 waves x 2 (94 %)
+]
+
+
+@pytest.fixture(scope="module")
+def R():
+    import backward_rmsnorm_fwd_two_amd as pkg
+    return pkg
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _oracle_all(c, eps, wb):
+    dxref, dwref = O.rmsnorm_vjp(c["x"], c["w"], c["dy"], eps, wb)
+    yref, _ = O.rmsnorm_fwd(c["x"], c["w"], eps, wb)
+    dhref, _ = O.fused_add_rmsnorm_vjp(c["x"], c["w"], c["dy"], c["residual"], eps, wb)
+    return dxref, dwref, yref, dhref
+
+
+@pytest.mark.parametrize("rows,D,dtype,geom", CASES)
+def test_dup_rows_plan_parity_bitwise(R, rows, D, dtype, geom):
+    c = I.generic(rows, D, dtype, seed=rows * 13 + D)
+    eps, wb = c["eps"], 1.0
+    x, w, dy, dr = (c[k].to(DEV) for k in ("x", "w", "dy", "residual"))
+    plans = {op: R.query_config(op, rows, D, x.dtype) for op in BACKWARD_OPS}
+    _say(f"dup rows {dtype} {rows}x{D}: {plans[2]}")
+    nv = 16 // x.element_size()
+    for op, q in plans.items():
+        assert (q["lanes_per_row"], q["vecs_per_lane"], q["vec_bytes"]) == (*geom, 16), (op, q)
+        assert geom[0] * geom[1] > D // nv, (op, q)   # more slots than vectors: duplicates
+
+    dx, dw = R.rmsnorm_vjp(x, w, dy, eps, wb)
+    y, gdx, gdw = R.rmsnorm_fwd_vjp(x, w, dy, eps, wb)
+    dh, hdw = R.fused_add_rmsnorm_vjp(x, w, dy, dr, eps, wb)
+    zdh, zdw = R.fused_add_rmsnorm_vjp(x, w, dy, torch.zeros_like(dr), eps, wb)
+    torch.cuda.synchronize()
+
+    dxref, dwref, yref, dhref = _oracle_all(c, eps, wb)
+    assert_close(dx, dxref, "dx")
+    assert_dw_close(dw, dwref, "dw")
+    assert_close(y, yref, "grad y")
+    assert_close(gdx, dxref, "grad dx")
+    assert_dw_close(gdw, dwref, "grad dw")
+    assert_close(dh, dhref, "dh")
+    assert_dw_close(hdw, dwref, "fused dw")
+
+    assert torch.equal(gdx, dx), "grad dx != VJP dx"
+    assert torch.equal(zdh, dx), "fused backward with zero d_new_residual != VJP dx"
+    if plans[3]["num_blocks"] == plans[2]["num_blocks"] and plans[3]["block_threads"] == plans[2]["block_threads"]:
+        assert torch.equal(gdw, dw), "grad dw != VJP dw on a shared grid"
+    if plans[4]["num_blocks"] == plans[2]["num_blocks"] and plans[4]["block_threads"] == plans[2]["block_threads"]:
+        assert torch.equal(zdw, dw), "fused dw != VJP dw on a shared grid"
+
+    # in place: the duplicate slots read columns their owners overwrite
+    xb = x.clone()
+    R.rmsnorm_vjp(xb, w, dy, eps, wb, dx=xb)
+    dyb = dy.clone()
+    R.rmsnorm_vjp(x, w, dyb, eps, wb, dx=dyb)
+    drb = dr.clone()
+    R.fused_add_rmsnorm_vjp(x, w, dy, drb, eps, wb, dh=drb)
+    torch.cuda.synchronize()
+    assert torch.equal(xb, dx), "dx over x"
+    assert torch.equal(dyb, dx), "dx over dy"
+    assert torch.equal(drb, dh), "dh over d_new_residual"
+
+
+# forced geometries on [rows, 2304] bf16 (288 vectors): (lanes, vectors per
+# lane, block, grid); grid 0 = automatic
+FORCED = [
+    (192, 2, 192, 0), (192, 2, 384, 0), (192, 2, 768, 7),
+    (320, 1, 320, 0), (320, 1, 640, 5), (320, 1, 1280, 0),
+    (384, 1, 384, 0), (384, 1, 768, 3),
+    (576, 1, 576, 0),                      # exactly twice the vectors: every slot past 288 a duplicate
+]
+
+
+@pytest.mark.parametrize("rows", [203, 64])
+def test_dup_rows_forced_geometries(R, rows):
+    D, dtype = 2304, "bfloat16"
+    c = I.generic(rows, D, dtype, seed=rows + 99)
+    eps, wb = c["eps"], 0.25
+    x, w, dy, dr = (c[k].to(DEV) for k in ("x", "w", "dy", "residual"))
+    dxref, dwref, yref, dhref = _oracle_all(c, eps, wb)
+    ran = 0
+    for lanes, k, block, nb in FORCED:
+        cfg = dict(lanes_per_row=lanes, vecs_per_lane=k, vec_bytes=16, block_threads=block, num_blocks=nb)
+        _say(f"dup forced rows={rows} {cfg}")
+        try:
+            dx, dw = R.rmsnorm_vjp(x, w, dy, eps, wb, cfg=cfg)
+        except R.RMSNormError as e:
+            # a block past the instance's bound (more than 768 threads)
+            assert e.status == E_CONFIG and block > 768, (cfg, e)
+            continue
+        y, gdx, gdw = R.rmsnorm_fwd_vjp(x, w, dy, eps, wb, cfg=cfg)
+        dh, hdw = R.fused_add_rmsnorm_vjp(x, w, dy, dr, eps, wb, cfg=cfg)
+        torch.cuda.synchronize()
+        assert_close(dx, dxref, f"dx {cfg}")
+        assert_dw_close(dw, dwref, f"dw {cfg}")
+        assert_close(y, yref, f"grad y {cfg}")
+        assert_close(gdx, dxref, f"grad dx {cfg}")
+        assert_dw_close(gdw, dwref, f"grad dw {cfg}")
+        assert_close(dh, dhref, f"dh {cfg}")
+        assert_dw_close(hdw, dwref, f"fused dw {cfg}")
+        ran += 1
+    assert ran >= len(FORCED) - 1
+    # more than twice the row's vectors: refused
+    for lanes, k in ((640, 1), (320, 2)):
+        cfg = dict(lanes_per_row=lanes, vecs_per_lane=k, vec_bytes=16, block_threads=lanes, num_blocks=0)
+        with pytest.raises(R.RMSNormError) as ei:
+            R.rmsnorm_vjp(x, w, dy, eps, wb, cfg=cfg)
+        assert ei.value.status == E_CONFIG, cfg

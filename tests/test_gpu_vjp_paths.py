@@ -269,12 +269,13 @@ def test_streaming_vjp_grid_follows_occupancy(R, rows, D, dtype):
 # (rows, D, dtype, op -> expected (lanes, vectors per lane) of the automatic
 # backward plan): dense 16-bit rows of 1536..2048 vectors without a pipelined
 # instance run the plain loop on 256 lanes x 8, one block per CU; sparser
-# rows keep 1024 lanes x 2
+# rows that 9 waves x 2 hold (1025..1152 vectors) run the duplicate-slot
+# instance there
 EIGHT = [
     (200, 13312, "bfloat16", {2: (256, 8), 3: (256, 8), 4: (256, 8)}),
     (150, 14336, "float16", {2: (448, 4), 3: (448, 4), 4: (448, 4)}),
     (130, 16384, "bfloat16", {2: (512, 4), 3: (512, 4), 4: (512, 4)}),
-    (300, 8200, "float16", {2: (1024, 2), 3: (1024, 2), 4: (1024, 2)}),
+    (300, 8200, "float16", {2: (576, 2), 3: (576, 2), 4: (576, 2)}),
 ]
 
 
