@@ -655,7 +655,8 @@ def wide_bench(R, dev, args) -> int:
 
 
 def widths_bench(R, dev, args) -> int:
-    """Every RMSNorm op across model widths (bf16, D = 1536 .. 16384,
+    """Every RMSNorm op across model widths (bf16, D = 1152 .. 16384, among
+    them widths that no lane count tiles exactly -- 1152, 2304, 3840, 5376 --
     rows = 2^25 / D: 64 MiB per row tensor), cold: buffer sets rotate so that
     no call finds its inputs in the 256 MB last-level cache.  Inputs
     are drawn on the device from a seeded generator (x, residual ~ N(0, 1),
@@ -682,8 +683,8 @@ def widths_bench(R, dev, args) -> int:
         return e0.elapsed_time(e1) * 1e3 / N
 
     grid = []
-    for D in (1536, 2048, 2560, 3072, 3584, 4096, 4608, 5120, 5632, 6144, 6656, 7168, 7680, 8192, 9216, 10240, 11264,
-              12288, 14336, 16384):
+    for D in (1152, 1536, 2048, 2304, 2560, 3072, 3584, 3840, 4096, 4608, 5120, 5376, 5632, 6144, 6656, 7168, 7680,
+              8192, 9216, 10240, 11264, 12288, 14336, 16384):
         grid.append(measure_ops(R, dev, (1 << 25) // D, D, 10, timed, gen))
     worst = min(r["vjp"]["GBps"] for r in grid)
     print(json.dumps({
