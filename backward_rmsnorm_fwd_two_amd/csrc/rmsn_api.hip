@@ -716,7 +716,8 @@ int fwd_impl(bool fused, const void* x, const void* res, const void* w, void* y,
     if (st != RMSN_OK) return st;
     const void* fn = nullptr;
     if (p.ovl) {
-        fn = rmsn::fwd_kernel_ovl(dt, p.k, fused);
+        fn = rmsn::fwd_kernel_ovl_fixed(dt, p.k, fused, p.lanes);
+        if (!fn) fn = rmsn::fwd_kernel_ovl(dt, p.k, fused);
     } else {
         fn = p.k > 0 && !p.fwd_generic ? rmsn::fwd_kernel_fixed_lanes(dt, p.nv, p.k, fused, p.lanes) : nullptr;
         if (!fn && !(p.k > 0 && rmsn::wave_rows(p.lanes))) fn = rmsn::fwd_kernel(dt, p.nv, p.k, fused);

@@ -242,12 +242,11 @@ __device__ __forceinline__ void fwd_process(const RowArgs& a, int64_t row0, int 
 // common geometries), so the row reduction compiles without branches on the
 // row width; 0: taken from the arguments.
 // OVL: rows that are not a whole number of vectors, the last vector
-// overlapped (generic instances only).
+// overlapped.
 template <typename T, int NV, int K, bool FUSED, int LANES = 0, bool OVL = false>
 __global__ __launch_bounds__(max_block_threads(FUSED ? 1 : 0, K, NV, sizeof(T))) void fwd_rows(RowArgs a) {
     static_assert(LANES == 0 || ((LANES & (LANES - 1)) == 0 && LANES <= 1024) || wave_rows_supported(LANES),
                   "lanes: a power of two or a supported whole number of waves");
-    static_assert(!OVL || LANES == 0, "overlapped rows run in the generic instances");
     __shared__ float red[2 * 16];
     const int lanes = LANES > 0 ? LANES : a.lanes;
     const RowSlot rs = row_slot<LANES>(a.lshift);

@@ -132,6 +132,7 @@ const void* vjp_kernel_dup(int dt, int nv, int k, int mode, int lanes);
 // Rows that are not a whole number of 16-byte vectors, the last vector
 // overlapped (forward, and the backward forms' plain row loop), or nullptr.
 const void* fwd_kernel_ovl(int dt, int k, bool fused);
+const void* fwd_kernel_ovl_fixed(int dt, int k, bool fused, int lanes);
 const void* vjp_kernel_ovl(int dt, int k, int mode);
 // Column-split backward forms: threads per block (both kernels), vectors per
 // thread in a statistics slice, rows per chunk of the apply kernel (their r
