@@ -78,17 +78,20 @@ __device__ __forceinline__ Cols<K> make_cols(int lanes, int lane, int nvec, int 
     return Cols<K>(lanes, lane, nvec, nv);
 }
 
-// Duplicate slots: a vector slot past the row's end (v >= nvec, with lanes *
-// K <= 2 nvec) takes the columns of vector v - nvec, which another slot owns.
-// It loads the same data and the same gain, and stores the very values the
-// owner stores; only the row sums and dw leave it out (ok[k] false).
+// Duplicate slots: a vector slot past the row's end (v >= nvec; the plan
+// keeps lanes * K <= 2 nvec) takes the columns of vector v - nvec, which
+// another slot owns.  It loads the same data and the same gain, and stores
+// the very values the owner stores; only the row sums and dw leave it out
+// (ok[k] false).  Past 2 nvec slots (never planned) it would take the row's
+// last vector, still inside the row.
 template <int K>
 __device__ __forceinline__ Cols<K> make_dup_cols(int lanes, int lane, int nvec, int nv) {
     Cols<K> c(lanes, lane, nvec, nv);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const int v = k * lanes + lane;
-        if (!c.ok[k]) c.off[k] = (int64_t)(v - nvec) * nv;
+        const int owner = v - nvec < nvec ? v - nvec : nvec - 1;
+        if (!c.ok[k]) c.off[k] = (int64_t)owner * nv;
     }
     return c;
 }
