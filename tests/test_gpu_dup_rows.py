@@ -46,6 +46,9 @@ CASES = [
     (130, 8200, "float16", (576, 2)),     # 1025 in 9 waves x 2 (89 %)
     (501, 1152, "float32", (320, 1)),     # fp32: 288 vectors in 5 waves x 1
     (90, 2900, "float32", (384, 2)),      # fp32: 725 in 6 waves x 2 (94 %)
+    (5, 5376, "float16", (704, 1)),       # few rows past the one-block rule: 3 blocks, one holding 1 row
+    (3, 8200, "bfloat16", (576, 2)),      # 2 blocks for 3 rows
+    (17, 1152, "bfloat16", (192, 1)),     # 17 rows in blocks of 4 slots (past 32 KiB): ragged groups
 ]
 
 
