@@ -268,14 +268,17 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
         // and fp32 rows of 512 lanes (D = 8192).
         const bool wide_ok = vjp;
         const int vmode = op == RMSN_OP_GRAD ? 1 : op == RMSN_OP_FUSED_VJP ? 2 : 0;
-        if (vb == 16 && !ovl &&
+        // (rows whose last vector is overlapped enter only for the
+        // backward forms' duplicate-slot layouts below)
+        const bool ovl_dup_only = ovl && vjp && lanes == 0 && k == 0;
+        if (vb == 16 && (!ovl || ovl_dup_only) &&
             (lanes == 0 ? k == 0 : (rmsn::wave_rows(lanes) || (wide_ok && k == 4 && lanes == 512)))) {
             // the first of 2, 1, 4 vectors per lane that tiles the row and
             // has an instance
             int wl = 0, wk = 0;
             const void* fn = nullptr;
             for (int kk : {2, 1, 4}) {
-                if (fn || (k != 0 && kk != k) || p->nvec % kk != 0 || (kk == 4 && !wide_ok)) continue;
+                if (fn || ovl || (k != 0 && kk != k) || p->nvec % kk != 0 || (kk == 4 && !wide_ok)) continue;
                 if ((few_rows_k1 || few_rows_vjp) && kk != 1) continue;
                 const int l = p->nvec / kk;
                 const bool tiles = (rmsn::wave_rows(l) && rmsn::wave_rows_supported(l)) || (kk == 4 && l == 512);
@@ -309,18 +312,32 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
             // 41.4 / 54.0 / 50.0 us; 2304 60.8 / 66.1 / 73.7 -> 40.3 / 52.4 /
             // 49.6; 5376 51.2 / 59.2 / 60.7 -> 40.7 / 52.7 / 50.6).  A
             // requested wave-row lane count with more slots than the row's
-            // vectors (at most twice as many) takes them too.
+            // vectors (at most twice as many) takes them too.  Rows whose
+            // last vector is overlapped (D = 500, 511, 2049, 4097, 8191 ...)
+            // take them as well, with as many slots as vectors included,
+            // instead of the masked plain loop (fp16 / bf16, 64 MiB tensors,
+            // VJP / grad call / fused backward: D = 2049 58.8 / 66.8 / 75.8
+            // -> 49.5 / 60.7 / 68.1 us; 4097 73.7 / 88.1 / 96.8 -> 54.7 /
+            // 67.6 / 65.0; 6001 67.4 / 86.1 / 84.3 -> 53.2 / 64.1 / 62.7).
+            // On rows of at most 128 vectors (one wave x 2) the grad call
+            // keeps the plain loop (D = 768 5.15 against 4.87 TB/s,
+            // overlapped D = 500 57.3 against 70.0 us), and so does the VJP
+            // on overlapped ones (42.5 against 44.2 us); the fused backward
+            // gains there too (500: 62.4 -> 52.4 us).
             bool dup = false;
-            if (!fn && vjp && !few_rows_vjp) {
+            const bool one_wave_keeps_plain =
+                lanes == 0 && p->nvec <= 128 && (op == RMSN_OP_GRAD || (ovl && op == RMSN_OP_VJP));
+            if (!fn && vjp && !few_rows_vjp && !one_wave_keeps_plain) {
                 double best = lanes == 0 ? 0.75 : 0.5;
                 for (int kk : {2, 1}) {
                     if (k != 0 && kk != k) continue;
                     const int l = lanes != 0 ? lanes : 64 * static_cast<int>((p->nvec + 64 * kk - 1) / (64 * kk));
                     const int64_t nslot = (int64_t)l * kk;
-                    if (nslot <= p->nvec || nslot > 2 * (int64_t)p->nvec) continue;
+                    if (nslot < p->nvec || (nslot == p->nvec && !ovl) || nslot > 2 * (int64_t)p->nvec) continue;
                     const double fill = static_cast<double>(p->nvec) / static_cast<double>(nslot);
                     if (fill < best || (dup && fill == best)) continue;
-                    const void* f = rmsn::vjp_kernel_dup(dt, p->nv, kk, vmode, l);
+                    const void* f = ovl ? rmsn::vjp_kernel_dup_ovl(dt, p->nv, kk, vmode, l)
+                                        : rmsn::vjp_kernel_dup(dt, p->nv, kk, vmode, l);
                     if (!f) continue;
                     fn = f;
                     wl = l;
@@ -854,7 +871,9 @@ int vjp_impl(const void* x, const void* w, const void* dy, void* y, const void* 
     const int mode = grad ? 1 : resgrad ? 2 : 0;
     if (p.k == -2) return colsplit_launch(p, x, w, dy, y, dres, dx, dw, dw_dt, ws, rows, D, dt, eps, wb, hs);
     const void* fn = nullptr;
-    if (p.ovl) {
+    if (p.dup && p.ovl) {
+        fn = rmsn::vjp_kernel_dup_ovl(dt, p.nv, p.k, mode, p.lanes);
+    } else if (p.ovl) {
         fn = rmsn::vjp_kernel_ovl(dt, p.k, mode);
     } else {
         fn = p.dup           ? rmsn::vjp_kernel_dup(dt, p.nv, p.k, mode, p.lanes)

@@ -80,18 +80,21 @@ __device__ __forceinline__ Cols<K> make_cols(int lanes, int lane, int nvec, int 
 
 // Duplicate slots: a vector slot past the row's end (v >= nvec; the plan
 // keeps lanes * K <= 2 nvec) takes the columns of vector v - nvec, which
-// another slot owns.  It loads the same data and the same gain, and stores
-// the very values the owner stores; only the row sums and dw leave it out
-// (ok[k] false).  Past 2 nvec slots (never planned) it would take the row's
-// last vector, still inside the row.
-template <int K>
-__device__ __forceinline__ Cols<K> make_dup_cols(int lanes, int lane, int nvec, int nv) {
-    Cols<K> c(lanes, lane, nvec, nv);
+// another slot owns (with OVL, the last vector's shifted columns).  It loads
+// the same data and the same gain, and stores the very values the owner
+// stores; only the row sums and dw leave it out (ok[k] false).  Past 2 nvec
+// slots (never planned) it would take the row's last vector, still inside
+// the row.
+template <int K, bool OVL>
+__device__ __forceinline__ Cols<K> make_dup_cols(int lanes, int lane, int nvec, int nv, int64_t D) {
+    Cols<K> c = make_cols<K, OVL>(lanes, lane, nvec, nv, D);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const int v = k * lanes + lane;
         const int owner = v - nvec < nvec ? v - nvec : nvec - 1;
-        if (!c.ok[k]) c.off[k] = (int64_t)owner * nv;
+        int64_t o = (int64_t)owner * nv;
+        if (OVL && o > D - nv) o = D - nv;
+        if (!c.ok[k]) c.off[k] = o;
     }
     return c;
 }
@@ -370,7 +373,9 @@ __device__ __forceinline__ void vjp_process(const RowArgs& a, int64_t row0, int 
 #pragma unroll
         for (int e = 0; e < NV; ++e) {
             if constexpr (DUP) {
-                const float xv = c.ok[k] ? elem(d.x[k], e) : 0.0f;  // a duplicate slot adds nothing
+                // a duplicate slot adds nothing, nor does an overlapped element
+                const bool live = c.ok[k] && (!OVL || e >= c.skip[k]);
+                const float xv = live ? elem(d.x[k], e) : 0.0f;
                 const float dv = elem(d.dy[k], e);
                 s2[0] = __builtin_fmaf(xv, xv, s2[0]);
                 s2[1] = __builtin_fmaf(dv * g[k][e], xv, s2[1]);
@@ -484,7 +489,8 @@ __global__ __launch_bounds__(!PIPE ? (OVL ? max_block_threads_ovl(2, K, NV, size
     static_assert(LANES == 0 || (PIPE && (((LANES & (LANES - 1)) == 0 && LANES <= kVjpPipeFixedMax) ||
                                           wave_rows_supported(LANES))),
                   "fixed lane counts are pipelined: powers of two or supported whole numbers of waves");
-    static_assert(!OVL || (!PIPE && LANES == 0), "overlapped rows run in the plain row loop");
+    static_assert(!OVL || (!PIPE && LANES == 0) || DUP,
+                  "overlapped rows run in the plain row loop or in the duplicate-slot instances");
     static_assert(!DUP || (PIPE && LANES > 0), "duplicate slots run in the pipelined fixed-width instances");
     extern __shared__ float dyn[];
     __shared__ float red[2 * 16 * 2];
@@ -501,7 +507,7 @@ __global__ __launch_bounds__(!PIPE ? (OVL ? max_block_threads_ovl(2, K, NV, size
     const int slot = rs.slot;
     const int nslots = rs.nslots;
     const Cols<K> c =
-        DUP ? make_dup_cols<K>(lanes, lane, a.nvec, NV) : make_cols<K, OVL>(lanes, lane, a.nvec, NV, a.D);
+        DUP ? make_dup_cols<K, OVL>(lanes, lane, a.nvec, NV, a.D) : make_cols<K, OVL>(lanes, lane, a.nvec, NV, a.D);
     const int64_t step = (int64_t)gridDim.x * nslots;
     int64_t row0 = (int64_t)blockIdx.x * nslots;
 
@@ -556,15 +562,15 @@ __global__ __launch_bounds__(!PIPE ? (OVL ? max_block_threads_ovl(2, K, NV, size
             for (;;) {  // ra holds group row0
                 if (next >= a.rows) {  // the block's last group, possibly ragged
                     if (kOneRow || row0 + nslots <= a.rows)
-                        vjp_process<T, NV, K, MODE, true, kOneRow, false, DUP>(a, row0, slot, lanes, c, g, acc,
+                        vjp_process<T, NV, K, MODE, true, kOneRow, OVL, DUP>(a, row0, slot, lanes, c, g, acc,
                                                                                ra, kDrOwn ? drs : ra.dr, red, parity);
                     else if constexpr (!kOneRow)
-                        vjp_process<T, NV, K, MODE, false>(a, row0, slot, lanes, c, g, acc, ra,
+                        vjp_process<T, NV, K, MODE, false, false, OVL, DUP>(a, row0, slot, lanes, c, g, acc, ra,
                                                            kDrOwn ? drs : ra.dr, red, parity);
                     break;
                 }
                 vjp_issue<T, NV, K, MODE, !kDrOwn>(a, next, slot, c, rb);
-                vjp_process<T, NV, K, MODE, true, kOneRow, false, DUP>(a, row0, slot, lanes, c, g, acc, ra,
+                vjp_process<T, NV, K, MODE, true, kOneRow, OVL, DUP>(a, row0, slot, lanes, c, g, acc, ra,
                                                                        kDrOwn ? drs : ra.dr, red, parity);
                 if constexpr (kDrOwn) vjp_issue_dr<T, NV, K>(a, next, slot, c, drs);
                 row0 = next;
@@ -572,15 +578,15 @@ __global__ __launch_bounds__(!PIPE ? (OVL ? max_block_threads_ovl(2, K, NV, size
                 // rb holds group row0
                 if (next >= a.rows) {  // the block's last group, possibly ragged
                     if (kOneRow || row0 + nslots <= a.rows)
-                        vjp_process<T, NV, K, MODE, true, kOneRow, false, DUP>(a, row0, slot, lanes, c, g, acc,
+                        vjp_process<T, NV, K, MODE, true, kOneRow, OVL, DUP>(a, row0, slot, lanes, c, g, acc,
                                                                                rb, kDrOwn ? drs : rb.dr, red, parity);
                     else if constexpr (!kOneRow)
-                        vjp_process<T, NV, K, MODE, false>(a, row0, slot, lanes, c, g, acc, rb,
+                        vjp_process<T, NV, K, MODE, false, false, OVL, DUP>(a, row0, slot, lanes, c, g, acc, rb,
                                                            kDrOwn ? drs : rb.dr, red, parity);
                     break;
                 }
                 vjp_issue<T, NV, K, MODE, !kDrOwn>(a, next, slot, c, ra);
-                vjp_process<T, NV, K, MODE, true, kOneRow, false, DUP>(a, row0, slot, lanes, c, g, acc, rb,
+                vjp_process<T, NV, K, MODE, true, kOneRow, OVL, DUP>(a, row0, slot, lanes, c, g, acc, rb,
                                                                        kDrOwn ? drs : rb.dr, red, parity);
                 if constexpr (kDrOwn) vjp_issue_dr<T, NV, K>(a, next, slot, c, drs);
                 row0 = next;

@@ -99,6 +99,15 @@ constexpr bool vjp_dup_fit(int lanes, int k, int itemsize, int mode) {
     return (k == 1 || k == 2) && lanes % 64 == 0 && lanes >= 64 && lanes <= 960 &&
            vjp_wave_rows_fit(lanes, k, itemsize, mode);
 }
+// The same for rows whose last vector is overlapped (the skip counts and
+// their selects take registers): the grad call and the fused backward hold
+// 16-bit rows of one vector per lane only, and the fp32 fused backward rows
+// of at most 13 waves with two, where the exact instances' budget holds
+// them without spills.
+constexpr bool vjp_dup_ovl_fit(int lanes, int k, int itemsize, int mode) {
+    return vjp_dup_fit(lanes, k, itemsize, mode) && (mode == 0 || k * (16 / itemsize) < kVjpPipeElems) &&
+           !(itemsize == 4 && mode == 2 && k == 2 && lanes > 832);
+}
 // Largest block of a pipelined instance with the lanes fixed at compile
 // time (its launch bound): wave rows as above; power-of-two lanes one row of
 // 256 lanes or more, or up to 256 threads of shorter rows.
@@ -127,8 +136,10 @@ const void* vjp_kernel_fixed_lanes(int dt, int nv, int k, int mode, int lanes);
 // The wave-row instances (lanes = 64 W, W not a power of two), or nullptr.
 const void* fwd_kernel_wave_rows(int dt, int nv, int k, bool fused, int lanes);
 const void* vjp_kernel_wave_rows(int dt, int nv, int k, int mode, int lanes);
-// The duplicate-slot instances (vjp_dup_fit), or nullptr.
+// The duplicate-slot instances (vjp_dup_fit), or nullptr; _ovl: for rows
+// whose last vector is overlapped.
 const void* vjp_kernel_dup(int dt, int nv, int k, int mode, int lanes);
+const void* vjp_kernel_dup_ovl(int dt, int nv, int k, int mode, int lanes);
 // Rows that are not a whole number of 16-byte vectors, the last vector
 // overlapped (forward, and the backward forms' plain row loop), or nullptr.
 const void* fwd_kernel_ovl(int dt, int k, bool fused);

@@ -39,7 +39,7 @@ if ROOT not in sys.path:
 METRIC = "achieved HBM GB/s (% of peak) for RMSNorm fwd+VJP, 8192x4096 fp16"
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SOURCES = ["rmsn_kernels.hpp", "rmsn_device.hpp", "rmsn_launch.hpp", "rmsn_vjp.hip", "rmsn_vjp_lanes.hip",
-                  "rmsn_vjp_waves.hip", "rmsn_vjp_dup.hip", "rmsn_fwd.hip", "rmsn_fwd_waves.hip", "rmsn_ovl.hip",
+                  "rmsn_vjp_waves.hip", "rmsn_vjp_dup.hip", "rmsn_vjp_dup_ovl.hip", "rmsn_fwd.hip", "rmsn_fwd_waves.hip", "rmsn_ovl.hip",
                   "rmsn_colsplit.hip", "rmsn_api.hip"]
 GATE_SOURCES = ["rmsn_gate.hip", "rmsn_device.hpp", "rmsn_api.hip"]
 
@@ -657,7 +657,9 @@ def wide_bench(R, dev, args) -> int:
 def widths_bench(R, dev, args) -> int:
     """Every RMSNorm op across model widths (bf16, D = 1152 .. 16384, among
     them widths that no lane count tiles exactly -- 1152, 2304, 3840, 5376 --
-    rows = 2^25 / D: 64 MiB per row tensor), cold: buffer sets rotate so that
+    rows = 2^25 / D: 64 MiB per row tensor; then fp16 odd widths whose rows
+    end in an overlapped vector, D = 2049, 4097, 6001, 8191), cold: buffer
+    sets rotate so that
     no call finds its inputs in the 256 MB last-level cache.  Inputs
     are drawn on the device from a seeded generator (x, residual ~ N(0, 1),
     dy, d_new_residual ~ N(0, 0.01), w ~ N(0, 0.1); weight_bias 1, eps
@@ -686,13 +688,17 @@ def widths_bench(R, dev, args) -> int:
     for D in (1152, 1536, 2048, 2304, 2560, 3072, 3584, 3840, 4096, 4608, 5120, 5376, 5632, 6144, 6656, 7168, 7680,
               8192, 9216, 10240, 11264, 12288, 14336, 16384):
         grid.append(measure_ops(R, dev, (1 << 25) // D, D, 10, timed, gen))
+    # odd widths (fp16 rows whose last 16-byte vector is overlapped), same
+    # 64 MiB tensors
+    odd = [measure_ops(R, dev, (1 << 25) // D, D, 10, timed, gen, dt=torch.float16) for D in (2049, 4097, 6001, 8191)]
     worst = min(r["vjp"]["GBps"] for r in grid)
     print(json.dumps({
         "metric": "achieved HBM GB/s of the RMSNorm VJP across model widths, bf16, 64 MiB tensors (value = worst D)",
         "value": worst, "unit": "GB/s", "n_gpus": 1, "steps": N, "warmup": 4, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "fwd, fused fwd, VJP, grad call, fused backward at bf16 [2^25 / D, D], "
-                               "D = 1536 .. 16384", "grid": grid},
+                               "D = 1152 .. 16384 (and fp16 odd widths D = 2049, 4097, 6001, 8191 under odd_grid)",
+                   "grid": grid, "odd_grid": odd},
     }), flush=True)
     return 0
 

@@ -16,7 +16,10 @@ are left out of the row sums and dw.  Checks:
   overwrite in place;
 - forced geometries (wave-row lane counts with more slots than vectors, one
   to four rows per block, small grids) against the oracle, and a request
-  with more than twice the row's vectors refused (RMSN_E_CONFIG)."""
+  with more than twice the row's vectors refused (RMSN_E_CONFIG);
+- rows whose last vector is overlapped (D x itemsize not a multiple of 16)
+  on duplicate slots: plan per form, every element against the oracle, in
+  place bit-identical to out of place."""
 import sys
 
 import numpy as np
@@ -162,3 +165,58 @@ def test_dup_rows_forced_geometries(R, rows):
         with pytest.raises(R.RMSNormError) as ei:
             R.rmsnorm_vjp(x, w, dy, eps, wb, cfg=cfg)
         assert ei.value.status == E_CONFIG, cfg
+
+
+# rows whose last vector is overlapped (D x itemsize not a multiple of 16):
+# (rows, D, dtype, {op: (lanes, vectors per lane)}); one-wave rows keep the
+# plain loop for the VJP and the grad call, and the 16-bit grad call and
+# fused backward take one vector per lane (two would not fit their
+# registers)
+OVL_CASES = [
+    (301, 500, "float16", {2: (32, 2), 3: (32, 2), 4: (64, 1)}),
+    (200, 2049, "bfloat16", {2: (320, 1), 3: (320, 1), 4: (320, 1)}),
+    (150, 4097, "float16", {2: (576, 1), 3: (576, 1), 4: (576, 1)}),
+    (100, 6001, "bfloat16", {2: (384, 2), 3: (768, 1), 4: (768, 1)}),
+    (64, 8191, "float16", {2: (512, 2), 3: (512, 2), 4: (512, 2)}),
+    (300, 1001, "float32", {2: (128, 2), 3: (128, 2), 4: (128, 2)}),
+]
+
+
+@pytest.mark.parametrize("rows,D,dtype,geoms", OVL_CASES)
+def test_dup_rows_overlapped_last_vector(R, rows, D, dtype, geoms):
+    c = I.generic(rows, D, dtype, seed=rows * 17 + D)
+    eps, wb = c["eps"], 0.5
+    x, w, dy, dr = (c[k].to(DEV) for k in ("x", "w", "dy", "residual"))
+    assert D * x.element_size() % 16 != 0
+    for op, geom in geoms.items():
+        q = R.query_config(op, rows, D, x.dtype)
+        _say(f"dup overlapped {dtype} {rows}x{D} op {op}: {q}")
+        assert (q["lanes_per_row"], q["vecs_per_lane"], q["vec_bytes"]) == (*geom, 16), (op, q)
+    dx, dw = R.rmsnorm_vjp(x, w, dy, eps, wb)
+    y, gdx, gdw = R.rmsnorm_fwd_vjp(x, w, dy, eps, wb)
+    dh, hdw = R.fused_add_rmsnorm_vjp(x, w, dy, dr, eps, wb)
+    zdh, _ = R.fused_add_rmsnorm_vjp(x, w, dy, torch.zeros_like(dr), eps, wb)
+    torch.cuda.synchronize()
+    dxref, dwref, yref, dhref = _oracle_all(c, eps, wb)
+    assert_close(dx, dxref, "dx")
+    assert_dw_close(dw, dwref, "dw")
+    assert_close(y, yref, "grad y")
+    assert_close(gdx, dxref, "grad dx")
+    assert_dw_close(gdw, dwref, "grad dw")
+    assert_close(dh, dhref, "dh")
+    assert_dw_close(hdw, dwref, "fused dw")
+    if geoms[3] == geoms[2]:
+        assert torch.equal(gdx, dx), "grad dx != VJP dx on the same layout"
+    if geoms[4] == geoms[2]:
+        assert torch.equal(zdh, dx), "fused backward with zero d_new_residual != VJP dx on the same layout"
+    # in place, the overlapped columns read by two slots included
+    xb = x.clone()
+    R.rmsnorm_vjp(xb, w, dy, eps, wb, dx=xb)
+    dyb = dy.clone()
+    R.rmsnorm_vjp(x, w, dyb, eps, wb, dx=dyb)
+    drb = dr.clone()
+    R.fused_add_rmsnorm_vjp(x, w, dy, drb, eps, wb, dh=drb)
+    torch.cuda.synchronize()
+    assert torch.equal(xb, dx), "dx over x"
+    assert torch.equal(dyb, dx), "dx over dy"
+    assert torch.equal(drb, dh), "dh over d_new_residual"
