@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "librmsnorm_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["rmsn_fwd.hip", "rmsn_fwd_waves.hip", "rmsn_vjp.hip", "rmsn_vjp_lanes.hip", "rmsn_vjp_waves.hip",
+SOURCES = ["rmsn_fwd.hip", "rmsn_fwd_waves.hip", "rmsn_fwd_waves_ovl.hip", "rmsn_vjp.hip", "rmsn_vjp_lanes.hip", "rmsn_vjp_waves.hip",
            "rmsn_vjp_dup.hip", "rmsn_vjp_dup_ovl.hip", "rmsn_ovl.hip", "rmsn_colsplit.hip", "rmsn_gate.hip",
            "rmsn_api.hip"]
 ARCH = "gfx950"

@@ -271,7 +271,8 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
         // (rows whose last vector is overlapped enter only for the
         // backward forms' duplicate-slot layouts below)
         const bool ovl_dup_only = ovl && vjp && lanes == 0 && k == 0;
-        if (vb == 16 && (!ovl || ovl_dup_only) &&
+        const bool ovl_fwd_waves = ovl && !vjp && lanes == 0 && k == 0 && !few_rows_k1;
+        if (vb == 16 && (!ovl || ovl_dup_only || ovl_fwd_waves) &&
             (lanes == 0 ? k == 0 : (rmsn::wave_rows(lanes) || (wide_ok && k == 4 && lanes == 512)))) {
             // the first of 2, 1, 4 vectors per lane that tiles the row and
             // has an instance
@@ -344,6 +345,39 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
                     wk = kk;
                     best = fill;
                     dup = true;
+                }
+            }
+            // Forward forms on rows whose last vector is overlapped: a whole
+            // number of waves (not a power of two) with one or two vectors
+            // per lane, the slots past the row's end masked, where it fills
+            // at least three quarters of its slots and more than the
+            // power-of-two layout below would (about half at D = 2049,
+            // 4097).  Rows of more than 512 vectors only where that layout
+            // (8 vectors per lane) fills under 65 % of its slots, and the
+            // fused forward only on rows of at most 256 vectors (fp16, 64
+            // MiB tensors, forward / fused forward: D = 4500 30.6 / 52.7 ->
+            // 28.1 / 49.3 us on 576 lanes; 3001 28.9 -> 27.3 and 2049 35.0
+            // -> 33.5 forward; 1500 50.1 -> 47.5 fused; but D = 7001 28.7 /
+            // 53.0 -> 31.7 / 57.9 on 448 x 2 against 128 x 8 at 85 % fill,
+            // 6001 bf16 -4 %, and the fused forward of 2049 57.5 -> 59.1).
+            const int64_t pk = p->nvec > 512 ? 8 : p->nvec > (op == RMSN_OP_FWD ? 128 : 256) ? 4 : 2;
+            const int64_t pl = std::min<int64_t>(1024, next_pow2((p->nvec + pk - 1) / pk));
+            const double pfill = static_cast<double>(p->nvec) /
+                                 static_cast<double>(pl * next_pow2((p->nvec + pl - 1) / pl));
+            const bool waves_pay = p->nvec > 512 ? pfill < 0.65 : (op == RMSN_OP_FWD || p->nvec <= 256);
+            if (!fn && ovl_fwd_waves && p->nvec <= 1024 && waves_pay) {
+                double best = std::max(0.75, pfill + 0.05);
+                for (int kk : {2, 1}) {
+                    const int l = 64 * static_cast<int>((p->nvec + 64 * kk - 1) / (64 * kk));
+                    if (!rmsn::wave_rows(l) || !rmsn::wave_rows_supported(l)) continue;
+                    const double fill = static_cast<double>(p->nvec) / (static_cast<double>(l) * kk);
+                    if (fill < best || (fn && fill == best)) continue;
+                    const void* f = rmsn::fwd_kernel_wave_rows_ovl(dt, p->nv, kk, op == RMSN_OP_FUSED, l);
+                    if (!f) continue;
+                    fn = f;
+                    wl = l;
+                    wk = kk;
+                    best = fill;
                 }
             }
             // one, two or four rows per block, as the registers allow
@@ -733,8 +767,9 @@ int fwd_impl(bool fused, const void* x, const void* res, const void* w, void* y,
     if (st != RMSN_OK) return st;
     const void* fn = nullptr;
     if (p.ovl) {
-        fn = rmsn::fwd_kernel_ovl_fixed(dt, p.k, fused, p.lanes);
-        if (!fn) fn = rmsn::fwd_kernel_ovl(dt, p.k, fused);
+        fn = rmsn::wave_rows(p.lanes) ? rmsn::fwd_kernel_wave_rows_ovl(dt, p.nv, p.k, fused, p.lanes)
+                                      : rmsn::fwd_kernel_ovl_fixed(dt, p.k, fused, p.lanes);
+        if (!fn && !rmsn::wave_rows(p.lanes)) fn = rmsn::fwd_kernel_ovl(dt, p.k, fused);
     } else {
         fn = p.k > 0 && !p.fwd_generic ? rmsn::fwd_kernel_fixed_lanes(dt, p.nv, p.k, fused, p.lanes) : nullptr;
         if (!fn && !(p.k > 0 && rmsn::wave_rows(p.lanes))) fn = rmsn::fwd_kernel(dt, p.nv, p.k, fused);

@@ -144,6 +144,7 @@ const void* vjp_kernel_dup_ovl(int dt, int nv, int k, int mode, int lanes);
 // overlapped (forward, and the backward forms' plain row loop), or nullptr.
 const void* fwd_kernel_ovl(int dt, int k, bool fused);
 const void* fwd_kernel_ovl_fixed(int dt, int k, bool fused, int lanes);
+const void* fwd_kernel_wave_rows_ovl(int dt, int nv, int k, bool fused, int lanes);
 const void* vjp_kernel_ovl(int dt, int k, int mode);
 // Column-split backward forms: threads per block (both kernels), vectors per
 // thread in a statistics slice, rows per chunk of the apply kernel (their r

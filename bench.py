@@ -39,7 +39,7 @@ if ROOT not in sys.path:
 METRIC = "achieved HBM GB/s (% of peak) for RMSNorm fwd+VJP, 8192x4096 fp16"
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SOURCES = ["rmsn_kernels.hpp", "rmsn_device.hpp", "rmsn_launch.hpp", "rmsn_vjp.hip", "rmsn_vjp_lanes.hip",
-                  "rmsn_vjp_waves.hip", "rmsn_vjp_dup.hip", "rmsn_vjp_dup_ovl.hip", "rmsn_fwd.hip", "rmsn_fwd_waves.hip", "rmsn_ovl.hip",
+                  "rmsn_vjp_waves.hip", "rmsn_vjp_dup.hip", "rmsn_vjp_dup_ovl.hip", "rmsn_fwd.hip", "rmsn_fwd_waves.hip", "rmsn_fwd_waves_ovl.hip", "rmsn_ovl.hip",
                   "rmsn_colsplit.hip", "rmsn_api.hip"]
 GATE_SOURCES = ["rmsn_gate.hip", "rmsn_device.hpp", "rmsn_api.hip"]
 

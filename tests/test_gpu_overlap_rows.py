@@ -111,11 +111,41 @@ def test_plan_narrow_below_one_vector(R):
     ("float16", 9), ("float16", 15), ("float16", 17), ("float16", 257), ("float16", 500),
     ("float16", 511), ("float16", 513), ("bfloat16", 1025), ("bfloat16", 3001), ("float16", 4097),
     ("float16", 8191), ("bfloat16", 12289), ("float32", 5), ("float32", 97), ("float32", 1023),
-    ("float32", 4099)])
+    ("float32", 4099), ("float16", 1500), ("float16", 2049), ("float16", 4500), ("bfloat16", 4700),
+    ("float32", 2251)])
 @pytest.mark.parametrize("rows", [1, 300])
 def test_every_form_matches_oracle(R, dtype, D, rows):
     _say(f"overlapped rows {dtype} {rows}x{D}")
     _check_every_form(R, rows, D, dtype, seed=D + rows)
+
+
+# (dtype, D): the forward's and the fused forward's (lanes, vectors per lane)
+# on rows of a whole number of waves, or None where the power-of-two layout
+# stays
+WAVE_FWD = [("float16", 1500, (192, 1), (192, 1)), ("float16", 2049, (320, 1), None),
+            ("bfloat16", 3001, (192, 2), None), ("float16", 4500, (576, 1), (576, 1)),
+            ("bfloat16", 4700, (320, 2), (320, 2)), ("float32", 2251, (576, 1), (576, 1)),
+            ("float16", 7001, None, None), ("float16", 8191, None, None)]
+
+
+@pytest.mark.parametrize("dtype,D,fwd,fused", WAVE_FWD)
+def test_forward_wave_rows_plan(R, dtype, D, fwd, fused):
+    """The forward forms on overlapped rows take a whole number of waves
+    (lanes 64 W, W not a power of two) where the row fills most of its slots
+    and the power-of-two layout would leave many masked; elsewhere they keep
+    the power-of-two layout."""
+    td = I.torch_dtype(dtype)
+    for op, want in ((0, fwd), (1, fused)):
+        q = R.query_config(op, 4096, D, td)
+        got = (q["lanes_per_row"], q["vecs_per_lane"])
+        lanes = q["lanes_per_row"]
+        wave = lanes > 64 and lanes & (lanes - 1) != 0
+        if want is None:
+            assert not wave, (op, q)
+        else:
+            assert got == want, (op, q)
+            assert q["block_threads"] in (lanes, 2 * lanes), q
+        assert lanes * q["vecs_per_lane"] * 16 >= D * _itemsize(dtype), q
 
 
 def test_small_axis_sweep_widths_full_size(R):
