@@ -319,7 +319,9 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
             // instead of the masked plain loop (fp16 / bf16, 64 MiB tensors,
             // VJP / grad call / fused backward: D = 2049 58.8 / 66.8 / 75.8
             // -> 49.5 / 60.7 / 68.1 us; 4097 73.7 / 88.1 / 96.8 -> 54.7 /
-            // 67.6 / 65.0; 6001 67.4 / 86.1 / 84.3 -> 53.2 / 64.1 / 62.7).
+            // 67.6 / 65.0; 6001 67.4 / 86.1 / 84.3 -> 53.2 / 64.1 / 62.7;
+            // the grad call and the fused backward on 1024 lanes x 1: 8191
+            // 79.0 / 78.9 -> 64.3 / 62.9).
             // On rows of at most 128 vectors (one wave x 2) the grad call
             // keeps the plain loop (D = 768 5.15 against 4.87 TB/s,
             // overlapped D = 500 57.3 against 70.0 us), and so does the VJP

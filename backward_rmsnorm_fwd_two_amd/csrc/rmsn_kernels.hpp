@@ -486,7 +486,8 @@ __global__ __launch_bounds__(!PIPE ? (OVL ? max_block_threads_ovl(2, K, NV, size
     static_assert(!PIPE || K * NV <= kVjpPipeElems ||
                       (K * NV <= kVjpPipeElemsWide && LANES > 0 && LANES <= kVjpPipeFixedMax),
                   "pipelined instances hold two row groups");
-    static_assert(LANES == 0 || (PIPE && (((LANES & (LANES - 1)) == 0 && LANES <= kVjpPipeFixedMax) ||
+    static_assert(LANES == 0 || (PIPE && (((LANES & (LANES - 1)) == 0 &&
+                                           (LANES <= kVjpPipeFixedMax || (DUP && LANES == 1024))) ||
                                           wave_rows_supported(LANES))),
                   "fixed lane counts are pipelined: powers of two or supported whole numbers of waves");
     static_assert(!OVL || (!PIPE && LANES == 0) || DUP,

@@ -103,10 +103,14 @@ constexpr bool vjp_dup_fit(int lanes, int k, int itemsize, int mode) {
 // their selects take registers): the grad call and the fused backward hold
 // 16-bit rows of one vector per lane only, and the fp32 fused backward rows
 // of at most 13 waves with two, where the exact instances' budget holds
-// them without spills.
+// them without spills.  So that 16-bit rows of 961..1024 vectors (D = 7681
+// .. 8191) need not fall back to the plain loop for those two forms, they
+// also come with one vector per lane on 1024 lanes (one row per block, the
+// same 128-VGPR budget as the 960-lane instances).
 constexpr bool vjp_dup_ovl_fit(int lanes, int k, int itemsize, int mode) {
-    return vjp_dup_fit(lanes, k, itemsize, mode) && (mode == 0 || k * (16 / itemsize) < kVjpPipeElems) &&
-           !(itemsize == 4 && mode == 2 && k == 2 && lanes > 832);
+    return (vjp_dup_fit(lanes, k, itemsize, mode) && (mode == 0 || k * (16 / itemsize) < kVjpPipeElems) &&
+            !(itemsize == 4 && mode == 2 && k == 2 && lanes > 832)) ||
+           (lanes == 1024 && k == 1 && itemsize == 2 && mode != 0);
 }
 // Largest block of a pipelined instance with the lanes fixed at compile
 // time (its launch bound): wave rows as above; power-of-two lanes one row of

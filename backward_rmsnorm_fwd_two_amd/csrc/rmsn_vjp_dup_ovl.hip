@@ -39,6 +39,7 @@ const void* pick_lanes(int lanes) {
         case 832: return one<T, K, MODE, 832>();
         case 896: return one<T, K, MODE, 896>();
         case 960: return one<T, K, MODE, 960>();
+        case 1024: return one<T, K, MODE, 1024>();
         default: return nullptr;
     }
 }

@@ -177,7 +177,8 @@ OVL_CASES = [
     (200, 2049, "bfloat16", {2: (320, 1), 3: (320, 1), 4: (320, 1)}),
     (150, 4097, "float16", {2: (576, 1), 3: (576, 1), 4: (576, 1)}),
     (100, 6001, "bfloat16", {2: (384, 2), 3: (768, 1), 4: (768, 1)}),
-    (64, 8191, "float16", {2: (512, 2), 3: (512, 2), 4: (512, 2)}),
+    (64, 8191, "float16", {2: (512, 2), 3: (1024, 1), 4: (1024, 1)}),
+    (37, 7700, "bfloat16", {2: (512, 2), 3: (1024, 1), 4: (1024, 1)}),
     (300, 1001, "float32", {2: (128, 2), 3: (128, 2), 4: (128, 2)}),
 ]
 
