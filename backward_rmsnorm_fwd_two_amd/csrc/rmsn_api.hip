@@ -355,18 +355,20 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
             // at least three quarters of its slots and more than the
             // power-of-two layout below would (about half at D = 2049,
             // 4097).  Rows of more than 512 vectors only where that layout
-            // (8 vectors per lane) fills under 65 % of its slots, and the
-            // fused forward only on rows of at most 256 vectors (fp16, 64
-            // MiB tensors, forward / fused forward: D = 4500 30.6 / 52.7 ->
-            // 28.1 / 49.3 us on 576 lanes; 3001 28.9 -> 27.3 and 2049 35.0
-            // -> 33.5 forward; 1500 50.1 -> 47.5 fused; but D = 7001 28.7 /
-            // 53.0 -> 31.7 / 57.9 on 448 x 2 against 128 x 8 at 85 % fill,
-            // 6001 bf16 -4 %, and the fused forward of 2049 57.5 -> 59.1).
-            const int64_t pk = p->nvec > 512 ? 8 : p->nvec > (op == RMSN_OP_FWD ? 128 : 256) ? 4 : 2;
+            // (8 vectors per lane) fills under 65 % of its slots; below, the
+            // forward on rows of more than 256 vectors and the fused forward
+            // on rows of at most 256 (fp16, 64 MiB tensors, forward / fused
+            // forward: D = 4500 30.6 / 52.7 -> 28.1 / 49.3 us on 576 lanes;
+            // 3001 28.9 -> 27.3 and 2049 35.0 -> 33.5 forward; 1500 50.1 ->
+            // 47.5 fused; but D = 7001 28.7 / 53.0 -> 31.7 / 57.9 on 448 x 2
+            // against 128 x 8 at 85 % fill, 6001 bf16 -4 %, the fused
+            // forward of 2049 57.5 -> 59.1, and the forward of 1300 27.5 ->
+            // 29.6 on 192 x 1 against 64 x 4).
+            const int64_t pk = p->nvec > 512 ? 8 : p->nvec > 256 ? 4 : 2;
             const int64_t pl = std::min<int64_t>(1024, next_pow2((p->nvec + pk - 1) / pk));
             const double pfill = static_cast<double>(p->nvec) /
                                  static_cast<double>(pl * next_pow2((p->nvec + pl - 1) / pl));
-            const bool waves_pay = p->nvec > 512 ? pfill < 0.65 : (op == RMSN_OP_FWD || p->nvec <= 256);
+            const bool waves_pay = p->nvec > 512 ? pfill < 0.65 : (op == RMSN_OP_FWD) == (p->nvec > 256);
             if (!fn && ovl_fwd_waves && p->nvec <= 1024 && waves_pay) {
                 double best = std::max(0.75, pfill + 0.05);
                 for (int kk : {2, 1}) {
@@ -472,15 +474,18 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
             if (op == RMSN_OP_FWD && vb == 16 && p->nvec > 1024 && p->nvec <= 2048) kt = 8;
             // Forward forms on overlapped rows (their vector counts rarely
             // fill a power of two): 8 vectors per lane on rows of 513..1024
-            // vectors, 4 from 129 (the forward) or 257 (the fused forward)
-            // -- fp16, 64 MiB tensors: forward D = 6001 33.0 -> 29.9 us,
-            // 8191 31.3 -> 28.5, 4097 39.8 -> 34.8; fused forward D = 2049
-            // 71.6 -> 58.9, 3001 60.9 -> 51.6, 6001 63.7 -> 54.9, 8191
-            // 57.5 -> 50.8 (D = 4500 ran 8 % slower that way).
+            // vectors, 4 from 257 -- fp16, 64 MiB tensors: forward D = 6001
+            // 33.0 -> 29.9 us, 8191 31.3 -> 28.5, 4097 39.8 -> 34.8; fused
+            // forward D = 2049 71.6 -> 58.9, 3001 60.9 -> 51.6, 6001 63.7 ->
+            // 54.9, 8191 57.5 -> 50.8 (D = 4500 ran 8 % slower that way).
+            // On rows of 129..256 vectors the forward keeps 2 (128 lanes;
+            // against 4 on 64: D = 1025 33.9 -> 33.1, 1201 31.6 -> 29.6,
+            // 1450 bf16 27.9 -> 25.9, 1500 27.1 -> 26.0, 1601 28.9 -> 27.4;
+            // 1100 28.1 -> 28.7), unlike rows of whole vectors (below).
             if (ovl && !vjp && p->nvec <= 1024) {
                 if (p->nvec > 512)
                     kt = 8;
-                else if (p->nvec > (op == RMSN_OP_FWD ? 128 : 256))
+                else if (p->nvec > 256)
                     kt = 4;
             }
             if (few_rows_k1 || few_rows_vjp) kt = 1;
@@ -492,7 +497,7 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
             // faster cold (bf16 64 MiB: D = 4608 25.3 vs 29.1 us, 2560 24.8
             // vs 27.0, 1536 23.7 vs 24.9, 3584 24.8 vs 25.0; full rows keep 2
             // vectors).
-            if (op == RMSN_OP_FWD && vb == 16 && kt == 2 && p->nvec > 128 && p->nvec <= 1024 &&
+            if (op == RMSN_OP_FWD && vb == 16 && !ovl && kt == 2 && p->nvec > 128 && p->nvec <= 1024 &&
                 (int64_t)p->nvec * 10 < (int64_t)lanes * k * 9) {
                 kt = 4;
                 lanes = std::min(1024, next_pow2((p->nvec + kt - 1) / kt));

@@ -122,7 +122,7 @@ def test_every_form_matches_oracle(R, dtype, D, rows):
 # (dtype, D): the forward's and the fused forward's (lanes, vectors per lane)
 # on rows of a whole number of waves, or None where the power-of-two layout
 # stays
-WAVE_FWD = [("float16", 1500, (192, 1), (192, 1)), ("float16", 2049, (320, 1), None),
+WAVE_FWD = [("float16", 1500, None, (192, 1)), ("float16", 1300, None, (192, 1)), ("float16", 2049, (320, 1), None),
             ("bfloat16", 3001, (192, 2), None), ("float16", 4500, (576, 1), (576, 1)),
             ("bfloat16", 4700, (320, 2), (320, 2)), ("float32", 2251, (576, 1), (576, 1)),
             ("float16", 7001, None, None), ("float16", 8191, None, None)]
