@@ -269,9 +269,11 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
         const bool wide_ok = vjp;
         const int vmode = op == RMSN_OP_GRAD ? 1 : op == RMSN_OP_FUSED_VJP ? 2 : 0;
         // (rows whose last vector is overlapped enter only for the
-        // backward forms' duplicate-slot layouts below)
+        // backward forms' duplicate-slot layouts and the forward forms'
+        // masked whole-wave layouts below, the latter also on request)
         const bool ovl_dup_only = ovl && vjp && lanes == 0 && k == 0;
-        const bool ovl_fwd_waves = ovl && !vjp && lanes == 0 && k == 0 && !few_rows_k1;
+        const bool ovl_fwd_req = ovl && !vjp && lanes != 0 && rmsn::wave_rows(lanes);
+        const bool ovl_fwd_waves = ovl && !vjp && ((lanes == 0 && k == 0 && !few_rows_k1) || ovl_fwd_req);
         if (vb == 16 && (!ovl || ovl_dup_only || ovl_fwd_waves) &&
             (lanes == 0 ? k == 0 : (rmsn::wave_rows(lanes) || (wide_ok && k == 4 && lanes == 512)))) {
             // the first of 2, 1, 4 vectors per lane that tiles the row and
@@ -369,10 +371,15 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
             const double pfill = static_cast<double>(p->nvec) /
                                  static_cast<double>(pl * next_pow2((p->nvec + pl - 1) / pl));
             const bool waves_pay = p->nvec > 512 ? pfill < 0.65 : (op == RMSN_OP_FWD) == (p->nvec > 256);
-            if (!fn && ovl_fwd_waves && p->nvec <= 1024 && waves_pay) {
-                double best = std::max(0.75, pfill + 0.05);
-                for (int kk : {2, 1}) {
-                    const int l = 64 * static_cast<int>((p->nvec + 64 * kk - 1) / (64 * kk));
+            // A requested whole-wave lane count (and vectors per lane, or
+            // the fewest that hold the row) is taken as asked.
+            if (!fn && ovl_fwd_waves && p->nvec <= 1024 && (waves_pay || ovl_fwd_req)) {
+                double best = ovl_fwd_req ? 0.0 : std::max(0.75, pfill + 0.05);
+                static constexpr int kAsked[2] = {1, 2}, kAuto[2] = {2, 1};
+                for (int i = 0; i < 2; ++i) {
+                    const int kk = (ovl_fwd_req ? kAsked : kAuto)[i];
+                    if (ovl_fwd_req && (fn || (k != 0 && kk != k) || (int64_t)lanes * kk < p->nvec)) continue;
+                    const int l = ovl_fwd_req ? lanes : 64 * static_cast<int>((p->nvec + 64 * kk - 1) / (64 * kk));
                     if (!rmsn::wave_rows(l) || !rmsn::wave_rows_supported(l)) continue;
                     const double fill = static_cast<double>(p->nvec) / (static_cast<double>(l) * kk);
                     if (fill < best || (fn && fill == best)) continue;

@@ -148,6 +148,37 @@ def test_forward_wave_rows_plan(R, dtype, D, fwd, fused):
         assert lanes * q["vecs_per_lane"] * 16 >= D * _itemsize(dtype), q
 
 
+@pytest.mark.parametrize("dtype,D,geoms", [
+    ("float16", 2049, [(192, 2, 0), (320, 1, 0), (320, 1, 640), (576, 1, 0), (960, 1, 0), (320, 2, 0)]),
+    ("bfloat16", 4097, [(576, 1, 0), (320, 2, 0), (704, 1, 0), (960, 1, 0), (576, 0, 0)]),
+    ("float32", 1001, [(192, 2, 384), (320, 1, 0), (448, 1, 896)])])
+def test_forced_forward_wave_rows(R, dtype, D, geoms):
+    """Requested whole-wave geometries (lanes 64 W, one or two vectors per
+    lane, one or two rows per block) of the forward forms on overlapped rows,
+    every element against the oracle at a ragged row count."""
+    rows = 301
+    c = I.generic(rows, D, dtype, seed=D + 7)
+    rng = np.random.default_rng(D)
+    dr = I.normal(rng, (rows, D), 0.0, 0.5, dtype)
+    xg, wg, drg = _gpu(c["x"]), _gpu(c["w"]), _gpu(dr)
+    eps = c["eps"]
+    yref, _ = O.rmsnorm_fwd(c["x"], c["w"], eps, 1.0)
+    nref, href = O.fused_add_rmsnorm_fwd(c["x"], dr, c["w"], eps, 1.0)
+    for lanes, k, block in geoms:
+        cfg = dict(lanes_per_row=lanes, vecs_per_lane=k, vec_bytes=16, block_threads=block, num_blocks=0)
+        _say(f"forced forward wave rows {dtype} {rows}x{D} {cfg}")
+        y = R.rmsnorm_fwd(xg, wg, eps, 1.0, cfg=cfg)
+        normed, newres = R.fused_add_rmsnorm_fwd(xg, drg, wg, eps, 1.0, cfg=cfg)
+        torch.cuda.synchronize()
+        assert_close(y, yref, f"{cfg} y")
+        assert_close(normed, nref, f"{cfg} normed")
+        np.testing.assert_array_equal(to64(newres), O.round_to(href, dtype), err_msg=f"{cfg} new_residual")
+    # a lane count too small for the row, and three vectors per lane, are refused
+    for bad in (dict(lanes_per_row=192, vecs_per_lane=1), dict(lanes_per_row=192, vecs_per_lane=4)):
+        with pytest.raises(R.RMSNormError):
+            R.rmsnorm_fwd(xg, wg, eps, 1.0, cfg=dict(vec_bytes=16, block_threads=0, num_blocks=0, **bad))
+
+
 def test_small_axis_sweep_widths_full_size(R):
     """The sweep's odd widths at their full 16384 rows, every element."""
     for D in (257, 500, 511, 513):
