@@ -131,7 +131,11 @@ typedef struct {
                                rows 512 lanes with 4, one row per block; the backward forms
                                also take wave rows with more vector slots than the row has
                                vectors (at most twice as many; the slots past the row's end
-                               redo slots inside it) */
+                               redo slots inside it); on rows that are not a whole number of
+                               16-byte vectors (the last one overlapped) the forward forms
+                               take wave rows with vecs_per_lane 1, 2 or 0 (the fewest that
+                               hold the row) and at least as many slots as vectors, the slots
+                               past the row's end masked, at most 1024 vectors per row */
     int32_t vecs_per_lane;  /* vectors each thread holds per row: 1, 2, 4 or 8;
                                -1 selects the streaming (looped) kernel; -2 the
                                column-split backward forms (backward entry points
