@@ -487,7 +487,7 @@ __global__ __launch_bounds__(!PIPE ? (OVL ? max_block_threads_ovl(2, K, NV, size
                       (K * NV <= kVjpPipeElemsWide && LANES > 0 && LANES <= kVjpPipeFixedMax),
                   "pipelined instances hold two row groups");
     static_assert(LANES == 0 || (PIPE && (((LANES & (LANES - 1)) == 0 &&
-                                           (LANES <= kVjpPipeFixedMax || (DUP && LANES == 1024))) ||
+                                           (LANES <= kVjpPipeFixedMax || (LANES == 1024 && K == 1))) ||
                                           wave_rows_supported(LANES))),
                   "fixed lane counts are pipelined: powers of two or supported whole numbers of waves");
     static_assert(!OVL || (!PIPE && LANES == 0) || DUP,

@@ -20,6 +20,9 @@ const void* pick_lanes(int lanes) {
         case 128: return reinterpret_cast<const void*>(&vjp_rows<T, NV, K, MODE, true, 128>);
         case 256: return reinterpret_cast<const void*>(&vjp_rows<T, NV, K, MODE, true, 256>);
         case 512: return reinterpret_cast<const void*>(&vjp_rows<T, NV, K, MODE, true, 512>);
+        case 1024:
+            if constexpr (K == 1) return reinterpret_cast<const void*>(&vjp_rows<T, NV, K, MODE, true, 1024>);
+            return nullptr;
         default: return nullptr;
     }
 }

@@ -67,7 +67,7 @@ CASES = [
     (64, 12288, "float32"),     # plain loop: 1024 lanes x 3 of 4 vectors (no wave instance)
     (200, 8192, "float32"),     # fp32: 512 lanes x 4 vectors, one row per block
     (1000, 1024, "bfloat16"),   # pipelined: 64 lanes, 4 slots
-    (1024, 8192, "bfloat16"),   # pipelined: a 512-lane row per 512-thread block
+    (1024, 8192, "bfloat16"),   # pipelined: a 1024-lane row (one vector per lane) per block
     (1023, 8192, "float16"),    # pipelined, odd row count
     (512, 4096, "float32"),     # pipelined: 512 lanes x 2 x 4 floats
     (300, 11264, "bfloat16"),   # wave rows: 11 waves x 2
@@ -101,12 +101,13 @@ def test_vjp_paths_match_oracle(R, rows, D, dtype):
 
 # The shapes of CASES whose pipelined row geometry also has a plain-loop
 # instance in a wider block (power-of-two lanes up to 512, at most 16
-# elements per lane); wave rows and four-vector rows have no plain-loop twin
-# at their width, and their dx is checked bitwise across rows per block and
-# grids by test_wave_rows_geometry_and_bitwise.
+# elements per lane); wave rows, four-vector rows and 16-bit rows of 1024
+# vectors (1024 lanes x 1, one row per block) have no plain-loop twin at
+# their width, and their dx is checked bitwise across rows per block and
+# grids by test_wave_rows_geometry_and_bitwise and the repeat tests.
 PLAIN_TWIN = [c for c in CASES if (c[0], c[1]) in {
     (8192, 4096), (8191, 4096), (4096, 512), (4093, 512), (2048, 1024), (2047, 1024), (200, 8192),
-    (1000, 1024), (1024, 8192), (1023, 8192), (512, 4096)}]
+    (1000, 1024), (512, 4096)}]
 
 
 @pytest.mark.parametrize("rows,D,dtype", PLAIN_TWIN)
@@ -410,7 +411,7 @@ def test_few_rows_one_block_every_form(R, rows, D, dtype):
 
 def test_few_rows_rule_stops_where_rows_do_not_fit_one_block(R):
     bf = torch.bfloat16
-    assert R.query_config(2, 3, 8192, bf)["vecs_per_lane"] == 2       # 48 KiB per tensor
+    assert R.query_config(2, 3, 7168, bf)["vecs_per_lane"] == 2       # 42 KiB per tensor (448 x 2)
     assert R.query_config(2, 5, 4096, bf)["vecs_per_lane"] == 2       # 40 KiB
     assert R.query_config(2, 129, 128, bf)["vecs_per_lane"] == 2      # 33 KiB
     assert R.query_config(2, 1, 4096, torch.float32)["vecs_per_lane"] == 2   # fp32 rows of 1024 vectors
