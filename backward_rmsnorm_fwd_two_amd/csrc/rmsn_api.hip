@@ -496,15 +496,19 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
                     kt = 4;
             }
             if (few_rows_k1 || few_rows_vjp) kt = 1;
-            // The backward forms of 16-bit rows of exactly 1024 vectors (D =
-            // 8192) take one vector per lane on 1024 lanes, one row per
-            // block, pipelined (four waves per SIMD against two on 512 x 2):
-            // 4096 x 8192 bf16 VJP / grad call / fused backward 44.7 / 55.6
-            // / 54.2 -> 41.9 / 53.6 / 52.2 us, 8192 x 8192 fp16 75.2 / 98.9
-            // / 96.5 -> 73.5 / 96.4 / 93.6, 32768 x 8192 bf16 265.1 / 369.9
-            // / 352.1 -> 261.3 / 363.2 / 355.5; fp32 rows of 1024 vectors
-            // ran alike and keep 512 x 2.
-            if (vjp && !few_rows_vjp && !ovl && s == 2 && vb == 16 && p->nvec == 1024) kt = 1;
+            // The backward forms of 16-bit rows of exactly 512 or 1024
+            // vectors (D = 4096, 8192) take one vector per lane on as many
+            // lanes, one row per block, pipelined (twice the waves per SIMD
+            // of 256 x 2 / 512 x 2): 8192 x 4096 fp16 VJP / grad call /
+            // fused backward 42.2 / 53.0 / 50.5 -> 40.7 / 51.1 / 49.4 us,
+            // 16384 x 4096 bf16 76.0 / 95.2 / 92.6 -> 73.0 / 93.2 / 91.2;
+            // 4096 x 8192 bf16 44.7 / 55.6 / 54.2 -> 41.9 / 53.6 / 52.2,
+            // 8192 x 8192 fp16 75.2 / 98.9 / 96.5 -> 73.5 / 96.4 / 93.6,
+            // 32768 x 8192 bf16 265.1 / 369.9 / 352.1 -> 261.3 / 363.2 /
+            // 355.5.  fp32 rows of 1024 vectors ran alike and keep 512 x 2;
+            // rows of 256 vectors ran 7-21 % slower on 256 x 1 (D = 2048
+            // fp16) and keep 128 x 2.
+            if (vjp && !few_rows_vjp && !ovl && s == 2 && vb == 16 && (p->nvec == 512 || p->nvec == 1024)) kt = 1;
             lanes = std::min(1024, next_pow2((p->nvec + kt - 1) / kt));
             k = next_pow2((p->nvec + lanes - 1) / lanes);
             // The plain forward of a row of 129..1024 vectors that this

@@ -42,7 +42,7 @@ def _say(msg):
 # (rows, D, dtype): pipelined shapes (D tiles exactly; full or ragged last
 # row groups) next to plain ones (D that does not tile)
 CASES = [
-    (8192, 4096, "float16"),    # pipelined: 256 lanes x 2 vectors, one slot
+    (8192, 4096, "float16"),    # pipelined: 512 lanes x 1 vector, one row per block
     (8191, 4096, "float16"),    # still pipelined (one slot), odd row count
     (4096, 512, "bfloat16"),    # pipelined: 32 lanes, 8 row slots
     (4093, 512, "bfloat16"),    # pipelined, 8 slots: the last group is ragged (masked exit path)
@@ -412,7 +412,7 @@ def test_few_rows_one_block_every_form(R, rows, D, dtype):
 def test_few_rows_rule_stops_where_rows_do_not_fit_one_block(R):
     bf = torch.bfloat16
     assert R.query_config(2, 3, 7168, bf)["vecs_per_lane"] == 2       # 42 KiB per tensor (448 x 2)
-    assert R.query_config(2, 5, 4096, bf)["vecs_per_lane"] == 2       # 40 KiB
+    assert R.query_config(2, 6, 3072, bf)["vecs_per_lane"] == 2       # 36 KiB (192 x 2)
     assert R.query_config(2, 129, 128, bf)["vecs_per_lane"] == 2      # 33 KiB
     assert R.query_config(2, 1, 4096, torch.float32)["vecs_per_lane"] == 2   # fp32 rows of 1024 vectors
     q = R.query_config(2, 17, 1001, torch.float16)                     # overlapped, 34 KiB
