@@ -283,6 +283,16 @@ int make_plan(int op, int64_t rows, int64_t D, int dt, const rmsn_config_t* cfg,
             for (int kk : {2, 1, 4}) {
                 if (fn || ovl || (k != 0 && kk != k) || p->nvec % kk != 0 || (kk == 4 && !wide_ok)) continue;
                 if ((few_rows_k1 || few_rows_vjp) && kk != 1) continue;
+                // The backward forms of 16-bit rows of 10 to 15 whole waves of
+                // vectors (D = 5120 ... 7680) take one vector per lane, one row
+                // per block, rather than two on half the lanes (bf16 / fp16,
+                // 64 MiB tensors, VJP / grad call / fused backward: D = 5120
+                // 42.2 / 52.7 / 52.8 -> 40.1 / 51.5 / 51.1 us, 6144 42.5 /
+                // 54.5 / 53.3 -> 39.9 / 52.9 / 52.1, 7168 44.2 / 55.3 / 53.3
+                // -> 41.3 / 53.3 / 52.3; at 3072 the two ran within 3 %).
+                if (vjp && lanes == 0 && k == 0 && kk == 2 && s == 2 && p->nvec >= 640 && p->nvec <= 960 &&
+                    p->nvec % 64 == 0)
+                    continue;
                 const int l = p->nvec / kk;
                 const bool tiles = (rmsn::wave_rows(l) && rmsn::wave_rows_supported(l)) || (kk == 4 && l == 512);
                 if ((lanes != 0 && l != lanes) || !tiles) continue;

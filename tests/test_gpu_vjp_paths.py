@@ -52,10 +52,10 @@ CASES = [
     (1200, 1536, "bfloat16"),   # wave rows: 3 waves x 1 vector, four rows per block
     (1202, 1536, "float16"),    # wave rows, four rows per block, rows % 4 == 2: ragged last group
     (601, 2560, "float16"),     # wave rows: 5 waves x 1, two rows per block, odd rows: ragged
-    (1001, 5120, "bfloat16"),   # wave rows: 5 waves x 2
-    (700, 6144, "float16"),     # wave rows: 6 waves x 2
+    (1001, 5120, "bfloat16"),   # wave rows: 10 waves x 1
+    (700, 6144, "float16"),     # wave rows: 12 waves x 1
     (513, 3584, "bfloat16"),    # wave rows: 7 waves x 1, two blocks per CU
-    (257, 7168, "float16"),     # wave rows: 7 waves x 2
+    (257, 7168, "float16"),     # wave rows: 14 waves x 1
     (300, 10240, "bfloat16"),   # wave rows: 10 waves x 2
     (300, 4608, "bfloat16"),    # wave rows: 9 waves x 1
     (200, 9216, "float16"),     # wave rows: 9 waves x 2
@@ -156,10 +156,10 @@ WAVE = [
     (1200, 1536, "bfloat16", 192, 1, 4, 1),
     (1202, 1536, "float16", 192, 1, 4, 1),
     (601, 2560, "float16", 320, 1, 2, 1),
-    (1001, 5120, "bfloat16", 320, 2, 1, 1),
-    (700, 6144, "float16", 384, 2, 1, 1),
+    (1001, 5120, "bfloat16", 640, 1, 1, 1),
+    (700, 6144, "float16", 768, 1, 1, 1),
+    (257, 7168, "float16", 896, 1, 1, 1),
     (513, 3584, "bfloat16", 448, 1, 1, 2),
-    (257, 7168, "float16", 448, 2, 1, 1),
     (300, 10240, "bfloat16", 640, 2, 1, 1),
     (300, 4608, "bfloat16", 576, 1, 1, 1),
     (200, 9216, "float16", 576, 2, 1, 1),
@@ -411,7 +411,7 @@ def test_few_rows_one_block_every_form(R, rows, D, dtype):
 
 def test_few_rows_rule_stops_where_rows_do_not_fit_one_block(R):
     bf = torch.bfloat16
-    assert R.query_config(2, 3, 7168, bf)["vecs_per_lane"] == 2       # 42 KiB per tensor (448 x 2)
+    assert R.query_config(2, 5, 3840, bf)["vecs_per_lane"] == 2       # 38 KiB (256 x 2, duplicate slots)
     assert R.query_config(2, 6, 3072, bf)["vecs_per_lane"] == 2       # 36 KiB (192 x 2)
     assert R.query_config(2, 129, 128, bf)["vecs_per_lane"] == 2      # 33 KiB
     assert R.query_config(2, 1, 4096, torch.float32)["vecs_per_lane"] == 2   # fp32 rows of 1024 vectors
